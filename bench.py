@@ -1,0 +1,241 @@
+"""Benchmark: achieved HBM bandwidth of gelu_and_mul_sparse, T=2048, d=16384, bf16.
+
+One step is one gelu_and_mul_sparse call over the whole [2048, 32768] bf16
+input (gate N(0,2) | up N(0,1), seed 2048016, z = Phi^-1(0.95)), inputs
+already resident in HBM.  Algorithmic bytes per call: read 2d + write d
+elements per row = 2048 * 3 * 16384 * 2 B = 201,326,592 B.  Input/output sets
+rotate so the working set (>= 1 GiB) is several times the 256 MB Infinity
+Cache; timing uses HIP events on the stream the kernels are launched on.
+
+Also measured in the same run: a streaming kernel with the same access
+pattern (the ceiling), silu_and_mul_bounded on the MoE decode buffer
+(M = 16384, d = 768, live 16384 and 2048), and the fp64 CPU oracle on a
+bounded sample of the same workload (the CPU baseline).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+Prints one JSON line.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s and % of peak, gelu_and_mul_sparse T=2048 d=16384 bf16"
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, AMD published peak
+T, D = 2048, 16384
+Z = 1.6448536
+ROTATE_BYTES = 1 << 30
+SILU_M, SILU_D = 16384, 768
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gelu_and_mul_sparse_T2048_d16384_bf16.traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "gated_activation_amd", "csrc", f)
+                  for f in ("gelu_sparse.hip", "ga_device.h")]
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=2000)
+    p.add_argument("--warmup", type=int, default=100)
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="approximate CPU time spent on the oracle baseline (0 = skip)")
+    p.add_argument("--no-side", action="store_true", help="skip the ceiling and silu measurements")
+    return p.parse_args()
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    for ln in open(TRAFFIC_FILE):
+        if "=" in ln and not ln.lstrip().startswith("#"):
+            k, v = ln.split("=", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    try:
+        return int(float(fields["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def time_calls(fn, n_sets, steps, warmup, stream):
+    import torch
+    for i in range(warmup):
+        fn(i % n_sets)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        fn(i % n_sets)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps      # ms per call
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the kernels are per-row and need no "
+              "cross-GPU exchange; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import gated_activation_amd as ga
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    props = torch.cuda.get_device_properties(dev)
+
+    # ---- inputs: one seeded set, replicated on the device past 1 GiB ----
+    seed = synth.large_row_seed(T, D)
+    xb = synth.gelu_large(T, D)
+    bytes_call = T * 3 * D * 2
+    n_sets = max(2, math.ceil(ROTATE_BYTES / bytes_call))
+    x0 = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
+    xs = [x0] + [x0.clone() for _ in range(n_sets - 1)]
+    outs = [torch.empty(T, D, dtype=torch.bfloat16, device=dev) for _ in range(n_sets)]
+    plan = ga.plan_gelu_and_mul_sparse(T, D, ga.GA_BF16, True, props.multi_processor_count)
+
+    def gelu(i):
+        ga.gelu_and_mul_sparse(xs[i], Z, out=outs[i])
+
+    ms = time_calls(gelu, n_sets, args.steps, args.warmup, stream)
+    gbps = bytes_call / (ms * 1e-3) / 1e9
+    gelu_out = outs[0].clone()      # kept for the parity check of the CPU leg
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "gelu_and_mul_sparse T=2048 d=16384 bf16 in/out, gate N(0,2) up N(0,1), "
+                        "z=1.6448536 (95% sparsity)",
+            "T": T, "d": D, "io_dtype": "bf16", "seed": seed, "z": Z,
+            "bytes_per_call": bytes_call, "rotation_sets": n_sets,
+            "plan": plan.as_dict(),
+            "device": f"{props.name} ({getattr(props, 'gcnArchName', '?')}, {props.multi_processor_count} CUs)",
+        },
+        "us_per_call": round(ms * 1e3, 3),
+        "pct_of_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbps, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(gbps / PEAK_HBM_GBPS, 4),
+            "traffic": recorded_traffic(),
+            "kernel": "gelu_sparse_vec_kernel<bf16, %d, %d>" % (plan.waves_per_row, plan.per_lane),
+        },
+    }
+
+    if not args.no_side:
+        # ---- streaming ceiling: same access pattern, no arithmetic ----
+        def xor(i):
+            ga.stream_xor_rows(xs[i], out=outs[i])
+        ms_c = time_calls(xor, n_sets, args.steps, args.warmup, stream)
+        ceil_gbps = bytes_call / (ms_c * 1e-3) / 1e9
+        result["copy_ceiling"] = {"GBps": round(ceil_gbps, 1), "us_per_call": round(ms_c * 1e3, 3),
+                                  "pct_of_peak": round(100 * ceil_gbps / PEAK_HBM_GBPS, 2)}
+        result["pct_of_copy_ceiling"] = round(100.0 * gbps / ceil_gbps, 2)
+
+        # ---- silu_and_mul_bounded on the MoE decode buffer ----
+        sb = synth.moe_buffer(SILU_M, SILU_D)
+        sx0 = torch.from_numpy(sb.view(np.int16)).to(dev).view(torch.bfloat16)
+        s_sets = max(2, math.ceil(ROTATE_BYTES / (SILU_M * 3 * SILU_D * 2)))
+        sxs = [sx0] + [sx0.clone() for _ in range(s_sets - 1)]
+        souts = [torch.empty(SILU_M, SILU_D, dtype=torch.bfloat16, device=dev) for _ in range(s_sets)]
+        live = torch.zeros(1, dtype=torch.int32, device=dev)
+        silu_res = {"M": SILU_M, "d": SILU_D, "io_dtype": "bf16",
+                    "plan": ga.plan_silu_and_mul_bounded(SILU_M, SILU_D, ga.GA_BF16, True,
+                                                         props.multi_processor_count).as_dict()}
+        for n_live in (SILU_M, 2048):
+            live.fill_(n_live)
+
+            def silu(i):
+                ga.silu_and_mul_bounded(sxs[i], live, out=souts[i])
+            ms_s = time_calls(silu, s_sets, args.steps, args.warmup, stream)
+            b = n_live * 3 * SILU_D * 2 + 4
+            silu_res[f"live{n_live}"] = {"us_per_call": round(ms_s * 1e3, 3),
+                                         "GBps": round(b / (ms_s * 1e-3) / 1e9, 1),
+                                         "pct_of_peak": round(100 * b / (ms_s * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+                                         "bytes": b}
+        result["silu_and_mul_bounded"] = silu_res
+
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"], result["parity_sample"] = cpu_baseline(xb, gelu_out, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(xb, gpu_out, seconds):
+    """The fp64 oracle, as it stands (one thread), on a bounded sample of the
+    same workload: blocks of 64 rows in order until about `seconds` have
+    passed.  Its first block is also compared with the GPU's output rows."""
+    import numpy as np
+    import torch
+    import oracle
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from parity import BF16, bits_of, compare, decode
+
+    o = oracle.get()
+    rows_done, t0 = 0, time.perf_counter()
+    parity = None
+    block = 64
+    while True:
+        r0 = rows_done % T
+        rows = xb[r0:r0 + block]
+        ref, st = o.gelu_and_mul_sparse(rows, oracle.BF16, Z, want_stats=True)
+        if parity is None:
+            got = bits_of(gpu_out[r0:r0 + block], BF16)
+            torch.cuda.synchronize()
+            t_pause = time.perf_counter()
+            parity = compare(got, ref, BF16, gate=decode(rows[:, :D], BF16), stats=st,
+                             label="bench sample")
+            parity["rows"] = f"{r0}..{r0 + block - 1}"
+            t0 += time.perf_counter() - t_pause
+        rows_done += block
+        if time.perf_counter() - t0 >= seconds:
+            break
+    elapsed = time.perf_counter() - t0
+    gbps = rows_done * 3 * D * 2 / elapsed / 1e9
+    del np
+    return ({"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+             "sample": f"{rows_done} rows of the T=2048 d=16384 bf16 workload (64-row blocks, "
+                       f"{elapsed:.1f} s, one thread, fp64)",
+             "us_per_call_equiv": round(elapsed / rows_done * T * 1e6, 1)},
+            parity)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,155 @@
+"""ctypes binding of libga.so.  Argument marshalling only."""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(HERE, "libga.so")
+
+GA_F32, GA_F16, GA_BF16 = 0, 1, 2
+GA_OK, GA_EINVAL, GA_EUNSUPPORTED, GA_EHIP = 0, 1, 2, 3
+GA_MAX_D = 65536
+# Phi^-1(0.95): the cutoff multiplier for a target sparsity of 95%.
+Z_SPARSITY_095 = 1.6448536
+
+_TORCH_DTYPE = {torch.float32: GA_F32, torch.float16: GA_F16, torch.bfloat16: GA_BF16}
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("waves_per_row", ctypes.c_int32),
+                ("per_lane", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("grid", ctypes.c_int64)]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+class GaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{status}: {message}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(library_path):
+        raise ImportError(
+            f"{library_path} is not built; run `python -m gated_activation_amd.build` "
+            "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(library_path)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    pplan = ctypes.POINTER(Plan)
+    sigs = {
+        "ga_gelu_and_mul_sparse": [vp, vp, i64, i64, i32, ctypes.c_float, vp, vp],
+        "ga_silu_and_mul_bounded": [vp, vp, i64, i64, i32, vp, vp],
+        "ga_gelu_and_mul_sparse_with_plan": [vp, vp, i64, i64, i32, ctypes.c_float, vp, pplan, vp],
+        "ga_silu_and_mul_bounded_with_plan": [vp, vp, i64, i64, i32, vp, pplan, vp],
+        "ga_plan_gelu_and_mul_sparse": [i64, i64, i32, i32, i32, pplan],
+        "ga_plan_silu_and_mul_bounded": [i64, i64, i32, i32, i32, pplan],
+        "ga_stream_xor_rows": [vp, vp, i64, i64, vp],
+    }
+    for name, args in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.ga_status_str.argtypes = [i32]
+    lib.ga_status_str.restype = ctypes.c_char_p
+    lib.ga_last_error.argtypes = []
+    lib.ga_last_error.restype = ctypes.c_char_p
+    lib.ga_version.argtypes = []
+    lib.ga_version.restype = i32
+    return lib
+
+
+lib = _load()
+
+
+def _check(status):
+    if status != GA_OK:
+        raise GaError(lib.ga_status_str(status).decode(), lib.ga_last_error().decode())
+
+
+def _stream_of(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _prep(x, out, name):
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise ValueError(f"{name}: x must be a CUDA (HIP) tensor")
+    if x.dim() != 2 or x.shape[1] % 2 != 0 or x.shape[1] == 0:
+        raise ValueError(f"{name}: x must be [rows, 2d] with d >= 1, got {tuple(x.shape)}")
+    if not x.is_contiguous():
+        raise ValueError(f"{name}: x must be contiguous")
+    if x.dtype not in _TORCH_DTYPE:
+        raise ValueError(f"{name}: unsupported dtype {x.dtype}")
+    rows, d = x.shape[0], x.shape[1] // 2
+    if out is None:
+        out = torch.empty((rows, d), dtype=x.dtype, device=x.device)
+    elif (out.shape != (rows, d) or out.dtype != x.dtype or out.device != x.device
+          or not out.is_contiguous()):
+        raise ValueError(f"{name}: out must be a contiguous [{rows}, {d}] {x.dtype} tensor on {x.device}")
+    return rows, d, out
+
+
+def _live_ptr(live_rows, x, name):
+    if live_rows is None:
+        return None
+    if (not isinstance(live_rows, torch.Tensor) or live_rows.dtype != torch.int32
+            or live_rows.device != x.device or live_rows.numel() < 1):
+        raise ValueError(f"{name}: live_rows must be an int32 tensor on {x.device}")
+    return ctypes.c_void_p(live_rows.data_ptr())
+
+
+def gelu_and_mul_sparse(x, z=Z_SPARSITY_095, out=None, live_rows=None, plan=None):
+    """Sparse GELU-and-multiply of x = [gate | up] ([T, 2d]) -> [T, d].
+    z = Phi^-1(target sparsity); live_rows (optional int32 device tensor)
+    limits the rows written; plan (optional Plan) forces a launch geometry."""
+    T, d, out = _prep(x, out, "gelu_and_mul_sparse")
+    live = _live_ptr(live_rows, x, "gelu_and_mul_sparse")
+    with torch.cuda.device(x.device):
+        args = (ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(out.data_ptr()), T, d,
+                _TORCH_DTYPE[x.dtype], ctypes.c_float(z), live)
+        if plan is None:
+            _check(lib.ga_gelu_and_mul_sparse(*args, _stream_of(x)))
+        else:
+            _check(lib.ga_gelu_and_mul_sparse_with_plan(*args, ctypes.byref(plan), _stream_of(x)))
+    return out
+
+
+def silu_and_mul_bounded(x, live_rows, out=None, plan=None):
+    """silu(gate) * up on rows [0, clamp(live_rows[0], 0, M)) of x = [gate | up]
+    ([M, 2d]); other rows of `out` are left as they are."""
+    M, d, out = _prep(x, out, "silu_and_mul_bounded")
+    live = _live_ptr(live_rows, x, "silu_and_mul_bounded")
+    if live is None:
+        raise ValueError("silu_and_mul_bounded: live_rows is required")
+    with torch.cuda.device(x.device):
+        args = (ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(out.data_ptr()), M, d,
+                _TORCH_DTYPE[x.dtype], live)
+        if plan is None:
+            _check(lib.ga_silu_and_mul_bounded(*args, _stream_of(x)))
+        else:
+            _check(lib.ga_silu_and_mul_bounded_with_plan(*args, ctypes.byref(plan), _stream_of(x)))
+    return out
+
+
+def stream_xor_rows(x, out=None):
+    """Measurement aid: out = first half XOR second half of each row of x,
+    16 bytes at a time (the streaming ceiling of this access pattern)."""
+    rows, d, out = _prep(x, out, "stream_xor_rows")
+    with torch.cuda.device(x.device):
+        _check(lib.ga_stream_xor_rows(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                      rows, d * x.element_size(), _stream_of(x)))
+    return out
+
+
+def plan_gelu_and_mul_sparse(T, d, dtype=GA_BF16, aligned=True, num_cus=256):
+    p = Plan()
+    _check(lib.ga_plan_gelu_and_mul_sparse(T, d, dtype, int(aligned), num_cus, ctypes.byref(p)))
+    return p
+
+
+def plan_silu_and_mul_bounded(M, d, dtype=GA_BF16, aligned=True, num_cus=256):
+    p = Plan()
+    _check(lib.ga_plan_silu_and_mul_bounded(M, d, dtype, int(aligned), num_cus, ctypes.byref(p)))
+    return p

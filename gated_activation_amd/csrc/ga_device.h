@@ -1,0 +1,172 @@
+// Device-side building blocks shared by the gated-activation kernels (gfx950,
+// wave64): element-type traits for 16-byte vectors, the wavefront and
+// workgroup sum, and the fp32 activation functions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ga {
+
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// Element traits.  A 16-byte vector holds PER16 elements; unpack widens them
+// to fp32, pack rounds fp32 to the element type (ties to even; gfx950 has a
+// two-lane convert for both 16-bit types).
+// ---------------------------------------------------------------------------
+template <int DT> struct Elem;
+
+template <> struct Elem<DT_F32> {
+    using storage = uint32_t;
+    static constexpr int PER16 = 4;
+    static __device__ __forceinline__ void unpack(const uint4 &v, float (&f)[4]) {
+        f[0] = __builtin_bit_cast(float, v.x);
+        f[1] = __builtin_bit_cast(float, v.y);
+        f[2] = __builtin_bit_cast(float, v.z);
+        f[3] = __builtin_bit_cast(float, v.w);
+    }
+    static __device__ __forceinline__ uint4 pack(const float (&f)[4]) {
+        return uint4{__builtin_bit_cast(uint32_t, f[0]), __builtin_bit_cast(uint32_t, f[1]),
+                     __builtin_bit_cast(uint32_t, f[2]), __builtin_bit_cast(uint32_t, f[3])};
+    }
+    static __device__ __forceinline__ float to_f32(storage s) { return __builtin_bit_cast(float, s); }
+    static __device__ __forceinline__ storage from_f32(float f) { return __builtin_bit_cast(uint32_t, f); }
+};
+
+template <> struct Elem<DT_BF16> {
+    using storage = uint16_t;
+    static constexpr int PER16 = 8;
+    // bf16 is the top half of an fp32: widening is a shift / mask.
+    static __device__ __forceinline__ void unpack2(uint32_t w, float &lo, float &hi) {
+        lo = __builtin_bit_cast(float, w << 16);
+        hi = __builtin_bit_cast(float, w & 0xFFFF0000u);
+    }
+    static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+    }
+    static __device__ __forceinline__ void unpack(const uint4 &v, float (&f)[8]) {
+        unpack2(v.x, f[0], f[1]);
+        unpack2(v.y, f[2], f[3]);
+        unpack2(v.z, f[4], f[5]);
+        unpack2(v.w, f[6], f[7]);
+    }
+    static __device__ __forceinline__ uint4 pack(const float (&f)[8]) {
+        return uint4{pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
+    }
+    static __device__ __forceinline__ float to_f32(storage s) {
+        return __builtin_bit_cast(float, (uint32_t)s << 16);
+    }
+    static __device__ __forceinline__ storage from_f32(float f) {
+        return (storage)(pack2(f, 0.0f) & 0xFFFFu);
+    }
+};
+
+template <> struct Elem<DT_F16> {
+    using storage = uint16_t;
+    static constexpr int PER16 = 8;
+    static __device__ __forceinline__ void unpack2(uint32_t w, float &lo, float &hi) {
+        const f16x2 h = __builtin_bit_cast(f16x2, w);
+        lo = (float)h.x;
+        hi = (float)h.y;
+    }
+    static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
+    }
+    static __device__ __forceinline__ void unpack(const uint4 &v, float (&f)[8]) {
+        unpack2(v.x, f[0], f[1]);
+        unpack2(v.y, f[2], f[3]);
+        unpack2(v.z, f[4], f[5]);
+        unpack2(v.w, f[6], f[7]);
+    }
+    static __device__ __forceinline__ uint4 pack(const float (&f)[8]) {
+        return uint4{pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
+    }
+    static __device__ __forceinline__ float to_f32(storage s) {
+        return (float)__builtin_bit_cast(_Float16, s);
+    }
+    static __device__ __forceinline__ storage from_f32(float f) {
+        return (storage)(pack2(f, 0.0f) & 0xFFFFu);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Reductions.  The wavefront sum pairs lanes symmetrically (xor 1, xor 2,
+// half-row mirror, row mirror: all DPP, fused into the adds), so every lane of
+// a 16-lane row holds the same row sum; the four row sums are then read into
+// scalar registers and added in a fixed order.  The result is bit-identical on
+// every lane and does not depend on scheduling.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp_move<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_move<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_move<0x141>(v);  // row_half_mirror
+    v += dpp_move<0x140>(v);  // row_mirror
+    const int b = __builtin_bit_cast(int, v);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+// Sum over a workgroup of WAVES wavefronts.  `slots` is LDS of WAVES floats
+// that no other thread reads or writes for the rest of this workgroup's
+// lifetime (each call site passes its own); wave partials are combined in
+// wave order, so the result is identical on every thread.
+template <int WAVES>
+__device__ __forceinline__ float block_sum(float v, float *slots) {
+    v = wave_sum(v);
+    if constexpr (WAVES == 1) {
+        return v;
+    } else {
+        if ((threadIdx.x & 63) == 0) slots[threadIdx.x >> 6] = v;
+        __syncthreads();
+        float t = slots[0];
+#pragma unroll
+        for (int i = 1; i < WAVES; ++i) t += slots[i];
+        return t;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Activations in fp32.
+//
+// tanh GELU for s >= 0: 0.5 s (1 + tanh w) = s / (1 + e^(-2w)) with
+// w = sqrt(2/pi) (s + 0.044715 s^3).  In base 2, e^(-2w) = 2^(-s (A + B s^2)),
+// A = 2 sqrt(2/pi) / ln 2, B = 0.044715 A.  For s >= 0 the exponent is <= 0,
+// so nothing overflows; at s = 0 the result is exactly 0.
+// ---------------------------------------------------------------------------
+constexpr float GELU_A = 2.302208198144325f;
+constexpr float GELU_B = 0.1029432395800235f;
+constexpr float LOG2_E = 1.4426950408889634f;
+
+__device__ __forceinline__ float gelu_tanh_nonneg(float s) {
+    const float t = s * __builtin_fmaf(GELU_B, s * s, GELU_A);
+    const float e = __builtin_amdgcn_exp2f(-t);
+    return s * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// silu(x) = x / (1 + e^-x); for x << 0 the power overflows to +inf and the
+// result is -0, for x >> 0 it underflows to 0 and the result is x.
+__device__ __forceinline__ float silu(float x) {
+    const float e = __builtin_amdgcn_exp2f(-x * LOG2_E);
+    return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+__device__ __forceinline__ int32_t clamp_live(const int32_t *live, int32_t rows) {
+    const int32_t n = *live;
+    return n < 0 ? 0 : (n > rows ? rows : n);
+}
+
+}  // namespace ga

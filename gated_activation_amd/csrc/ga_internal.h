@@ -1,0 +1,36 @@
+// Host-side interface between the C-ABI (api.hip) and the kernel translation
+// units.  Each launcher enqueues one kernel on `stream` and returns the HIP
+// status of the launch, or hipErrorInvalidValue when no kernel is
+// instantiated for the requested geometry.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ga {
+
+// Geometries with a compiled kernel.
+bool gelu_vec_available(int dtype, int waves, int vec_per_lane);
+bool gelu_elem_available(int dtype, int waves, int elem_per_lane);
+bool silu_available(int path, int dtype, int per_lane);
+
+constexpr int SILU_BLOCK = 256;
+
+hipError_t launch_gelu_vec(int dtype, int waves, int vec_per_lane, int64_t grid,
+                           const void *in, void *out, int32_t T, int32_t d, int32_t nvec,
+                           float z, const int32_t *live, hipStream_t stream);
+
+hipError_t launch_gelu_elem(int dtype, int waves, int elem_per_lane, int64_t grid,
+                            const void *in, void *out, int32_t T, int32_t d,
+                            float z, const int32_t *live, hipStream_t stream);
+
+// path 0: 16-byte items (nitems_row = d / elements per 16 bytes),
+// path 1: single elements (nitems_row = d).
+hipError_t launch_silu(int path, int dtype, int per_lane, int64_t grid,
+                       const void *in, void *out, int32_t M, uint32_t nitems_row,
+                       const int32_t *live, hipStream_t stream);
+
+hipError_t launch_xor_rows(int64_t grid, const void *in, void *out, int32_t rows,
+                           uint32_t nvec_row, hipStream_t stream);
+
+}  // namespace ga

@@ -1,0 +1,160 @@
+/*
+ * ga.h -- fused row-wise gated activations on AMD Instinct MI355X (gfx950).
+ *
+ * Two operations of a transformer FFN / MoE layer, on rows of an input laid
+ * out as [rows, 2d] with the gate in columns [0, d) and up in [d, 2d):
+ *
+ *   ga_gelu_and_mul_sparse   Gemma3n-style sparse GELU-and-multiply (vLLM PR
+ *       48498, "[Performance] Add Triton kernel for Gemma3n sparse GELU",
+ *       section Purpose): per row, mean and population std of the gate,
+ *       cutoff = mean + z * std, out = gelu_tanh(max(gate - cutoff, 0)) * up,
+ *       where gelu_tanh(s) = 0.5 s (1 + tanh(sqrt(2/pi) (s + 0.044715 s^3)))
+ *       and z = Phi^-1(target sparsity) (1.6448536 for 95%).
+ *   ga_silu_and_mul_bounded  silu(gate) * up over only the live rows of a
+ *       capture-sized MoE buffer (Megatron-LM PR 6328, "Size MoE activation
+ *       kernel grid to the row count", section What changed and why): the
+ *       launch shape depends on the buffer capacity only, and the live count
+ *       is read on the device, so one launch can be replayed from a graph
+ *       while the count changes.
+ *
+ * Arithmetic is fp32 inside the kernels; the result is rounded once, to
+ * nearest even, to the element type.  Input and output share one element
+ * type: fp32, fp16 or bf16.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named in/out/live_rows are DEVICE pointers on the current HIP
+ *     device; the caller owns all memory.  Tensors are dense and row-major
+ *     (row stride 2d elements for in, d for out).  The library allocates
+ *     nothing on the device and keeps no state apart from a per-device cache
+ *     of the compute-unit count.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Launches are
+ *     asynchronous on that stream and never synchronise, so they may be
+ *     recorded into a HIP graph by stream capture.
+ *   - All argument checks happen on the host before any HIP call; a rejected
+ *     call touches no memory.  ga_last_error() then returns a message.
+ *   - Out-of-range device live counts are clamped to [0, rows]; they cannot
+ *     be reported (no synchronisation).
+ *   - Any alignment natural to the element type is accepted; when in and out
+ *     are 16-byte aligned and a row's bytes are a multiple of 16, 16-byte
+ *     vector loads and stores are used, else a per-element path.
+ */
+#ifndef GA_H
+#define GA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GA_F32 = 0, GA_F16 = 1, GA_BF16 = 2 } ga_dtype;
+
+typedef enum {
+    GA_OK = 0,
+    GA_EINVAL = 1,       /* malformed argument (null pointer, negative size, ...) */
+    GA_EUNSUPPORTED = 2, /* well-formed but outside what the kernels handle;
+                            callers fall back to another implementation */
+    GA_EHIP = 3          /* the HIP runtime reported an error at launch */
+} ga_status;
+
+/* A hipStream_t, passed opaquely so this header needs no HIP include. */
+typedef void *ga_stream;
+
+/* Largest d (elements per half row) the kernels take. */
+#define GA_MAX_D 65536
+
+/* Launch geometry.  Filled by the planners, or by a caller that wants a
+ * specific geometry (a tuning sweep); see ga_gelu_and_mul_sparse_with_plan. */
+typedef struct {
+    int32_t path;          /* 0: 16-byte vector path, 1: per-element path */
+    int32_t waves_per_row; /* gelu: 64-lane wavefronts sharing one row (1,2,4,8,16) */
+    int32_t per_lane;      /* gelu vector path: 16-byte gate vectors per lane (1,2,4,8);
+                              gelu element path: gate elements per lane (4,16,64);
+                              silu: 16-byte (or element) items per lane per step (1,2,4) */
+    int32_t block;         /* threads per workgroup */
+    int64_t grid;          /* workgroups launched (silu: from the capacity M only) */
+} ga_plan;
+
+/*
+ * Sparse GELU-and-multiply.
+ *   in        [T, 2d] device array of `dtype`; gate = cols [0,d), up = cols [d,2d).
+ *   out       [T, d] device array of `dtype`; must not overlap `in`.
+ *   T         rows (tokens), 0 <= T <= INT32_MAX; T == 0 launches nothing.
+ *   d         elements per half row, 1 <= d <= GA_MAX_D (larger: GA_EUNSUPPORTED).
+ *   dtype     a ga_dtype.
+ *   z         cutoff multiplier Phi^-1(target sparsity); must be finite.
+ *   live_rows NULL: all T rows.  Else a device int32; rows r with
+ *             r >= clamp(*live_rows, 0, T) are left untouched.
+ * Returns GA_OK once the launch is enqueued.
+ */
+ga_status ga_gelu_and_mul_sparse(const void *in, void *out, int64_t T, int64_t d,
+                                 int32_t dtype, float z, const int32_t *live_rows,
+                                 ga_stream stream);
+
+/*
+ * Bounded SiLU-and-multiply over the live rows of a capture-sized buffer.
+ *   in        [M, 2d] device array; gate = cols [0,d), up = cols [d,2d).
+ *   out       [M, d] device array; must not overlap `in`.
+ *   M         buffer capacity in rows, 0 <= M <= INT32_MAX.
+ *   d         1 <= d <= GA_MAX_D.
+ *   live_rows required device int32; rows [0, clamp(*live_rows, 0, M)) are
+ *             computed, every other row of `out` is left untouched.
+ * The grid depends on (M, d, dtype, alignment, device) only, never on the
+ * live count, so a captured launch stays valid when the count changes.
+ */
+ga_status ga_silu_and_mul_bounded(const void *in, void *out, int64_t M, int64_t d,
+                                  int32_t dtype, const int32_t *live_rows,
+                                  ga_stream stream);
+
+/*
+ * Host-only planners (no HIP call, usable without a GPU): the geometry the
+ * entry points above would launch for these sizes.  `aligned` says whether
+ * the 16-byte vector path applies (both base pointers 16-byte aligned and
+ * d * element size a multiple of 16); `num_cus` is the device's compute-unit
+ * count (256 on MI355X).
+ */
+ga_status ga_plan_gelu_and_mul_sparse(int64_t T, int64_t d, int32_t dtype, int32_t aligned,
+                                      int32_t num_cus, ga_plan *plan);
+ga_status ga_plan_silu_and_mul_bounded(int64_t M, int64_t d, int32_t dtype, int32_t aligned,
+                                       int32_t num_cus, ga_plan *plan);
+
+/*
+ * The same operations with an explicit geometry (for tuning sweeps and the
+ * geometry-independence tests).  The plan must name an instantiated kernel
+ * (the values listed in ga_plan) and cover the row: vector path
+ * waves_per_row * 64 * per_lane * (16 / element size) >= d, element path
+ * waves_per_row * 64 * per_lane >= d; else GA_EUNSUPPORTED.  `block` is
+ * derived (waves_per_row * 64 for gelu); silu takes its grid from the plan.
+ */
+ga_status ga_gelu_and_mul_sparse_with_plan(const void *in, void *out, int64_t T, int64_t d,
+                                           int32_t dtype, float z, const int32_t *live_rows,
+                                           const ga_plan *plan, ga_stream stream);
+ga_status ga_silu_and_mul_bounded_with_plan(const void *in, void *out, int64_t M, int64_t d,
+                                            int32_t dtype, const int32_t *live_rows,
+                                            const ga_plan *plan, ga_stream stream);
+
+/*
+ * Measurement aid, not part of the activations: a streaming kernel with the
+ * same access pattern (read the two halves of rows [0, rows) of in[rows, 2w]
+ * 16 bytes at a time, write out[rows, w] = first half XOR second half).  Its
+ * bandwidth is the ceiling a row-wise gated activation can reach on the
+ * device.  `w_bytes` (bytes per half row) must be a positive multiple of 16
+ * and both pointers 16-byte aligned.
+ */
+ga_status ga_stream_xor_rows(const void *in, void *out, int64_t rows, int64_t w_bytes,
+                             ga_stream stream);
+
+/* Static name of a status code. */
+const char *ga_status_str(int32_t status);
+
+/* Message describing the last non-OK status returned on this thread. */
+const char *ga_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int32_t ga_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GA_H */

@@ -9,23 +9,50 @@ Random numbers come from a counter-based generator: value i of a stream is
 the SplitMix64 finaliser (Steele, Lea and Flood, "Fast splittable
 pseudorandom number generators", OOPSLA 2014) applied to key + (i+1)*gamma.
 Normals use the Box-Muller cosine branch on two uniforms; Student-t(3) is
-Z / sqrt(chi2_3 / 3) with chi2_3 a sum of three squared normals.  numpy's own
-generators are not used, so the streams do not depend on a numpy version.
+Z / sqrt(chi2_3 / 3) with chi2_3 a sum of three squared normals.  The streams
+run in a small C core (synth_core.c, glibc's log/cos/sqrt), not in numpy,
+whose vectorised transcendentals can differ between host CPUs.
 
 Every array returned is raw element bits: uint16 for bf16/fp16, uint32 for
 fp32 (dtype codes 0 = fp32, 1 = fp16, 2 = bf16).
 """
+import ctypes
+import os
+
 import numpy as np
+
+from . import build as _build
 
 F32, F16, BF16 = 0, 1, 2
 DTYPE_NAMES = {"f32": F32, "f16": F16, "bf16": BF16}
 _GAMMA = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
-_CHUNK = 1 << 22
+_THREADS = max(1, min(16, os.cpu_count() or 1))
 
 # stream identifiers inside one seed
 S_GATE, S_UP, S_OFFSET, S_KIND = 1, 2, 3, 4
+
+
+def _core():
+    global _CORE
+    if _CORE is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        lib = ctypes.CDLL(_build.LIB)
+        u64, i64, vp = ctypes.c_uint64, ctypes.c_int64, ctypes.c_void_p
+        lib.synth_normal.argtypes = [u64, i64, i64, ctypes.c_double, ctypes.c_double, vp, ctypes.c_int]
+        lib.synth_raw64.argtypes = [u64, i64, i64, vp]
+        lib.synth_uniform.argtypes = [u64, i64, i64, vp]
+        lib.synth_normal_rows_bf16.argtypes = [u64, i64, i64, ctypes.c_double, ctypes.c_double,
+                                               vp, i64, ctypes.c_int]
+        for f in (lib.synth_normal, lib.synth_raw64, lib.synth_uniform, lib.synth_normal_rows_bf16):
+            f.restype = None
+        _CORE = lib
+    return _CORE
+
+
+_CORE = None
 
 
 def _mix(x):
@@ -44,24 +71,23 @@ def stream_key(seed: int, stream: int) -> np.uint64:
 
 def raw64(key, start: int, n: int) -> np.ndarray:
     """Values start .. start+n-1 of the stream with this key (uint64)."""
-    i = np.arange(start + 1, start + n + 1, dtype=np.uint64)
-    with np.errstate(over="ignore"):
-        return _mix(np.uint64(key) + i * _GAMMA)
+    out = np.empty(n, np.uint64)
+    _core().synth_raw64(int(key), start, n, out.ctypes.data)
+    return out
 
 
 def uniform(key, start: int, n: int) -> np.ndarray:
     """Uniforms in (0, 1]: the top 53 bits, plus one, times 2^-53."""
-    r = raw64(key, start, n)
-    return ((r >> np.uint64(11)).astype(np.float64) + 1.0) * (2.0 ** -53)
-
-
-def normal(key, start: int, n: int) -> np.ndarray:
-    """Standard normals; normal j uses stream values 2(start+j) and 2(start+j)+1."""
     out = np.empty(n, np.float64)
-    for c0 in range(0, n, _CHUNK):
-        m = min(_CHUNK, n - c0)
-        u = uniform(key, 2 * (start + c0), 2 * m)
-        out[c0:c0 + m] = np.sqrt(-2.0 * np.log(u[0::2])) * np.cos(2.0 * np.pi * u[1::2])
+    _core().synth_uniform(int(key), start, n, out.ctypes.data)
+    return out
+
+
+def normal(key, start: int, n: int, scale: float = 1.0, shift: float = 0.0) -> np.ndarray:
+    """shift + scale * standard normals; normal j uses stream values
+    2(start+j) and 2(start+j)+1 (Box-Muller, cosine branch)."""
+    out = np.empty(n, np.float64)
+    _core().synth_normal(int(key), start, n, float(scale), float(shift), out.ctypes.data, _THREADS)
     return out
 
 
@@ -103,21 +129,31 @@ def bits_to_float(bits: np.ndarray, dtype: int) -> np.ndarray:
 # in columns [0, d), up in [d, 2d).  "N(a, b)" means mean a, std b.
 # ---------------------------------------------------------------------------
 
-def _rows(gate: np.ndarray, up: np.ndarray, dtype: int) -> np.ndarray:
-    T, d = gate.shape
-    x = np.empty((T, 2 * d), np.uint32 if dtype == F32 else np.uint16)
-    x[:, :d] = to_bits(gate, dtype)
-    x[:, d:] = to_bits(up, dtype)
-    return x
+def normal_rows_into(out: np.ndarray, key, scale: float = 1.0, shift: float = 0.0,
+                     dtype: int = BF16) -> None:
+    """Fill the [rows, d] view `out` (row stride may exceed d) with element
+    (r, i) = to_bits(shift + scale * normal(r * d + i)).  Same bits as the
+    numpy route, done in one threaded pass for bf16."""
+    rows, d = out.shape
+    if dtype == BF16 and out.dtype == np.uint16 and out.strides[1] == 2:
+        _core().synth_normal_rows_bf16(int(key), rows, d, float(scale), float(shift),
+                                       out.ctypes.data, out.strides[0] // 2, _THREADS)
+    else:
+        out[...] = to_bits(normal(key, 0, rows * d, scale, shift).reshape(rows, d), dtype)
+
+
+def _empty_rows(T: int, d: int, dtype: int) -> np.ndarray:
+    return np.empty((T, 2 * d), np.uint32 if dtype == F32 else np.uint16)
 
 
 def gelu_iid(T: int, d: int, seed: int = 0, dtype: int = BF16,
              gate_std: float = 1.0) -> np.ndarray:
     """Gate N(0, gate_std) and up N(0, 1), i.i.d.  T=4, d=2048, seed 0 is the
     small check case; gate_std=2 with seed T*1000 + d//1024 the large-row case."""
-    g = gate_std * normal(stream_key(seed, S_GATE), 0, T * d).reshape(T, d)
-    u = normal(stream_key(seed, S_UP), 0, T * d).reshape(T, d)
-    return _rows(g, u, dtype)
+    x = _empty_rows(T, d, dtype)
+    normal_rows_into(x[:, :d], stream_key(seed, S_GATE), scale=gate_std, dtype=dtype)
+    normal_rows_into(x[:, d:], stream_key(seed, S_UP), dtype=dtype)
+    return x
 
 
 def gelu_offset_rows(T: int, d: int = 8192, seed: int = None,
@@ -127,8 +163,10 @@ def gelu_offset_rows(T: int, d: int = 8192, seed: int = None,
     seed = T if seed is None else seed
     off = 0.5 * normal(stream_key(seed, S_OFFSET), 0, T)
     g = normal(stream_key(seed, S_GATE), 0, T * d).reshape(T, d) + off[:, None]
-    u = normal(stream_key(seed, S_UP), 0, T * d).reshape(T, d)
-    return _rows(g, u, dtype)
+    x = _empty_rows(T, d, dtype)
+    x[:, :d] = to_bits(g, dtype)
+    normal_rows_into(x[:, d:], stream_key(seed, S_UP), dtype=dtype)
+    return x
 
 
 def large_row_seed(T: int, d: int) -> int:
@@ -164,8 +202,10 @@ def edge_rows(T: int, d: int, dtype: int, seed: int = None) -> np.ndarray:
             g[r] = 100.0
         else:
             g[r] = student_t3(kg, r * d, d)
-    u = normal(stream_key(seed, S_UP), 0, T * d).reshape(T, d)
-    return _rows(g, u, dtype)
+    x = _empty_rows(T, d, dtype)
+    x[:, :d] = to_bits(g, dtype)
+    normal_rows_into(x[:, d:], stream_key(seed, S_UP), dtype=dtype)
+    return x
 
 
 def moe_buffer(M: int = 16384, d: int = 768, seed: int = 7,

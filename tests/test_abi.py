@@ -1,0 +1,190 @@
+"""The C-ABI on the host: exports, argument checks and the launch planner.
+
+No kernel runs here: every call below is rejected by a host-side check, or has
+zero rows, before the library makes any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_activation_amd as ga
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ga.h")
+L = ga.lib
+BF16, F16, F32 = ga.GA_BF16, ga.GA_F16, ga.GA_F32
+OK, EINVAL, EUNSUP = ga.GA_OK, ga.GA_EINVAL, ga.GA_EUNSUPPORTED
+Z = ctypes.c_float(1.6448536)
+# Fake device addresses: never dereferenced, since every call is rejected (or
+# has no rows) before a launch.
+IN = ctypes.c_void_p(0x7F0000000000)
+OUT = ctypes.c_void_p(0x7F1000000000)
+LIVE = ctypes.c_void_p(0x7F2000000000)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ga_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert "ga_gelu_and_mul_sparse" in names and "ga_silu_and_mul_bounded" in names
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version():
+    assert L.ga_status_str(OK) == b"GA_OK"
+    assert L.ga_status_str(EINVAL) == b"GA_EINVAL"
+    assert L.ga_status_str(EUNSUP) == b"GA_EUNSUPPORTED"
+    assert L.ga_status_str(ga.GA_EHIP) == b"GA_EHIP"
+    assert L.ga_version() >= 100
+
+
+def gelu(in_=IN, out=OUT, T=4, d=2048, dt=BF16, z=Z, live=None):
+    return L.ga_gelu_and_mul_sparse(in_, out, T, d, dt, z, live, None)
+
+
+def silu(in_=IN, out=OUT, M=16, d=768, dt=BF16, live=LIVE):
+    return L.ga_silu_and_mul_bounded(in_, out, M, d, dt, live, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(in_=None), EINVAL),
+    (dict(out=None), EINVAL),
+    (dict(T=-1), EINVAL),
+    (dict(T=2 ** 31), EINVAL),
+    (dict(d=0), EINVAL),
+    (dict(d=-5), EINVAL),
+    (dict(d=65537), EUNSUP),
+    (dict(dt=3), EINVAL),
+    (dict(dt=-1), EINVAL),
+    (dict(z=ctypes.c_float(float("nan"))), EINVAL),
+    (dict(z=ctypes.c_float(float("inf"))), EINVAL),
+    (dict(out=IN), EINVAL),                                    # in place
+    (dict(out=ctypes.c_void_p(0x7F0000000000 + 4 * 4096 * 2 - 2)), EINVAL),  # partial overlap
+    (dict(in_=ctypes.c_void_p(0x7F0000000001)), EINVAL),       # not element aligned
+    (dict(T=0), OK),                                           # nothing to do, no launch
+    (dict(T=0, d=1, dt=F32), OK),
+])
+def test_gelu_argument_checks(kwargs, status):
+    assert gelu(**kwargs) == status
+    if status != OK:
+        assert len(L.ga_last_error()) > 0
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(in_=None), EINVAL),
+    (dict(live=None), EINVAL),
+    (dict(M=-1), EINVAL),
+    (dict(d=0), EINVAL),
+    (dict(dt=9), EINVAL),
+    (dict(d=65537), EUNSUP),
+    (dict(M=2 ** 21, d=1024), EUNSUP),                         # M * d >= 2^31
+    (dict(out=IN), EINVAL),
+    (dict(M=0), OK),
+])
+def test_silu_argument_checks(kwargs, status):
+    assert silu(**kwargs) == status
+
+
+def test_stream_xor_rows_checks():
+    assert L.ga_stream_xor_rows(IN, OUT, 4, 24, None) == EINVAL       # not a multiple of 16
+    assert L.ga_stream_xor_rows(None, OUT, 4, 32, None) == EINVAL
+    assert L.ga_stream_xor_rows(IN, IN, 4, 32, None) == EINVAL
+    assert L.ga_stream_xor_rows(IN, OUT, 0, 32, None) == OK
+
+
+def test_gelu_planner_known_shapes():
+    p = ga.plan_gelu_and_mul_sparse(2048, 16384, BF16)
+    assert (p.path, p.waves_per_row, p.per_lane, p.block, p.grid) == (0, 4, 8, 256, 2048)
+    p = ga.plan_gelu_and_mul_sparse(512, 8192, BF16)
+    assert (p.path, p.waves_per_row, p.per_lane) == (0, 2, 8)
+    p = ga.plan_gelu_and_mul_sparse(4, 2048, BF16)
+    assert (p.path, p.waves_per_row, p.per_lane) == (0, 1, 4)
+    p = ga.plan_gelu_and_mul_sparse(1, 32768, BF16)
+    assert (p.path, p.waves_per_row, p.per_lane) == (0, 8, 8)
+    p = ga.plan_gelu_and_mul_sparse(7, 8191, F16)            # odd d: element path
+    assert p.path == 1 and p.waves_per_row * 64 * p.per_lane >= 8191
+    p = ga.plan_gelu_and_mul_sparse(7, 8192, F16, aligned=False)
+    assert p.path == 1
+
+
+@pytest.mark.parametrize("dt", [BF16, F16, F32])
+def test_gelu_planner_covers_every_d(dt):
+    """Every d the library takes maps to an instantiated kernel covering the
+    row (checked by the library's own plan validation, with zero rows)."""
+    es = 4 if dt == F32 else 2
+    ds = sorted(set(list(range(1, 600)) + [2 ** k + o for k in range(9, 17) for o in (-9, -1, 0, 1, 8)]
+                    + [2000, 3000, 8191, 65536]))
+    for d in ds:
+        if d > 65536:
+            continue
+        for aligned in (True, False):
+            p = ga.plan_gelu_and_mul_sparse(3, d, dt, aligned=aligned)
+            assert p.block == p.waves_per_row * 64 and p.grid == 3
+            if p.path == 0:
+                assert aligned and (d * es) % 16 == 0
+            # With zero rows the entry point validates the plan and returns.
+            base_in = ctypes.c_void_p(0x7F0000000000)
+            base_out = ctypes.c_void_p(0x7F8000000000)
+            st = L.ga_gelu_and_mul_sparse_with_plan(base_in, base_out, 0, d, dt, Z, None,
+                                                    ctypes.byref(p), None)
+            assert st == OK, (d, dt, aligned, p.as_dict(), L.ga_last_error())
+
+
+def test_gelu_with_plan_rejects_bad_geometry():
+    p = ga.Plan(path=0, waves_per_row=1, per_lane=1, block=64, grid=1)
+    st = L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 2048, BF16, Z, None, ctypes.byref(p), None)
+    assert st == EUNSUP                                           # covers 512 < 2048
+    p = ga.Plan(path=0, waves_per_row=3, per_lane=8, block=192, grid=1)
+    assert L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 64, BF16, Z, None, ctypes.byref(p), None) == EUNSUP
+    p = ga.Plan(path=1, waves_per_row=16, per_lane=2, block=1024, grid=1)
+    assert L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 64, BF16, Z, None, ctypes.byref(p), None) == EUNSUP
+    p = ga.Plan(path=2, waves_per_row=1, per_lane=4, block=64, grid=1)
+    assert L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 64, BF16, Z, None, ctypes.byref(p), None) == EINVAL
+    # vector path on a base that is not 16-byte aligned
+    p = ga.plan_gelu_and_mul_sparse(1, 64, BF16)
+    st = L.ga_gelu_and_mul_sparse_with_plan(ctypes.c_void_p(0x7F0000000002), OUT, 0, 64, BF16, Z, None,
+                                            ctypes.byref(p), None)
+    assert st == EUNSUP
+
+
+def test_silu_planner_depends_on_capacity_only():
+    p = ga.plan_silu_and_mul_bounded(16384, 768, BF16, num_cus=256)
+    assert p.path == 0 and p.block == 256 and 1 <= p.grid <= 256 * 8
+    # The planner has no live-count input at all; the grid grows with M up to
+    # eight workgroups per compute unit, then the kernel strides.
+    small = ga.plan_silu_and_mul_bounded(4, 768, BF16, num_cus=256)
+    assert small.grid == 1
+    big = ga.plan_silu_and_mul_bounded(1 << 20, 768, BF16, num_cus=256)
+    assert big.grid == 256 * 8
+    assert ga.plan_silu_and_mul_bounded(100, 777, BF16).path == 1
+    for M in (1, 7, 64, 1000, 16384):
+        for d in (1, 8, 768, 777, 4096):
+            p = ga.plan_silu_and_mul_bounded(M, d, BF16)
+            st = L.ga_silu_and_mul_bounded_with_plan(IN, OUT, 0, d, BF16, LIVE, ctypes.byref(p), None)
+            assert st == OK
+
+
+def test_silu_with_plan_rejects_bad_geometry():
+    p = ga.Plan(path=0, waves_per_row=0, per_lane=3, block=256, grid=4)
+    assert L.ga_silu_and_mul_bounded_with_plan(IN, OUT, 0, 768, BF16, LIVE, ctypes.byref(p), None) == EUNSUP
+    p = ga.Plan(path=0, waves_per_row=0, per_lane=2, block=256, grid=0)
+    assert L.ga_silu_and_mul_bounded_with_plan(IN, OUT, 0, 768, BF16, LIVE, ctypes.byref(p), None) == EINVAL
+    p = ga.Plan(path=0, waves_per_row=0, per_lane=4, block=256, grid=2 ** 22)
+    assert L.ga_silu_and_mul_bounded_with_plan(IN, OUT, 0, 768, BF16, LIVE, ctypes.byref(p), None) == EUNSUP
+
+
+def test_python_wrapper_rejects_host_tensors():
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ga.gelu_and_mul_sparse(x)
+    with pytest.raises(ValueError):
+        ga.silu_and_mul_bounded(x, None)

@@ -1,0 +1,165 @@
+"""gelu_and_mul_sparse on the GPU against the fp64 oracle (needs an MI355X).
+
+Cases follow the workloads on the pages (vLLM PR 48498: token counts 1-2048,
+intermediate sizes 2048-32768, small d = 1, 31, 128 over fp16/bf16/fp32),
+with seeded synthetic rows (synth/): the small check case, the d = 8192 token
+sweep with per-row offsets, large rows up to d = 32768, and the edge mix
+(variance cancellation, constant rows, Student-t(3) tails, odd d, three z).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_activation_amd as ga
+import oracle
+import synth
+from parity import (BF16, F16, F32, Z95, Z99, bits_of, check_canary, compare,
+                    decode, sentinel_buffer, to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "these tests need a GPU"
+    props = torch.cuda.get_device_properties(0)
+    print(f"device: {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}",
+          flush=True)
+
+
+def run_and_check(x_bits, dtype, z, rows_sample=None, plan=None, live=None, label=""):
+    """GPU call on the whole input; oracle on all rows (or the sampled ones)."""
+    o = oracle.get()
+    T, two_d = x_bits.shape
+    d = two_d // 2
+    x = to_device(x_bits, dtype)
+    buf, out = sentinel_buffer(T, d, dtype)
+    live_t = None if live is None else torch.tensor([live], dtype=torch.int32, device="cuda")
+    ga.gelu_and_mul_sparse(x, z, out=out, live_rows=live_t, plan=plan)
+    torch.cuda.synchronize()
+    got = bits_of(out, dtype)
+    check_canary(buf, T, d, dtype)
+    n = T if live is None else max(0, min(live, T))
+    rows = np.arange(n) if rows_sample is None else np.array(sorted(set(rows_sample)) if n else [], int)
+    rows = rows[rows < n]
+    if rows.size:
+        ref, st = o.gelu_and_mul_sparse(x_bits[rows], dtype, z, want_stats=True)
+        gate = decode(x_bits[rows, :d], dtype)
+        res = compare(got[rows], ref, dtype, gate=gate, stats=st, label=label)
+    else:
+        res = {}
+    assert np.all(got[n:] == synth.SENTINEL[dtype]), f"{label}: rows beyond the live count were written"
+    return res
+
+
+def test_small_check_case():
+    """T=4, d=2048, bf16, gate/up N(0,1), seed 0, z = Phi^-1(0.95)."""
+    x = synth.gelu_iid(4, 2048, seed=0)
+    res = run_and_check(x, BF16, Z95, label="T4 d2048")
+    assert res["bitexact_frac"] > 0.99
+
+
+@pytest.mark.parametrize("T", [1, 2, 8, 32, 128, 512, 2048])
+def test_token_sweep_d8192(T):
+    """Gate N(0,1) + per-row offset N(0,0.5), up N(0,1), seed = T."""
+    x = synth.gelu_offset_rows(T, 8192)
+    run_and_check(x, BF16, Z95, label=f"sweep T{T}")
+
+
+@pytest.mark.parametrize("d", [16384, 32768])
+@pytest.mark.parametrize("T", [1, 64, 2048])
+def test_large_rows(T, d):
+    """Gate N(0,2), up N(0,1): 32 KB and 64 KB gate rows.  At T = 2048 the
+    oracle checks 64 sampled rows (first, last, spread between)."""
+    x = synth.gelu_large(T, d)
+    sample = None if T <= 64 else list(np.linspace(0, T - 1, 64).astype(int))
+    run_and_check(x, BF16, Z95, rows_sample=sample, label=f"large T{T} d{d}")
+
+
+@pytest.mark.parametrize("z", [0.0, Z95, Z99], ids=["z0", "z95", "z99"])
+@pytest.mark.parametrize("T", [1, 7, 333])
+@pytest.mark.parametrize("d", [2000, 3000, 8191])
+@pytest.mark.parametrize("dt", [F16, BF16], ids=["f16", "bf16"])
+def test_edge_mix(dt, d, T, z):
+    x = synth.edge_rows(T, d, dt)
+    run_and_check(x, dt, z, label=f"edge dt{dt} d{d} T{T} z{z}")
+
+
+@pytest.mark.parametrize("z", [0.0, Z95])
+@pytest.mark.parametrize("d", [1, 31, 128])
+@pytest.mark.parametrize("dt", [F32, F16, BF16], ids=["f32", "f16", "bf16"])
+def test_small_d_all_dtypes(dt, d, z):
+    x = synth.gelu_iid(5, d, seed=100 + d, dtype=dt, gate_std=1.5)
+    run_and_check(x, dt, z, label=f"small dt{dt} d{d}")
+
+
+@pytest.mark.parametrize("dt", [F32, F16])
+def test_other_dtypes_large(dt):
+    x = synth.gelu_iid(96, 8192, seed=55, dtype=dt, gate_std=2.0)
+    run_and_check(x, dt, Z95, label=f"dt{dt} T96 d8192")
+
+
+@pytest.mark.parametrize("live", [0, 1, 37, 64, 100, -3])
+def test_live_rows_bound(live):
+    x = synth.gelu_iid(64, 2048, seed=7)
+    run_and_check(x, BF16, Z95, live=live, label=f"live {live}")
+
+
+def _all_vector_plans(d, dtype):
+    per16 = 4 if dtype == F32 else 8
+    for w in (1, 2, 4, 8, 16):
+        for v in (1, 2, 4, 8):
+            if w * 64 * v * per16 >= d:
+                yield ga.Plan(path=0, waves_per_row=w, per_lane=v, block=64 * w, grid=0)
+
+
+def test_every_vector_geometry_matches_oracle():
+    """Every compiled vector geometry that covers the row gives an
+    oracle-matching result (reduction order differs between them)."""
+    x = synth.gelu_offset_rows(24, 8192, seed=77)
+    for p in _all_vector_plans(8192, BF16):
+        run_and_check(x, BF16, Z95, plan=p, label=f"plan w{p.waves_per_row} v{p.per_lane}")
+
+
+def test_element_path_on_aligned_rows():
+    x = synth.gelu_offset_rows(24, 4096, seed=78)
+    for w, e in ((1, 64), (4, 16), (16, 4), (4, 64), (16, 16)):
+        p = ga.Plan(path=1, waves_per_row=w, per_lane=e, block=64 * w, grid=0)
+        run_and_check(x, BF16, Z95, plan=p, label=f"elem w{w} e{e}")
+
+
+@pytest.mark.parametrize("shift", [1, 3, 7])
+def test_misaligned_base_pointers(shift):
+    """Bases off 16-byte alignment by `shift` elements take the element path."""
+    T, d = 9, 2048
+    xb = synth.gelu_iid(T, d, seed=shift)
+    flat = torch.zeros(T * 2 * d + 16, dtype=torch.bfloat16, device="cuda")
+    x = flat[shift: shift + T * 2 * d].view(T, 2 * d)
+    x.copy_(to_device(xb, BF16))
+    buf = torch.zeros(T * d + 16, dtype=torch.bfloat16, device="cuda")
+    out = buf[shift: shift + T * d].view(T, d)
+    ga.gelu_and_mul_sparse(x, Z95, out=out)
+    torch.cuda.synchronize()
+    o = oracle.get()
+    ref, st = o.gelu_and_mul_sparse(xb, BF16, Z95, want_stats=True)
+    compare(bits_of(out, BF16), ref, BF16, gate=decode(xb[:, :d], BF16), stats=st, label="misaligned")
+    assert not bits_of(buf[:shift], BF16).any() and not bits_of(buf[shift + T * d:], BF16).any()
+
+
+def test_repeat_runs_are_bit_identical():
+    x = to_device(synth.gelu_large(64, 16384), BF16)
+    a = ga.gelu_and_mul_sparse(x, Z95)
+    b = ga.gelu_and_mul_sparse(x, Z95)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_constant_rows_give_exact_zeros():
+    T, d = 6, 16384
+    vals = np.array([0.0, 100.0, -3.5, 1e-3, 7.25, -250.0])
+    xb = np.concatenate([synth.to_bits(np.repeat(vals[:, None], d, 1), BF16),
+                         synth.to_bits(np.ones((T, d)), BF16)], axis=1)
+    for z in (0.0, Z95):
+        out = ga.gelu_and_mul_sparse(to_device(xb, BF16), z)
+        torch.cuda.synchronize()
+        assert np.all(decode(bits_of(out, BF16), BF16) == 0.0)

@@ -66,3 +66,27 @@ def test_stable_digest_of_small_case():
         want = [ln.split("=", 1)[1].strip() for ln in f if ln.startswith("input_sha256")][0]
     assert h == want
     assert math.isfinite(float(synth.bits_to_float(x, synth.BF16).sum()))
+
+
+def test_fused_bf16_rows_match_numpy_rounding():
+    k = synth.stream_key(9, 1)
+    a = np.empty((37, 300), np.uint16)
+    synth.normal_rows_into(a, k, scale=2.0, shift=0.5)
+    b = synth.to_bits(synth.normal(k, 0, 37 * 300, 2.0, 0.5).reshape(37, 300), synth.BF16)
+    assert np.array_equal(a, b)
+    # strided destination (the gate half of a [rows, 2d] buffer)
+    x = np.zeros((37, 600), np.uint16)
+    synth.normal_rows_into(x[:, :300], k, scale=2.0, shift=0.5)
+    assert np.array_equal(x[:, :300], b) and not x[:, 300:].any()
+
+
+def test_c_core_matches_numpy_rederivation():
+    k = synth.stream_key(3, 1)
+    i = np.arange(1, 1001, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        r = synth._mix(np.uint64(k) + i * synth._GAMMA)
+    assert np.array_equal(r, synth.raw64(k, 0, 1000))
+    u = ((r >> np.uint64(11)).astype(np.float64) + 1.0) * 2.0 ** -53
+    assert np.array_equal(u, synth.uniform(k, 0, 1000))
+    z = np.sqrt(-2 * np.log(u[0::2])) * np.cos(2 * np.pi * u[1::2])
+    assert np.abs(z - synth.normal(k, 0, 500)).max() < 1e-14
