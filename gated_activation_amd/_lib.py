@@ -18,7 +18,8 @@ _TORCH_DTYPE = {torch.float32: GA_F32, torch.float16: GA_F16, torch.bfloat16: GA
 
 class Plan(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("waves_per_row", ctypes.c_int32),
-                ("per_lane", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("per_lane", ctypes.c_int32), ("up_late", ctypes.c_int32),
+                ("block", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("grid", ctypes.c_int64)]
 
     def as_dict(self):

@@ -98,9 +98,9 @@ ga_status launched(const char *op, hipError_t e) {
 // ---------------------------------------------------------------------------
 ga_status check_gelu_plan(const ga_plan *p, int64_t d, int32_t dtype) {
     if (p->path == 0) {
-        if (!ga::gelu_vec_available(dtype, p->waves_per_row, p->per_lane))
-            return fail(GA_EUNSUPPORTED, "gelu plan: no vector kernel for waves=%d per_lane=%d",
-                        p->waves_per_row, p->per_lane);
+        if (!ga::gelu_vec_available(dtype, p->waves_per_row, p->per_lane, p->up_late))
+            return fail(GA_EUNSUPPORTED, "gelu plan: no vector kernel for waves=%d per_lane=%d up_late=%d",
+                        p->waves_per_row, p->per_lane, p->up_late);
         const int64_t per16 = 16 / (int64_t)elem_size(dtype);
         if ((int64_t)p->waves_per_row * 64 * p->per_lane * per16 < d)
             return fail(GA_EUNSUPPORTED, "gelu plan: geometry covers fewer than d elements");
@@ -122,7 +122,7 @@ ga_status launch_gelu(const void *in, void *out, int64_t T, int64_t d, int32_t d
     if (p.path == 0) {
         const int32_t nvec = (int32_t)(d * (int64_t)elem_size(dtype) / 16);
         return launched("ga_gelu_and_mul_sparse",
-                        ga::launch_gelu_vec(dtype, p.waves_per_row, p.per_lane, T, in, out, (int32_t)T,
+                        ga::launch_gelu_vec(dtype, p.waves_per_row, p.per_lane, p.up_late, T, in, out, (int32_t)T,
                                             (int32_t)d, nvec, z, live, s));
     }
     return launched("ga_gelu_and_mul_sparse",
@@ -170,14 +170,22 @@ ga_status ga_plan_gelu_and_mul_sparse(int64_t T, int64_t d, int32_t dtype, int32
     ga_plan p{};
     const int64_t nvec = (int64_t)d * (int64_t)es / 16;
     if (aligned && ((size_t)d * es) % 16 == 0 && nvec <= 16 * 64 * 8) {
-        // Aim for 8 vectors (128 bytes of gate, 128 of up) in flight per lane,
-        // then widen the workgroup until the row is covered, at most 16 waves.
-        int w = next_pow2((nvec + 64 * 8 - 1) / (64 * 8));
+        // Vectors per lane: 1 for rows up to 512 vectors, 2 up to 1024, else
+        // 4; then enough waves (at most 16) to cover the row, and more vectors
+        // per lane only when 16 waves are not enough.  Measured on MI355X:
+        // wide workgroups with a few vectors per lane keep the most bytes in
+        // flight per compute unit.
+        const int target = nvec <= 512 ? 1 : nvec <= 1024 ? 2 : 4;
+        int w = next_pow2((nvec + 64 * target - 1) / (64 * target));
         if (w > 16) w = 16;
         int v = next_pow2((nvec + 64 * w - 1) / (64 * w));
         p.path = 0;
         p.waves_per_row = w;
         p.per_lane = v;
+        // With at least ~4 rows per compute unit, loading up after the
+        // statistics frees registers for more resident rows; with fewer rows
+        // the shorter dependency chain of loading it early wins.
+        p.up_late = T >= 1024 ? 1 : 0;
     } else {
         // Element path: up to 16 elements per lane, 1, 4 or 16 waves.
         const int64_t lanes = (d + 15) / 16;
@@ -203,16 +211,16 @@ ga_status ga_plan_silu_and_mul_bounded(int64_t M, int64_t d, int32_t dtype, int3
     if (num_cus < 1) return fail(GA_EINVAL, "plan: num_cus %d", (int)num_cus);
     ga_plan p{};
     p.path = (aligned && ((size_t)d * es) % 16 == 0) ? 0 : 1;
-    p.per_lane = p.path == 0 ? 2 : 4;
+    p.per_lane = 1;
     p.waves_per_row = 0;
     p.block = ga::SILU_BLOCK;
-    // Enough workgroups to cover the whole capacity in one step, capped at
-    // eight per compute unit; the grid-stride loop takes the rest.  The live
-    // count plays no part.
+    // One item per lane per step and up to sixteen workgroups per compute
+    // unit (measured best on MI355X for the decode buffer); the grid-stride
+    // loop covers larger buffers.  The live count plays no part.
     const int64_t items = M * (p.path == 0 ? d * (int64_t)es / 16 : d);
     const int64_t per_wg = (int64_t)ga::SILU_BLOCK * p.per_lane;
     int64_t g = (items + per_wg - 1) / per_wg;
-    const int64_t cap = (int64_t)num_cus * 8;
+    const int64_t cap = (int64_t)num_cus * 16;
     if (g > cap) g = cap;
     if (g < 1) g = 1;
     p.grid = g;

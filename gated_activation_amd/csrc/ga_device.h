@@ -15,6 +15,32 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
+// 16-byte global loads and stores.  Every input byte is read once and every
+// output byte written once, so the nontemporal forms (streaming hint on the
+// cache policy) are the default; NT = false gives the plain forms.
+// ---------------------------------------------------------------------------
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ uint4 ld16(const uint4 *p) {
+    if constexpr (NT) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+        return uint4{v.x, v.y, v.z, v.w};
+    } else {
+        return *p;
+    }
+}
+
+template <bool NT>
+__device__ __forceinline__ void st16(uint4 *p, const uint4 &v) {
+    if constexpr (NT) {
+        __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4 *>(p));
+    } else {
+        *p = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Element traits.  A 16-byte vector holds PER16 elements; unpack widens them
 // to fp32, pack rounds fp32 to the element type (ties to even; gfx950 has a
 // two-lane convert for both 16-bit types).

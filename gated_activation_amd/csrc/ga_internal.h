@@ -10,13 +10,13 @@
 namespace ga {
 
 // Geometries with a compiled kernel.
-bool gelu_vec_available(int dtype, int waves, int vec_per_lane);
+bool gelu_vec_available(int dtype, int waves, int vec_per_lane, int up_late);
 bool gelu_elem_available(int dtype, int waves, int elem_per_lane);
 bool silu_available(int path, int dtype, int per_lane);
 
 constexpr int SILU_BLOCK = 256;
 
-hipError_t launch_gelu_vec(int dtype, int waves, int vec_per_lane, int64_t grid,
+hipError_t launch_gelu_vec(int dtype, int waves, int vec_per_lane, int up_late, int64_t grid,
                            const void *in, void *out, int32_t T, int32_t d, int32_t nvec,
                            float z, const int32_t *live, hipStream_t stream);
 

@@ -21,7 +21,11 @@ namespace ga {
 
 // Vector path: d * sizeof(elem) % 16 == 0 and 16-byte aligned bases.
 // nvec = 16-byte vectors per half row.  Lane t holds vectors t, t + NT, ...
-template <int DT, int WAVES, int VPL>
+// UP selects when the up row is loaded: 0 = right behind the gate (in flight
+// during both reductions), 1 = after the statistics, all vectors at once,
+// 2 = after the statistics, UPCHUNK vectors at a time (fewer registers, so
+// more rows resident per compute unit).
+template <int DT, int WAVES, int VPL, bool NONTEMP = true, int UP = 0, int UPCHUNK = 2>
 __global__ __launch_bounds__(WAVES * 64) void gelu_sparse_vec_kernel(
     const uint4 *__restrict__ in, uint4 *__restrict__ out, int32_t T, int32_t d, int32_t nvec,
     float z, const int32_t *__restrict__ live) {
@@ -42,12 +46,14 @@ __global__ __launch_bounds__(WAVES * 64) void gelu_sparse_vec_kernel(
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
         const int j = k * NT + t;
-        gv[k] = j < nvec ? grow[j] : uint4{0u, 0u, 0u, 0u};
+        gv[k] = j < nvec ? ld16<NONTEMP>(grow + j) : uint4{0u, 0u, 0u, 0u};
     }
+    if constexpr (UP == 0) {
 #pragma unroll
-    for (int k = 0; k < VPL; ++k) {
-        const int j = k * NT + t;
-        uv[k] = j < nvec ? urow[j] : uint4{0u, 0u, 0u, 0u};
+        for (int k = 0; k < VPL; ++k) {
+            const int j = k * NT + t;
+            uv[k] = j < nvec ? ld16<NONTEMP>(urow + j) : uint4{0u, 0u, 0u, 0u};
+        }
     }
 
     // Row mean (vectors past the row end were loaded as zeros).
@@ -78,17 +84,36 @@ __global__ __launch_bounds__(WAVES * 64) void gelu_sparse_vec_kernel(
     const float var = block_sum<WAVES>(q, red[1]) / (float)d;
     const float cut = __builtin_fmaf(z, __builtin_sqrtf(var), mean);
 
+    if constexpr (UP == 1) {
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            const int j = k * NT + t;
+            uv[k] = j < nvec ? ld16<NONTEMP>(urow + j) : uint4{0u, 0u, 0u, 0u};
+        }
+    }
+
     // Apply and store.
+    constexpr int CH = UP == 2 ? (UPCHUNK < VPL ? UPCHUNK : VPL) : VPL;
 #pragma unroll
-    for (int k = 0; k < VPL; ++k) {
-        const int j = k * NT + t;
-        if (j < nvec) {
-            float g[PER], u[PER], y[PER];
-            E::unpack(gv[k], g);
-            E::unpack(uv[k], u);
+    for (int k0 = 0; k0 < VPL; k0 += CH) {
+        if constexpr (UP == 2) {
 #pragma unroll
-            for (int e = 0; e < PER; ++e) y[e] = gelu_tanh_nonneg(__builtin_fmaxf(g[e] - cut, 0.0f)) * u[e];
-            orow[j] = E::pack(y);
+            for (int k = k0; k < k0 + CH; ++k) {
+                const int j = k * NT + t;
+                uv[k] = j < nvec ? ld16<NONTEMP>(urow + j) : uint4{0u, 0u, 0u, 0u};
+            }
+        }
+#pragma unroll
+        for (int k = k0; k < k0 + CH; ++k) {
+            const int j = k * NT + t;
+            if (j < nvec) {
+                float g[PER], u[PER], y[PER];
+                E::unpack(gv[k], g);
+                E::unpack(uv[k], u);
+#pragma unroll
+                for (int e = 0; e < PER; ++e) y[e] = gelu_tanh_nonneg(__builtin_fmaxf(g[e] - cut, 0.0f)) * u[e];
+                st16<NONTEMP>(orow + j, E::pack(y));
+            }
         }
     }
 }
@@ -152,12 +177,16 @@ namespace {
 
 using GeluVecFn = void (*)(const uint4 *, uint4 *, int32_t, int32_t, int32_t, float, const int32_t *);
 
-#define GA_GV(DT, W) \
-    { &gelu_sparse_vec_kernel<DT, W, 1>, &gelu_sparse_vec_kernel<DT, W, 2>, \
-      &gelu_sparse_vec_kernel<DT, W, 4>, &gelu_sparse_vec_kernel<DT, W, 8> }
-#define GA_GVD(DT) { GA_GV(DT, 1), GA_GV(DT, 2), GA_GV(DT, 4), GA_GV(DT, 8), GA_GV(DT, 16) }
-const GeluVecFn kGeluVec[3][5][4] = {GA_GVD(DT_F32), GA_GVD(DT_F16), GA_GVD(DT_BF16)};
+// Index [dtype][up_late][log2 waves][log2 vectors per lane]; late up loads go
+// one vector at a time.
+#define GA_GV(DT, U, W) \
+    { &gelu_sparse_vec_kernel<DT, W, 1, true, U, 1>, &gelu_sparse_vec_kernel<DT, W, 2, true, U, 1>, \
+      &gelu_sparse_vec_kernel<DT, W, 4, true, U, 1>, &gelu_sparse_vec_kernel<DT, W, 8, true, U, 1> }
+#define GA_GVU(DT, U) { GA_GV(DT, U, 1), GA_GV(DT, U, 2), GA_GV(DT, U, 4), GA_GV(DT, U, 8), GA_GV(DT, U, 16) }
+#define GA_GVD(DT) { GA_GVU(DT, 0), GA_GVU(DT, 2) }
+const GeluVecFn kGeluVec[3][2][5][4] = {GA_GVD(DT_F32), GA_GVD(DT_F16), GA_GVD(DT_BF16)};
 #undef GA_GV
+#undef GA_GVU
 #undef GA_GVD
 
 #define GA_GE(DT, W) \
@@ -189,9 +218,10 @@ int elem_index(int waves, int epl, int *wi, int *ei) {
 
 }  // namespace
 
-bool gelu_vec_available(int dtype, int waves, int vpl) {
+bool gelu_vec_available(int dtype, int waves, int vpl, int up_late) {
     int wi, vi;
-    return dtype >= 0 && dtype <= 2 && vec_index(waves, vpl, &wi, &vi) == 0;
+    return dtype >= 0 && dtype <= 2 && (up_late == 0 || up_late == 1) &&
+           vec_index(waves, vpl, &wi, &vi) == 0;
 }
 
 bool gelu_elem_available(int dtype, int waves, int epl) {
@@ -199,13 +229,13 @@ bool gelu_elem_available(int dtype, int waves, int epl) {
     return dtype >= 0 && dtype <= 2 && elem_index(waves, epl, &wi, &ei) == 0;
 }
 
-hipError_t launch_gelu_vec(int dtype, int waves, int vpl, int64_t grid, const void *in, void *out,
-                           int32_t T, int32_t d, int32_t nvec, float z, const int32_t *live,
+hipError_t launch_gelu_vec(int dtype, int waves, int vpl, int up_late, int64_t grid, const void *in,
+                           void *out, int32_t T, int32_t d, int32_t nvec, float z, const int32_t *live,
                            hipStream_t stream) {
     int wi, vi;
-    if (!gelu_vec_available(dtype, waves, vpl) || vec_index(waves, vpl, &wi, &vi) != 0)
+    if (!gelu_vec_available(dtype, waves, vpl, up_late) || vec_index(waves, vpl, &wi, &vi) != 0)
         return hipErrorInvalidValue;
-    const GeluVecFn fn = kGeluVec[dtype][wi][vi];
+    const GeluVecFn fn = kGeluVec[dtype][up_late][wi][vi];
     const uint4 *a_in = static_cast<const uint4 *>(in);
     uint4 *a_out = static_cast<uint4 *>(out);
     void *args[] = {&a_in, &a_out, &T, &d, &nvec, &z, &live};

@@ -19,7 +19,7 @@
 namespace ga {
 
 // 16-byte items; nvec = vectors per half row.
-template <int DT, int PL>
+template <int DT, int PL, bool NONTEMP = true>
 __global__ __launch_bounds__(SILU_BLOCK) void silu_bounded_vec_kernel(
     const uint4 *__restrict__ in, uint4 *__restrict__ out, int32_t M, uint32_t nvec,
     const int32_t *__restrict__ live) {
@@ -36,8 +36,8 @@ __global__ __launch_bounds__(SILU_BLOCK) void silu_bounded_vec_kernel(
             if (j < total) {
                 const uint32_t row = j / nvec;
                 const size_t off = (size_t)row * 2 * nvec + (j - row * nvec);
-                gv[k] = in[off];
-                uv[k] = in[off + nvec];
+                gv[k] = ld16<NONTEMP>(in + off);
+                uv[k] = ld16<NONTEMP>(in + off + nvec);
             }
         }
 #pragma unroll
@@ -49,7 +49,7 @@ __global__ __launch_bounds__(SILU_BLOCK) void silu_bounded_vec_kernel(
                 E::unpack(uv[k], u);
 #pragma unroll
                 for (int e = 0; e < PER; ++e) y[e] = silu(g[e]) * u[e];
-                out[j] = E::pack(y);
+                st16<NONTEMP>(out + j, E::pack(y));
             }
         }
     }
@@ -79,6 +79,7 @@ __global__ __launch_bounds__(SILU_BLOCK) void silu_bounded_elem_kernel(
 
 // Streaming ceiling with the same access pattern: read both halves of each
 // row 16 bytes at a time, write their XOR.
+template <bool NONTEMP = true>
 __global__ __launch_bounds__(SILU_BLOCK) void xor_rows_kernel(const uint4 *__restrict__ in,
                                                               uint4 *__restrict__ out, int32_t rows,
                                                               uint32_t nvec) {
@@ -94,14 +95,14 @@ __global__ __launch_bounds__(SILU_BLOCK) void xor_rows_kernel(const uint4 *__res
             if (j < total) {
                 const uint32_t row = j / nvec;
                 const size_t off = (size_t)row * 2 * nvec + (j - row * nvec);
-                a[k] = in[off];
-                b[k] = in[off + nvec];
+                a[k] = ld16<NONTEMP>(in + off);
+                b[k] = ld16<NONTEMP>(in + off + nvec);
             }
         }
 #pragma unroll
         for (int k = 0; k < PL; ++k) {
             const uint32_t j = base + k * SILU_BLOCK;
-            if (j < total) out[j] = uint4{a[k].x ^ b[k].x, a[k].y ^ b[k].y, a[k].z ^ b[k].z, a[k].w ^ b[k].w};
+            if (j < total) st16<NONTEMP>(out + j, uint4{a[k].x ^ b[k].x, a[k].y ^ b[k].y, a[k].z ^ b[k].z, a[k].w ^ b[k].w});
         }
     }
 }
@@ -142,7 +143,7 @@ hipError_t launch_xor_rows(int64_t grid, const void *in, void *out, int32_t rows
     const void *a_in = in;
     void *a_out = out;
     void *args[] = {&a_in, &a_out, &rows, &nvec_row};
-    return hipLaunchKernel((const void *)&xor_rows_kernel, dim3((uint32_t)grid), dim3(SILU_BLOCK), args,
+    return hipLaunchKernel((const void *)&xor_rows_kernel<true>, dim3((uint32_t)grid), dim3(SILU_BLOCK), args,
                            0, stream);
 }
 

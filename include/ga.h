@@ -71,7 +71,11 @@ typedef struct {
     int32_t per_lane;      /* gelu vector path: 16-byte gate vectors per lane (1,2,4,8);
                               gelu element path: gate elements per lane (4,16,64);
                               silu: 16-byte (or element) items per lane per step (1,2,4) */
+    int32_t up_late;       /* gelu vector path: 0 = load the up row together with the gate
+                              row (shortest latency), 1 = load it after the statistics, one
+                              vector at a time (fewer registers, more rows resident) */
     int32_t block;         /* threads per workgroup */
+    int32_t reserved;      /* zero */
     int64_t grid;          /* workgroups launched (silu: from the capacity M only) */
 } ga_plan;
 

@@ -101,18 +101,20 @@ def test_stream_xor_rows_checks():
 
 
 def test_gelu_planner_known_shapes():
-    p = ga.plan_gelu_and_mul_sparse(2048, 16384, BF16)
-    assert (p.path, p.waves_per_row, p.per_lane, p.block, p.grid) == (0, 4, 8, 256, 2048)
-    p = ga.plan_gelu_and_mul_sparse(512, 8192, BF16)
-    assert (p.path, p.waves_per_row, p.per_lane) == (0, 2, 8)
-    p = ga.plan_gelu_and_mul_sparse(4, 2048, BF16)
-    assert (p.path, p.waves_per_row, p.per_lane) == (0, 1, 4)
-    p = ga.plan_gelu_and_mul_sparse(1, 32768, BF16)
-    assert (p.path, p.waves_per_row, p.per_lane) == (0, 8, 8)
+    # (T, d) -> (path, waves per row, vectors per lane, up loaded late)
+    want = {(2048, 16384): (0, 8, 4, 1), (512, 8192): (0, 8, 2, 0), (2048, 8192): (0, 8, 2, 1),
+            (4, 2048): (0, 4, 1, 0), (1, 32768): (0, 16, 4, 0), (2048, 32768): (0, 16, 4, 1),
+            (64, 65536): (0, 16, 8, 0)}
+    for (T, d), w in want.items():
+        p = ga.plan_gelu_and_mul_sparse(T, d, BF16)
+        assert (p.path, p.waves_per_row, p.per_lane, p.up_late) == w, (T, d, p.as_dict())
+        assert p.block == 64 * p.waves_per_row and p.grid == T
     p = ga.plan_gelu_and_mul_sparse(7, 8191, F16)            # odd d: element path
     assert p.path == 1 and p.waves_per_row * 64 * p.per_lane >= 8191
     p = ga.plan_gelu_and_mul_sparse(7, 8192, F16, aligned=False)
     assert p.path == 1
+    p = ga.plan_gelu_and_mul_sparse(7, 65536, F32)           # beyond the vector reach
+    assert p.path == 1 and p.waves_per_row * 64 * p.per_lane >= 65536
 
 
 @pytest.mark.parametrize("dt", [BF16, F16, F32])
@@ -142,6 +144,10 @@ def test_gelu_with_plan_rejects_bad_geometry():
     p = ga.Plan(path=0, waves_per_row=1, per_lane=1, block=64, grid=1)
     st = L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 2048, BF16, Z, None, ctypes.byref(p), None)
     assert st == EUNSUP                                           # covers 512 < 2048
+    p = ga.Plan(path=0, waves_per_row=4, per_lane=1, up_late=2, block=256, grid=1)
+    assert L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 2048, BF16, Z, None, ctypes.byref(p), None) == EUNSUP
+    p = ga.Plan(path=0, waves_per_row=4, per_lane=1, up_late=1, block=256, grid=1)
+    assert L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 2048, BF16, Z, None, ctypes.byref(p), None) == OK
     p = ga.Plan(path=0, waves_per_row=3, per_lane=8, block=192, grid=1)
     assert L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 64, BF16, Z, None, ctypes.byref(p), None) == EUNSUP
     p = ga.Plan(path=1, waves_per_row=16, per_lane=2, block=1024, grid=1)
@@ -157,13 +163,13 @@ def test_gelu_with_plan_rejects_bad_geometry():
 
 def test_silu_planner_depends_on_capacity_only():
     p = ga.plan_silu_and_mul_bounded(16384, 768, BF16, num_cus=256)
-    assert p.path == 0 and p.block == 256 and 1 <= p.grid <= 256 * 8
+    assert p.path == 0 and p.block == 256 and 1 <= p.grid <= 256 * 16
     # The planner has no live-count input at all; the grid grows with M up to
-    # eight workgroups per compute unit, then the kernel strides.
+    # sixteen workgroups per compute unit, then the kernel strides.
     small = ga.plan_silu_and_mul_bounded(4, 768, BF16, num_cus=256)
-    assert small.grid == 1
+    assert small.grid == 2          # 4 rows x 96 vectors, 256 per workgroup
     big = ga.plan_silu_and_mul_bounded(1 << 20, 768, BF16, num_cus=256)
-    assert big.grid == 256 * 8
+    assert big.grid == 256 * 16
     assert ga.plan_silu_and_mul_bounded(100, 777, BF16).path == 1
     for M in (1, 7, 64, 1000, 16384):
         for d in (1, 8, 768, 777, 4096):

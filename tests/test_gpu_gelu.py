@@ -110,7 +110,8 @@ def _all_vector_plans(d, dtype):
     for w in (1, 2, 4, 8, 16):
         for v in (1, 2, 4, 8):
             if w * 64 * v * per16 >= d:
-                yield ga.Plan(path=0, waves_per_row=w, per_lane=v, block=64 * w, grid=0)
+                for late in (0, 1):
+                    yield ga.Plan(path=0, waves_per_row=w, per_lane=v, up_late=late, block=64 * w, grid=0)
 
 
 def test_every_vector_geometry_matches_oracle():
@@ -118,7 +119,7 @@ def test_every_vector_geometry_matches_oracle():
     oracle-matching result (reduction order differs between them)."""
     x = synth.gelu_offset_rows(24, 8192, seed=77)
     for p in _all_vector_plans(8192, BF16):
-        run_and_check(x, BF16, Z95, plan=p, label=f"plan w{p.waves_per_row} v{p.per_lane}")
+        run_and_check(x, BF16, Z95, plan=p, label=f"plan w{p.waves_per_row} v{p.per_lane} late{p.up_late}")
 
 
 def test_element_path_on_aligned_rows():
@@ -163,3 +164,20 @@ def test_constant_rows_give_exact_zeros():
         out = ga.gelu_and_mul_sparse(to_device(xb, BF16), z)
         torch.cuda.synchronize()
         assert np.all(decode(bits_of(out, BF16), BF16) == 0.0)
+
+
+@pytest.mark.parametrize("dt,tiny", [(F16, 2.0 ** -20), (BF16, 2.0 ** -130), (F32, 2.0 ** -140)],
+                         ids=["f16", "bf16", "f32"])
+def test_subnormal_outputs_are_rounded_not_flushed(dt, tiny):
+    """One element passes the cutoff (hand-worked row: gate 0,...,0,8) and up
+    is a subnormal of the type, so the exact output is subnormal too: it must
+    round to nearest even like the oracle, not flush to zero."""
+    gate = np.array([0.0] * 7 + [8.0])
+    up = np.full(8, tiny)
+    xb = np.concatenate([synth.to_bits(gate, dt), synth.to_bits(up, dt)])[None, :]
+    out = ga.gelu_and_mul_sparse(to_device(xb, dt), Z95)
+    torch.cuda.synchronize()
+    ref = oracle.get().gelu_and_mul_sparse(xb, dt, Z95)
+    got = bits_of(out, dt)
+    assert decode(ref, dt)[0, 7] != 0.0
+    assert np.array_equal(got, ref), (got, ref)
