@@ -13,5 +13,5 @@ from ._lib import (  # noqa: F401
     GA_BF16, GA_F16, GA_F32, GA_OK, GA_EINVAL, GA_EUNSUPPORTED, GA_EHIP, GA_MAX_D,
     GaError, Plan, Z_SPARSITY_095, lib, library_path,
     gelu_and_mul_sparse, silu_and_mul_bounded, stream_xor_rows,
-    plan_gelu_and_mul_sparse, plan_silu_and_mul_bounded,
+    plan_gelu_and_mul_sparse, plan_silu_and_mul_bounded, workspace_for,
 )

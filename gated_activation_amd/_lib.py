@@ -19,8 +19,14 @@ _TORCH_DTYPE = {torch.float32: GA_F32, torch.float16: GA_F16, torch.bfloat16: GA
 class Plan(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("waves_per_row", ctypes.c_int32),
                 ("per_lane", ctypes.c_int32), ("up_late", ctypes.c_int32),
-                ("block", ctypes.c_int32), ("reserved", ctypes.c_int32),
-                ("grid", ctypes.c_int64)]
+                ("block", ctypes.c_int32), ("splits", ctypes.c_int32),
+                ("grid", ctypes.c_int64), ("spin_limit", ctypes.c_uint32),
+                ("reserved", ctypes.c_int32)]
+
+    def __init__(self, **kw):
+        kw.setdefault("splits", 1)
+        kw.setdefault("spin_limit", 1 << 16)
+        super().__init__(**kw)
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -43,9 +49,11 @@ def _load():
     sigs = {
         "ga_gelu_and_mul_sparse": [vp, vp, i64, i64, i32, ctypes.c_float, vp, vp],
         "ga_silu_and_mul_bounded": [vp, vp, i64, i64, i32, vp, vp],
-        "ga_gelu_and_mul_sparse_with_plan": [vp, vp, i64, i64, i32, ctypes.c_float, vp, pplan, vp],
+        "ga_gelu_and_mul_sparse_with_plan": [vp, vp, i64, i64, i32, ctypes.c_float, vp, pplan, vp,
+                                             ctypes.c_size_t, vp],
+        "ga_gelu_and_mul_sparse_ws": [vp, vp, i64, i64, i32, ctypes.c_float, vp, vp, ctypes.c_size_t, vp],
         "ga_silu_and_mul_bounded_with_plan": [vp, vp, i64, i64, i32, vp, pplan, vp],
-        "ga_plan_gelu_and_mul_sparse": [i64, i64, i32, i32, i32, pplan],
+        "ga_plan_gelu_and_mul_sparse": [i64, i64, i32, i32, i32, i32, pplan],
         "ga_plan_silu_and_mul_bounded": [i64, i64, i32, i32, i32, pplan],
         "ga_stream_xor_rows": [vp, vp, i64, i64, vp],
     }
@@ -59,6 +67,8 @@ def _load():
     lib.ga_last_error.restype = ctypes.c_char_p
     lib.ga_version.argtypes = []
     lib.ga_version.restype = i32
+    lib.ga_gelu_and_mul_sparse_workspace_bytes.argtypes = [i64]
+    lib.ga_gelu_and_mul_sparse_workspace_bytes.restype = ctypes.c_size_t
     return lib
 
 
@@ -101,19 +111,48 @@ def _live_ptr(live_rows, x, name):
     return ctypes.c_void_p(live_rows.data_ptr())
 
 
-def gelu_and_mul_sparse(x, z=Z_SPARSITY_095, out=None, live_rows=None, plan=None):
+_WORKSPACES = {}
+
+
+def workspace_for(x, T):
+    """The zero-filled split-row workspace for x's device and current stream
+    (allocated once, grown when a call needs more; never created during
+    graph capture, where the call then runs without one)."""
+    need = int(lib.ga_gelu_and_mul_sparse_workspace_bytes(T))
+    key = (x.device.index, torch.cuda.current_stream(x.device).cuda_stream)
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < need:
+        if torch.cuda.is_current_stream_capturing():
+            return None
+        ws = torch.zeros(max(need, 1 << 16), dtype=torch.uint8, device=x.device)
+        _WORKSPACES[key] = ws
+    return ws
+
+
+def gelu_and_mul_sparse(x, z=Z_SPARSITY_095, out=None, live_rows=None, plan=None, workspace=None):
     """Sparse GELU-and-multiply of x = [gate | up] ([T, 2d]) -> [T, d].
     z = Phi^-1(target sparsity); live_rows (optional int32 device tensor)
-    limits the rows written; plan (optional Plan) forces a launch geometry."""
+    limits the rows written; plan (optional Plan) forces a launch geometry.
+    workspace: None = the cached per-stream workspace (lets few rows split
+    over several workgroups), False = none, or a zero-filled uint8 tensor."""
     T, d, out = _prep(x, out, "gelu_and_mul_sparse")
     live = _live_ptr(live_rows, x, "gelu_and_mul_sparse")
     with torch.cuda.device(x.device):
+        if workspace is None:
+            workspace = workspace_for(x, T) if T > 0 else None
+        elif workspace is False:
+            workspace = None
+        ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
         args = (ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(out.data_ptr()), T, d,
                 _TORCH_DTYPE[x.dtype], ctypes.c_float(z), live)
-        if plan is None:
-            _check(lib.ga_gelu_and_mul_sparse(*args, _stream_of(x)))
+        if plan is not None:
+            _check(lib.ga_gelu_and_mul_sparse_with_plan(*args, ctypes.byref(plan), ws_ptr, ws_bytes,
+                                                        _stream_of(x)))
+        elif ws_ptr is not None:
+            _check(lib.ga_gelu_and_mul_sparse_ws(*args, ws_ptr, ws_bytes, _stream_of(x)))
         else:
-            _check(lib.ga_gelu_and_mul_sparse_with_plan(*args, ctypes.byref(plan), _stream_of(x)))
+            _check(lib.ga_gelu_and_mul_sparse(*args, _stream_of(x)))
     return out
 
 
@@ -144,9 +183,10 @@ def stream_xor_rows(x, out=None):
     return out
 
 
-def plan_gelu_and_mul_sparse(T, d, dtype=GA_BF16, aligned=True, num_cus=256):
+def plan_gelu_and_mul_sparse(T, d, dtype=GA_BF16, aligned=True, num_cus=256, with_workspace=True):
     p = Plan()
-    _check(lib.ga_plan_gelu_and_mul_sparse(T, d, dtype, int(aligned), num_cus, ctypes.byref(p)))
+    _check(lib.ga_plan_gelu_and_mul_sparse(T, d, dtype, int(aligned), num_cus, int(with_workspace),
+                                           ctypes.byref(p)))
     return p
 
 

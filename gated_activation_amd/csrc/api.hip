@@ -6,6 +6,7 @@
 // kernel launch itself; nothing allocates, copies or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <cmath>
@@ -96,15 +97,32 @@ ga_status launched(const char *op, hipError_t e) {
 // ---------------------------------------------------------------------------
 // Geometry checks shared by the planners and the *_with_plan entry points.
 // ---------------------------------------------------------------------------
-ga_status check_gelu_plan(const ga_plan *p, int64_t d, int32_t dtype) {
+constexpr uint32_t kDefaultSpinLimit = 1u << 16;
+constexpr int64_t kSplitMaxRows = 65535;  // grid y limit
+
+ga_status check_gelu_plan(const ga_plan *p, int64_t T, int64_t d, int32_t dtype) {
     if (p->path == 0) {
-        if (!ga::gelu_vec_available(dtype, p->waves_per_row, p->per_lane, p->up_late))
-            return fail(GA_EUNSUPPORTED, "gelu plan: no vector kernel for waves=%d per_lane=%d up_late=%d",
-                        p->waves_per_row, p->per_lane, p->up_late);
         const int64_t per16 = 16 / (int64_t)elem_size(dtype);
-        if ((int64_t)p->waves_per_row * 64 * p->per_lane * per16 < d)
-            return fail(GA_EUNSUPPORTED, "gelu plan: geometry covers fewer than d elements");
+        const int64_t nvec = (d + per16 - 1) / per16;
+        if (p->splits == 1) {
+            if (!ga::gelu_vec_available(dtype, p->waves_per_row, p->per_lane, p->up_late))
+                return fail(GA_EUNSUPPORTED, "gelu plan: no vector kernel for waves=%d per_lane=%d up_late=%d",
+                            p->waves_per_row, p->per_lane, p->up_late);
+            if ((int64_t)p->waves_per_row * 64 * p->per_lane < nvec)
+                return fail(GA_EUNSUPPORTED, "gelu plan: geometry covers fewer than d elements");
+        } else {
+            if (!ga::gelu_split_available(dtype, p->waves_per_row, p->per_lane, p->splits) || p->up_late != 0)
+                return fail(GA_EUNSUPPORTED, "gelu plan: no split kernel for waves=%d per_lane=%d splits=%d",
+                            p->waves_per_row, p->per_lane, p->splits);
+            const int64_t chunk = (int64_t)p->waves_per_row * 64 * p->per_lane;
+            if (chunk * p->splits < nvec || chunk * (p->splits - 1) >= nvec)
+                return fail(GA_EUNSUPPORTED, "gelu plan: %d splits of %lld vectors do not tile a %lld-vector row",
+                            p->splits, (long long)chunk, (long long)nvec);
+            if (T > kSplitMaxRows) return fail(GA_EUNSUPPORTED, "gelu plan: split rows need T <= %lld",
+                                               (long long)kSplitMaxRows);
+        }
     } else if (p->path == 1) {
+        if (p->splits != 1) return fail(GA_EUNSUPPORTED, "gelu plan: the element path does not split rows");
         if (!ga::gelu_elem_available(dtype, p->waves_per_row, p->per_lane))
             return fail(GA_EUNSUPPORTED, "gelu plan: no element kernel for waves=%d per_lane=%d",
                         p->waves_per_row, p->per_lane);
@@ -117,10 +135,14 @@ ga_status check_gelu_plan(const ga_plan *p, int64_t d, int32_t dtype) {
 }
 
 ga_status launch_gelu(const void *in, void *out, int64_t T, int64_t d, int32_t dtype, float z,
-                      const int32_t *live, const ga_plan &p, ga_stream stream) {
+                      const int32_t *live, const ga_plan &p, void *workspace, ga_stream stream) {
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (p.path == 0) {
         const int32_t nvec = (int32_t)(d * (int64_t)elem_size(dtype) / 16);
+        if (p.splits > 1)
+            return launched("ga_gelu_and_mul_sparse",
+                            ga::launch_gelu_split(dtype, p.waves_per_row, p.per_lane, p.splits, in, out, (int32_t)T,
+                                                  (int32_t)d, nvec, z, live, workspace, p.spin_limit, s));
         return launched("ga_gelu_and_mul_sparse",
                         ga::launch_gelu_vec(dtype, p.waves_per_row, p.per_lane, p.up_late, T, in, out, (int32_t)T,
                                             (int32_t)d, nvec, z, live, s));
@@ -128,6 +150,19 @@ ga_status launch_gelu(const void *in, void *out, int64_t T, int64_t d, int32_t d
     return launched("ga_gelu_and_mul_sparse",
                     ga::launch_gelu_elem(dtype, p.waves_per_row, p.per_lane, T, in, out, (int32_t)T,
                                          (int32_t)d, z, live, s));
+}
+
+// Vectors per lane and waves for `nvec` vectors of one workgroup: 1 vector
+// per lane up to 512 vectors, 2 up to 1024, else 4 (at most max_v); enough
+// waves (at most 16) to cover them.  Measured on MI355X: wide workgroups with
+// a few vectors per lane keep the most bytes in flight per compute unit.
+void pick_waves(int64_t nvec, int max_v, int *w_out, int *v_out) {
+    int target = nvec <= 512 ? 1 : nvec <= 1024 ? 2 : 4;
+    if (target > max_v) target = max_v;
+    int w = next_pow2((nvec + 64 * target - 1) / (64 * target));
+    if (w > 16) w = 16;
+    *w_out = w;
+    *v_out = next_pow2((nvec + 64 * w - 1) / (64 * w));
 }
 
 // Flat item count of the live region must fit the kernels' 32-bit indices.
@@ -160,25 +195,20 @@ ga_status check_silu_plan(const ga_plan *p, int64_t M, int64_t d, int32_t dtype)
 extern "C" {
 
 ga_status ga_plan_gelu_and_mul_sparse(int64_t T, int64_t d, int32_t dtype, int32_t aligned,
-                                      int32_t num_cus, ga_plan *plan) {
-    (void)num_cus;  // one workgroup per row: the row count sets the grid
+                                      int32_t num_cus, int32_t with_workspace, ga_plan *plan) {
     if (plan == nullptr) return fail(GA_EINVAL, "plan: null output");
     if (T < 0 || T > INT32_MAX || d < 1) return fail(GA_EINVAL, "plan: bad sizes");
     const size_t es = elem_size(dtype);
     if (es == 0) return fail(GA_EINVAL, "plan: unknown dtype %d", (int)dtype);
     if (d > GA_MAX_D) return fail(GA_EUNSUPPORTED, "plan: d above %d", GA_MAX_D);
+    if (num_cus < 1) num_cus = 256;
     ga_plan p{};
+    p.splits = 1;
+    p.spin_limit = kDefaultSpinLimit;
     const int64_t nvec = (int64_t)d * (int64_t)es / 16;
     if (aligned && ((size_t)d * es) % 16 == 0 && nvec <= 16 * 64 * 8) {
-        // Vectors per lane: 1 for rows up to 512 vectors, 2 up to 1024, else
-        // 4; then enough waves (at most 16) to cover the row, and more vectors
-        // per lane only when 16 waves are not enough.  Measured on MI355X:
-        // wide workgroups with a few vectors per lane keep the most bytes in
-        // flight per compute unit.
-        const int target = nvec <= 512 ? 1 : nvec <= 1024 ? 2 : 4;
-        int w = next_pow2((nvec + 64 * target - 1) / (64 * target));
-        if (w > 16) w = 16;
-        int v = next_pow2((nvec + 64 * w - 1) / (64 * w));
+        int w, v;
+        pick_waves(nvec, 8, &w, &v);
         p.path = 0;
         p.waves_per_row = w;
         p.per_lane = v;
@@ -186,6 +216,25 @@ ga_status ga_plan_gelu_and_mul_sparse(int64_t T, int64_t d, int32_t dtype, int32
         // statistics frees registers for more resident rows; with fewer rows
         // the shorter dependency chain of loading it early wins.
         p.up_late = T >= 1024 ? 1 : 0;
+        // Few long rows: split each over several workgroups that exchange
+        // partial statistics.  Measured on MI355X, the exchange costs about
+        // a microsecond, which pays off once a row has >= 2048 vectors
+        // (32 KB of bf16 gate) and there are at most 64 rows per 2048
+        // vectors; splits aim at ~512-vector chunks and ~256 workgroups.
+        if (with_workspace && T >= 1 && T <= kSplitMaxRows && nvec >= 2048 && T * 2048 <= 64 * nvec) {
+            int64_t splits = std::min<int64_t>(nvec / 512, std::max<int64_t>(2, 256 / T));
+            if (splits > ga::SPLIT_MAX) splits = ga::SPLIT_MAX;
+            int sw, sv;
+            pick_waves((nvec + splits - 1) / splits, 4, &sw, &sv);
+            const int64_t chunk = (int64_t)sw * 64 * sv;
+            splits = (nvec + chunk - 1) / chunk;   // every split owns >= 1 vector
+            if (splits >= 2 && splits <= ga::SPLIT_MAX) {
+                p.waves_per_row = sw;
+                p.per_lane = sv;
+                p.up_late = 0;
+                p.splits = (int32_t)splits;
+            }
+        }
     } else {
         // Element path: up to 16 elements per lane, 1, 4 or 16 waves.
         const int64_t lanes = (d + 15) / 16;
@@ -196,9 +245,13 @@ ga_status ga_plan_gelu_and_mul_sparse(int64_t T, int64_t d, int32_t dtype, int32
         p.per_lane = per <= 4 ? 4 : per <= 16 ? 16 : 64;
     }
     p.block = p.waves_per_row * 64;
-    p.grid = T;
+    p.grid = T * p.splits;
     *plan = p;
     return GA_OK;
+}
+
+size_t ga_gelu_and_mul_sparse_workspace_bytes(int64_t T) {
+    return T < 1 ? 0 : ga::split_workspace_bytes(T > kSplitMaxRows ? kSplitMaxRows : T);
 }
 
 ga_status ga_plan_silu_and_mul_bounded(int64_t M, int64_t d, int32_t dtype, int32_t aligned,
@@ -228,18 +281,48 @@ ga_status ga_plan_silu_and_mul_bounded(int64_t M, int64_t d, int32_t dtype, int3
     return GA_OK;
 }
 
+ga_status check_workspace(const ga_plan &p, int64_t T, const void *workspace, size_t workspace_bytes) {
+    if (p.path != 0 || p.splits <= 1) return GA_OK;
+    if (workspace == nullptr) return fail(GA_EINVAL, "ga_gelu_and_mul_sparse: a split plan needs a workspace");
+    if ((uintptr_t)workspace % 256 != 0) return fail(GA_EINVAL, "ga_gelu_and_mul_sparse: workspace not 256-byte aligned");
+    if (workspace_bytes < ga::split_workspace_bytes(T))
+        return fail(GA_EINVAL, "ga_gelu_and_mul_sparse: workspace of %zu bytes, %zu needed", workspace_bytes,
+                    ga::split_workspace_bytes(T));
+    return GA_OK;
+}
+
 ga_status ga_gelu_and_mul_sparse_with_plan(const void *in, void *out, int64_t T, int64_t d,
                                            int32_t dtype, float z, const int32_t *live_rows,
-                                           const ga_plan *plan, ga_stream stream) {
+                                           const ga_plan *plan, void *workspace, size_t workspace_bytes,
+                                           ga_stream stream) {
     ga_status st = check_rows("ga_gelu_and_mul_sparse", in, out, T, d, dtype);
     if (st != GA_OK) return st;
     if (!std::isfinite(z)) return fail(GA_EINVAL, "ga_gelu_and_mul_sparse: z is not finite");
     if (plan == nullptr) return fail(GA_EINVAL, "ga_gelu_and_mul_sparse: null plan");
-    if ((st = check_gelu_plan(plan, d, dtype)) != GA_OK) return st;
+    if ((st = check_gelu_plan(plan, T, d, dtype)) != GA_OK) return st;
     if (plan->path == 0 && !vector_aligned(in, out, d, dtype))
         return fail(GA_EUNSUPPORTED, "ga_gelu_and_mul_sparse: vector path needs 16-byte rows and bases");
+    if ((st = check_workspace(*plan, T, workspace, workspace_bytes)) != GA_OK) return st;
     if (T == 0) return GA_OK;
-    return launch_gelu(in, out, T, d, dtype, z, live_rows, *plan, stream);
+    return launch_gelu(in, out, T, d, dtype, z, live_rows, *plan, workspace, stream);
+}
+
+ga_status ga_gelu_and_mul_sparse_ws(const void *in, void *out, int64_t T, int64_t d, int32_t dtype, float z,
+                                    const int32_t *live_rows, void *workspace, size_t workspace_bytes,
+                                    ga_stream stream) {
+    ga_status st = check_rows("ga_gelu_and_mul_sparse", in, out, T, d, dtype);
+    if (st != GA_OK) return st;
+    if (!std::isfinite(z)) return fail(GA_EINVAL, "ga_gelu_and_mul_sparse: z is not finite");
+    if (T == 0) return GA_OK;
+    const bool have_ws = workspace != nullptr && (uintptr_t)workspace % 256 == 0 &&
+                         workspace_bytes >= ga::split_workspace_bytes(T > kSplitMaxRows ? 1 : T);
+    int cus = 256;
+    if (have_ws && (st = current_cus(&cus)) != GA_OK) return st;
+    ga_plan p;
+    if ((st = ga_plan_gelu_and_mul_sparse(T, d, dtype, vector_aligned(in, out, d, dtype), cus, have_ws, &p)) != GA_OK)
+        return st;
+    if ((st = check_workspace(p, T, workspace, workspace_bytes)) != GA_OK) return st;
+    return launch_gelu(in, out, T, d, dtype, z, live_rows, p, workspace, stream);
 }
 
 ga_status ga_gelu_and_mul_sparse(const void *in, void *out, int64_t T, int64_t d, int32_t dtype,
@@ -249,9 +332,9 @@ ga_status ga_gelu_and_mul_sparse(const void *in, void *out, int64_t T, int64_t d
     if (!std::isfinite(z)) return fail(GA_EINVAL, "ga_gelu_and_mul_sparse: z is not finite");
     if (T == 0) return GA_OK;
     ga_plan p;
-    if ((st = ga_plan_gelu_and_mul_sparse(T, d, dtype, vector_aligned(in, out, d, dtype), 0, &p)) != GA_OK)
+    if ((st = ga_plan_gelu_and_mul_sparse(T, d, dtype, vector_aligned(in, out, d, dtype), 256, 0, &p)) != GA_OK)
         return st;
-    return launch_gelu(in, out, T, d, dtype, z, live_rows, p, stream);
+    return launch_gelu(in, out, T, d, dtype, z, live_rows, p, nullptr, stream);
 }
 
 ga_status ga_silu_and_mul_bounded_with_plan(const void *in, void *out, int64_t M, int64_t d,

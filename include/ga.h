@@ -67,16 +67,21 @@ typedef void *ga_stream;
  * specific geometry (a tuning sweep); see ga_gelu_and_mul_sparse_with_plan. */
 typedef struct {
     int32_t path;          /* 0: 16-byte vector path, 1: per-element path */
-    int32_t waves_per_row; /* gelu: 64-lane wavefronts sharing one row (1,2,4,8,16) */
-    int32_t per_lane;      /* gelu vector path: 16-byte gate vectors per lane (1,2,4,8);
-                              gelu element path: gate elements per lane (4,16,64);
-                              silu: 16-byte (or element) items per lane per step (1,2,4) */
+    int32_t waves_per_row; /* gelu: 64-lane wavefronts per workgroup (1,2,4,8,16) */
+    int32_t per_lane;      /* gelu vector path: 16-byte gate vectors per lane (1,2,4,8;
+                              split rows 1,2,4); gelu element path: gate elements per
+                              lane (4,16,64); silu: items per lane per step (1,2,4) */
     int32_t up_late;       /* gelu vector path: 0 = load the up row together with the gate
                               row (shortest latency), 1 = load it after the statistics, one
-                              vector at a time (fewer registers, more rows resident) */
+                              vector at a time (fewer registers, more rows resident);
+                              split rows: 0 only */
     int32_t block;         /* threads per workgroup */
-    int32_t reserved;      /* zero */
+    int32_t splits;        /* gelu vector path: workgroups sharing one row; 1, or 2, 4, 8,
+                              16 (needs a workspace, see ga_gelu_and_mul_sparse_ws) */
     int64_t grid;          /* workgroups launched (silu: from the capacity M only) */
+    uint32_t spin_limit;   /* split rows: polls of a row's arrival counter before a
+                              workgroup computes the whole row's statistics itself */
+    int32_t reserved;      /* zero */
 } ga_plan;
 
 /*
@@ -111,14 +116,36 @@ ga_status ga_silu_and_mul_bounded(const void *in, void *out, int64_t M, int64_t 
                                   ga_stream stream);
 
 /*
+ * Sparse GELU-and-multiply with a workspace, for few rows: when the planner
+ * splits each row over several workgroups (T small against the compute-unit
+ * count), they exchange per-chunk (mean, M2) partials through `workspace`
+ * and combine them (Chan's parallel-variance formula, in a fixed order) so
+ * every workgroup of a row uses the same cutoff.  Otherwise this is
+ * ga_gelu_and_mul_sparse and the workspace is not touched.
+ *   workspace        device memory of at least
+ *                    ga_gelu_and_mul_sparse_workspace_bytes(T) bytes, 256-byte
+ *                    aligned, zero-filled before its first use; the kernels keep
+ *                    it valid for every later call (its counters only grow), so
+ *                    it is zeroed once, not per call, and survives graph replay.
+ *   Calls that share a workspace must not run concurrently (the same stream
+ *   serialises them).  A row's workgroups wait for each other for a bounded
+ *   number of polls; past it a workgroup computes the row's statistics on
+ *   its own, so a launch always completes with a correct result.
+ */
+size_t ga_gelu_and_mul_sparse_workspace_bytes(int64_t T);
+ga_status ga_gelu_and_mul_sparse_ws(const void *in, void *out, int64_t T, int64_t d,
+                                    int32_t dtype, float z, const int32_t *live_rows,
+                                    void *workspace, size_t workspace_bytes, ga_stream stream);
+
+/*
  * Host-only planners (no HIP call, usable without a GPU): the geometry the
  * entry points above would launch for these sizes.  `aligned` says whether
  * the 16-byte vector path applies (both base pointers 16-byte aligned and
  * d * element size a multiple of 16); `num_cus` is the device's compute-unit
- * count (256 on MI355X).
+ * count (256 on MI355X); `with_workspace` allows split rows.
  */
 ga_status ga_plan_gelu_and_mul_sparse(int64_t T, int64_t d, int32_t dtype, int32_t aligned,
-                                      int32_t num_cus, ga_plan *plan);
+                                      int32_t num_cus, int32_t with_workspace, ga_plan *plan);
 ga_status ga_plan_silu_and_mul_bounded(int64_t M, int64_t d, int32_t dtype, int32_t aligned,
                                        int32_t num_cus, ga_plan *plan);
 
@@ -126,13 +153,16 @@ ga_status ga_plan_silu_and_mul_bounded(int64_t M, int64_t d, int32_t dtype, int3
  * The same operations with an explicit geometry (for tuning sweeps and the
  * geometry-independence tests).  The plan must name an instantiated kernel
  * (the values listed in ga_plan) and cover the row: vector path
- * waves_per_row * 64 * per_lane * (16 / element size) >= d, element path
- * waves_per_row * 64 * per_lane >= d; else GA_EUNSUPPORTED.  `block` is
- * derived (waves_per_row * 64 for gelu); silu takes its grid from the plan.
+ * splits * waves_per_row * 64 * per_lane * (16 / element size) >= d, with
+ * every split owning at least one vector; element path
+ * waves_per_row * 64 * per_lane >= d; else GA_EUNSUPPORTED.  `block` and
+ * `grid` are derived for gelu; silu takes its grid from the plan.  A split
+ * plan needs the workspace described above (else GA_EINVAL) and T <= 65535.
  */
 ga_status ga_gelu_and_mul_sparse_with_plan(const void *in, void *out, int64_t T, int64_t d,
                                            int32_t dtype, float z, const int32_t *live_rows,
-                                           const ga_plan *plan, ga_stream stream);
+                                           const ga_plan *plan, void *workspace,
+                                           size_t workspace_bytes, ga_stream stream);
 ga_status ga_silu_and_mul_bounded_with_plan(const void *in, void *out, int64_t M, int64_t d,
                                             int32_t dtype, const int32_t *live_rows,
                                             const ga_plan *plan, ga_stream stream);

@@ -22,6 +22,8 @@ Z = ctypes.c_float(1.6448536)
 IN = ctypes.c_void_p(0x7F0000000000)
 OUT = ctypes.c_void_p(0x7F1000000000)
 LIVE = ctypes.c_void_p(0x7F2000000000)
+WS = ctypes.c_void_p(0x7F3000000000)
+WS_BYTES = 1 << 30
 
 
 def declared_functions():
@@ -101,20 +103,54 @@ def test_stream_xor_rows_checks():
 
 
 def test_gelu_planner_known_shapes():
-    # (T, d) -> (path, waves per row, vectors per lane, up loaded late)
-    want = {(2048, 16384): (0, 8, 4, 1), (512, 8192): (0, 8, 2, 0), (2048, 8192): (0, 8, 2, 1),
-            (4, 2048): (0, 4, 1, 0), (1, 32768): (0, 16, 4, 0), (2048, 32768): (0, 16, 4, 1),
-            (64, 65536): (0, 16, 8, 0)}
+    # (T, d) -> (path, waves per workgroup, vectors per lane, up loaded late, splits)
+    want = {(2048, 16384): (0, 8, 4, 1, 1), (512, 8192): (0, 8, 2, 0, 1), (2048, 8192): (0, 8, 2, 1, 1),
+            (4, 2048): (0, 4, 1, 0, 1), (2048, 32768): (0, 16, 4, 1, 1), (1, 8192): (0, 8, 2, 0, 1),
+            # few long rows split over workgroups (with a workspace)
+            (1, 32768): (0, 8, 1, 0, 8), (64, 16384): (0, 8, 1, 0, 4), (64, 32768): (0, 8, 2, 0, 4),
+            (128, 32768): (0, 8, 4, 0, 2), (65, 16384): (0, 8, 4, 0, 1), (64, 65536): (0, 8, 4, 0, 4)}
     for (T, d), w in want.items():
         p = ga.plan_gelu_and_mul_sparse(T, d, BF16)
-        assert (p.path, p.waves_per_row, p.per_lane, p.up_late) == w, (T, d, p.as_dict())
-        assert p.block == 64 * p.waves_per_row and p.grid == T
+        assert (p.path, p.waves_per_row, p.per_lane, p.up_late, p.splits) == w, (T, d, p.as_dict())
+        assert p.block == 64 * p.waves_per_row and p.grid == T * p.splits
+    # without a workspace the rows are never split
+    p = ga.plan_gelu_and_mul_sparse(1, 32768, BF16, with_workspace=False)
+    assert (p.splits, p.waves_per_row, p.per_lane) == (1, 16, 4)
     p = ga.plan_gelu_and_mul_sparse(7, 8191, F16)            # odd d: element path
-    assert p.path == 1 and p.waves_per_row * 64 * p.per_lane >= 8191
+    assert p.path == 1 and p.splits == 1 and p.waves_per_row * 64 * p.per_lane >= 8191
     p = ga.plan_gelu_and_mul_sparse(7, 8192, F16, aligned=False)
     assert p.path == 1
     p = ga.plan_gelu_and_mul_sparse(7, 65536, F32)           # beyond the vector reach
     assert p.path == 1 and p.waves_per_row * 64 * p.per_lane >= 65536
+
+
+def test_workspace_size_and_split_plan_checks():
+    assert L.ga_gelu_and_mul_sparse_workspace_bytes(0) == 0
+    assert L.ga_gelu_and_mul_sparse_workspace_bytes(1) == 144
+    assert L.ga_gelu_and_mul_sparse_workspace_bytes(64) == 64 * 144
+    split = ga.plan_gelu_and_mul_sparse(8, 16384, BF16)
+    assert split.splits == 4
+    call = lambda p, T=8, ws=WS, nb=WS_BYTES, d=16384: L.ga_gelu_and_mul_sparse_with_plan(  # noqa: E731
+        IN, OUT, T, d, BF16, Z, None, ctypes.byref(p), ws, nb, None)
+    assert call(split, ws=None) == EINVAL                                # needs a workspace
+    assert call(split, nb=8 * 144 - 1) == EINVAL                          # too small
+    assert call(split, ws=ctypes.c_void_p(0x7F3000000010)) == EINVAL     # not 256-byte aligned
+    assert call(split, T=0) == OK
+    bad = ga.Plan(path=0, waves_per_row=8, per_lane=1, block=512, splits=5)   # 5 x 512 > 2048 + 512
+    assert call(bad, T=0) == EUNSUP
+    bad = ga.Plan(path=0, waves_per_row=8, per_lane=1, block=512, splits=3)   # 3 x 512 < 2048
+    assert call(bad, T=0) == EUNSUP
+    bad = ga.Plan(path=0, waves_per_row=8, per_lane=1, up_late=1, block=512, splits=4)
+    assert call(bad, T=0) == EUNSUP
+    bad = ga.Plan(path=0, waves_per_row=8, per_lane=8, block=512, splits=2)   # 8 per lane: no split kernel
+    assert call(bad, T=0, d=65536) == EUNSUP
+    bad = ga.Plan(path=1, waves_per_row=4, per_lane=16, block=256, splits=2)
+    assert call(bad, T=0, d=4096) == EUNSUP
+    assert call(ga.Plan(path=0, waves_per_row=4, per_lane=2, block=256, splits=3), T=0, d=12288) == OK
+    assert call(split, T=65536, nb=1 << 40) == EUNSUP                    # beyond the grid's y limit
+    # the workspace entry point validates like the others
+    assert L.ga_gelu_and_mul_sparse_ws(None, OUT, 4, 64, BF16, Z, None, WS, WS_BYTES, None) == EINVAL
+    assert L.ga_gelu_and_mul_sparse_ws(IN, OUT, 0, 64, BF16, Z, None, WS, WS_BYTES, None) == OK
 
 
 @pytest.mark.parametrize("dt", [BF16, F16, F32])
@@ -129,35 +165,35 @@ def test_gelu_planner_covers_every_d(dt):
             continue
         for aligned in (True, False):
             p = ga.plan_gelu_and_mul_sparse(3, d, dt, aligned=aligned)
-            assert p.block == p.waves_per_row * 64 and p.grid == 3
+            assert p.block == p.waves_per_row * 64 and p.grid == 3 * p.splits
             if p.path == 0:
                 assert aligned and (d * es) % 16 == 0
             # With zero rows the entry point validates the plan and returns.
             base_in = ctypes.c_void_p(0x7F0000000000)
             base_out = ctypes.c_void_p(0x7F8000000000)
             st = L.ga_gelu_and_mul_sparse_with_plan(base_in, base_out, 0, d, dt, Z, None,
-                                                    ctypes.byref(p), None)
+                                                    ctypes.byref(p), WS, WS_BYTES, None)
             assert st == OK, (d, dt, aligned, p.as_dict(), L.ga_last_error())
 
 
 def test_gelu_with_plan_rejects_bad_geometry():
     p = ga.Plan(path=0, waves_per_row=1, per_lane=1, block=64, grid=1)
-    st = L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 2048, BF16, Z, None, ctypes.byref(p), None)
+    st = L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 2048, BF16, Z, None, ctypes.byref(p), WS, WS_BYTES, None)
     assert st == EUNSUP                                           # covers 512 < 2048
     p = ga.Plan(path=0, waves_per_row=4, per_lane=1, up_late=2, block=256, grid=1)
-    assert L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 2048, BF16, Z, None, ctypes.byref(p), None) == EUNSUP
+    assert L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 2048, BF16, Z, None, ctypes.byref(p), WS, WS_BYTES, None) == EUNSUP
     p = ga.Plan(path=0, waves_per_row=4, per_lane=1, up_late=1, block=256, grid=1)
-    assert L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 2048, BF16, Z, None, ctypes.byref(p), None) == OK
+    assert L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 2048, BF16, Z, None, ctypes.byref(p), WS, WS_BYTES, None) == OK
     p = ga.Plan(path=0, waves_per_row=3, per_lane=8, block=192, grid=1)
-    assert L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 64, BF16, Z, None, ctypes.byref(p), None) == EUNSUP
+    assert L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 64, BF16, Z, None, ctypes.byref(p), WS, WS_BYTES, None) == EUNSUP
     p = ga.Plan(path=1, waves_per_row=16, per_lane=2, block=1024, grid=1)
-    assert L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 64, BF16, Z, None, ctypes.byref(p), None) == EUNSUP
+    assert L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 64, BF16, Z, None, ctypes.byref(p), WS, WS_BYTES, None) == EUNSUP
     p = ga.Plan(path=2, waves_per_row=1, per_lane=4, block=64, grid=1)
-    assert L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 64, BF16, Z, None, ctypes.byref(p), None) == EINVAL
+    assert L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 64, BF16, Z, None, ctypes.byref(p), WS, WS_BYTES, None) == EINVAL
     # vector path on a base that is not 16-byte aligned
     p = ga.plan_gelu_and_mul_sparse(1, 64, BF16)
     st = L.ga_gelu_and_mul_sparse_with_plan(ctypes.c_void_p(0x7F0000000002), OUT, 0, 64, BF16, Z, None,
-                                            ctypes.byref(p), None)
+                                            ctypes.byref(p), WS, WS_BYTES, None)
     assert st == EUNSUP
 
 

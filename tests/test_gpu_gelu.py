@@ -181,3 +181,95 @@ def test_subnormal_outputs_are_rounded_not_flushed(dt, tiny):
     got = bits_of(out, dt)
     assert decode(ref, dt)[0, 7] != 0.0
     assert np.array_equal(got, ref), (got, ref)
+
+
+# ---------------------------------------------------------------------------
+# Few long rows split over several workgroups (workspace entry point).
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,d", [(1, 16384), (8, 16384), (64, 16384), (1, 32768), (64, 32768),
+                                 (128, 32768), (3, 65536)])
+def test_split_rows_default_plan(T, d):
+    assert ga.plan_gelu_and_mul_sparse(T, d, ga.GA_BF16).splits > 1
+    x = synth.gelu_large(T, d)
+    run_and_check(x, BF16, Z95, label=f"split T{T} d{d}")
+
+
+def _tiling_plans(nvec):
+    """Every split plan whose chunks tile a row of nvec vectors: S = ceil(nvec /
+    chunk) workgroups, each owning at least one vector."""
+    for w in (1, 2, 4, 8, 16):
+        for v in (1, 2, 4):
+            chunk = w * 64 * v
+            S = -(-nvec // chunk)
+            if 2 <= S <= 16:
+                yield ga.Plan(path=0, waves_per_row=w, per_lane=v, block=64 * w, splits=S)
+
+
+def test_split_rows_every_split_count():
+    """Split counts 2..16, uneven counter shares included (rows of 1024, 1100
+    and 1600 vectors), give oracle-matching output."""
+    seen = set()
+    for d in (8192, 8800, 12800):
+        x = synth.gelu_offset_rows(6, d, seed=91)
+        for p in _tiling_plans(d // 8):
+            seen.add(p.splits)
+            run_and_check(x, BF16, Z95, plan=p, label=f"d{d} S{p.splits} w{p.waves_per_row} v{p.per_lane}")
+    assert seen >= {2, 3, 4, 5, 7, 8, 9, 13, 16}, seen
+
+
+def test_split_rows_forced_fallback():
+    """With a poll bound of zero every workgroup computes the whole row's
+    statistics itself: the result must still match the oracle."""
+    x = synth.gelu_large(8, 16384)
+    p = ga.plan_gelu_and_mul_sparse(8, 16384, ga.GA_BF16)
+    p.spin_limit = 0
+    run_and_check(x, BF16, Z95, plan=p, label="fallback")
+
+
+def test_split_workspace_reused_across_shapes():
+    """One workspace serves calls of different T and split counts in any
+    order (each call adds exactly 16 to a row's counter)."""
+    ws = torch.zeros(ga.lib.ga_gelu_and_mul_sparse_workspace_bytes(128), dtype=torch.uint8, device="cuda")
+    o = oracle.get()
+    for T, d, S in ((8, 16384, 4), (2, 8800, 3), (128, 32768, 2), (8, 12800, 7), (64, 16384, 16),
+                    (1, 32768, 8), (3, 8800, 9)):
+        xb = synth.gelu_iid(T, d, seed=T * 7 + S, gate_std=1.3)
+        nvec = d // 8
+        plan = next(p for p in _tiling_plans(nvec) if p.splits == S)
+        out = ga.gelu_and_mul_sparse(to_device(xb, BF16), Z95, plan=plan, workspace=ws)
+        torch.cuda.synchronize()
+        ref, st = o.gelu_and_mul_sparse(xb, BF16, Z95, want_stats=True)
+        compare(bits_of(out, BF16), ref, BF16, gate=decode(xb[:, :d], BF16), stats=st, label=f"reuse T{T} S{S}")
+    counters = ws.view(torch.int32).cpu().numpy()[::36][:128]
+    assert np.all(counters % 16 == 0) and counters.max() > 0
+
+
+@pytest.mark.parametrize("live", [0, 3, 8, 20])
+def test_split_rows_live_bound(live):
+    x = synth.gelu_large(8, 32768)
+    run_and_check(x, BF16, Z95, live=live, label=f"split live {live}")
+
+
+@pytest.mark.parametrize("dt", [F16, F32], ids=["f16", "f32"])
+def test_split_rows_other_dtypes(dt):
+    x = synth.gelu_iid(4, 16384, seed=123, dtype=dt, gate_std=2.0)
+    assert ga.plan_gelu_and_mul_sparse(4, 16384, dt).splits > 1
+    run_and_check(x, dt, Z95, label=f"split dt{dt}")
+
+
+def test_split_rows_constant_and_edge_rows():
+    """Constant rows still give exact zeros through the partial combine;
+    near-constant N(100, 0.01) and Student-t rows match the oracle."""
+    for dt in (F16, BF16):
+        x = synth.edge_rows(10, 16384, dt, seed=5)
+        assert ga.plan_gelu_and_mul_sparse(10, 16384, dt).splits > 1
+        for z in (0.0, Z95):
+            run_and_check(x, dt, z, label=f"split edge dt{dt} z{z}")
+    T, d = 5, 32768
+    vals = np.array([0.0, 100.0, -3.5, 7.25, -250.0])
+    xb = np.concatenate([synth.to_bits(np.repeat(vals[:, None], d, 1), BF16),
+                         synth.to_bits(np.ones((T, d)), BF16)], axis=1)
+    out = ga.gelu_and_mul_sparse(to_device(xb, BF16), 0.0)
+    torch.cuda.synchronize()
+    assert np.all(decode(bits_of(out, BF16), BF16) == 0.0)

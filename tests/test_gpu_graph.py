@@ -18,12 +18,19 @@ pytestmark = pytest.mark.gpu
 def test_graph_replay_with_changing_live_counts():
     Ms, ds = 4096, 768
     Tg, dg = 256, 8192
+    Tq, dq = 8, 32768        # few long rows: the split-row path
     xs_b = synth.moe_buffer(Ms, ds, seed=11)
     xg_b = synth.gelu_offset_rows(Tg, dg, seed=12)
     o = oracle.get()
     ref_s = o.silu_and_mul_bounded(xs_b, BF16, Ms)
     ref_g, st_g = o.gelu_and_mul_sparse(xg_b, BF16, Z95, want_stats=True)
-    xs, xg = to_device(xs_b, BF16), to_device(xg_b, BF16)
+    xq_b = synth.gelu_large(Tq, dq)
+    ref_q, st_q = o.gelu_and_mul_sparse(xq_b, BF16, Z95, want_stats=True)
+    assert ga.plan_gelu_and_mul_sparse(Tq, dq, ga.GA_BF16).splits > 1
+    xs, xg, xq = to_device(xs_b, BF16), to_device(xg_b, BF16), to_device(xq_b, BF16)
+    _, out_q = sentinel_buffer(Tq, dq, BF16)
+    live_q = torch.tensor([Tq], dtype=torch.int32, device="cuda")
+    ws_q = torch.zeros(ga.lib.ga_gelu_and_mul_sparse_workspace_bytes(Tq), dtype=torch.uint8, device="cuda")
     _, out_s = sentinel_buffer(Ms, ds, BF16)
     _, out_g = sentinel_buffer(Tg, dg, BF16)
     live_s = torch.tensor([Ms], dtype=torch.int32, device="cuda")
@@ -33,19 +40,25 @@ def test_graph_replay_with_changing_live_counts():
     # warm-up outside capture, then record
     ga.silu_and_mul_bounded(xs, live_s, out=out_s)
     ga.gelu_and_mul_sparse(xg, Z95, out=out_g, live_rows=live_g)
+    ga.gelu_and_mul_sparse(xq, Z95, out=out_q, live_rows=live_q, workspace=ws_q)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         ga.silu_and_mul_bounded(xs, live_s, out=out_s)
         ga.gelu_and_mul_sparse(xg, Z95, out=out_g, live_rows=live_g)
+        ga.gelu_and_mul_sparse(xq, Z95, out=out_q, live_rows=live_q, workspace=ws_q)
     torch.cuda.synchronize()
 
     gate = decode(xg_b[:, :dg], BF16)
+    gate_q = decode(xq_b[:, :dq], BF16)
     for n_s, n_g in ((64, 1), (4096, 256), (0, 0), (1000, 77), (5000, 300), (17, 128)):
+        n_q = n_g % (Tq + 1)
         out_s.view(torch.int16).fill_(sentinel)
         out_g.view(torch.int16).fill_(sentinel)
+        out_q.view(torch.int16).fill_(sentinel)
         live_s.fill_(n_s)
         live_g.fill_(n_g)
+        live_q.fill_(n_q)
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
@@ -55,3 +68,6 @@ def test_graph_replay_with_changing_live_counts():
         assert np.all(got_s[ks:] == synth.SENTINEL[BF16])
         compare(got_g[:kg], ref_g[:kg], BF16, gate=gate[:kg], stats=st_g[:, :kg], label=f"graph gelu {n_g}")
         assert np.all(got_g[kg:] == synth.SENTINEL[BF16])
+        got_q = bits_of(out_q, BF16)
+        compare(got_q[:n_q], ref_q[:n_q], BF16, gate=gate_q[:n_q], stats=st_q[:, :n_q], label=f"graph split {n_q}")
+        assert np.all(got_q[n_q:] == synth.SENTINEL[BF16])
