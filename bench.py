@@ -45,7 +45,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="approximate CPU time spent on the oracle baseline (0 = skip)")
-    p.add_argument("--no-side", action="store_true", help="skip the ceiling and silu measurements")
+    p.add_argument("--no-side", action="store_true", help="skip the ceiling, silu and sweep measurements")
     return p.parse_args()
 
 
@@ -224,10 +224,53 @@ def main():
         ms_g = time_graph(gelu, n_sets, min(args.steps, 640), 10, stream)
         result["graph_replay_us_per_call"] = round(ms_g * 1e3, 3)
 
+        result["sweep"] = sweep(dev, stream, props.multi_processor_count)
+
     if args.cpu_seconds > 0:
         result["cpu_baseline"], result["parity_sample"] = cpu_baseline(xb, gelu_out, args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
+
+
+SWEEP = [(T, 8192) for T in (1, 2, 8, 32, 128, 512, 2048)] + \
+        [(T, d) for d in (16384, 32768) for T in (1, 64, 2048)]
+
+
+def sweep(dev, stream, num_cus):
+    """gelu_and_mul_sparse over the token sweep (d = 8192, gate N(0,1) plus a
+    per-row offset) and the large-row shapes (gate N(0,2)), bf16, each timed
+    by replaying a graph of 64 launches over distinct buffers (a split-row
+    workspace passed explicitly so few-row shapes take the split path).
+    Shapes under ~256 MB in total may be served from the Infinity Cache."""
+    import numpy as np
+    import torch
+    import gated_activation_amd as ga
+    import synth
+    out = []
+    per_graph = 64
+    for T, d in SWEEP:
+        xb = synth.gelu_offset_rows(T, d) if d == 8192 else synth.gelu_large(T, d)
+        x0 = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
+        bytes_call = T * 3 * d * 2
+        n_sets = int(min(per_graph, max(2, math.ceil(ROTATE_BYTES / bytes_call))))
+        xs = [x0] + [x0.clone() for _ in range(n_sets - 1)]
+        outs = [torch.empty(T, d, dtype=torch.bfloat16, device=dev) for _ in range(n_sets)]
+        ws = torch.zeros(max(1, ga.lib.ga_gelu_and_mul_sparse_workspace_bytes(T)), dtype=torch.uint8,
+                         device=dev)
+
+        def call(i):
+            ga.gelu_and_mul_sparse(xs[i], Z, out=outs[i], workspace=ws)
+        reps = 4 if bytes_call > (64 << 20) else 16
+        ms = time_graph(call, n_sets, reps * per_graph, 10, stream, per_graph=per_graph)
+        plan = ga.plan_gelu_and_mul_sparse(T, d, ga.GA_BF16, True, num_cus, True)
+        gbps = bytes_call / (ms * 1e-3) / 1e9
+        out.append({"T": T, "d": d, "us_per_call": round(ms * 1e3, 3), "GBps": round(gbps, 1),
+                    "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2), "bytes": bytes_call,
+                    "working_set_MB": round(n_sets * bytes_call / 1e6, 1),
+                    "plan": f"splits={plan.splits} waves={plan.waves_per_row} per_lane={plan.per_lane} "
+                            f"up_late={plan.up_late}"})
+        del xs, outs, ws
+    return out
 
 
 def cpu_baseline(xb, gpu_out, seconds):

@@ -41,7 +41,11 @@ def _load(path=None):
     for name in ("gao_decode_array", "gao_encode_array"):
         getattr(lib, name).restype = None
         getattr(lib, name).argtypes = [vp, i64, ctypes.c_int, vp]
-    for name in ("gao_gelu_tanh_array", "gao_silu_array"):
+    lib.gao_gelu_and_mul.restype = ctypes.c_int
+    lib.gao_gelu_and_mul.argtypes = [vp, vp, i64, i64, ctypes.c_int, ctypes.c_int, i64, vp]
+    lib.gao_squared_relu_bounded.restype = ctypes.c_int
+    lib.gao_squared_relu_bounded.argtypes = [vp, vp, i64, i64, ctypes.c_int, i64, vp]
+    for name in ("gao_gelu_tanh_array", "gao_silu_array", "gao_gelu_erf_array", "gao_squared_relu_array"):
         getattr(lib, name).restype = None
         getattr(lib, name).argtypes = [vp, i64, vp]
     return lib
@@ -74,11 +78,20 @@ class Oracle:
         self.lib.gao_gelu_tanh_array(s.ctypes.data, s.size, out.ctypes.data)
         return out
 
-    def silu(self, x):
+    def _map(self, fn, x):
         x = np.ascontiguousarray(x, dtype=np.float64)
         out = np.empty(x.shape, np.float64)
-        self.lib.gao_silu_array(x.ctypes.data, x.size, out.ctypes.data)
+        fn(x.ctypes.data, x.size, out.ctypes.data)
         return out
+
+    def silu(self, x):
+        return self._map(self.lib.gao_silu_array, x)
+
+    def gelu_erf(self, x):
+        return self._map(self.lib.gao_gelu_erf_array, x)
+
+    def squared_relu(self, x):
+        return self._map(self.lib.gao_squared_relu_array, x)
 
     def row_stats(self, g):
         g = np.ascontiguousarray(g, dtype=np.float64)
@@ -125,6 +138,34 @@ class Oracle:
         rc = self.lib.gao_silu_and_mul_bounded(
             x.ctypes.data, y.ctypes.data, M, d, dtype, int(live),
             None if f64 is None else f64.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return (y, f64) if want_f64 else y
+
+    def gelu_and_mul(self, x_bits, dtype, approximate, live=None, out=None, want_f64=False):
+        """Non-sparse GELU-and-multiply; approximate: True = tanh form,
+        False = exact erf form."""
+        x = np.ascontiguousarray(x_bits, dtype=BITS_DTYPE[dtype])
+        T, two_d = x.shape
+        d = two_d // 2
+        assert two_d == 2 * d and d >= 1
+        live = T if live is None else int(live)
+        y = np.zeros((T, d), BITS_DTYPE[dtype]) if out is None else np.array(out, copy=True)
+        f64 = np.full((T, d), np.nan) if want_f64 else None
+        rc = self.lib.gao_gelu_and_mul(x.ctypes.data, y.ctypes.data, T, d, dtype, int(bool(approximate)),
+                                       live, None if f64 is None else f64.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return (y, f64) if want_f64 else y
+
+    def squared_relu_bounded(self, x_bits, dtype, live, out=None, want_f64=False):
+        """Bounded squared ReLU of x[M, d] (not gated)."""
+        x = np.ascontiguousarray(x_bits, dtype=BITS_DTYPE[dtype])
+        M, d = x.shape
+        y = np.zeros((M, d), BITS_DTYPE[dtype]) if out is None else np.array(out, copy=True)
+        f64 = np.full((M, d), np.nan) if want_f64 else None
+        rc = self.lib.gao_squared_relu_bounded(x.ctypes.data, y.ctypes.data, M, d, dtype, int(live),
+                                               None if f64 is None else f64.ctypes.data)
         if rc != 0:
             raise ValueError("oracle rejected the arguments")
         return (y, f64) if want_f64 else y

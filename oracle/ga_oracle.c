@@ -15,6 +15,10 @@
  *   - Megatron-LM PR 6328 "Size MoE activation kernel grid to the row count",
  *     section "What changed and why": an elementwise silu(gate) * up over the
  *     live rows of a capture-sized MoE buffer, bounded by a device row count.
+ *   - the same vLLM page, section Purpose: the provider is chosen per
+ *     "approximation mode", so plain GELU-and-multiply exists in a tanh and
+ *     an exact (erf) form; Megatron-LM PR 6328, section Scope and risks:
+ *     the squared-ReLU activation kernel shares the bounded-row pattern.
  *
  * Readings taken where the pages are silent (each also listed in the design
  * notes): the std is the population std (divide by d); the cutoff is
@@ -136,6 +140,19 @@ double gao_gelu_tanh(double s)
     return 0.5 * s * (1.0 + tanh(k * (s + 0.044715 * s * s * s)));
 }
 
+/* Exact GELU: x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)). */
+double gao_gelu_erf(double x)
+{
+    return 0.5 * x * (1.0 + erf(x / sqrt(2.0)));
+}
+
+/* Squared ReLU: max(x, 0)^2. */
+double gao_squared_relu(double x)
+{
+    const double r = x > 0.0 ? x : 0.0;
+    return r * r;
+}
+
 /* SiLU: x * sigmoid(x) = x / (1 + e^-x). */
 double gao_silu(double x)
 {
@@ -214,6 +231,44 @@ int gao_silu_and_mul_bounded(const void *in, void *out, int64_t M, int64_t d,
     return 0;
 }
 
+/* GELU-and-multiply without the sparsity step: out = gelu(gate) * up on rows
+ * [0, clamp(live, 0, T)) of in[T, 2d]; approximate != 0 selects the tanh
+ * form, 0 the exact erf form.  Rows beyond the live count are not written. */
+int gao_gelu_and_mul(const void *in, void *out, int64_t T, int64_t d, int dtype,
+                     int approximate, int64_t live, double *out_f64)
+{
+    if (!in || !out || T < 0 || d < 1 || !gao_elem_size(dtype)) return -1;
+    const int64_t n = clamp_live(live, T);
+    for (int64_t r = 0; r < n; ++r) {
+        for (int64_t i = 0; i < d; ++i) {
+            const double gate = load_elem(in, r * 2 * d + i, dtype);
+            const double up = load_elem(in, r * 2 * d + d + i, dtype);
+            const double act = approximate ? gao_gelu_tanh(gate) : gao_gelu_erf(gate);
+            const double y = act * up;
+            if (out_f64) out_f64[r * d + i] = y;
+            store_elem(out, r * d + i, dtype, y);
+        }
+    }
+    return 0;
+}
+
+/* Bounded squared ReLU (not gated): in[M, d] -> out[M, d] = max(x, 0)^2 on
+ * rows [0, clamp(live, 0, M)); the other rows are not written. */
+int gao_squared_relu_bounded(const void *in, void *out, int64_t M, int64_t d, int dtype,
+                             int64_t live, double *out_f64)
+{
+    if (!in || !out || M < 0 || d < 1 || !gao_elem_size(dtype)) return -1;
+    const int64_t n = clamp_live(live, M);
+    for (int64_t r = 0; r < n; ++r) {
+        for (int64_t i = 0; i < d; ++i) {
+            const double y = gao_squared_relu(load_elem(in, r * d + i, dtype));
+            if (out_f64) out_f64[r * d + i] = y;
+            store_elem(out, r * d + i, dtype, y);
+        }
+    }
+    return 0;
+}
+
 /* Array helpers so the pins can test each step over many points at once. */
 void gao_decode_array(const void *bits, int64_t n, int dtype, double *out)
 {
@@ -233,4 +288,14 @@ void gao_gelu_tanh_array(const double *s, int64_t n, double *out)
 void gao_silu_array(const double *x, int64_t n, double *out)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = gao_silu(x[i]);
+}
+
+void gao_gelu_erf_array(const double *x, int64_t n, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = gao_gelu_erf(x[i]);
+}
+
+void gao_squared_relu_array(const double *x, int64_t n, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = gao_squared_relu(x[i]);
 }

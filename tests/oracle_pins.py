@@ -380,7 +380,66 @@ def pin_silu_bounded(o):
             assert np.all(y[n:] == synth.SENTINEL[dt])
 
 
+def pin_gelu_erf(o):
+    x = np.linspace(0.0, 12.0, 2401)
+    ref = torch.nn.functional.gelu(torch.from_numpy(x), approximate="none").numpy()
+    assert np.allclose(o.gelu_erf(x), ref, rtol=1e-14, atol=1e-300), "erf gelu vs torch"
+    y = np.linspace(-6.0, 0.0, 601)          # 1 + erf cancels on this side
+    ref = torch.nn.functional.gelu(torch.from_numpy(y), approximate="none").numpy()
+    assert np.allclose(o.gelu_erf(y), ref, rtol=1e-8, atol=1e-300)
+    # x Phi(x) - (-x) Phi(-x) = x (Phi(x) + Phi(-x)) = x;  gelu(1) = Phi(1).
+    z = np.linspace(-8.0, 8.0, 321)
+    assert np.allclose(o.gelu_erf(z) - o.gelu_erf(-z), z, rtol=1e-13, atol=1e-13)
+    assert math.isclose(o.gelu_erf(np.array([1.0]))[0], 0.5 * math.erfc(-1.0 / math.sqrt(2.0)), rel_tol=1e-15)
+    assert o.gelu_erf(np.array([0.0]))[0] == 0.0
+
+
+def pin_squared_relu(o):
+    x = np.concatenate([np.linspace(-5.0, 5.0, 1001), [0.0, -0.0, 1e-200, 1e150]])
+    got = o.squared_relu(x)
+    ref = (torch.nn.functional.relu(torch.from_numpy(x)) ** 2).numpy()
+    assert np.array_equal(got, ref)
+    assert np.array_equal(o.squared_relu(2.0 * x[:1001]), 4.0 * got[:1001])   # degree-2 homogeneous
+    assert np.all(got[x <= 0] == 0.0)
+
+
+def pin_gelu_and_mul(o):
+    for dt, T, d, seed in ((BF16, 7, 333, 51), (F16, 5, 64, 52), (F32, 3, 1000, 53)):
+        x = synth.gelu_iid(T, d, seed=seed, dtype=dt, gate_std=2.5)
+        g = torch.from_numpy(o.decode(x[:, :d], dt))
+        u = torch.from_numpy(o.decode(x[:, d:], dt))
+        for approximate, mode in ((True, "tanh"), (False, "none")):
+            y, f64 = o.gelu_and_mul(x, dt, approximate, want_f64=True)
+            ref = (torch.nn.functional.gelu(g, approximate=mode) * u).numpy()
+            # Negative gates: 1 + tanh(w) (or 1 + erf) cancels; both sides then
+            # agree to an absolute ~1e-16 |gate|, not relatively.
+            assert np.allclose(f64, ref, rtol=1e-12, atol=1e-13), (dt, mode)
+            assert np.array_equal(y, o.encode(f64, dt))
+        ta = o.gelu_and_mul(x, dt, True, want_f64=True)[1]
+        te = o.gelu_and_mul(x, dt, False, want_f64=True)[1]
+        assert 1e-5 < np.abs(ta - te).max() < 1e-2 * np.abs(o.decode(x[:, d:], dt)).max()
+        sentinel = np.full((T, d), synth.SENTINEL[dt])
+        part = o.gelu_and_mul(x, dt, False, live=2, out=sentinel)
+        assert np.all(part[2:] == synth.SENTINEL[dt])
+        assert np.array_equal(part[:2], o.gelu_and_mul(x, dt, False)[:2])
+
+
+def pin_squared_relu_bounded(o):
+    M, d = 30, 257
+    for dt in (BF16, F16, F32):
+        x = synth.to_bits(3.0 * synth.normal(synth.stream_key(61, 1), 0, M * d).reshape(M, d), dt)
+        ref = (torch.nn.functional.relu(torch.from_numpy(o.decode(x, dt))) ** 2).numpy()
+        sentinel = np.full((M, d), synth.SENTINEL[dt])
+        for live in (0, 11, M, M + 3, -1):
+            y, f64 = o.squared_relu_bounded(x, dt, live, out=sentinel, want_f64=True)
+            n = max(0, min(live, M))
+            assert np.array_equal(f64[:n], ref[:n])
+            assert np.array_equal(y[:n], o.encode(ref[:n], dt))
+            assert np.all(y[n:] == synth.SENTINEL[dt])
+
+
 ALL_PINS = [pin_decode, pin_encode_fp32, pin_encode_fp16, pin_encode_bf16,
             pin_roundtrip, pin_gelu, pin_silu, pin_row_stats,
             pin_gelu_sparse_composition, pin_gelu_sparse_invariants,
-            pin_survival_fraction, pin_brute_force_1x8, pin_silu_bounded]
+            pin_survival_fraction, pin_brute_force_1x8, pin_silu_bounded,
+            pin_gelu_erf, pin_squared_relu, pin_gelu_and_mul, pin_squared_relu_bounded]

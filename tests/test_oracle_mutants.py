@@ -46,6 +46,16 @@ MUTANTS = {
     "silu_sign": ("x / (1.0 + exp(-x))", "x / (1.0 + exp(x))"),
     "silu_operands_swapped": ("gao_silu(gate) * up", "gao_silu(up) * gate"),
     "silu_ignores_live": ("const int64_t n = clamp_live(live, M);", "const int64_t n = M;"),
+    "erf_argument_unscaled": ("erf(x / sqrt(2.0))", "erf(x / 2.0)"),
+    "erf_gelu_half_dropped": ("return 0.5 * x * (1.0 + erf", "return x * (1.0 + erf"),
+    "squared_relu_not_squared": ("return r * r;", "return r;"),
+    "squared_relu_leaks_negatives": ("const double r = x > 0.0 ? x : 0.0;", "const double r = x;"),
+    "gelu_and_mul_modes_swapped": ("approximate ? gao_gelu_tanh(gate) : gao_gelu_erf(gate)",
+                                   "approximate ? gao_gelu_erf(gate) : gao_gelu_tanh(gate)"),
+    "gelu_and_mul_up_from_gate": ("const double up = load_elem(in, r * 2 * d + d + i, dtype);\n"
+                                  "            const double act",
+                                  "const double up = load_elem(in, r * 2 * d + i, dtype);\n"
+                                  "            const double act"),
 }
 
 
