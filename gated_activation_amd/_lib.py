@@ -56,6 +56,8 @@ def _load():
         "ga_plan_gelu_and_mul_sparse": [i64, i64, i32, i32, i32, i32, pplan],
         "ga_plan_silu_and_mul_bounded": [i64, i64, i32, i32, i32, pplan],
         "ga_stream_xor_rows": [vp, vp, i64, i64, vp],
+        "ga_gelu_and_mul": [vp, vp, i64, i64, i32, i32, vp, vp],
+        "ga_squared_relu_bounded": [vp, vp, i64, i64, i32, vp, vp],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -67,6 +69,8 @@ def _load():
     lib.ga_last_error.restype = ctypes.c_char_p
     lib.ga_version.argtypes = []
     lib.ga_version.restype = i32
+    lib.ga_z_from_sparsity.argtypes = [ctypes.c_double]
+    lib.ga_z_from_sparsity.restype = ctypes.c_double
     lib.ga_gelu_and_mul_sparse_workspace_bytes.argtypes = [i64]
     lib.ga_gelu_and_mul_sparse_workspace_bytes.restype = ctypes.c_size_t
     return lib
@@ -84,16 +88,17 @@ def _stream_of(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def _prep(x, out, name):
+def _prep(x, out, name, gated=True):
     if not isinstance(x, torch.Tensor) or not x.is_cuda:
         raise ValueError(f"{name}: x must be a CUDA (HIP) tensor")
-    if x.dim() != 2 or x.shape[1] % 2 != 0 or x.shape[1] == 0:
-        raise ValueError(f"{name}: x must be [rows, 2d] with d >= 1, got {tuple(x.shape)}")
+    cols = 2 if gated else 1
+    if x.dim() != 2 or x.shape[1] % cols != 0 or x.shape[1] == 0:
+        raise ValueError(f"{name}: x must be [rows, {cols}d] with d >= 1, got {tuple(x.shape)}")
     if not x.is_contiguous():
         raise ValueError(f"{name}: x must be contiguous")
     if x.dtype not in _TORCH_DTYPE:
         raise ValueError(f"{name}: unsupported dtype {x.dtype}")
-    rows, d = x.shape[0], x.shape[1] // 2
+    rows, d = x.shape[0], x.shape[1] // cols
     if out is None:
         out = torch.empty((rows, d), dtype=x.dtype, device=x.device)
     elif (out.shape != (rows, d) or out.dtype != x.dtype or out.device != x.device
@@ -171,6 +176,39 @@ def silu_and_mul_bounded(x, live_rows, out=None, plan=None):
         else:
             _check(lib.ga_silu_and_mul_bounded_with_plan(*args, ctypes.byref(plan), _stream_of(x)))
     return out
+
+
+def gelu_and_mul(x, approximate="tanh", out=None, live_rows=None):
+    """gelu(gate) * up of x = [gate | up] ([T, 2d]) -> [T, d]; approximate
+    "tanh" or "none" (the exact erf form); live_rows optional."""
+    if approximate not in ("tanh", "none"):
+        raise ValueError("gelu_and_mul: approximate must be 'tanh' or 'none'")
+    T, d, out = _prep(x, out, "gelu_and_mul")
+    live = _live_ptr(live_rows, x, "gelu_and_mul")
+    with torch.cuda.device(x.device):
+        _check(lib.ga_gelu_and_mul(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(out.data_ptr()), T, d,
+                                   _TORCH_DTYPE[x.dtype], 1 if approximate == "tanh" else 0, live,
+                                   _stream_of(x)))
+    return out
+
+
+def squared_relu_bounded(x, live_rows, out=None):
+    """max(x, 0)^2 on rows [0, clamp(live_rows[0], 0, M)) of x ([M, d], not
+    gated); other rows of `out` are left as they are."""
+    M, d, out = _prep(x, out, "squared_relu_bounded", gated=False)
+    live = _live_ptr(live_rows, x, "squared_relu_bounded")
+    if live is None:
+        raise ValueError("squared_relu_bounded: live_rows is required")
+    with torch.cuda.device(x.device):
+        _check(lib.ga_squared_relu_bounded(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(out.data_ptr()), M, d,
+                                           _TORCH_DTYPE[x.dtype], live, _stream_of(x)))
+    return out
+
+
+def z_from_sparsity(target_sparsity):
+    """Phi^-1(target_sparsity): the cutoff multiplier for a target fraction of
+    zeros (0.95 -> 1.6448536...)."""
+    return float(lib.ga_z_from_sparsity(float(target_sparsity)))
 
 
 def stream_xor_rows(x, out=None):

@@ -1,4 +1,4 @@
-// The C-ABI of libga.so: argument checks, the launch heuristic, dispatch.
+// The C-ABI of libga.so: argument checks, launch planning, dispatch.
 //
 // Every check runs on the host before any HIP call, so a rejected call has no
 // side effect and the checks can be exercised without a GPU.  The only HIP
@@ -8,8 +8,8 @@
 
 #include <algorithm>
 #include <atomic>
-#include <cstdarg>
 #include <cmath>
+#include <cstdarg>
 #include <cstdio>
 #include <cstring>
 
@@ -18,6 +18,9 @@
 
 namespace {
 
+// ---------------------------------------------------------------------------
+// Errors, sizes, pointer checks
+// ---------------------------------------------------------------------------
 thread_local char g_last_error[256] = "";
 
 ga_status fail(ga_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -29,6 +32,11 @@ ga_status fail(ga_status st, const char *fmt, ...) {
     return st;
 }
 
+ga_status launched(const char *op, hipError_t e) {
+    if (e != hipSuccess) return fail(GA_EHIP, "%s: launch failed: %s", op, hipGetErrorString(e));
+    return GA_OK;
+}
+
 size_t elem_size(int32_t dtype) {
     return dtype == GA_F32 ? 4 : (dtype == GA_F16 || dtype == GA_BF16) ? 2 : 0;
 }
@@ -38,6 +46,8 @@ bool overlaps(const void *a, size_t abytes, const void *b, size_t bbytes) {
     return a0 < b0 + bbytes && b0 < a0 + abytes;
 }
 
+// The 16-byte path: both bases 16-byte aligned and every row a whole number
+// of 16-byte vectors.
 bool vector_aligned(const void *in, const void *out, int64_t d, int32_t dtype) {
     return ((uintptr_t)in % 16 == 0) && ((uintptr_t)out % 16 == 0) &&
            ((size_t)d * elem_size(dtype)) % 16 == 0;
@@ -49,18 +59,20 @@ int next_pow2(int64_t v) {
     return p;
 }
 
-// Shared checks of the two operations: [rows, 2d] in, [rows, d] out.
+// Checks of [rows, cols_in * d] in and [rows, d] out: cols_in is 2 for the
+// gated layout (gate | up) and 1 for the ungated one.
 ga_status check_rows(const char *op, const void *in, const void *out, int64_t rows, int64_t d,
-                     int32_t dtype) {
+                     int32_t dtype, int cols_in = 2) {
     if (in == nullptr || out == nullptr) return fail(GA_EINVAL, "%s: null in/out pointer", op);
-    if (rows < 0 || rows > INT32_MAX) return fail(GA_EINVAL, "%s: row count %lld out of [0, 2^31)", op, (long long)rows);
+    if (rows < 0 || rows > INT32_MAX)
+        return fail(GA_EINVAL, "%s: row count %lld out of [0, 2^31)", op, (long long)rows);
     if (d < 1) return fail(GA_EINVAL, "%s: d = %lld must be >= 1", op, (long long)d);
     const size_t es = elem_size(dtype);
     if (es == 0) return fail(GA_EINVAL, "%s: unknown dtype %d", op, (int)dtype);
     if (d > GA_MAX_D) return fail(GA_EUNSUPPORTED, "%s: d = %lld above %d", op, (long long)d, GA_MAX_D);
     if ((uintptr_t)in % es != 0 || (uintptr_t)out % es != 0)
         return fail(GA_EINVAL, "%s: pointer not aligned to the element size", op);
-    const size_t in_bytes = (size_t)rows * 2 * (size_t)d * es;
+    const size_t in_bytes = (size_t)rows * (size_t)cols_in * (size_t)d * es;
     const size_t out_bytes = (size_t)rows * (size_t)d * es;
     if (rows > 0 && overlaps(in, in_bytes, out, out_bytes))
         return fail(GA_EINVAL, "%s: in and out overlap (in-place is not supported)", op);
@@ -83,22 +95,31 @@ ga_status current_cus(int *cus) {
     }
     int c = 0;
     e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess || c <= 0) return fail(GA_EHIP, "hipDeviceGetAttribute(CU count): %s", hipGetErrorString(e));
+    if (e != hipSuccess || c <= 0)
+        return fail(GA_EHIP, "hipDeviceGetAttribute(CU count): %s", hipGetErrorString(e));
     if (dev >= 0 && dev < 64) g_cus[dev].store(c, std::memory_order_relaxed);
     *cus = c;
     return GA_OK;
 }
 
-ga_status launched(const char *op, hipError_t e) {
-    if (e != hipSuccess) return fail(GA_EHIP, "%s: launch failed: %s", op, hipGetErrorString(e));
-    return GA_OK;
-}
-
 // ---------------------------------------------------------------------------
-// Geometry checks shared by the planners and the *_with_plan entry points.
+// gelu_and_mul_sparse: planning, plan checks, launch
 // ---------------------------------------------------------------------------
 constexpr uint32_t kDefaultSpinLimit = 1u << 16;
-constexpr int64_t kSplitMaxRows = 65535;  // grid y limit
+constexpr int64_t kSplitMaxRows = 65535;  // the grid's y limit
+
+// Vectors per lane and waves for `nvec` vectors of one workgroup: 1 vector
+// per lane up to 512 vectors, 2 up to 1024, else 4 (at most max_v); enough
+// waves (at most 16) to cover them.  Measured on MI355X: wide workgroups with
+// a few vectors per lane keep the most bytes in flight per compute unit.
+void pick_waves(int64_t nvec, int max_v, int *w_out, int *v_out) {
+    int target = nvec <= 512 ? 1 : nvec <= 1024 ? 2 : 4;
+    if (target > max_v) target = max_v;
+    int w = next_pow2((nvec + 64 * target - 1) / (64 * target));
+    if (w > 16) w = 16;
+    *w_out = w;
+    *v_out = next_pow2((nvec + 64 * w - 1) / (64 * w));
+}
 
 ga_status check_gelu_plan(const ga_plan *p, int64_t T, int64_t d, int32_t dtype) {
     if (p->path == 0) {
@@ -118,8 +139,8 @@ ga_status check_gelu_plan(const ga_plan *p, int64_t T, int64_t d, int32_t dtype)
             if (chunk * p->splits < nvec || chunk * (p->splits - 1) >= nvec)
                 return fail(GA_EUNSUPPORTED, "gelu plan: %d splits of %lld vectors do not tile a %lld-vector row",
                             p->splits, (long long)chunk, (long long)nvec);
-            if (T > kSplitMaxRows) return fail(GA_EUNSUPPORTED, "gelu plan: split rows need T <= %lld",
-                                               (long long)kSplitMaxRows);
+            if (T > kSplitMaxRows)
+                return fail(GA_EUNSUPPORTED, "gelu plan: split rows need T <= %lld", (long long)kSplitMaxRows);
         }
     } else if (p->path == 1) {
         if (p->splits != 1) return fail(GA_EUNSUPPORTED, "gelu plan: the element path does not split rows");
@@ -134,66 +155,127 @@ ga_status check_gelu_plan(const ga_plan *p, int64_t T, int64_t d, int32_t dtype)
     return GA_OK;
 }
 
+ga_status check_workspace(const ga_plan &p, int64_t T, const void *workspace, size_t workspace_bytes) {
+    if (p.path != 0 || p.splits <= 1) return GA_OK;
+    if (workspace == nullptr) return fail(GA_EINVAL, "ga_gelu_and_mul_sparse: a split plan needs a workspace");
+    if ((uintptr_t)workspace % 256 != 0)
+        return fail(GA_EINVAL, "ga_gelu_and_mul_sparse: workspace not 256-byte aligned");
+    if (workspace_bytes < ga::split_workspace_bytes(T))
+        return fail(GA_EINVAL, "ga_gelu_and_mul_sparse: workspace of %zu bytes, %zu needed", workspace_bytes,
+                    ga::split_workspace_bytes(T));
+    return GA_OK;
+}
+
 ga_status launch_gelu(const void *in, void *out, int64_t T, int64_t d, int32_t dtype, float z,
                       const int32_t *live, const ga_plan &p, void *workspace, ga_stream stream) {
+    const char *name = "ga_gelu_and_mul_sparse";
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (p.path == 0) {
         const int32_t nvec = (int32_t)(d * (int64_t)elem_size(dtype) / 16);
         if (p.splits > 1)
-            return launched("ga_gelu_and_mul_sparse",
-                            ga::launch_gelu_split(dtype, p.waves_per_row, p.per_lane, p.splits, in, out, (int32_t)T,
-                                                  (int32_t)d, nvec, z, live, workspace, p.spin_limit, s));
-        return launched("ga_gelu_and_mul_sparse",
-                        ga::launch_gelu_vec(dtype, p.waves_per_row, p.per_lane, p.up_late, T, in, out, (int32_t)T,
-                                            (int32_t)d, nvec, z, live, s));
+            return launched(name, ga::launch_gelu_split(dtype, p.waves_per_row, p.per_lane, p.splits, in, out,
+                                                        (int32_t)T, (int32_t)d, nvec, z, live, workspace,
+                                                        p.spin_limit, s));
+        return launched(name, ga::launch_gelu_vec(dtype, p.waves_per_row, p.per_lane, p.up_late, T, in, out,
+                                                  (int32_t)T, (int32_t)d, nvec, z, live, s));
     }
-    return launched("ga_gelu_and_mul_sparse",
-                    ga::launch_gelu_elem(dtype, p.waves_per_row, p.per_lane, T, in, out, (int32_t)T,
-                                         (int32_t)d, z, live, s));
+    return launched(name, ga::launch_gelu_elem(dtype, p.waves_per_row, p.per_lane, T, in, out, (int32_t)T,
+                                               (int32_t)d, z, live, s));
 }
 
-// Vectors per lane and waves for `nvec` vectors of one workgroup: 1 vector
-// per lane up to 512 vectors, 2 up to 1024, else 4 (at most max_v); enough
-// waves (at most 16) to cover them.  Measured on MI355X: wide workgroups with
-// a few vectors per lane keep the most bytes in flight per compute unit.
-void pick_waves(int64_t nvec, int max_v, int *w_out, int *v_out) {
-    int target = nvec <= 512 ? 1 : nvec <= 1024 ? 2 : 4;
-    if (target > max_v) target = max_v;
-    int w = next_pow2((nvec + 64 * target - 1) / (64 * target));
-    if (w > 16) w = 16;
-    *w_out = w;
-    *v_out = next_pow2((nvec + 64 * w - 1) / (64 * w));
-}
-
+// ---------------------------------------------------------------------------
+// Elementwise family (silu_and_mul_bounded, gelu_and_mul, squared ReLU)
+// ---------------------------------------------------------------------------
 // Flat item count of the live region must fit the kernels' 32-bit indices.
-constexpr int64_t kSiluMaxItems = (int64_t)1 << 31;
+constexpr int64_t kMaxItems = (int64_t)1 << 31;
 
-ga_status launch_silu(const void *in, void *out, int64_t M, int64_t d, int32_t dtype,
-                      const int32_t *live, const ga_plan &p, ga_stream stream) {
-    const int64_t items_row = p.path == 0 ? d * (int64_t)elem_size(dtype) / 16 : d;
-    return launched("ga_silu_and_mul_bounded",
-                    ga::launch_silu(p.path, dtype, p.per_lane, p.grid, in, out, (int32_t)M,
-                                    (uint32_t)items_row, live, static_cast<hipStream_t>(stream)));
+// One item (16 bytes, or one element) per lane per step and up to sixteen
+// workgroups per compute unit (measured best on MI355X for the decode
+// buffer); the grid-stride loop covers larger buffers.  The grid depends on
+// the capacity, never on a live count.
+ga_plan plan_act(int64_t rows, int64_t d, size_t es, bool aligned, int num_cus) {
+    ga_plan p{};
+    p.path = (aligned && ((size_t)d * es) % 16 == 0) ? 0 : 1;
+    p.per_lane = 1;
+    p.waves_per_row = 0;
+    p.splits = 1;
+    p.block = ga::SILU_BLOCK;
+    const int64_t items = rows * (p.path == 0 ? d * (int64_t)es / 16 : d);
+    const int64_t per_wg = (int64_t)ga::SILU_BLOCK * p.per_lane;
+    int64_t g = (items + per_wg - 1) / per_wg;
+    const int64_t cap = (int64_t)num_cus * 16;
+    if (g > cap) g = cap;
+    if (g < 1) g = 1;
+    p.grid = g;
+    return p;
 }
 
-ga_status check_silu_plan(const ga_plan *p, int64_t M, int64_t d, int32_t dtype) {
-    if (!ga::silu_available(p->path, dtype, p->per_lane))
-        return fail(GA_EUNSUPPORTED, "silu plan: no kernel for path=%d per_lane=%d", p->path, p->per_lane);
-    if (p->grid < 1 || p->grid > INT32_MAX) return fail(GA_EINVAL, "silu plan: grid %lld", (long long)p->grid);
+ga_status check_act_plan(const ga_plan *p, int op, int64_t rows, int64_t d, int32_t dtype) {
+    if (!ga::act_available(op, p->path, dtype, p->per_lane))
+        return fail(GA_EUNSUPPORTED, "plan: no kernel for path=%d per_lane=%d", p->path, p->per_lane);
+    if (p->grid < 1 || p->grid > INT32_MAX) return fail(GA_EINVAL, "plan: grid %lld", (long long)p->grid);
     const int64_t items_row = p->path == 0 ? d * (int64_t)elem_size(dtype) / 16 : d;
     // The kernels step through items with 32-bit counters: both the region
     // and one grid-wide step must stay below 2^31 so their sum cannot wrap.
-    if (p->grid * ga::SILU_BLOCK * p->per_lane > kSiluMaxItems)
-        return fail(GA_EUNSUPPORTED, "silu plan: grid too large for 32-bit item indices");
-    if (M * items_row >= kSiluMaxItems)
-        return fail(GA_EUNSUPPORTED, "silu: M * d too large for 32-bit item indices");
+    if (p->grid * ga::SILU_BLOCK * p->per_lane > kMaxItems)
+        return fail(GA_EUNSUPPORTED, "plan: grid too large for 32-bit item indices");
+    if (rows * items_row >= kMaxItems)
+        return fail(GA_EUNSUPPORTED, "plan: rows * d too large for 32-bit item indices");
     return GA_OK;
+}
+
+ga_status launch_act(const char *name, int op, const void *in, void *out, int64_t rows, int64_t d,
+                     int32_t dtype, const int32_t *live, const ga_plan &p, ga_stream stream) {
+    const int64_t items_row = p.path == 0 ? d * (int64_t)elem_size(dtype) / 16 : d;
+    return launched(name, ga::launch_act(op, p.path, dtype, p.per_lane, p.grid, in, out, (int32_t)rows,
+                                         (uint32_t)items_row, live, static_cast<hipStream_t>(stream)));
+}
+
+// Shared body of the elementwise entry points.  live may be null (all rows)
+// unless the op requires it.
+ga_status run_act(const char *name, int op, const void *in, void *out, int64_t rows, int64_t d,
+                  int32_t dtype, const int32_t *live, bool live_required, ga_stream stream) {
+    const int cols_in = op == ga::OP_SQUARED_RELU ? 1 : 2;
+    ga_status st = check_rows(name, in, out, rows, d, dtype, cols_in);
+    if (st != GA_OK) return st;
+    if (live_required && live == nullptr) return fail(GA_EINVAL, "%s: live_rows is required", name);
+    if (rows * d >= kMaxItems) return fail(GA_EUNSUPPORTED, "%s: rows * d >= 2^31", name);
+    if (rows == 0) return GA_OK;
+    int cus = 0;
+    if ((st = current_cus(&cus)) != GA_OK) return st;
+    const ga_plan p = plan_act(rows, d, elem_size(dtype), vector_aligned(in, out, d, dtype), cus);
+    return launch_act(name, op, in, out, rows, d, dtype, live, p, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Inverse normal CDF, for z = Phi^-1(target sparsity).  Newton's method on
+// Phi(z) = p (p <= 1/2), with Phi(z) = erfc(-z / sqrt 2) / 2 from the C
+// library, started from Abramowitz & Stegun 26.2.23 (a rational
+// approximation with absolute error below 4.5e-4).
+// ---------------------------------------------------------------------------
+double normal_quantile_lower(double p) {
+    const double t = std::sqrt(-2.0 * std::log(p));
+    double z = -(t - (2.515517 + 0.802853 * t + 0.010328 * t * t) /
+                         (1.0 + 1.432788 * t + 0.189269 * t * t + 0.001308 * t * t * t));
+    const double inv_sqrt_2pi = 0.39894228040143267794;
+    for (int it = 0; it < 60; ++it) {
+        const double cdf = 0.5 * std::erfc(-z * 0.70710678118654752440);
+        const double pdf = inv_sqrt_2pi * std::exp(-0.5 * z * z);
+        if (pdf == 0.0) break;
+        const double step = (cdf - p) / pdf;
+        z -= step;
+        if (std::fabs(step) <= 1e-16 * (1.0 + std::fabs(z))) break;
+    }
+    return z;
 }
 
 }  // namespace
 
 extern "C" {
 
+// ---------------------------------------------------------------------------
+// gelu_and_mul_sparse
+// ---------------------------------------------------------------------------
 ga_status ga_plan_gelu_and_mul_sparse(int64_t T, int64_t d, int32_t dtype, int32_t aligned,
                                       int32_t num_cus, int32_t with_workspace, ga_plan *plan) {
     if (plan == nullptr) return fail(GA_EINVAL, "plan: null output");
@@ -227,7 +309,7 @@ ga_status ga_plan_gelu_and_mul_sparse(int64_t T, int64_t d, int32_t dtype, int32
             int sw, sv;
             pick_waves((nvec + splits - 1) / splits, 4, &sw, &sv);
             const int64_t chunk = (int64_t)sw * 64 * sv;
-            splits = (nvec + chunk - 1) / chunk;   // every split owns >= 1 vector
+            splits = (nvec + chunk - 1) / chunk;  // every split owns >= 1 vector
             if (splits >= 2 && splits <= ga::SPLIT_MAX) {
                 p.waves_per_row = sw;
                 p.per_lane = sv;
@@ -251,50 +333,12 @@ ga_status ga_plan_gelu_and_mul_sparse(int64_t T, int64_t d, int32_t dtype, int32
 }
 
 size_t ga_gelu_and_mul_sparse_workspace_bytes(int64_t T) {
-    return T < 1 ? 0 : ga::split_workspace_bytes(T > kSplitMaxRows ? kSplitMaxRows : T);
+    return T < 1 ? 0 : ga::split_workspace_bytes(std::min<int64_t>(T, kSplitMaxRows));
 }
 
-ga_status ga_plan_silu_and_mul_bounded(int64_t M, int64_t d, int32_t dtype, int32_t aligned,
-                                       int32_t num_cus, ga_plan *plan) {
-    if (plan == nullptr) return fail(GA_EINVAL, "plan: null output");
-    if (M < 0 || M > INT32_MAX || d < 1) return fail(GA_EINVAL, "plan: bad sizes");
-    const size_t es = elem_size(dtype);
-    if (es == 0) return fail(GA_EINVAL, "plan: unknown dtype %d", (int)dtype);
-    if (d > GA_MAX_D) return fail(GA_EUNSUPPORTED, "plan: d above %d", GA_MAX_D);
-    if (num_cus < 1) return fail(GA_EINVAL, "plan: num_cus %d", (int)num_cus);
-    ga_plan p{};
-    p.path = (aligned && ((size_t)d * es) % 16 == 0) ? 0 : 1;
-    p.per_lane = 1;
-    p.waves_per_row = 0;
-    p.block = ga::SILU_BLOCK;
-    // One item per lane per step and up to sixteen workgroups per compute
-    // unit (measured best on MI355X for the decode buffer); the grid-stride
-    // loop covers larger buffers.  The live count plays no part.
-    const int64_t items = M * (p.path == 0 ? d * (int64_t)es / 16 : d);
-    const int64_t per_wg = (int64_t)ga::SILU_BLOCK * p.per_lane;
-    int64_t g = (items + per_wg - 1) / per_wg;
-    const int64_t cap = (int64_t)num_cus * 16;
-    if (g > cap) g = cap;
-    if (g < 1) g = 1;
-    p.grid = g;
-    *plan = p;
-    return GA_OK;
-}
-
-ga_status check_workspace(const ga_plan &p, int64_t T, const void *workspace, size_t workspace_bytes) {
-    if (p.path != 0 || p.splits <= 1) return GA_OK;
-    if (workspace == nullptr) return fail(GA_EINVAL, "ga_gelu_and_mul_sparse: a split plan needs a workspace");
-    if ((uintptr_t)workspace % 256 != 0) return fail(GA_EINVAL, "ga_gelu_and_mul_sparse: workspace not 256-byte aligned");
-    if (workspace_bytes < ga::split_workspace_bytes(T))
-        return fail(GA_EINVAL, "ga_gelu_and_mul_sparse: workspace of %zu bytes, %zu needed", workspace_bytes,
-                    ga::split_workspace_bytes(T));
-    return GA_OK;
-}
-
-ga_status ga_gelu_and_mul_sparse_with_plan(const void *in, void *out, int64_t T, int64_t d,
-                                           int32_t dtype, float z, const int32_t *live_rows,
-                                           const ga_plan *plan, void *workspace, size_t workspace_bytes,
-                                           ga_stream stream) {
+ga_status ga_gelu_and_mul_sparse_with_plan(const void *in, void *out, int64_t T, int64_t d, int32_t dtype,
+                                           float z, const int32_t *live_rows, const ga_plan *plan,
+                                           void *workspace, size_t workspace_bytes, ga_stream stream) {
     ga_status st = check_rows("ga_gelu_and_mul_sparse", in, out, T, d, dtype);
     if (st != GA_OK) return st;
     if (!std::isfinite(z)) return fail(GA_EINVAL, "ga_gelu_and_mul_sparse: z is not finite");
@@ -314,19 +358,19 @@ ga_status ga_gelu_and_mul_sparse_ws(const void *in, void *out, int64_t T, int64_
     if (st != GA_OK) return st;
     if (!std::isfinite(z)) return fail(GA_EINVAL, "ga_gelu_and_mul_sparse: z is not finite");
     if (T == 0) return GA_OK;
-    const bool have_ws = workspace != nullptr && (uintptr_t)workspace % 256 == 0 &&
-                         workspace_bytes >= ga::split_workspace_bytes(T > kSplitMaxRows ? 1 : T);
+    const bool have_ws = workspace != nullptr && (uintptr_t)workspace % 256 == 0 && T <= kSplitMaxRows &&
+                         workspace_bytes >= ga::split_workspace_bytes(T);
     int cus = 256;
     if (have_ws && (st = current_cus(&cus)) != GA_OK) return st;
     ga_plan p;
-    if ((st = ga_plan_gelu_and_mul_sparse(T, d, dtype, vector_aligned(in, out, d, dtype), cus, have_ws, &p)) != GA_OK)
+    if ((st = ga_plan_gelu_and_mul_sparse(T, d, dtype, vector_aligned(in, out, d, dtype), cus, have_ws, &p)) !=
+        GA_OK)
         return st;
-    if ((st = check_workspace(p, T, workspace, workspace_bytes)) != GA_OK) return st;
     return launch_gelu(in, out, T, d, dtype, z, live_rows, p, workspace, stream);
 }
 
-ga_status ga_gelu_and_mul_sparse(const void *in, void *out, int64_t T, int64_t d, int32_t dtype,
-                                 float z, const int32_t *live_rows, ga_stream stream) {
+ga_status ga_gelu_and_mul_sparse(const void *in, void *out, int64_t T, int64_t d, int32_t dtype, float z,
+                                 const int32_t *live_rows, ga_stream stream) {
     ga_status st = check_rows("ga_gelu_and_mul_sparse", in, out, T, d, dtype);
     if (st != GA_OK) return st;
     if (!std::isfinite(z)) return fail(GA_EINVAL, "ga_gelu_and_mul_sparse: z is not finite");
@@ -337,36 +381,63 @@ ga_status ga_gelu_and_mul_sparse(const void *in, void *out, int64_t T, int64_t d
     return launch_gelu(in, out, T, d, dtype, z, live_rows, p, nullptr, stream);
 }
 
-ga_status ga_silu_and_mul_bounded_with_plan(const void *in, void *out, int64_t M, int64_t d,
-                                            int32_t dtype, const int32_t *live_rows,
-                                            const ga_plan *plan, ga_stream stream) {
-    ga_status st = check_rows("ga_silu_and_mul_bounded", in, out, M, d, dtype);
+double ga_z_from_sparsity(double target_sparsity) {
+    const double p = target_sparsity;
+    if (!(p > 0.0 && p < 1.0)) return std::nan("");
+    if (p == 0.5) return 0.0;
+    return p < 0.5 ? normal_quantile_lower(p) : -normal_quantile_lower(1.0 - p);
+}
+
+// ---------------------------------------------------------------------------
+// Elementwise family
+// ---------------------------------------------------------------------------
+ga_status ga_plan_silu_and_mul_bounded(int64_t M, int64_t d, int32_t dtype, int32_t aligned, int32_t num_cus,
+                                       ga_plan *plan) {
+    if (plan == nullptr) return fail(GA_EINVAL, "plan: null output");
+    if (M < 0 || M > INT32_MAX || d < 1) return fail(GA_EINVAL, "plan: bad sizes");
+    const size_t es = elem_size(dtype);
+    if (es == 0) return fail(GA_EINVAL, "plan: unknown dtype %d", (int)dtype);
+    if (d > GA_MAX_D) return fail(GA_EUNSUPPORTED, "plan: d above %d", GA_MAX_D);
+    if (num_cus < 1) return fail(GA_EINVAL, "plan: num_cus %d", (int)num_cus);
+    *plan = plan_act(M, d, es, aligned != 0, num_cus);
+    return GA_OK;
+}
+
+ga_status ga_silu_and_mul_bounded_with_plan(const void *in, void *out, int64_t M, int64_t d, int32_t dtype,
+                                            const int32_t *live_rows, const ga_plan *plan, ga_stream stream) {
+    const char *name = "ga_silu_and_mul_bounded";
+    ga_status st = check_rows(name, in, out, M, d, dtype);
     if (st != GA_OK) return st;
-    if (live_rows == nullptr) return fail(GA_EINVAL, "ga_silu_and_mul_bounded: live_rows is required");
-    if (plan == nullptr) return fail(GA_EINVAL, "ga_silu_and_mul_bounded: null plan");
-    if ((st = check_silu_plan(plan, M, d, dtype)) != GA_OK) return st;
+    if (live_rows == nullptr) return fail(GA_EINVAL, "%s: live_rows is required", name);
+    if (plan == nullptr) return fail(GA_EINVAL, "%s: null plan", name);
+    if ((st = check_act_plan(plan, ga::OP_SILU_MUL, M, d, dtype)) != GA_OK) return st;
     if (plan->path == 0 && !vector_aligned(in, out, d, dtype))
-        return fail(GA_EUNSUPPORTED, "ga_silu_and_mul_bounded: vector path needs 16-byte rows and bases");
+        return fail(GA_EUNSUPPORTED, "%s: vector path needs 16-byte rows and bases", name);
     if (M == 0) return GA_OK;
-    return launch_silu(in, out, M, d, dtype, live_rows, *plan, stream);
+    return launch_act(name, ga::OP_SILU_MUL, in, out, M, d, dtype, live_rows, *plan, stream);
 }
 
 ga_status ga_silu_and_mul_bounded(const void *in, void *out, int64_t M, int64_t d, int32_t dtype,
                                   const int32_t *live_rows, ga_stream stream) {
-    ga_status st = check_rows("ga_silu_and_mul_bounded", in, out, M, d, dtype);
-    if (st != GA_OK) return st;
-    if (live_rows == nullptr) return fail(GA_EINVAL, "ga_silu_and_mul_bounded: live_rows is required");
-    const int64_t items = M * d;  // upper bound on items of either path
-    if (items >= kSiluMaxItems) return fail(GA_EUNSUPPORTED, "ga_silu_and_mul_bounded: M * d >= 2^31");
-    if (M == 0) return GA_OK;
-    int cus = 0;
-    if ((st = current_cus(&cus)) != GA_OK) return st;
-    ga_plan p;
-    if ((st = ga_plan_silu_and_mul_bounded(M, d, dtype, vector_aligned(in, out, d, dtype), cus, &p)) != GA_OK)
-        return st;
-    return launch_silu(in, out, M, d, dtype, live_rows, p, stream);
+    return run_act("ga_silu_and_mul_bounded", ga::OP_SILU_MUL, in, out, M, d, dtype, live_rows, true, stream);
 }
 
+ga_status ga_gelu_and_mul(const void *in, void *out, int64_t T, int64_t d, int32_t dtype, int32_t approximate,
+                          const int32_t *live_rows, ga_stream stream) {
+    if (approximate != GA_GELU_ERF && approximate != GA_GELU_TANH)
+        return fail(GA_EINVAL, "ga_gelu_and_mul: approximate must be GA_GELU_ERF or GA_GELU_TANH");
+    const int op = approximate == GA_GELU_TANH ? ga::OP_GELU_TANH_MUL : ga::OP_GELU_ERF_MUL;
+    return run_act("ga_gelu_and_mul", op, in, out, T, d, dtype, live_rows, false, stream);
+}
+
+ga_status ga_squared_relu_bounded(const void *in, void *out, int64_t M, int64_t d, int32_t dtype,
+                                  const int32_t *live_rows, ga_stream stream) {
+    return run_act("ga_squared_relu_bounded", ga::OP_SQUARED_RELU, in, out, M, d, dtype, live_rows, true, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Measurement aid and diagnostics
+// ---------------------------------------------------------------------------
 ga_status ga_stream_xor_rows(const void *in, void *out, int64_t rows, int64_t w_bytes, ga_stream stream) {
     if (in == nullptr || out == nullptr) return fail(GA_EINVAL, "ga_stream_xor_rows: null pointer");
     if (rows < 0 || rows > INT32_MAX || w_bytes < 16 || w_bytes % 16 != 0)
@@ -374,7 +445,7 @@ ga_status ga_stream_xor_rows(const void *in, void *out, int64_t rows, int64_t w_
     if ((uintptr_t)in % 16 != 0 || (uintptr_t)out % 16 != 0)
         return fail(GA_EINVAL, "ga_stream_xor_rows: pointers must be 16-byte aligned");
     const int64_t nvec = w_bytes / 16;
-    if (rows * nvec >= kSiluMaxItems) return fail(GA_EUNSUPPORTED, "ga_stream_xor_rows: too large");
+    if (rows * nvec >= kMaxItems) return fail(GA_EUNSUPPORTED, "ga_stream_xor_rows: too large");
     if (overlaps(in, (size_t)rows * 2 * (size_t)w_bytes, out, (size_t)rows * (size_t)w_bytes))
         return fail(GA_EINVAL, "ga_stream_xor_rows: in and out overlap");
     if (rows == 0) return GA_OK;
@@ -383,8 +454,8 @@ ga_status ga_stream_xor_rows(const void *in, void *out, int64_t rows, int64_t w_
     if (st != GA_OK) return st;
     int64_t g = (rows * nvec + ga::SILU_BLOCK * 4 - 1) / (ga::SILU_BLOCK * 4);
     if (g > (int64_t)cus * 8) g = (int64_t)cus * 8;
-    return launched("ga_stream_xor_rows",
-                    ga::launch_xor_rows(g, in, out, (int32_t)rows, (uint32_t)nvec, static_cast<hipStream_t>(stream)));
+    return launched("ga_stream_xor_rows", ga::launch_xor_rows(g, in, out, (int32_t)rows, (uint32_t)nvec,
+                                                              static_cast<hipStream_t>(stream)));
 }
 
 const char *ga_status_str(int32_t status) {

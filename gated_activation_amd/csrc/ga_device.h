@@ -168,19 +168,26 @@ __device__ __forceinline__ float block_sum(float v, float *slots) {
 // ---------------------------------------------------------------------------
 // Activations in fp32.
 //
-// tanh GELU for s >= 0: 0.5 s (1 + tanh w) = s / (1 + e^(-2w)) with
+// tanh GELU: 0.5 s (1 + tanh w) = s / (1 + e^(-2w)) with
 // w = sqrt(2/pi) (s + 0.044715 s^3).  In base 2, e^(-2w) = 2^(-s (A + B s^2)),
-// A = 2 sqrt(2/pi) / ln 2, B = 0.044715 A.  For s >= 0 the exponent is <= 0,
-// so nothing overflows; at s = 0 the result is exactly 0.
+// A = 2 sqrt(2/pi) / ln 2, B = 0.044715 A.  For s >= 0 the exponent is <= 0
+// and at s = 0 the result is exactly 0; for s << 0 the power overflows to +inf
+// and the result is -0, the function's limit.
 // ---------------------------------------------------------------------------
 constexpr float GELU_A = 2.302208198144325f;
 constexpr float GELU_B = 0.1029432395800235f;
 constexpr float LOG2_E = 1.4426950408889634f;
 
-__device__ __forceinline__ float gelu_tanh_nonneg(float s) {
+__device__ __forceinline__ float gelu_tanh(float s) {
     const float t = s * __builtin_fmaf(GELU_B, s * s, GELU_A);
-    const float e = __builtin_amdgcn_exp2f(-t);
-    return s * __builtin_amdgcn_rcpf(1.0f + e);
+    return s * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-t));
+}
+
+// Exact GELU, x Phi(x) = 0.5 x erfc(-x / sqrt 2): the erfc form has no
+// cancellation for negative x (1 + erf(y) = erfc(-y)).  erfcf is the ROCm
+// device library's.
+__device__ __forceinline__ float gelu_erf(float x) {
+    return 0.5f * x * erfcf(-x * 0.70710678118654752f);
 }
 
 // silu(x) = x / (1 + e^-x); for x << 0 the power overflows to +inf and the

@@ -12,7 +12,9 @@ namespace ga {
 // Geometries with a compiled kernel.
 bool gelu_vec_available(int dtype, int waves, int vec_per_lane, int up_late);
 bool gelu_elem_available(int dtype, int waves, int elem_per_lane);
-bool silu_available(int path, int dtype, int per_lane);
+// Elementwise activation ops sharing one kernel family.
+enum : int { OP_SILU_MUL = 0, OP_GELU_TANH_MUL = 1, OP_GELU_ERF_MUL = 2, OP_SQUARED_RELU = 3, OP_COUNT = 4 };
+bool act_available(int op, int path, int dtype, int per_lane);
 
 constexpr int SILU_BLOCK = 256;
 
@@ -36,10 +38,9 @@ hipError_t launch_gelu_elem(int dtype, int waves, int elem_per_lane, int64_t gri
                             float z, const int32_t *live, hipStream_t stream);
 
 // path 0: 16-byte items (nitems_row = d / elements per 16 bytes),
-// path 1: single elements (nitems_row = d).
-hipError_t launch_silu(int path, int dtype, int per_lane, int64_t grid,
-                       const void *in, void *out, int32_t M, uint32_t nitems_row,
-                       const int32_t *live, hipStream_t stream);
+// path 1: single elements (nitems_row = d).  live may be null (all M rows).
+hipError_t launch_act(int op, int path, int dtype, int per_lane, int64_t grid, const void *in, void *out,
+                      int32_t M, uint32_t nitems_row, const int32_t *live, hipStream_t stream);
 
 hipError_t launch_xor_rows(int64_t grid, const void *in, void *out, int32_t rows,
                            uint32_t nvec_row, hipStream_t stream);

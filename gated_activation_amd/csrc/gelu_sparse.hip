@@ -111,7 +111,7 @@ __global__ __launch_bounds__(WAVES * 64) void gelu_sparse_vec_kernel(
                 E::unpack(gv[k], g);
                 E::unpack(uv[k], u);
 #pragma unroll
-                for (int e = 0; e < PER; ++e) y[e] = gelu_tanh_nonneg(__builtin_fmaxf(g[e] - cut, 0.0f)) * u[e];
+                for (int e = 0; e < PER; ++e) y[e] = gelu_tanh(__builtin_fmaxf(g[e] - cut, 0.0f)) * u[e];
                 st16<NONTEMP>(orow + j, E::pack(y));
             }
         }
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(WAVES * 64) void gelu_sparse_elem_kernel(
     for (int k = 0; k < EPL; ++k) {
         const int i = k * NT + t;
         if (i < d) {
-            const float y = gelu_tanh_nonneg(__builtin_fmaxf(g[k] - cut, 0.0f)) * E::to_f32(urow[i]);
+            const float y = gelu_tanh(__builtin_fmaxf(g[k] - cut, 0.0f)) * E::to_f32(urow[i]);
             orow[i] = E::from_f32(y);
         }
     }

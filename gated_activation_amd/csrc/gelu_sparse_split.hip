@@ -199,7 +199,7 @@ __global__ __launch_bounds__(WAVES * 64) void gelu_sparse_split_kernel(
             E::unpack(gv[k], g);
             E::unpack(uv[k], u);
 #pragma unroll
-            for (int e = 0; e < PER; ++e) y[e] = gelu_tanh_nonneg(__builtin_fmaxf(g[e] - cut, 0.0f)) * u[e];
+            for (int e = 0; e < PER; ++e) y[e] = gelu_tanh(__builtin_fmaxf(g[e] - cut, 0.0f)) * u[e];
             st16<NONTEMP>(orow + v0 + i, E::pack(y));
         }
     }

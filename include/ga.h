@@ -138,6 +138,35 @@ ga_status ga_gelu_and_mul_sparse_ws(const void *in, void *out, int64_t T, int64_
                                     void *workspace, size_t workspace_bytes, ga_stream stream);
 
 /*
+ * GELU-and-multiply without the sparsity step (vLLM PR 48498, section
+ * Purpose: the provider is chosen per "approximation mode"):
+ * out = gelu(gate) * up, gelu in the tanh form (GA_GELU_TANH, the same
+ * constants as above) or the exact form x * Phi(x) (GA_GELU_ERF).
+ *   in [T, 2d], out [T, d]; live_rows NULL for all rows, else a device int32
+ *   bounding the rows written (as for ga_silu_and_mul_bounded).
+ */
+typedef enum { GA_GELU_ERF = 0, GA_GELU_TANH = 1 } ga_gelu_approx;
+ga_status ga_gelu_and_mul(const void *in, void *out, int64_t T, int64_t d, int32_t dtype,
+                          int32_t approximate, const int32_t *live_rows, ga_stream stream);
+
+/*
+ * Bounded squared ReLU, not gated (Megatron-LM PR 6328, section Scope and
+ * risks, names the squared-ReLU activation kernel as sharing the bounded
+ * row pattern): out[r, i] = max(in[r, i], 0)^2 for rows below
+ * clamp(*live_rows, 0, M) of in[M, d]; other rows of out[M, d] untouched.
+ * live_rows is required; the grid depends on M only.
+ */
+ga_status ga_squared_relu_bounded(const void *in, void *out, int64_t M, int64_t d, int32_t dtype,
+                                  const int32_t *live_rows, ga_stream stream);
+
+/*
+ * Host-only helper: z = Phi^-1(target_sparsity), the cutoff multiplier for
+ * a target fraction of zeros (0.95 -> 1.6448536...).  NaN outside (0, 1).
+ * Newton's method on the normal CDF, to full double precision.
+ */
+double ga_z_from_sparsity(double target_sparsity);
+
+/*
  * Host-only planners (no HIP call, usable without a GPU): the geometry the
  * entry points above would launch for these sizes.  `aligned` says whether
  * the 16-byte vector path applies (both base pointers 16-byte aligned and
@@ -146,6 +175,8 @@ ga_status ga_gelu_and_mul_sparse_ws(const void *in, void *out, int64_t T, int64_
  */
 ga_status ga_plan_gelu_and_mul_sparse(int64_t T, int64_t d, int32_t dtype, int32_t aligned,
                                       int32_t num_cus, int32_t with_workspace, ga_plan *plan);
+/* The elementwise ops (silu_and_mul_bounded, gelu_and_mul, squared ReLU)
+ * share one kernel family and this planner; M is the row capacity. */
 ga_status ga_plan_silu_and_mul_bounded(int64_t M, int64_t d, int32_t dtype, int32_t aligned,
                                        int32_t num_cus, ga_plan *plan);
 

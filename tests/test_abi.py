@@ -230,3 +230,42 @@ def test_python_wrapper_rejects_host_tensors():
         ga.gelu_and_mul_sparse(x)
     with pytest.raises(ValueError):
         ga.silu_and_mul_bounded(x, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(approx=2), EINVAL), (dict(approx=-1), EINVAL), (dict(in_=None), EINVAL),
+    (dict(d=0), EINVAL), (dict(d=65537), EUNSUP), (dict(out=IN), EINVAL),
+    (dict(T=0), OK), (dict(T=0, approx=0), OK),
+])
+def test_gelu_and_mul_argument_checks(kwargs, status):
+    a = dict(in_=IN, out=OUT, T=4, d=768, dt=BF16, approx=1, live=None)
+    a.update(kwargs)
+    assert L.ga_gelu_and_mul(a["in_"], a["out"], a["T"], a["d"], a["dt"], a["approx"], a["live"], None) == status
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(live=None), EINVAL), (dict(in_=None), EINVAL), (dict(M=-2), EINVAL),
+    (dict(out=IN), EINVAL),
+    # ungated layout: in is [M, d], so an output right after it does not overlap
+    (dict(out=ctypes.c_void_p(0x7F0000000000 + 16 * 768 * 2), M=0), OK),
+    (dict(M=0), OK),
+])
+def test_squared_relu_argument_checks(kwargs, status):
+    a = dict(in_=IN, out=OUT, M=16, d=768, dt=BF16, live=LIVE)
+    a.update(kwargs)
+    assert L.ga_squared_relu_bounded(a["in_"], a["out"], a["M"], a["d"], a["dt"], a["live"], None) == status
+
+
+def test_z_from_sparsity_against_scipy_and_closed_form():
+    import math
+    from scipy.stats import norm
+    ps = [1e-12, 1e-6, 0.01, 0.05, 0.25, 0.5, 0.75, 0.9, 0.95, 0.99, 0.999, 1 - 1e-9]
+    for p in ps:
+        z = ga.z_from_sparsity(p)
+        assert math.isclose(z, norm.ppf(p), rel_tol=1e-13, abs_tol=1e-15), p
+        assert math.isclose(0.5 * math.erfc(-z / math.sqrt(2.0)), p, rel_tol=1e-12), p   # Phi(z) = p
+        q = 1.0 - p                                   # Phi^-1(q) = -Phi^-1(1 - q)
+        assert math.isclose(ga.z_from_sparsity(q), -ga.z_from_sparsity(1.0 - q), rel_tol=1e-13, abs_tol=1e-15)
+    assert ga.z_from_sparsity(0.95) == pytest.approx(1.6448536269514722, rel=1e-15)
+    for bad in (0.0, 1.0, -0.5, 2.0, float("nan")):
+        assert math.isnan(ga.z_from_sparsity(bad))
