@@ -225,6 +225,7 @@ def main():
         result["graph_replay_us_per_call"] = round(ms_g * 1e3, 3)
 
         result["sweep"] = sweep(dev, stream, props.multi_processor_count)
+        result["siblings"] = siblings(dev, stream)
 
     if args.cpu_seconds > 0:
         result["cpu_baseline"], result["parity_sample"] = cpu_baseline(xb, gelu_out, args.cpu_seconds)
@@ -271,6 +272,48 @@ def sweep(dev, stream, num_cus):
                             f"up_late={plan.up_late}"})
         del xs, outs, ws
     return out
+
+
+def siblings(dev, stream):
+    """The other ops of the family, graph-replayed over rotating buffers:
+    gelu_and_mul (tanh and erf) on the headline shape, and the bounded
+    squared ReLU (not gated: read d, write d per row) on an MoE buffer."""
+    import numpy as np
+    import torch
+    import gated_activation_amd as ga
+    import synth
+    res = {}
+    xb = synth.gelu_large(T, D)
+    x0 = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
+    bytes_call = T * 3 * D * 2
+    n_sets = max(2, math.ceil(ROTATE_BYTES / bytes_call))
+    xs = [x0] + [x0.clone() for _ in range(n_sets - 1)]
+    outs = [torch.empty(T, D, dtype=torch.bfloat16, device=dev) for _ in range(n_sets)]
+    for mode in ("tanh", "none"):
+        def call(i, mode=mode):
+            ga.gelu_and_mul(xs[i], mode, out=outs[i])
+        ms = time_graph(call, n_sets, 256, 10, stream)
+        res[f"gelu_and_mul_{mode}_T{T}_d{D}"] = {
+            "us_per_call": round(ms * 1e3, 3), "GBps": round(bytes_call / (ms * 1e-3) / 1e9, 1),
+            "pct_of_peak": round(100 * bytes_call / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2)}
+    del xs, outs
+    M, d = SILU_M, 2 * SILU_D
+    q0 = torch.from_numpy(synth.moe_buffer(M, SILU_D).view(np.int16)).to(dev).view(torch.bfloat16).view(M, d)
+    q_sets = max(2, math.ceil(ROTATE_BYTES / (M * 2 * d * 2)))
+    qs = [q0] + [q0.clone() for _ in range(q_sets - 1)]
+    qouts = [torch.empty(M, d, dtype=torch.bfloat16, device=dev) for _ in range(q_sets)]
+    live = torch.zeros(1, dtype=torch.int32, device=dev)
+    for n_live in (M, 2048):
+        live.fill_(n_live)
+
+        def call(i):
+            ga.squared_relu_bounded(qs[i], live, out=qouts[i])
+        ms = time_graph(call, q_sets, 640, 10, stream)
+        b = n_live * 2 * d * 2 + 4
+        res[f"squared_relu_bounded_M{M}_d{d}_live{n_live}"] = {
+            "us_per_call": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+            "pct_of_peak": round(100 * b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2)}
+    return res
 
 
 def cpu_baseline(xb, gpu_out, seconds):

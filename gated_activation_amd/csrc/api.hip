@@ -189,21 +189,23 @@ ga_status launch_gelu(const void *in, void *out, int64_t T, int64_t d, int32_t d
 // Flat item count of the live region must fit the kernels' 32-bit indices.
 constexpr int64_t kMaxItems = (int64_t)1 << 31;
 
-// One item (16 bytes, or one element) per lane per step and up to sixteen
-// workgroups per compute unit (measured best on MI355X for the decode
-// buffer); the grid-stride loop covers larger buffers.  The grid depends on
-// the capacity, never on a live count.
+// Items (16 bytes, or one element) per lane per step and workgroups, as
+// measured best on MI355X: one item per lane and up to sixteen workgroups per
+// compute unit up to 2M items (the MoE decode buffer), two items per lane
+// beyond, and up to 32 workgroups per compute unit beyond 4M items.  The
+// grid-stride loop covers the rest.  The grid depends on the capacity, never
+// on a live count.
 ga_plan plan_act(int64_t rows, int64_t d, size_t es, bool aligned, int num_cus) {
     ga_plan p{};
     p.path = (aligned && ((size_t)d * es) % 16 == 0) ? 0 : 1;
-    p.per_lane = 1;
+    const int64_t items = rows * (p.path == 0 ? d * (int64_t)es / 16 : d);
+    p.per_lane = items > ((int64_t)2 << 20) ? 2 : 1;
     p.waves_per_row = 0;
     p.splits = 1;
     p.block = ga::SILU_BLOCK;
-    const int64_t items = rows * (p.path == 0 ? d * (int64_t)es / 16 : d);
     const int64_t per_wg = (int64_t)ga::SILU_BLOCK * p.per_lane;
     int64_t g = (items + per_wg - 1) / per_wg;
-    const int64_t cap = (int64_t)num_cus * 16;
+    const int64_t cap = (int64_t)num_cus * (items > ((int64_t)4 << 20) ? 32 : 16);
     if (g > cap) g = cap;
     if (g < 1) g = 1;
     p.grid = g;
@@ -452,8 +454,9 @@ ga_status ga_stream_xor_rows(const void *in, void *out, int64_t rows, int64_t w_
     int cus = 0;
     ga_status st = current_cus(&cus);
     if (st != GA_OK) return st;
-    int64_t g = (rows * nvec + ga::SILU_BLOCK * 4 - 1) / (ga::SILU_BLOCK * 4);
-    if (g > (int64_t)cus * 8) g = (int64_t)cus * 8;
+    // Two vectors per lane, one pass over the rows (measured fastest).
+    int64_t g = (rows * nvec + ga::SILU_BLOCK * 2 - 1) / (ga::SILU_BLOCK * 2);
+    if (g > (int64_t)cus * 64) g = (int64_t)cus * 64;
     return launched("ga_stream_xor_rows", ga::launch_xor_rows(g, in, out, (int32_t)rows, (uint32_t)nvec,
                                                               static_cast<hipStream_t>(stream)));
 }

@@ -125,7 +125,7 @@ template <bool NONTEMP = true>
 __global__ __launch_bounds__(SILU_BLOCK) void xor_rows_kernel(const uint4 *__restrict__ in,
                                                               uint4 *__restrict__ out, int32_t rows,
                                                               uint32_t nvec) {
-    constexpr int PL = 4;
+    constexpr int PL = 2;
     constexpr uint32_t CHUNK = SILU_BLOCK * PL;
     const uint32_t total = (uint32_t)rows * nvec;
     const uint32_t step = gridDim.x * CHUNK;

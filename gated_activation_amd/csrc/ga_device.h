@@ -183,11 +183,24 @@ __device__ __forceinline__ float gelu_tanh(float s) {
     return s * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-t));
 }
 
-// Exact GELU, x Phi(x) = 0.5 x erfc(-x / sqrt 2): the erfc form has no
-// cancellation for negative x (1 + erf(y) = erfc(-y)).  erfcf is the ROCm
-// device library's.
+// erfc(a) for a >= 0 by Abramowitz & Stegun 7.1.26 (Hastings' rational
+// approximation): erfc(a) = t (c1 + t (c2 + t (c3 + t (c4 + t c5)))) e^(-a^2),
+// t = 1 / (1 + p a), absolute error below 1.5e-7.
+__device__ __forceinline__ float erfc_nonneg(float a) {
+    const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, a, 1.0f));
+    float poly = __builtin_fmaf(1.061405429f, t, -1.453152027f);
+    poly = __builtin_fmaf(poly, t, 1.421413741f);
+    poly = __builtin_fmaf(poly, t, -0.284496736f);
+    poly = __builtin_fmaf(poly, t, 0.254829592f);
+    return poly * t * __builtin_amdgcn_exp2f(-a * a * LOG2_E);
+}
+
+// Exact GELU, x Phi(x) = 0.5 x erfc(-x / sqrt 2).  With a = |x| / sqrt 2:
+// x < 0 gives 0.5 x erfc(a) (no cancellation), x >= 0 gives
+// x (1 - 0.5 erfc(a)) since erfc(-a) = 2 - erfc(a).
 __device__ __forceinline__ float gelu_erf(float x) {
-    return 0.5f * x * erfcf(-x * 0.70710678118654752f);
+    const float c = erfc_nonneg(__builtin_fabsf(x) * 0.70710678118654752f);
+    return x < 0.0f ? 0.5f * x * c : x * __builtin_fmaf(-0.5f, c, 1.0f);
 }
 
 // silu(x) = x / (1 + e^-x); for x << 0 the power overflows to +inf and the

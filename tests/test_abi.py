@@ -205,7 +205,9 @@ def test_silu_planner_depends_on_capacity_only():
     small = ga.plan_silu_and_mul_bounded(4, 768, BF16, num_cus=256)
     assert small.grid == 2          # 4 rows x 96 vectors, 256 per workgroup
     big = ga.plan_silu_and_mul_bounded(1 << 20, 768, BF16, num_cus=256)
-    assert big.grid == 256 * 16
+    assert big.grid == 256 * 32 and big.per_lane == 2     # > 4M items: 2 per lane, 32 per CU
+    mid = ga.plan_silu_and_mul_bounded(16384, 1536, BF16, num_cus=256)
+    assert mid.per_lane == 2 and mid.grid == 256 * 16     # 3.1M items
     assert ga.plan_silu_and_mul_bounded(100, 777, BF16).path == 1
     for M in (1, 7, 64, 1000, 16384):
         for d in (1, 8, 768, 777, 4096):
