@@ -41,6 +41,9 @@ def _load(path=None):
     for name in ("gao_decode_array", "gao_encode_array"):
         getattr(lib, name).restype = None
         getattr(lib, name).argtypes = [vp, i64, ctypes.c_int, vp]
+    lib.gao_gelu_and_mul_sparse_rt.restype = ctypes.c_int
+    lib.gao_gelu_and_mul_sparse_rt.argtypes = [vp, vp, i64, i64, ctypes.c_int, ctypes.c_float, i64,
+                                               vp, vp, vp, vp]
     lib.gao_gelu_and_mul.restype = ctypes.c_int
     lib.gao_gelu_and_mul.argtypes = [vp, vp, i64, i64, ctypes.c_int, ctypes.c_int, i64, vp]
     lib.gao_squared_relu_bounded.restype = ctypes.c_int
@@ -127,6 +130,27 @@ class Oracle:
         if want_stats:
             res.append(stats)
         return res[0] if len(res) == 1 else tuple(res)
+
+    def gelu_and_mul_sparse_rt(self, x_bits, dtype, z, live=None, out=None, cut=None):
+        """Round-trip form (intermediates rounded to the element type).
+        Returns (out bits, stats[3, T]) with stats = exact mean, exact std,
+        rounded cutoff used; `cut` (per-row, element-type values) overrides
+        the computed cutoffs."""
+        x = np.ascontiguousarray(x_bits, dtype=BITS_DTYPE[dtype])
+        T, two_d = x.shape
+        d = two_d // 2
+        assert two_d == 2 * d and d >= 1
+        live = T if live is None else int(live)
+        y = np.zeros((T, d), BITS_DTYPE[dtype]) if out is None else np.array(out, copy=True)
+        stats = np.full((3, T), np.nan)
+        cut_arr = None if cut is None else np.ascontiguousarray(cut, dtype=np.float64)
+        rc = self.lib.gao_gelu_and_mul_sparse_rt(
+            x.ctypes.data, y.ctypes.data, T, d, dtype, float(z), live,
+            None if cut_arr is None else cut_arr.ctypes.data,
+            stats[0].ctypes.data, stats[1].ctypes.data, stats[2].ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return y, stats
 
     def silu_and_mul_bounded(self, x_bits, dtype, live, out=None, want_f64=False):
         x = np.ascontiguousarray(x_bits, dtype=BITS_DTYPE[dtype])

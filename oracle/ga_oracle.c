@@ -212,6 +212,62 @@ int gao_gelu_and_mul_sparse(const void *in, void *out, int64_t T, int64_t d,
     return 0;
 }
 
+/* Round a double to the element type and back (the value a tensor of that
+ * type would hold). */
+static double round_to(double v, int dtype)
+{
+    return gao_decode(gao_encode_rne(v, dtype), dtype);
+}
+
+/* Sparse GELU-and-multiply in "round-trip" form: the native composition of
+ * the op keeps every intermediate tensor in the input type (vLLM PR 48498,
+ * Test Result, "Cross-architecture warp and dtype validation": the Triton
+ * kernel rounds intermediates to reproduce native PyTorch's rounding at
+ * operation boundaries).  Reading taken: each of mean, std, z, z * std,
+ * cutoff = mean + z * std, gate - cutoff, gelu_tanh(.) and the product is
+ * rounded to the element type; each step is computed exactly (in double)
+ * from already-rounded operands.  cut_in (may be NULL): per-row cutoffs to
+ * use instead of computing them (already in the element type).
+ * Optional outputs: row_mean / row_std (exact, before rounding), row_cut
+ * (the rounded cutoff used). */
+int gao_gelu_and_mul_sparse_rt(const void *in, void *out, int64_t T, int64_t d, int dtype, float z,
+                               int64_t live, const double *cut_in, double *row_mean, double *row_std,
+                               double *row_cut)
+{
+    if (!in || !out || T < 0 || d < 1 || !gao_elem_size(dtype)) return -1;
+    const int64_t n = clamp_live(live, T);
+    double *g = (double *)malloc(sizeof(double) * (size_t)d);
+    if (!g) return -1;
+    for (int64_t r = 0; r < n; ++r) {
+        const int64_t row = r * 2 * d;
+        for (int64_t i = 0; i < d; ++i) g[i] = load_elem(in, row + i, dtype);
+        double mean, std;
+        gao_row_stats(g, d, &mean, &std);
+        double cut;
+        if (cut_in) {
+            cut = cut_in[r];
+        } else {
+            const double mean_t = round_to(mean, dtype);
+            const double std_t = round_to(std, dtype);
+            const double z_t = round_to((double)z, dtype);
+            const double zs_t = round_to(z_t * std_t, dtype);
+            cut = round_to(mean_t + zs_t, dtype);
+        }
+        if (row_mean) row_mean[r] = mean;
+        if (row_std) row_std[r] = std;
+        if (row_cut) row_cut[r] = cut;
+        for (int64_t i = 0; i < d; ++i) {
+            double s = round_to(g[i] - cut, dtype);
+            if (!(s > 0.0)) s = 0.0;                 /* relu */
+            const double h = round_to(gao_gelu_tanh(s), dtype);
+            const double up = load_elem(in, row + d + i, dtype);
+            store_elem(out, r * d + i, dtype, h * up);
+        }
+    }
+    free(g);
+    return 0;
+}
+
 /* Bounded SiLU-and-multiply: rows [0, clamp(live, 0, M)) of in[M, 2d] give
  * out[r, i] = silu(gate) * up; rows beyond the live count are not written. */
 int gao_silu_and_mul_bounded(const void *in, void *out, int64_t M, int64_t d,

@@ -438,8 +438,57 @@ def pin_squared_relu_bounded(o):
             assert np.all(y[n:] == synth.SENTINEL[dt])
 
 
+def _torch_eager_sparse(x_bits, d, dtype, z):
+    """The op as native torch composes it on tensors of the element type:
+    every intermediate tensor holds that type."""
+    tdt = {BF16: torch.bfloat16, F16: torch.float16, F32: torch.float32}[dtype]
+    view = np.int32 if dtype == F32 else np.int16
+    xt = torch.from_numpy(np.ascontiguousarray(x_bits).view(view)).view(tdt)
+    g, u = xt[:, :d], xt[:, d:]
+    mean = g.mean(-1, keepdim=True)
+    std = g.std(-1, keepdim=True, correction=0)
+    cut = mean + std * torch.tensor(z, dtype=torch.float32).to(tdt)
+    y = torch.nn.functional.gelu(torch.relu(g - cut), approximate="tanh") * u
+    bits = y.contiguous().view(torch.int32 if dtype == F32 else torch.int16).numpy()
+    return bits.view(np.uint32 if dtype == F32 else np.uint16), cut.float().numpy()[:, 0]
+
+
+def pin_gelu_sparse_roundtrip(o):
+    """Round-trip form against torch's eager composition in the element type
+    (torch rounds every op's result to the tensor type)."""
+    cases = [(BF16, synth.gelu_offset_rows(48, 2048, seed=71), 2048, Z95),
+             (F16, synth.gelu_iid(32, 4096, seed=72, dtype=F16, gate_std=1.5), 4096, Z99),
+             (BF16, synth.edge_rows(15, 3000, BF16, seed=73), 3000, 0.0),
+             (F16, synth.edge_rows(15, 2000, F16, seed=74), 2000, Z95),
+             (F32, synth.gelu_iid(8, 1024, seed=75, dtype=F32), 1024, Z95)]
+    for dt, x, d, z in cases:
+        y, st = o.gelu_and_mul_sparse_rt(x, dt, z)
+        ref, cut = _torch_eager_sparse(x, d, dt, z)
+        if dt == F32:
+            # torch's fp32 statistics and tanh are not correctly rounded: the
+            # cutoffs agree to an ulp or so and the outputs to ~1e-7.
+            assert np.allclose(cut, st[2], rtol=1e-6, atol=1e-6)
+            assert np.allclose(o.decode(y, dt), o.decode(ref, dt), rtol=1e-5, atol=1e-6)
+            continue
+        assert np.array_equal(cut, st[2]), (dt, d)
+        assert (y == ref).mean() > 0.9999, (dt, d, (y == ref).mean())
+        yd, rd = o.decode(y, dt), o.decode(ref, dt)
+        ulp = np.abs(rd) * 2.0 ** -(8 if dt == BF16 else 11) + 2.0 ** -24
+        assert np.all(np.abs(yd - rd) <= 2 * ulp)
+    # The rounded multiplier moves the cutoff: bf16 holds z = 1.6448536 as
+    # 1.6484375, so the round-trip result differs from the one-rounding form.
+    x = synth.gelu_iid(16, 2048, seed=76)
+    assert not np.array_equal(o.gelu_and_mul_sparse_rt(x, BF16, Z95)[0], o.gelu_and_mul_sparse(x, BF16, Z95))
+    assert float(o.decode(o.encode(np.array([Z95]), BF16), BF16)[0]) == 1.6484375
+    # A supplied cutoff replaces the computed one.
+    y1, st1 = o.gelu_and_mul_sparse_rt(x, BF16, Z95)
+    y2, st2 = o.gelu_and_mul_sparse_rt(x, BF16, 0.0, cut=st1[2])
+    assert np.array_equal(y1, y2) and np.array_equal(st1[2], st2[2])
+
+
 ALL_PINS = [pin_decode, pin_encode_fp32, pin_encode_fp16, pin_encode_bf16,
             pin_roundtrip, pin_gelu, pin_silu, pin_row_stats,
             pin_gelu_sparse_composition, pin_gelu_sparse_invariants,
             pin_survival_fraction, pin_brute_force_1x8, pin_silu_bounded,
-            pin_gelu_erf, pin_squared_relu, pin_gelu_and_mul, pin_squared_relu_bounded]
+            pin_gelu_erf, pin_squared_relu, pin_gelu_and_mul, pin_squared_relu_bounded,
+            pin_gelu_sparse_roundtrip]

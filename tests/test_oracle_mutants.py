@@ -46,6 +46,14 @@ MUTANTS = {
     "silu_sign": ("x / (1.0 + exp(-x))", "x / (1.0 + exp(x))"),
     "silu_operands_swapped": ("gao_silu(gate) * up", "gao_silu(up) * gate"),
     "silu_ignores_live": ("const int64_t n = clamp_live(live, M);", "const int64_t n = M;"),
+    "roundtrip_z_not_rounded": ("const double z_t = round_to((double)z, dtype);",
+                                "const double z_t = (double)z;"),
+    "roundtrip_shift_not_rounded": ("double s = round_to(g[i] - cut, dtype);", "double s = g[i] - cut;"),
+    "roundtrip_gelu_not_rounded": ("const double h = round_to(gao_gelu_tanh(s), dtype);",
+                                   "const double h = gao_gelu_tanh(s);"),
+    "roundtrip_mean_not_rounded": ("const double mean_t = round_to(mean, dtype);", "const double mean_t = mean;"),
+    "roundtrip_sample_std": ("const double std_t = round_to(std, dtype);",
+                             "const double std_t = round_to(std * sqrt((double)d / (double)(d > 1 ? d - 1 : 1)), dtype);"),
     "erf_argument_unscaled": ("erf(x / sqrt(2.0))", "erf(x / 2.0)"),
     "erf_gelu_half_dropped": ("return 0.5 * x * (1.0 + erf", "return x * (1.0 + erf"),
     "squared_relu_not_squared": ("return r * r;", "return r;"),
