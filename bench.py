@@ -276,7 +276,8 @@ def sweep(dev, stream, num_cus):
 
 def siblings(dev, stream):
     """The other ops of the family, graph-replayed over rotating buffers:
-    gelu_and_mul (tanh and erf) on the headline shape, and the bounded
+    gelu_and_mul (tanh and erf) and the round-trip form of
+    gelu_and_mul_sparse on the headline shape, and the bounded
     squared ReLU (not gated: read d, write d per row) on an MoE buffer."""
     import numpy as np
     import torch
@@ -296,6 +297,14 @@ def siblings(dev, stream):
         res[f"gelu_and_mul_{mode}_T{T}_d{D}"] = {
             "us_per_call": round(ms * 1e3, 3), "GBps": round(bytes_call / (ms * 1e-3) / 1e9, 1),
             "pct_of_peak": round(100 * bytes_call / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2)}
+
+    # The round-trip form of the headline op (intermediates rounded to bf16).
+    def call(i):
+        ga.gelu_and_mul_sparse(xs[i], Z, out=outs[i], round_intermediates=True)
+    ms = time_graph(call, n_sets, 256, 10, stream)
+    res[f"gelu_and_mul_sparse_round_trip_T{T}_d{D}"] = {
+        "us_per_call": round(ms * 1e3, 3), "GBps": round(bytes_call / (ms * 1e-3) / 1e9, 1),
+        "pct_of_peak": round(100 * bytes_call / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2)}
     del xs, outs
     M, d = SILU_M, 2 * SILU_D
     q0 = torch.from_numpy(synth.moe_buffer(M, SILU_D).view(np.int16)).to(dev).view(torch.bfloat16).view(M, d)

@@ -6,14 +6,15 @@ stream through the C-ABI.  Every step of the computation runs in the HIP
 kernels; PyTorch only supplies device memory and the stream.  If the library
 is not built, importing this package raises: there is no fallback.
 
-    gelu_and_mul_sparse(x, z)           x: [T, 2d] -> [T, d]
+    gelu_and_mul_sparse(x, z)           x: [T, 2d] -> [T, d] (round_intermediates=True:
+                                        the round-trip form)
     silu_and_mul_bounded(x, live_rows)  x: [M, 2d] -> [M, d] (live rows only)
     gelu_and_mul(x, approximate)        x: [T, 2d] -> [T, d] (tanh or erf GELU)
     squared_relu_bounded(x, live_rows)  x: [M, d]  -> [M, d] (live rows only)
     z_from_sparsity(p)                  Phi^-1(p), host-side
 """
 from ._lib import (  # noqa: F401
-    GA_BF16, GA_F16, GA_F32, GA_OK, GA_EINVAL, GA_EUNSUPPORTED, GA_EHIP, GA_MAX_D,
+    GA_BF16, GA_F16, GA_F32, GA_OK, GA_EINVAL, GA_EUNSUPPORTED, GA_EHIP, GA_MAX_D, GA_ROUND_INTERMEDIATES,
     GaError, Plan, Z_SPARSITY_095, lib, library_path,
     gelu_and_mul_sparse, silu_and_mul_bounded, stream_xor_rows,
     gelu_and_mul, squared_relu_bounded, z_from_sparsity,

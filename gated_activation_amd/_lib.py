@@ -10,6 +10,7 @@ library_path = os.path.join(HERE, "libga.so")
 GA_F32, GA_F16, GA_BF16 = 0, 1, 2
 GA_OK, GA_EINVAL, GA_EUNSUPPORTED, GA_EHIP = 0, 1, 2, 3
 GA_MAX_D = 65536
+GA_ROUND_INTERMEDIATES = 1
 # Phi^-1(0.95): the cutoff multiplier for a target sparsity of 95%.
 Z_SPARSITY_095 = 1.6448536
 
@@ -21,7 +22,7 @@ class Plan(ctypes.Structure):
                 ("per_lane", ctypes.c_int32), ("up_late", ctypes.c_int32),
                 ("block", ctypes.c_int32), ("splits", ctypes.c_int32),
                 ("grid", ctypes.c_int64), ("spin_limit", ctypes.c_uint32),
-                ("reserved", ctypes.c_int32)]
+                ("flags", ctypes.c_int32)]
 
     def __init__(self, **kw):
         kw.setdefault("splits", 1)
@@ -52,6 +53,7 @@ def _load():
         "ga_gelu_and_mul_sparse_with_plan": [vp, vp, i64, i64, i32, ctypes.c_float, vp, pplan, vp,
                                              ctypes.c_size_t, vp],
         "ga_gelu_and_mul_sparse_ws": [vp, vp, i64, i64, i32, ctypes.c_float, vp, vp, ctypes.c_size_t, vp],
+        "ga_gelu_and_mul_sparse_ex": [vp, vp, i64, i64, i32, ctypes.c_float, vp, i32, vp, ctypes.c_size_t, vp],
         "ga_silu_and_mul_bounded_with_plan": [vp, vp, i64, i64, i32, vp, pplan, vp],
         "ga_plan_gelu_and_mul_sparse": [i64, i64, i32, i32, i32, i32, pplan],
         "ga_plan_silu_and_mul_bounded": [i64, i64, i32, i32, i32, pplan],
@@ -134,15 +136,27 @@ def workspace_for(x, T):
     return ws
 
 
-def gelu_and_mul_sparse(x, z=Z_SPARSITY_095, out=None, live_rows=None, plan=None, workspace=None):
+def gelu_and_mul_sparse(x, z=Z_SPARSITY_095, out=None, live_rows=None, plan=None, workspace=None,
+                        round_intermediates=False):
     """Sparse GELU-and-multiply of x = [gate | up] ([T, 2d]) -> [T, d].
     z = Phi^-1(target sparsity); live_rows (optional int32 device tensor)
-    limits the rows written; plan (optional Plan) forces a launch geometry.
-    workspace: None = the cached per-stream workspace (lets few rows split
-    over several workgroups), False = none, or a zero-filled uint8 tensor."""
+    limits the rows written; plan (optional Plan) forces a launch geometry
+    (its `flags` then select the form).  workspace: None = the cached
+    per-stream workspace (lets few rows split over several workgroups),
+    False = none, or a zero-filled uint8 tensor.  round_intermediates: the
+    round-trip form, which rounds each intermediate to the input dtype as an
+    eager PyTorch composition does (never split, no workspace)."""
     T, d, out = _prep(x, out, "gelu_and_mul_sparse")
     live = _live_ptr(live_rows, x, "gelu_and_mul_sparse")
     with torch.cuda.device(x.device):
+        if round_intermediates:
+            if plan is not None:
+                raise ValueError("gelu_and_mul_sparse: pass round_intermediates through plan.flags")
+            _check(lib.ga_gelu_and_mul_sparse_ex(
+                ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(out.data_ptr()), T, d,
+                _TORCH_DTYPE[x.dtype], ctypes.c_float(z), live, GA_ROUND_INTERMEDIATES, None, 0,
+                _stream_of(x)))
+            return out
         if workspace is None:
             workspace = workspace_for(x, T) if T > 0 else None
         elif workspace is False:

@@ -122,6 +122,10 @@ void pick_waves(int64_t nvec, int max_v, int *w_out, int *v_out) {
 }
 
 ga_status check_gelu_plan(const ga_plan *p, int64_t T, int64_t d, int32_t dtype) {
+    if ((p->flags & ~GA_ROUND_INTERMEDIATES) != 0)
+        return fail(GA_EINVAL, "gelu plan: unknown flag bits 0x%x", (unsigned)p->flags);
+    if ((p->flags & GA_ROUND_INTERMEDIATES) && p->splits != 1)
+        return fail(GA_EUNSUPPORTED, "gelu plan: the round-trip form does not split rows");
     if (p->path == 0) {
         const int64_t per16 = 16 / (int64_t)elem_size(dtype);
         const int64_t nvec = (d + per16 - 1) / per16;
@@ -170,16 +174,17 @@ ga_status launch_gelu(const void *in, void *out, int64_t T, int64_t d, int32_t d
                       const int32_t *live, const ga_plan &p, void *workspace, ga_stream stream) {
     const char *name = "ga_gelu_and_mul_sparse";
     const hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool rt = (p.flags & GA_ROUND_INTERMEDIATES) != 0;
     if (p.path == 0) {
         const int32_t nvec = (int32_t)(d * (int64_t)elem_size(dtype) / 16);
         if (p.splits > 1)
             return launched(name, ga::launch_gelu_split(dtype, p.waves_per_row, p.per_lane, p.splits, in, out,
                                                         (int32_t)T, (int32_t)d, nvec, z, live, workspace,
                                                         p.spin_limit, s));
-        return launched(name, ga::launch_gelu_vec(dtype, p.waves_per_row, p.per_lane, p.up_late, T, in, out,
+        return launched(name, ga::launch_gelu_vec(dtype, p.waves_per_row, p.per_lane, p.up_late, rt, T, in, out,
                                                   (int32_t)T, (int32_t)d, nvec, z, live, s));
     }
-    return launched(name, ga::launch_gelu_elem(dtype, p.waves_per_row, p.per_lane, T, in, out, (int32_t)T,
+    return launched(name, ga::launch_gelu_elem(dtype, p.waves_per_row, p.per_lane, rt, T, in, out, (int32_t)T,
                                                (int32_t)d, z, live, s));
 }
 
@@ -213,6 +218,7 @@ ga_plan plan_act(int64_t rows, int64_t d, size_t es, bool aligned, int num_cus) 
 }
 
 ga_status check_act_plan(const ga_plan *p, int op, int64_t rows, int64_t d, int32_t dtype) {
+    if (p->flags != 0) return fail(GA_EINVAL, "plan: flags must be zero for this op");
     if (!ga::act_available(op, p->path, dtype, p->per_lane))
         return fail(GA_EUNSUPPORTED, "plan: no kernel for path=%d per_lane=%d", p->path, p->per_lane);
     if (p->grid < 1 || p->grid > INT32_MAX) return fail(GA_EINVAL, "plan: grid %lld", (long long)p->grid);
@@ -353,14 +359,18 @@ ga_status ga_gelu_and_mul_sparse_with_plan(const void *in, void *out, int64_t T,
     return launch_gelu(in, out, T, d, dtype, z, live_rows, *plan, workspace, stream);
 }
 
-ga_status ga_gelu_and_mul_sparse_ws(const void *in, void *out, int64_t T, int64_t d, int32_t dtype, float z,
-                                    const int32_t *live_rows, void *workspace, size_t workspace_bytes,
-                                    ga_stream stream) {
+ga_status ga_gelu_and_mul_sparse_ex(const void *in, void *out, int64_t T, int64_t d, int32_t dtype, float z,
+                                    const int32_t *live_rows, int32_t flags, void *workspace,
+                                    size_t workspace_bytes, ga_stream stream) {
     ga_status st = check_rows("ga_gelu_and_mul_sparse", in, out, T, d, dtype);
     if (st != GA_OK) return st;
     if (!std::isfinite(z)) return fail(GA_EINVAL, "ga_gelu_and_mul_sparse: z is not finite");
+    if ((flags & ~GA_ROUND_INTERMEDIATES) != 0)
+        return fail(GA_EINVAL, "ga_gelu_and_mul_sparse: unknown flag bits 0x%x", (unsigned)flags);
     if (T == 0) return GA_OK;
-    const bool have_ws = workspace != nullptr && (uintptr_t)workspace % 256 == 0 && T <= kSplitMaxRows &&
+    // The round-trip form has no split-row kernel.
+    const bool have_ws = !(flags & GA_ROUND_INTERMEDIATES) && workspace != nullptr &&
+                         (uintptr_t)workspace % 256 == 0 && T <= kSplitMaxRows &&
                          workspace_bytes >= ga::split_workspace_bytes(T);
     int cus = 256;
     if (have_ws && (st = current_cus(&cus)) != GA_OK) return st;
@@ -368,7 +378,14 @@ ga_status ga_gelu_and_mul_sparse_ws(const void *in, void *out, int64_t T, int64_
     if ((st = ga_plan_gelu_and_mul_sparse(T, d, dtype, vector_aligned(in, out, d, dtype), cus, have_ws, &p)) !=
         GA_OK)
         return st;
+    p.flags = flags;
     return launch_gelu(in, out, T, d, dtype, z, live_rows, p, workspace, stream);
+}
+
+ga_status ga_gelu_and_mul_sparse_ws(const void *in, void *out, int64_t T, int64_t d, int32_t dtype, float z,
+                                    const int32_t *live_rows, void *workspace, size_t workspace_bytes,
+                                    ga_stream stream) {
+    return ga_gelu_and_mul_sparse_ex(in, out, T, d, dtype, z, live_rows, 0, workspace, workspace_bytes, stream);
 }
 
 ga_status ga_gelu_and_mul_sparse(const void *in, void *out, int64_t T, int64_t d, int32_t dtype, float z,

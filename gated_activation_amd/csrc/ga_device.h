@@ -62,6 +62,8 @@ template <> struct Elem<DT_F32> {
     }
     static __device__ __forceinline__ float to_f32(storage s) { return __builtin_bit_cast(float, s); }
     static __device__ __forceinline__ storage from_f32(float f) { return __builtin_bit_cast(uint32_t, f); }
+    // The value an fp32 tensor holds: the number itself.
+    static __device__ __forceinline__ float round(float f) { return f; }
 };
 
 template <> struct Elem<DT_BF16> {
@@ -89,6 +91,10 @@ template <> struct Elem<DT_BF16> {
     }
     static __device__ __forceinline__ storage from_f32(float f) {
         return (storage)(pack2(f, 0.0f) & 0xFFFFu);
+    }
+    // The value a bf16 tensor would hold: round to nearest even and widen.
+    static __device__ __forceinline__ float round(float f) {
+        return __builtin_bit_cast(float, pack2(f, 0.0f) << 16);
     }
 };
 
@@ -118,6 +124,8 @@ template <> struct Elem<DT_F16> {
     static __device__ __forceinline__ storage from_f32(float f) {
         return (storage)(pack2(f, 0.0f) & 0xFFFFu);
     }
+    // The value an fp16 tensor would hold: round to nearest even and widen.
+    static __device__ __forceinline__ float round(float f) { return (float)(_Float16)f; }
 };
 
 // ---------------------------------------------------------------------------
@@ -208,6 +216,35 @@ __device__ __forceinline__ float gelu_erf(float x) {
 __device__ __forceinline__ float silu(float x) {
     const float e = __builtin_amdgcn_exp2f(-x * LOG2_E);
     return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// The cutoff from the row's fp32 mean and variance.  RT (round-trip form):
+// every intermediate is rounded to the element type as a tensor of that type
+// would hold it -- mean, std, z, z * std, mean + z * std.  Contraction is off
+// there: the compiler narrows these fp16 steps to half precision and would
+// otherwise fuse z * std + mean into one fma, dropping a rounding.
+template <typename E, bool RT>
+__device__ __forceinline__ float sparse_cutoff(float mean, float var, float z) {
+    if constexpr (RT) {
+#pragma clang fp contract(off)
+        const float zs = E::round(E::round(z) * E::round(__builtin_sqrtf(var)));
+        return E::round(E::round(mean) + zs);
+    } else {
+        return __builtin_fmaf(z, __builtin_sqrtf(var), mean);
+    }
+}
+
+// gelu_tanh(relu(g - cut)) * up; RT rounds g - cut and the GELU output to the
+// element type (the final rounding is the store's).
+template <typename E, bool RT>
+__device__ __forceinline__ float sparse_apply(float g, float cut, float up) {
+    if constexpr (RT) {
+#pragma clang fp contract(off)
+        const float s = __builtin_fmaxf(E::round(g - cut), 0.0f);
+        return E::round(gelu_tanh(s)) * up;
+    } else {
+        return gelu_tanh(__builtin_fmaxf(g - cut, 0.0f)) * up;
+    }
 }
 
 __device__ __forceinline__ int32_t clamp_live(const int32_t *live, int32_t rows) {

@@ -29,11 +29,13 @@ hipError_t launch_gelu_split(int dtype, int waves, int vec_per_lane, int splits,
                              int32_t T, int32_t d, int32_t nvec, float z, const int32_t *live, void *workspace,
                              uint32_t spin_limit, hipStream_t stream);
 
-hipError_t launch_gelu_vec(int dtype, int waves, int vec_per_lane, int up_late, int64_t grid,
+// round_trip selects the form that rounds each intermediate (mean, std, z,
+// z * std, cutoff, gate - cutoff, GELU output) to the element type.
+hipError_t launch_gelu_vec(int dtype, int waves, int vec_per_lane, int up_late, bool round_trip, int64_t grid,
                            const void *in, void *out, int32_t T, int32_t d, int32_t nvec,
                            float z, const int32_t *live, hipStream_t stream);
 
-hipError_t launch_gelu_elem(int dtype, int waves, int elem_per_lane, int64_t grid,
+hipError_t launch_gelu_elem(int dtype, int waves, int elem_per_lane, bool round_trip, int64_t grid,
                             const void *in, void *out, int32_t T, int32_t d,
                             float z, const int32_t *live, hipStream_t stream);
 

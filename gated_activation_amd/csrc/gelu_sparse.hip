@@ -25,7 +25,8 @@ namespace ga {
 // during both reductions), 1 = after the statistics, all vectors at once,
 // 2 = after the statistics, UPCHUNK vectors at a time (fewer registers, so
 // more rows resident per compute unit).
-template <int DT, int WAVES, int VPL, bool NONTEMP = true, int UP = 0, int UPCHUNK = 2>
+// RT: round-trip form (intermediates rounded to the element type).
+template <int DT, int WAVES, int VPL, bool NONTEMP = true, int UP = 0, int UPCHUNK = 2, bool RT = false>
 __global__ __launch_bounds__(WAVES * 64) void gelu_sparse_vec_kernel(
     const uint4 *__restrict__ in, uint4 *__restrict__ out, int32_t T, int32_t d, int32_t nvec,
     float z, const int32_t *__restrict__ live) {
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(WAVES * 64) void gelu_sparse_vec_kernel(
         }
     }
     const float var = block_sum<WAVES>(q, red[1]) / (float)d;
-    const float cut = __builtin_fmaf(z, __builtin_sqrtf(var), mean);
+    const float cut = sparse_cutoff<E, RT>(mean, var, z);
 
     if constexpr (UP == 1) {
 #pragma unroll
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(WAVES * 64) void gelu_sparse_vec_kernel(
                 E::unpack(gv[k], g);
                 E::unpack(uv[k], u);
 #pragma unroll
-                for (int e = 0; e < PER; ++e) y[e] = gelu_tanh(__builtin_fmaxf(g[e] - cut, 0.0f)) * u[e];
+                for (int e = 0; e < PER; ++e) y[e] = sparse_apply<E, RT>(g[e], cut, u[e]);
                 st16<NONTEMP>(orow + j, E::pack(y));
             }
         }
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(WAVES * 64) void gelu_sparse_vec_kernel(
 // Element path: any d and any alignment natural to the type.  Lane t holds
 // elements t, t + NT, ... of the gate row as fp32; up is read in the apply
 // loop.
-template <int DT, int WAVES, int EPL>
+template <int DT, int WAVES, int EPL, bool RT = false>
 __global__ __launch_bounds__(WAVES * 64) void gelu_sparse_elem_kernel(
     const typename Elem<DT>::storage *__restrict__ in, typename Elem<DT>::storage *__restrict__ out,
     int32_t T, int32_t d, float z, const int32_t *__restrict__ live) {
@@ -157,13 +158,13 @@ __global__ __launch_bounds__(WAVES * 64) void gelu_sparse_elem_kernel(
         }
     }
     const float var = block_sum<WAVES>(q, red[1]) / (float)d;
-    const float cut = __builtin_fmaf(z, __builtin_sqrtf(var), mean);
+    const float cut = sparse_cutoff<E, RT>(mean, var, z);
 
 #pragma unroll
     for (int k = 0; k < EPL; ++k) {
         const int i = k * NT + t;
         if (i < d) {
-            const float y = gelu_tanh(__builtin_fmaxf(g[k] - cut, 0.0f)) * E::to_f32(urow[i]);
+            const float y = sparse_apply<E, RT>(g[k], cut, E::to_f32(urow[i]));
             orow[i] = E::from_f32(y);
         }
     }
@@ -177,23 +178,28 @@ namespace {
 
 using GeluVecFn = void (*)(const uint4 *, uint4 *, int32_t, int32_t, int32_t, float, const int32_t *);
 
-// Index [dtype][up_late][log2 waves][log2 vectors per lane]; late up loads go
-// one vector at a time.
-#define GA_GV(DT, U, W) \
-    { &gelu_sparse_vec_kernel<DT, W, 1, true, U, 1>, &gelu_sparse_vec_kernel<DT, W, 2, true, U, 1>, \
-      &gelu_sparse_vec_kernel<DT, W, 4, true, U, 1>, &gelu_sparse_vec_kernel<DT, W, 8, true, U, 1> }
-#define GA_GVU(DT, U) { GA_GV(DT, U, 1), GA_GV(DT, U, 2), GA_GV(DT, U, 4), GA_GV(DT, U, 8), GA_GV(DT, U, 16) }
-#define GA_GVD(DT) { GA_GVU(DT, 0), GA_GVU(DT, 2) }
-const GeluVecFn kGeluVec[3][2][5][4] = {GA_GVD(DT_F32), GA_GVD(DT_F16), GA_GVD(DT_BF16)};
+// Index [round trip][dtype][up_late][log2 waves][log2 vectors per lane]; late
+// up loads go one vector at a time.
+#define GA_GV(RT, DT, U, W)                                                                            \
+    { &gelu_sparse_vec_kernel<DT, W, 1, true, U, 1, RT>, &gelu_sparse_vec_kernel<DT, W, 2, true, U, 1, RT>, \
+      &gelu_sparse_vec_kernel<DT, W, 4, true, U, 1, RT>, &gelu_sparse_vec_kernel<DT, W, 8, true, U, 1, RT> }
+#define GA_GVU(RT, DT, U) \
+    { GA_GV(RT, DT, U, 1), GA_GV(RT, DT, U, 2), GA_GV(RT, DT, U, 4), GA_GV(RT, DT, U, 8), GA_GV(RT, DT, U, 16) }
+#define GA_GVD(RT, DT) { GA_GVU(RT, DT, 0), GA_GVU(RT, DT, 2) }
+const GeluVecFn kGeluVec[2][3][2][5][4] = {
+    {GA_GVD(false, DT_F32), GA_GVD(false, DT_F16), GA_GVD(false, DT_BF16)},
+    {GA_GVD(true, DT_F32), GA_GVD(true, DT_F16), GA_GVD(true, DT_BF16)}};
 #undef GA_GV
 #undef GA_GVU
 #undef GA_GVD
 
-#define GA_GE(DT, W) \
-    { (const void *)&gelu_sparse_elem_kernel<DT, W, 4>, (const void *)&gelu_sparse_elem_kernel<DT, W, 16>, \
-      (const void *)&gelu_sparse_elem_kernel<DT, W, 64> }
-#define GA_GED(DT) { GA_GE(DT, 1), GA_GE(DT, 4), GA_GE(DT, 16) }
-const void *const kGeluElem[3][3][3] = {GA_GED(DT_F32), GA_GED(DT_F16), GA_GED(DT_BF16)};
+#define GA_GE(RT, DT, W)                                                                           \
+    { (const void *)&gelu_sparse_elem_kernel<DT, W, 4, RT>, (const void *)&gelu_sparse_elem_kernel<DT, W, 16, RT>, \
+      (const void *)&gelu_sparse_elem_kernel<DT, W, 64, RT> }
+#define GA_GED(RT, DT) { GA_GE(RT, DT, 1), GA_GE(RT, DT, 4), GA_GE(RT, DT, 16) }
+const void *const kGeluElem[2][3][3][3] = {
+    {GA_GED(false, DT_F32), GA_GED(false, DT_F16), GA_GED(false, DT_BF16)},
+    {GA_GED(true, DT_F32), GA_GED(true, DT_F16), GA_GED(true, DT_BF16)}};
 #undef GA_GE
 #undef GA_GED
 
@@ -229,25 +235,25 @@ bool gelu_elem_available(int dtype, int waves, int epl) {
     return dtype >= 0 && dtype <= 2 && elem_index(waves, epl, &wi, &ei) == 0;
 }
 
-hipError_t launch_gelu_vec(int dtype, int waves, int vpl, int up_late, int64_t grid, const void *in,
-                           void *out, int32_t T, int32_t d, int32_t nvec, float z, const int32_t *live,
-                           hipStream_t stream) {
+hipError_t launch_gelu_vec(int dtype, int waves, int vpl, int up_late, bool round_trip, int64_t grid,
+                           const void *in, void *out, int32_t T, int32_t d, int32_t nvec, float z,
+                           const int32_t *live, hipStream_t stream) {
     int wi, vi;
     if (!gelu_vec_available(dtype, waves, vpl, up_late) || vec_index(waves, vpl, &wi, &vi) != 0)
         return hipErrorInvalidValue;
-    const GeluVecFn fn = kGeluVec[dtype][up_late][wi][vi];
+    const GeluVecFn fn = kGeluVec[round_trip ? 1 : 0][dtype][up_late][wi][vi];
     const uint4 *a_in = static_cast<const uint4 *>(in);
     uint4 *a_out = static_cast<uint4 *>(out);
     void *args[] = {&a_in, &a_out, &T, &d, &nvec, &z, &live};
     return hipLaunchKernel((const void *)fn, dim3((uint32_t)grid), dim3(waves * 64), args, 0, stream);
 }
 
-hipError_t launch_gelu_elem(int dtype, int waves, int epl, int64_t grid, const void *in, void *out,
-                            int32_t T, int32_t d, float z, const int32_t *live, hipStream_t stream) {
+hipError_t launch_gelu_elem(int dtype, int waves, int epl, bool round_trip, int64_t grid, const void *in,
+                            void *out, int32_t T, int32_t d, float z, const int32_t *live, hipStream_t stream) {
     int wi, ei;
     if (!gelu_elem_available(dtype, waves, epl) || elem_index(waves, epl, &wi, &ei) != 0)
         return hipErrorInvalidValue;
-    const void *fn = kGeluElem[dtype][wi][ei];
+    const void *fn = kGeluElem[round_trip ? 1 : 0][dtype][wi][ei];
     const void *a_in = in;
     void *a_out = out;
     void *args[] = {&a_in, &a_out, &T, &d, &z, &live};

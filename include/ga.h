@@ -81,8 +81,23 @@ typedef struct {
     int64_t grid;          /* workgroups launched (silu: from the capacity M only) */
     uint32_t spin_limit;   /* split rows: polls of a row's arrival counter before a
                               workgroup computes the whole row's statistics itself */
-    int32_t reserved;      /* zero */
+    int32_t flags;         /* gelu_and_mul_sparse: 0 or GA_ROUND_INTERMEDIATES (not
+                              with split rows); silu: zero */
 } ga_plan;
+
+/*
+ * Round-trip form of gelu_and_mul_sparse (vLLM PR 48498, section
+ * Cross-architecture warp and dtype validation and the review thread that
+ * follows it: the Triton kernel rounds intermediates to the input dtype so
+ * that it reproduces native PyTorch, whose every operation returns a tensor
+ * of that dtype).  The pages do not list the rounding points; this library
+ * rounds where an eager PyTorch composition of the op stores a tensor: the
+ * row mean, the row std, z, z * std, the cutoff mean + z * std, gate -
+ * cutoff, the GELU output, and the product.  Statistics are still computed
+ * in fp32 from the input values.  For fp32 data the form differs from the
+ * default only by the fp32 roundings of those intermediates.
+ */
+#define GA_ROUND_INTERMEDIATES 1
 
 /*
  * Sparse GELU-and-multiply.
@@ -138,6 +153,16 @@ ga_status ga_gelu_and_mul_sparse_ws(const void *in, void *out, int64_t T, int64_
                                     void *workspace, size_t workspace_bytes, ga_stream stream);
 
 /*
+ * ga_gelu_and_mul_sparse_ws with flags: 0 (the same as _ws) or
+ * GA_ROUND_INTERMEDIATES (the round-trip form above; it never splits rows,
+ * so the workspace may then be NULL).  Unknown flag bits: GA_EINVAL.
+ */
+ga_status ga_gelu_and_mul_sparse_ex(const void *in, void *out, int64_t T, int64_t d,
+                                    int32_t dtype, float z, const int32_t *live_rows,
+                                    int32_t flags, void *workspace, size_t workspace_bytes,
+                                    ga_stream stream);
+
+/*
  * GELU-and-multiply without the sparsity step (vLLM PR 48498, section
  * Purpose: the provider is chosen per "approximation mode"):
  * out = gelu(gate) * up, gelu in the tanh form (GA_GELU_TANH, the same
@@ -189,6 +214,8 @@ ga_status ga_plan_silu_and_mul_bounded(int64_t M, int64_t d, int32_t dtype, int3
  * waves_per_row * 64 * per_lane >= d; else GA_EUNSUPPORTED.  `block` and
  * `grid` are derived for gelu; silu takes its grid from the plan.  A split
  * plan needs the workspace described above (else GA_EINVAL) and T <= 65535.
+ * `flags` selects the round-trip form for gelu (no split rows with it) and
+ * must be zero for silu.  The planners leave it zero.
  */
 ga_status ga_gelu_and_mul_sparse_with_plan(const void *in, void *out, int64_t T, int64_t d,
                                            int32_t dtype, float z, const int32_t *live_rows,

@@ -197,6 +197,34 @@ def test_gelu_with_plan_rejects_bad_geometry():
     assert st == EUNSUP
 
 
+def test_round_trip_flag_checks():
+    """The round-trip form: accepted on the plain and element paths, refused
+    with split rows; unknown bits are malformed; silu plans take no flags."""
+    RT = ga.GA_ROUND_INTERMEDIATES
+    ex = lambda flags, T=0, d=2048, ws=None, nb=0: L.ga_gelu_and_mul_sparse_ex(  # noqa: E731
+        IN, OUT, T, d, BF16, Z, None, flags, ws, nb, None)
+    assert ex(0) == OK and ex(RT) == OK
+    assert ex(2) == EINVAL and ex(RT | 4) == EINVAL and ex(-1) == EINVAL
+    assert ex(RT, T=0, ws=WS, nb=WS_BYTES) == OK
+    assert L.ga_gelu_and_mul_sparse_ex(None, OUT, 4, 64, BF16, Z, None, RT, None, 0, None) == EINVAL
+    wp = lambda p, d=16384: L.ga_gelu_and_mul_sparse_with_plan(  # noqa: E731
+        IN, OUT, 0, d, BF16, Z, None, ctypes.byref(p), WS, WS_BYTES, None)
+    for d in (64, 2048, 16384, 65536, 777):
+        p = ga.plan_gelu_and_mul_sparse(2048, d, BF16, aligned=d % 8 == 0)
+        assert p.flags == 0
+        p.flags = RT
+        assert wp(p, d) == OK, (d, L.ga_last_error())
+    split = ga.plan_gelu_and_mul_sparse(8, 16384, BF16)
+    assert split.splits > 1
+    split.flags = RT
+    assert wp(split) == EUNSUP
+    split.flags = 8
+    assert wp(split) == EINVAL
+    s = ga.plan_silu_and_mul_bounded(16384, 768, BF16)
+    s.flags = RT
+    assert L.ga_silu_and_mul_bounded_with_plan(IN, OUT, 0, 768, BF16, LIVE, ctypes.byref(s), None) == EINVAL
+
+
 def test_silu_planner_depends_on_capacity_only():
     p = ga.plan_silu_and_mul_bounded(16384, 768, BF16, num_cus=256)
     assert p.path == 0 and p.block == 256 and 1 <= p.grid <= 256 * 16
