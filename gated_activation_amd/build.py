@@ -14,11 +14,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libga.so")
-SOURCES = ["api.hip", "gelu_sparse.hip", "gelu_sparse_split.hip", "elementwise.hip"]
+SOURCES = ["api.hip", "gelu_sparse.hip", "gelu_sparse_split.hip", "gelu_sparse_realign.hip", "elementwise.hip"]
 ARCH = "gfx950"
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
+def build(verbose: bool = False, jobs: int = 8) -> str:
     hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
     objs = []
     procs = []

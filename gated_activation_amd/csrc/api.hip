@@ -15,6 +15,7 @@
 
 #include "../../include/ga.h"
 #include "ga_internal.h"
+#include "ga_realign.h"
 
 namespace {
 
@@ -146,6 +147,14 @@ ga_status check_gelu_plan(const ga_plan *p, int64_t T, int64_t d, int32_t dtype)
             if (T > kSplitMaxRows)
                 return fail(GA_EUNSUPPORTED, "gelu plan: split rows need T <= %lld", (long long)kSplitMaxRows);
         }
+    } else if (p->path == 2) {
+        if (p->splits != 1) return fail(GA_EUNSUPPORTED, "gelu plan: the realigning path does not split rows");
+        if (!ga::gelu_realign_available(dtype, p->waves_per_row, p->per_lane, p->up_late))
+            return fail(GA_EUNSUPPORTED, "gelu plan: no realigning kernel for waves=%d per_lane=%d up_late=%d",
+                        p->waves_per_row, p->per_lane, p->up_late);
+        const int32_t per = 16 / (int32_t)elem_size(dtype);
+        if ((int64_t)p->waves_per_row * 64 * p->per_lane < ga::realign_blocks_max((int32_t)d, per))
+            return fail(GA_EUNSUPPORTED, "gelu plan: geometry covers fewer than the row's 16-byte blocks");
     } else if (p->path == 1) {
         if (p->splits != 1) return fail(GA_EUNSUPPORTED, "gelu plan: the element path does not split rows");
         if (!ga::gelu_elem_available(dtype, p->waves_per_row, p->per_lane))
@@ -173,6 +182,7 @@ ga_status check_workspace(const ga_plan &p, int64_t T, const void *workspace, si
 ga_status launch_gelu(const void *in, void *out, int64_t T, int64_t d, int32_t dtype, float z,
                       const int32_t *live, const ga_plan &p, void *workspace, ga_stream stream) {
     const char *name = "ga_gelu_and_mul_sparse";
+    if ((uintptr_t)live % 4 != 0) return fail(GA_EINVAL, "%s: live_rows is not 4-byte aligned", name);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const bool rt = (p.flags & GA_ROUND_INTERMEDIATES) != 0;
     if (p.path == 0) {
@@ -184,6 +194,9 @@ ga_status launch_gelu(const void *in, void *out, int64_t T, int64_t d, int32_t d
         return launched(name, ga::launch_gelu_vec(dtype, p.waves_per_row, p.per_lane, p.up_late, rt, T, in, out,
                                                   (int32_t)T, (int32_t)d, nvec, z, live, s));
     }
+    if (p.path == 2)
+        return launched(name, ga::launch_gelu_realign(dtype, p.waves_per_row, p.per_lane, p.up_late, rt, T, in, out,
+                                                      (int32_t)T, (int32_t)d, z, live, s));
     return launched(name, ga::launch_gelu_elem(dtype, p.waves_per_row, p.per_lane, rt, T, in, out, (int32_t)T,
                                                (int32_t)d, z, live, s));
 }
@@ -234,6 +247,7 @@ ga_status check_act_plan(const ga_plan *p, int op, int64_t rows, int64_t d, int3
 
 ga_status launch_act(const char *name, int op, const void *in, void *out, int64_t rows, int64_t d,
                      int32_t dtype, const int32_t *live, const ga_plan &p, ga_stream stream) {
+    if ((uintptr_t)live % 4 != 0) return fail(GA_EINVAL, "%s: live_rows is not 4-byte aligned", name);
     const int64_t items_row = p.path == 0 ? d * (int64_t)elem_size(dtype) / 16 : d;
     return launched(name, ga::launch_act(op, p.path, dtype, p.per_lane, p.grid, in, out, (int32_t)rows,
                                          (uint32_t)items_row, live, static_cast<hipStream_t>(stream)));
@@ -247,6 +261,7 @@ ga_status run_act(const char *name, int op, const void *in, void *out, int64_t r
     ga_status st = check_rows(name, in, out, rows, d, dtype, cols_in);
     if (st != GA_OK) return st;
     if (live_required && live == nullptr) return fail(GA_EINVAL, "%s: live_rows is required", name);
+    if ((uintptr_t)live % 4 != 0) return fail(GA_EINVAL, "%s: live_rows is not 4-byte aligned", name);
     if (rows * d >= kMaxItems) return fail(GA_EUNSUPPORTED, "%s: rows * d >= 2^31", name);
     if (rows == 0) return GA_OK;
     int cus = 0;
@@ -325,6 +340,25 @@ ga_status ga_plan_gelu_and_mul_sparse(int64_t T, int64_t d, int32_t dtype, int32
                 p.splits = (int32_t)splits;
             }
         }
+    } else if (ga::realign_blocks_max((int32_t)d, (int32_t)(16 / es)) <= 16 * 64 * 8) {
+        // Rows that are not 16-byte aligned: 16-byte blocks in each stream's
+        // own alignment, realigned through LDS.  Measured on MI355X: with
+        // many rows (T >= 1024) the smallest workgroup (>= 2 waves) that
+        // needs at most 5 blocks per lane, with up loaded chunk by chunk,
+        // keeps the most rows resident; with fewer rows, wide workgroups
+        // with about 2 blocks per lane and up loaded with the gate.
+        const int64_t blocks = ga::realign_blocks_max((int32_t)d, (int32_t)(16 / es));
+        int w;
+        if (T >= 1024) {
+            w = 2;
+            while (w < 16 && (blocks + 64 * w - 1) / (64 * w) > 5) w *= 2;
+        } else {
+            w = std::min(16, next_pow2((blocks + 127) / 128));
+        }
+        p.path = 2;
+        p.waves_per_row = w;
+        p.per_lane = (int32_t)((blocks + 64 * w - 1) / (64 * w));
+        p.up_late = T >= 1024 ? 1 : 0;
     } else {
         // Element path: up to 16 elements per lane, 1, 4 or 16 waves.
         const int64_t lanes = (d + 15) / 16;
@@ -367,6 +401,8 @@ ga_status ga_gelu_and_mul_sparse_ex(const void *in, void *out, int64_t T, int64_
     if (!std::isfinite(z)) return fail(GA_EINVAL, "ga_gelu_and_mul_sparse: z is not finite");
     if ((flags & ~GA_ROUND_INTERMEDIATES) != 0)
         return fail(GA_EINVAL, "ga_gelu_and_mul_sparse: unknown flag bits 0x%x", (unsigned)flags);
+    if ((uintptr_t)live_rows % 4 != 0)
+        return fail(GA_EINVAL, "ga_gelu_and_mul_sparse: live_rows is not 4-byte aligned");
     if (T == 0) return GA_OK;
     // The round-trip form has no split-row kernel.
     const bool have_ws = !(flags & GA_ROUND_INTERMEDIATES) && workspace != nullptr &&
@@ -428,6 +464,7 @@ ga_status ga_silu_and_mul_bounded_with_plan(const void *in, void *out, int64_t M
     ga_status st = check_rows(name, in, out, M, d, dtype);
     if (st != GA_OK) return st;
     if (live_rows == nullptr) return fail(GA_EINVAL, "%s: live_rows is required", name);
+    if ((uintptr_t)live_rows % 4 != 0) return fail(GA_EINVAL, "%s: live_rows is not 4-byte aligned", name);
     if (plan == nullptr) return fail(GA_EINVAL, "%s: null plan", name);
     if ((st = check_act_plan(plan, ga::OP_SILU_MUL, M, d, dtype)) != GA_OK) return st;
     if (plan->path == 0 && !vector_aligned(in, out, d, dtype))

@@ -29,6 +29,15 @@ hipError_t launch_gelu_split(int dtype, int waves, int vec_per_lane, int splits,
                              int32_t T, int32_t d, int32_t nvec, float z, const int32_t *live, void *workspace,
                              uint32_t spin_limit, hipStream_t stream);
 
+// Realigning path for rows that are not 16-byte aligned: waves 1, 2, 4, 8,
+// 16; vectors per lane 1 .. 8 (16-byte blocks per lane, covering the most
+// blocks a row can touch); up_late 0 (up loaded with the gate) or 1 (chunk
+// by chunk after the statistics).
+bool gelu_realign_available(int dtype, int waves, int vec_per_lane, int up_late);
+hipError_t launch_gelu_realign(int dtype, int waves, int vec_per_lane, int up_late, bool round_trip, int64_t grid,
+                               const void *in, void *out, int32_t T, int32_t d, float z,
+                               const int32_t *live, hipStream_t stream);
+
 // round_trip selects the form that rounds each intermediate (mean, std, z,
 // z * std, cutoff, gate - cutoff, GELU output) to the element type.
 hipError_t launch_gelu_vec(int dtype, int waves, int vec_per_lane, int up_late, bool round_trip, int64_t grid,

@@ -33,10 +33,13 @@
  *   - All argument checks happen on the host before any HIP call; a rejected
  *     call touches no memory.  ga_last_error() then returns a message.
  *   - Out-of-range device live counts are clamped to [0, rows]; they cannot
- *     be reported (no synchronisation).
+ *     be reported (no synchronisation).  A live_rows pointer must be 4-byte
+ *     aligned (GA_EINVAL otherwise).
  *   - Any alignment natural to the element type is accepted; when in and out
  *     are 16-byte aligned and a row's bytes are a multiple of 16, 16-byte
- *     vector loads and stores are used, else a per-element path.
+ *     vector loads and stores are used.  Otherwise gelu_and_mul_sparse moves
+ *     each stream in its own 16-byte blocks and realigns them through LDS
+ *     (rows up to 8192 blocks), and the other ops take a per-element path.
  */
 #ifndef GA_H
 #define GA_H
@@ -66,15 +69,17 @@ typedef void *ga_stream;
 /* Launch geometry.  Filled by the planners, or by a caller that wants a
  * specific geometry (a tuning sweep); see ga_gelu_and_mul_sparse_with_plan. */
 typedef struct {
-    int32_t path;          /* 0: 16-byte vector path, 1: per-element path */
+    int32_t path;          /* 0: 16-byte vector path, 1: per-element path,
+                              2: gelu realigning path (rows off 16-byte alignment) */
     int32_t waves_per_row; /* gelu: 64-lane wavefronts per workgroup (1,2,4,8,16) */
     int32_t per_lane;      /* gelu vector path: 16-byte gate vectors per lane (1,2,4,8;
                               split rows 1,2,4); gelu element path: gate elements per
-                              lane (4,16,64); silu: items per lane per step (1,2,4) */
-    int32_t up_late;       /* gelu vector path: 0 = load the up row together with the gate
-                              row (shortest latency), 1 = load it after the statistics, one
-                              vector at a time (fewer registers, more rows resident);
-                              split rows: 0 only */
+                              lane (4,16,64); gelu realigning path: 16-byte blocks per
+                              lane (1..8); silu: items per lane per step (1,2,4) */
+    int32_t up_late;       /* gelu vector and realigning paths: 0 = load the up row together
+                              with the gate row (shortest latency), 1 = load it after the
+                              statistics, a vector (a chunk) at a time (fewer registers, more
+                              rows resident); split rows: 0 only */
     int32_t block;         /* threads per workgroup */
     int32_t splits;        /* gelu vector path: workgroups sharing one row; 1, or 2, 4, 8,
                               16 (needs a workspace, see ga_gelu_and_mul_sparse_ws) */
@@ -211,7 +216,10 @@ ga_status ga_plan_silu_and_mul_bounded(int64_t M, int64_t d, int32_t dtype, int3
  * (the values listed in ga_plan) and cover the row: vector path
  * splits * waves_per_row * 64 * per_lane * (16 / element size) >= d, with
  * every split owning at least one vector; element path
- * waves_per_row * 64 * per_lane >= d; else GA_EUNSUPPORTED.  `block` and
+ * waves_per_row * 64 * per_lane >= d; realigning path (any alignment)
+ * waves_per_row * 64 * per_lane >= (d + 2 * e - 2) / e with e = 16 / element
+ * size (the most 16-byte blocks a row can touch); else GA_EUNSUPPORTED.
+ * `block` and
  * `grid` are derived for gelu; silu takes its grid from the plan.  A split
  * plan needs the workspace described above (else GA_EINVAL) and T <= 65535.
  * `flags` selects the round-trip form for gelu (no split rows with it) and

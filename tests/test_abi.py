@@ -95,6 +95,15 @@ def test_silu_argument_checks(kwargs, status):
     assert silu(**kwargs) == status
 
 
+def test_misaligned_live_count_is_rejected():
+    bad = ctypes.c_void_p(0x7F2000000002)
+    assert L.ga_gelu_and_mul_sparse(IN, OUT, 4, 2048, BF16, Z, bad, None) == EINVAL
+    assert L.ga_silu_and_mul_bounded(IN, OUT, 16, 768, BF16, bad, None) == EINVAL
+    assert L.ga_squared_relu_bounded(IN, OUT, 16, 768, BF16, bad, None) == EINVAL
+    assert L.ga_gelu_and_mul(IN, OUT, 16, 768, BF16, 1, bad, None) == EINVAL
+    assert b"aligned" in L.ga_last_error()
+
+
 def test_stream_xor_rows_checks():
     assert L.ga_stream_xor_rows(IN, OUT, 4, 24, None) == EINVAL       # not a multiple of 16
     assert L.ga_stream_xor_rows(None, OUT, 4, 32, None) == EINVAL
@@ -116,12 +125,18 @@ def test_gelu_planner_known_shapes():
     # without a workspace the rows are never split
     p = ga.plan_gelu_and_mul_sparse(1, 32768, BF16, with_workspace=False)
     assert (p.splits, p.waves_per_row, p.per_lane) == (1, 16, 4)
-    p = ga.plan_gelu_and_mul_sparse(7, 8191, F16)            # odd d: element path
-    assert p.path == 1 and p.splits == 1 and p.waves_per_row * 64 * p.per_lane >= 8191
-    p = ga.plan_gelu_and_mul_sparse(7, 8192, F16, aligned=False)
-    assert p.path == 1
+    p = ga.plan_gelu_and_mul_sparse(7, 8191, F16)            # odd d: realigning path
+    assert p.path == 2 and p.splits == 1 and p.waves_per_row * 64 * p.per_lane >= (8191 + 14) // 8
+    p = ga.plan_gelu_and_mul_sparse(7, 8192, F16, aligned=False)    # few rows: wide, 2 blocks per lane
+    assert (p.path, p.waves_per_row, p.per_lane, p.up_late) == (2, 16, 2, 0)
+    p = ga.plan_gelu_and_mul_sparse(2048, 8191, BF16)                 # many rows: narrow, up late
+    assert (p.path, p.waves_per_row, p.per_lane, p.up_late) == (2, 4, 5, 1)
+    p = ga.plan_gelu_and_mul_sparse(2048, 511, BF16)
+    assert (p.path, p.waves_per_row, p.per_lane, p.up_late) == (2, 2, 1, 1)
     p = ga.plan_gelu_and_mul_sparse(7, 65536, F32)           # beyond the vector reach
     assert p.path == 1 and p.waves_per_row * 64 * p.per_lane >= 65536
+    p = ga.plan_gelu_and_mul_sparse(7, 65536, BF16, aligned=False)   # 8193 blocks: element path
+    assert p.path == 1
 
 
 def test_workspace_size_and_split_plan_checks():
@@ -188,8 +203,18 @@ def test_gelu_with_plan_rejects_bad_geometry():
     assert L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 64, BF16, Z, None, ctypes.byref(p), WS, WS_BYTES, None) == EUNSUP
     p = ga.Plan(path=1, waves_per_row=16, per_lane=2, block=1024, grid=1)
     assert L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 64, BF16, Z, None, ctypes.byref(p), WS, WS_BYTES, None) == EUNSUP
-    p = ga.Plan(path=2, waves_per_row=1, per_lane=4, block=64, grid=1)
+    p = ga.Plan(path=3, waves_per_row=1, per_lane=4, block=64, grid=1)
     assert L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 64, BF16, Z, None, ctypes.byref(p), WS, WS_BYTES, None) == EINVAL
+    # realigning path: must cover the most blocks a row can touch, 1..8 per lane
+    wp = lambda p, d: L.ga_gelu_and_mul_sparse_with_plan(  # noqa: E731
+        IN, OUT, 0, d, BF16, Z, None, ctypes.byref(p), WS, WS_BYTES, None)
+    assert wp(ga.Plan(path=2, waves_per_row=8, per_lane=5, block=512), 16384) == OK     # 2049 blocks
+    assert wp(ga.Plan(path=2, waves_per_row=8, per_lane=4, block=512), 16384) == EUNSUP  # 2048 < 2049
+    assert wp(ga.Plan(path=2, waves_per_row=8, per_lane=9, block=512), 16384) == EUNSUP
+    assert wp(ga.Plan(path=2, waves_per_row=3, per_lane=8, block=192), 64) == EUNSUP
+    assert wp(ga.Plan(path=2, waves_per_row=8, per_lane=5, up_late=1, block=512), 16384) == OK
+    assert wp(ga.Plan(path=2, waves_per_row=8, per_lane=5, up_late=2, block=512), 16384) == EUNSUP
+    assert wp(ga.Plan(path=2, waves_per_row=1, per_lane=1, block=64), 1) == OK
     # vector path on a base that is not 16-byte aligned
     p = ga.plan_gelu_and_mul_sparse(1, 64, BF16)
     st = L.ga_gelu_and_mul_sparse_with_plan(ctypes.c_void_p(0x7F0000000002), OUT, 0, 64, BF16, Z, None,

@@ -13,7 +13,7 @@ import torch
 import gated_activation_amd as ga
 import oracle
 import synth
-from parity import (BF16, F16, F32, Z95, Z99, bits_of, check_canary, compare,
+from parity import (BF16, F16, F32, TORCH_DTYPE, Z95, Z99, bits_of, check_canary, compare,
                     decode, sentinel_buffer, to_device)
 
 pytestmark = pytest.mark.gpu
@@ -131,7 +131,7 @@ def test_element_path_on_aligned_rows():
 
 @pytest.mark.parametrize("shift", [1, 3, 7])
 def test_misaligned_base_pointers(shift):
-    """Bases off 16-byte alignment by `shift` elements take the element path."""
+    """Bases off 16-byte alignment by `shift` elements (the realigning path)."""
     T, d = 9, 2048
     xb = synth.gelu_iid(T, d, seed=shift)
     flat = torch.zeros(T * 2 * d + 16, dtype=torch.bfloat16, device="cuda")
@@ -145,6 +145,71 @@ def test_misaligned_base_pointers(shift):
     ref, st = o.gelu_and_mul_sparse(xb, BF16, Z95, want_stats=True)
     compare(bits_of(out, BF16), ref, BF16, gate=decode(xb[:, :d], BF16), stats=st, label="misaligned")
     assert not bits_of(buf[:shift], BF16).any() and not bits_of(buf[shift + T * d:], BF16).any()
+
+
+def run_offset(xb, dt, z, in_shift, out_shift, plan=None, rows_sample=None, label=""):
+    """Input and output views that start in_shift / out_shift elements past a
+    16-byte boundary; every element of the output buffer outside the view
+    must keep its sentinel bits."""
+    T, two_d = xb.shape
+    d = two_d // 2
+    tdt = TORCH_DTYPE[dt]
+    # NaN around the input view: an end block that reaches past the row
+    # reads these, and they must not reach the statistics or the output.
+    flat = torch.full((T * two_d + 16,), float("nan"), dtype=tdt, device="cuda")
+    x = flat[in_shift: in_shift + T * two_d].view(T, two_d)
+    x.copy_(to_device(xb, dt))
+    buf, _ = sentinel_buffer(T * d + 16, 1, dt)
+    out = buf[out_shift: out_shift + T * d].view(tdt).view(T, d)
+    ga.gelu_and_mul_sparse(x, z, out=out, plan=plan)
+    torch.cuda.synchronize()
+    everything = bits_of(buf, dt)
+    outside = np.concatenate([everything[:out_shift], everything[out_shift + T * d:]])
+    assert np.all(outside == synth.SENTINEL[dt]), f"{label}: wrote outside the output view"
+    rows = np.arange(T) if rows_sample is None else np.array(sorted(set(rows_sample)), int)
+    ref, st = oracle.get().gelu_and_mul_sparse(xb[rows], dt, z, want_stats=True)
+    got = everything[out_shift: out_shift + T * d].reshape(T, d)[rows]
+    return compare(got, ref, dt, gate=decode(xb[rows, :d], dt), stats=st, label=label)
+
+
+@pytest.mark.parametrize("dt", [BF16, F16, F32], ids=["bf16", "f16", "f32"])
+@pytest.mark.parametrize("d", [1, 5, 31, 1000, 8191, 16383, 16384])
+def test_realigning_path_every_phase_mix(dt, d):
+    """Rows off a 16-byte boundary (shifted bases, odd d: phases change from
+    row to row) take the realigning path; input and output shifts vary
+    independently."""
+    T = 37 if d <= 8191 else 9
+    xb = synth.gelu_iid(T, d, seed=300 + d + dt, dtype=dt, gate_std=1.4)
+    per = 4 if dt == F32 else 8
+    for i_s, o_s in ((0, 1), (1, 0), (3, 3), (per - 1, 2 % per), (1, per - 1)):
+        if d % per == 0 and i_s == 0 and o_s == 0:
+            continue
+        plan = ga.plan_gelu_and_mul_sparse(T, d, dt, aligned=False)
+        assert plan.path == 2
+        run_offset(xb, dt, Z95, i_s, o_s, label=f"realign dt{dt} d{d} shifts {i_s},{o_s}")
+
+
+def test_realigning_path_every_geometry():
+    """Every realigning geometry that covers the row, with up loaded early or
+    late, on shifted and on aligned rows, matches the oracle."""
+    d = 8192
+    xb = synth.gelu_offset_rows(12, d, seed=79)
+    nblk = (d + 14) // 8
+    for w in (1, 2, 4, 8, 16):
+        for v in range(1, 9):
+            if w * 64 * v < nblk:
+                continue
+            for late in (0, 1):
+                p = ga.Plan(path=2, waves_per_row=w, per_lane=v, up_late=late, block=64 * w)
+                for i_s, o_s in ((0, 0), (5, 2), (2, 5)):
+                    run_offset(xb, BF16, Z95, i_s, o_s, plan=p,
+                               label=f"realign w{w} v{v} late{late} shifts {i_s},{o_s}")
+
+
+def test_realigning_path_headline_rows():
+    """T = 2048, d = 16384 bf16 one element off alignment (sampled rows)."""
+    xb = synth.gelu_large(2048, 16384)
+    run_offset(xb, BF16, Z95, 1, 1, rows_sample=list(np.linspace(0, 2047, 48).astype(int)), label="realign headline")
 
 
 def test_repeat_runs_are_bit_identical():

@@ -142,7 +142,8 @@ def test_live_rows():
         run_rt(x, BF16, Z95, live=live, label=f"rt live {live}")
 
 
-@pytest.mark.parametrize("geom", [(0, 16, 1, 0), (0, 8, 2, 0), (0, 4, 4, 1), (0, 2, 8, 1), (1, 16, 16, 0)],
+@pytest.mark.parametrize("geom", [(0, 16, 1, 0), (0, 8, 2, 0), (0, 4, 4, 1), (0, 2, 8, 1), (1, 16, 16, 0),
+                                  (2, 8, 3, 0), (2, 4, 5, 0)],
                          ids=lambda g: f"path{g[0]}_w{g[1]}_pl{g[2]}_late{g[3]}")
 def test_every_geometry(geom):
     """The form is the same for any launch geometry of d = 8192 bf16."""
