@@ -276,8 +276,9 @@ def sweep(dev, stream, num_cus):
 
 def siblings(dev, stream):
     """The other ops of the family, graph-replayed over rotating buffers:
-    gelu_and_mul (tanh and erf) and the round-trip form of
-    gelu_and_mul_sparse on the headline shape, and the bounded
+    gelu_and_mul (tanh and erf), the round-trip form of gelu_and_mul_sparse
+    and its realigning path (a base one element off 16-byte alignment, and
+    d = 16383) on the headline shape, and the bounded
     squared ReLU (not gated: read d, write d per row) on an MoE buffer."""
     import numpy as np
     import torch
@@ -305,7 +306,34 @@ def siblings(dev, stream):
     res[f"gelu_and_mul_sparse_round_trip_T{T}_d{D}"] = {
         "us_per_call": round(ms * 1e3, 3), "GBps": round(bytes_call / (ms * 1e-3) / 1e9, 1),
         "pct_of_peak": round(100 * bytes_call / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2)}
-    del xs, outs
+
+    # Rows off 16-byte alignment (the realigning path): the headline input
+    # viewed one element past a 16-byte boundary, and an odd d.
+    bases = [torch.empty(x0.numel() + 8, dtype=torch.bfloat16, device=dev) for _ in range(n_sets)]
+    shifted = [b[1:1 + x0.numel()].view(T, 2 * D) for b in bases]
+    for a in shifted:
+        a.copy_(x0)
+
+    def call(i):
+        ga.gelu_and_mul_sparse(shifted[i], Z, out=outs[i])
+    ms = time_graph(call, n_sets, 256, 10, stream)
+    res[f"gelu_and_mul_sparse_shifted_base_T{T}_d{D}"] = {
+        "us_per_call": round(ms * 1e3, 3), "GBps": round(bytes_call / (ms * 1e-3) / 1e9, 1),
+        "pct_of_peak": round(100 * bytes_call / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2)}
+    del shifted, bases
+    d_odd = D - 1
+    odd = [torch.from_numpy(synth.gelu_large(T, d_odd).view(np.int16)).to(dev).view(torch.bfloat16)]
+    odd += [odd[0].clone() for _ in range(n_sets - 1)]
+    odd_out = [torch.empty(T, d_odd, dtype=torch.bfloat16, device=dev) for _ in range(n_sets)]
+
+    def call(i):
+        ga.gelu_and_mul_sparse(odd[i], Z, out=odd_out[i])
+    ms = time_graph(call, n_sets, 256, 10, stream)
+    b_odd = T * 3 * d_odd * 2
+    res[f"gelu_and_mul_sparse_T{T}_d{d_odd}"] = {
+        "us_per_call": round(ms * 1e3, 3), "GBps": round(b_odd / (ms * 1e-3) / 1e9, 1),
+        "pct_of_peak": round(100 * b_odd / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2)}
+    del odd, odd_out, xs, outs
     M, d = SILU_M, 2 * SILU_D
     q0 = torch.from_numpy(synth.moe_buffer(M, SILU_D).view(np.int16)).to(dev).view(torch.bfloat16).view(M, d)
     q_sets = max(2, math.ceil(ROTATE_BYTES / (M * 2 * d * 2)))
