@@ -234,12 +234,14 @@ def main():
 
 
 SWEEP = [(T, 8192) for T in (1, 2, 8, 32, 128, 512, 2048)] + \
-        [(T, d) for d in (16384, 32768) for T in (1, 64, 2048)]
+        [(T, d) for d in (16384, 32768) for T in (1, 64, 2048)] + \
+        [(65536, d) for d in (64, 128, 256)]
 
 
 def sweep(dev, stream, num_cus):
     """gelu_and_mul_sparse over the token sweep (d = 8192, gate N(0,1) plus a
-    per-row offset) and the large-row shapes (gate N(0,2)), bf16, each timed
+    per-row offset), the large-row shapes (gate N(0,2)) and short rows at
+    T = 65536 (gate N(0,2); the packed-rows path), bf16, each timed
     by replaying a graph of 64 launches over distinct buffers (a split-row
     workspace passed explicitly so few-row shapes take the split path).
     Shapes under ~256 MB in total may be served from the Infinity Cache."""
@@ -265,11 +267,11 @@ def sweep(dev, stream, num_cus):
         ms = time_graph(call, n_sets, reps * per_graph, 10, stream, per_graph=per_graph)
         plan = ga.plan_gelu_and_mul_sparse(T, d, ga.GA_BF16, True, num_cus, True)
         gbps = bytes_call / (ms * 1e-3) / 1e9
+        geom = (f"packed lanes_per_row={plan.lanes_per_row} per_lane={plan.per_lane}" if plan.path == 3 else
+                f"splits={plan.splits} waves={plan.waves_per_row} per_lane={plan.per_lane} up_late={plan.up_late}")
         out.append({"T": T, "d": d, "us_per_call": round(ms * 1e3, 3), "GBps": round(gbps, 1),
                     "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2), "bytes": bytes_call,
-                    "working_set_MB": round(n_sets * bytes_call / 1e6, 1),
-                    "plan": f"splits={plan.splits} waves={plan.waves_per_row} per_lane={plan.per_lane} "
-                            f"up_late={plan.up_late}"})
+                    "working_set_MB": round(n_sets * bytes_call / 1e6, 1), "plan": geom})
         del xs, outs, ws
     return out
 

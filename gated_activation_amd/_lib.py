@@ -22,7 +22,8 @@ class Plan(ctypes.Structure):
                 ("per_lane", ctypes.c_int32), ("up_late", ctypes.c_int32),
                 ("block", ctypes.c_int32), ("splits", ctypes.c_int32),
                 ("grid", ctypes.c_int64), ("spin_limit", ctypes.c_uint32),
-                ("flags", ctypes.c_int32)]
+                ("flags", ctypes.c_int32), ("lanes_per_row", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
     def __init__(self, **kw):
         kw.setdefault("splits", 1)

@@ -127,6 +127,8 @@ ga_status check_gelu_plan(const ga_plan *p, int64_t T, int64_t d, int32_t dtype)
         return fail(GA_EINVAL, "gelu plan: unknown flag bits 0x%x", (unsigned)p->flags);
     if ((p->flags & GA_ROUND_INTERMEDIATES) && p->splits != 1)
         return fail(GA_EUNSUPPORTED, "gelu plan: the round-trip form does not split rows");
+    if ((p->path != 3 && p->lanes_per_row != 0) || p->reserved != 0)
+        return fail(GA_EINVAL, "gelu plan: lanes_per_row is for the packed-rows path; reserved must be zero");
     if (p->path == 0) {
         const int64_t per16 = 16 / (int64_t)elem_size(dtype);
         const int64_t nvec = (d + per16 - 1) / per16;
@@ -147,6 +149,15 @@ ga_status check_gelu_plan(const ga_plan *p, int64_t T, int64_t d, int32_t dtype)
             if (T > kSplitMaxRows)
                 return fail(GA_EUNSUPPORTED, "gelu plan: split rows need T <= %lld", (long long)kSplitMaxRows);
         }
+    } else if (p->path == 3) {
+        if (p->splits != 1 || p->up_late != 0)
+            return fail(GA_EUNSUPPORTED, "gelu plan: the packed-rows path takes splits=1, up_late=0");
+        if (!ga::gelu_rows_available(dtype, p->lanes_per_row, p->per_lane))
+            return fail(GA_EUNSUPPORTED, "gelu plan: no packed-rows kernel for lanes_per_row=%d per_lane=%d",
+                        p->lanes_per_row, p->per_lane);
+        const int64_t per16 = 16 / (int64_t)elem_size(dtype);
+        if ((int64_t)p->lanes_per_row * p->per_lane * per16 < d)
+            return fail(GA_EUNSUPPORTED, "gelu plan: geometry covers fewer than d elements");
     } else if (p->path == 2) {
         if (p->splits != 1) return fail(GA_EUNSUPPORTED, "gelu plan: the realigning path does not split rows");
         if (!ga::gelu_realign_available(dtype, p->waves_per_row, p->per_lane, p->up_late))
@@ -193,6 +204,13 @@ ga_status launch_gelu(const void *in, void *out, int64_t T, int64_t d, int32_t d
                                                         p.spin_limit, s));
         return launched(name, ga::launch_gelu_vec(dtype, p.waves_per_row, p.per_lane, p.up_late, rt, T, in, out,
                                                   (int32_t)T, (int32_t)d, nvec, z, live, s));
+    }
+    if (p.path == 3) {
+        const int32_t nvec = (int32_t)(d * (int64_t)elem_size(dtype) / 16);
+        const int64_t rows_per_block = ga::ROWS_BLOCK / p.lanes_per_row;
+        return launched(name, ga::launch_gelu_rows(dtype, p.lanes_per_row, p.per_lane, rt,
+                                                   (T + rows_per_block - 1) / rows_per_block, in, out, (int32_t)T,
+                                                   (int32_t)d, nvec, z, live, s));
     }
     if (p.path == 2)
         return launched(name, ga::launch_gelu_realign(dtype, p.waves_per_row, p.per_lane, p.up_late, rt, T, in, out,
@@ -311,7 +329,16 @@ ga_status ga_plan_gelu_and_mul_sparse(int64_t T, int64_t d, int32_t dtype, int32
     p.splits = 1;
     p.spin_limit = kDefaultSpinLimit;
     const int64_t nvec = (int64_t)d * (int64_t)es / 16;
-    if (aligned && ((size_t)d * es) % 16 == 0 && nvec <= 16 * 64 * 8) {
+    if (aligned && ((size_t)d * es) % 16 == 0 && nvec <= 32) {
+        // Short rows: several rows per wavefront, a group of G lanes per row
+        // with one vector each (measured on MI355X at T = 65536: d = 64 bf16
+        // 14 % -> 52 % of peak, d = 128 29 % -> 62 %, d = 256 57 % -> 71 %).
+        int g = next_pow2((int)nvec);
+        g = g < 4 ? 4 : g > 32 ? 32 : g;
+        p.path = 3;
+        p.lanes_per_row = g;
+        p.per_lane = next_pow2((int)((nvec + g - 1) / g));
+    } else if (aligned && ((size_t)d * es) % 16 == 0 && nvec <= 16 * 64 * 8) {
         int w, v;
         pick_waves(nvec, 8, &w, &v);
         p.path = 0;
@@ -368,8 +395,14 @@ ga_status ga_plan_gelu_and_mul_sparse(int64_t T, int64_t d, int32_t dtype, int32
         p.waves_per_row = w;
         p.per_lane = per <= 4 ? 4 : per <= 16 ? 16 : 64;
     }
-    p.block = p.waves_per_row * 64;
-    p.grid = T * p.splits;
+    if (p.path == 3) {
+        const int64_t rows_per_block = ga::ROWS_BLOCK / p.lanes_per_row;
+        p.block = ga::ROWS_BLOCK;
+        p.grid = (T + rows_per_block - 1) / rows_per_block;
+    } else {
+        p.block = p.waves_per_row * 64;
+        p.grid = T * p.splits;
+    }
     *plan = p;
     return GA_OK;
 }
@@ -386,7 +419,7 @@ ga_status ga_gelu_and_mul_sparse_with_plan(const void *in, void *out, int64_t T,
     if (!std::isfinite(z)) return fail(GA_EINVAL, "ga_gelu_and_mul_sparse: z is not finite");
     if (plan == nullptr) return fail(GA_EINVAL, "ga_gelu_and_mul_sparse: null plan");
     if ((st = check_gelu_plan(plan, T, d, dtype)) != GA_OK) return st;
-    if (plan->path == 0 && !vector_aligned(in, out, d, dtype))
+    if ((plan->path == 0 || plan->path == 3) && !vector_aligned(in, out, d, dtype))
         return fail(GA_EUNSUPPORTED, "ga_gelu_and_mul_sparse: vector path needs 16-byte rows and bases");
     if ((st = check_workspace(*plan, T, workspace, workspace_bytes)) != GA_OK) return st;
     if (T == 0) return GA_OK;

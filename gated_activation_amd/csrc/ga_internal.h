@@ -29,6 +29,15 @@ hipError_t launch_gelu_split(int dtype, int waves, int vec_per_lane, int splits,
                              int32_t T, int32_t d, int32_t nvec, float z, const int32_t *live, void *workspace,
                              uint32_t spin_limit, hipStream_t stream);
 
+// Packed-rows path for short aligned rows: ROWS_BLOCK threads per workgroup,
+// lanes_per_row in {4, 8, 16, 32} lanes per row, vec_per_lane in {1, 2, 4};
+// grid = ceil(T / (ROWS_BLOCK / lanes_per_row)).
+constexpr int ROWS_BLOCK = 256;
+bool gelu_rows_available(int dtype, int lanes_per_row, int vec_per_lane);
+hipError_t launch_gelu_rows(int dtype, int lanes_per_row, int vec_per_lane, bool round_trip, int64_t grid,
+                            const void *in, void *out, int32_t T, int32_t d, int32_t nvec, float z,
+                            const int32_t *live, hipStream_t stream);
+
 // Realigning path for rows that are not 16-byte aligned: waves 1, 2, 4, 8,
 // 16; vectors per lane 1 .. 8 (16-byte blocks per lane, covering the most
 // blocks a row can touch); up_late 0 (up loaded with the gate) or 1 (chunk

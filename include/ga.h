@@ -70,12 +70,15 @@ typedef void *ga_stream;
  * specific geometry (a tuning sweep); see ga_gelu_and_mul_sparse_with_plan. */
 typedef struct {
     int32_t path;          /* 0: 16-byte vector path, 1: per-element path,
-                              2: gelu realigning path (rows off 16-byte alignment) */
+                              2: gelu realigning path (rows off 16-byte alignment),
+                              3: gelu packed-rows path (short aligned rows, several
+                              rows per wavefront) */
     int32_t waves_per_row; /* gelu: 64-lane wavefronts per workgroup (1,2,4,8,16) */
     int32_t per_lane;      /* gelu vector path: 16-byte gate vectors per lane (1,2,4,8;
                               split rows 1,2,4); gelu element path: gate elements per
                               lane (4,16,64); gelu realigning path: 16-byte blocks per
-                              lane (1..8); silu: items per lane per step (1,2,4) */
+                              lane (1..8); gelu packed rows: vectors per lane (1,2,4);
+                              silu: items per lane per step (1,2,4) */
     int32_t up_late;       /* gelu vector and realigning paths: 0 = load the up row together
                               with the gate row (shortest latency), 1 = load it after the
                               statistics, a vector (a chunk) at a time (fewer registers, more
@@ -88,6 +91,10 @@ typedef struct {
                               workgroup computes the whole row's statistics itself */
     int32_t flags;         /* gelu_and_mul_sparse: 0 or GA_ROUND_INTERMEDIATES (not
                               with split rows); silu: zero */
+    int32_t lanes_per_row; /* gelu packed-rows path: lanes sharing one row (4, 8, 16, 32;
+                              a 256-lane workgroup holds 256 / lanes_per_row rows);
+                              other paths: zero */
+    int32_t reserved;      /* zero */
 } ga_plan;
 
 /*
@@ -218,7 +225,8 @@ ga_status ga_plan_silu_and_mul_bounded(int64_t M, int64_t d, int32_t dtype, int3
  * every split owning at least one vector; element path
  * waves_per_row * 64 * per_lane >= d; realigning path (any alignment)
  * waves_per_row * 64 * per_lane >= (d + 2 * e - 2) / e with e = 16 / element
- * size (the most 16-byte blocks a row can touch); else GA_EUNSUPPORTED.
+ * size (the most 16-byte blocks a row can touch); packed rows (16-byte rows
+ * and bases only) lanes_per_row * per_lane * e >= d; else GA_EUNSUPPORTED.
  * `block` and
  * `grid` are derived for gelu; silu takes its grid from the plan.  A split
  * plan needs the workspace described above (else GA_EINVAL) and T <= 65535.

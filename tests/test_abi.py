@@ -122,6 +122,11 @@ def test_gelu_planner_known_shapes():
         p = ga.plan_gelu_and_mul_sparse(T, d, BF16)
         assert (p.path, p.waves_per_row, p.per_lane, p.up_late, p.splits) == w, (T, d, p.as_dict())
         assert p.block == 64 * p.waves_per_row and p.grid == T * p.splits
+    # short rows: packed, several rows per wavefront
+    for d, g, v in ((8, 4, 1), (24, 4, 1), (64, 8, 1), (128, 16, 1), (256, 32, 1), (200, 32, 1)):
+        p = ga.plan_gelu_and_mul_sparse(4096, d, BF16)
+        assert (p.path, p.lanes_per_row, p.per_lane, p.block, p.grid) == (3, g, v, 256, 4096 * g // 256), (d, p.as_dict())
+    assert ga.plan_gelu_and_mul_sparse(4096, 264, BF16).path == 0      # 33 vectors: one row per workgroup
     # without a workspace the rows are never split
     p = ga.plan_gelu_and_mul_sparse(1, 32768, BF16, with_workspace=False)
     assert (p.splits, p.waves_per_row, p.per_lane) == (1, 16, 4)
@@ -180,9 +185,13 @@ def test_gelu_planner_covers_every_d(dt):
             continue
         for aligned in (True, False):
             p = ga.plan_gelu_and_mul_sparse(3, d, dt, aligned=aligned)
-            assert p.block == p.waves_per_row * 64 and p.grid == 3 * p.splits
+            if p.path == 3:   # packed rows: 256 lanes, 256 / lanes_per_row rows per workgroup
+                assert p.block == 256 and p.grid == -(-3 // (256 // p.lanes_per_row))
+                assert aligned and (d * es) % 16 == 0 and d * es <= 32 * 16
+            else:
+                assert p.block == p.waves_per_row * 64 and p.grid == 3 * p.splits
             if p.path == 0:
-                assert aligned and (d * es) % 16 == 0
+                assert aligned and (d * es) % 16 == 0 and d * es > 32 * 16
             # With zero rows the entry point validates the plan and returns.
             base_in = ctypes.c_void_p(0x7F0000000000)
             base_out = ctypes.c_void_p(0x7F8000000000)
@@ -203,8 +212,23 @@ def test_gelu_with_plan_rejects_bad_geometry():
     assert L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 64, BF16, Z, None, ctypes.byref(p), WS, WS_BYTES, None) == EUNSUP
     p = ga.Plan(path=1, waves_per_row=16, per_lane=2, block=1024, grid=1)
     assert L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 64, BF16, Z, None, ctypes.byref(p), WS, WS_BYTES, None) == EUNSUP
-    p = ga.Plan(path=3, waves_per_row=1, per_lane=4, block=64, grid=1)
+    p = ga.Plan(path=4, waves_per_row=1, per_lane=4, block=64, grid=1)
     assert L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 64, BF16, Z, None, ctypes.byref(p), WS, WS_BYTES, None) == EINVAL
+    # packed rows: lanes_per_row in {4, 8, 16, 32}, 1, 2 or 4 vectors per lane, covering d
+    rows = lambda g, v, d=256, **kw: L.ga_gelu_and_mul_sparse_with_plan(  # noqa: E731
+        IN, OUT, 0, d, BF16, Z, None, ctypes.byref(ga.Plan(path=3, lanes_per_row=g, per_lane=v, **kw)),
+        WS, WS_BYTES, None)
+    assert rows(16, 2) == OK and rows(32, 1) == OK and rows(4, 4, d=128) == OK
+    assert rows(16, 1) == EUNSUP                      # 16 x 1 x 8 < 256
+    assert rows(64, 1) == EUNSUP and rows(8, 3) == EUNSUP
+    assert rows(16, 2, up_late=1) == EUNSUP
+    assert L.ga_gelu_and_mul_sparse_with_plan(ctypes.c_void_p(0x7F0000000002), OUT, 0, 256, BF16, Z, None,
+                                              ctypes.byref(ga.Plan(path=3, lanes_per_row=16, per_lane=2)),
+                                              WS, WS_BYTES, None) == EUNSUP   # needs 16-byte bases
+    # lanes_per_row belongs to the packed-rows path; reserved must be zero
+    assert L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 2048, BF16, Z, None, ctypes.byref(
+        ga.Plan(path=0, waves_per_row=4, per_lane=1, lanes_per_row=8)), WS, WS_BYTES, None) == EINVAL
+    assert rows(16, 2, reserved=1) == EINVAL
     # realigning path: must cover the most blocks a row can touch, 1..8 per lane
     wp = lambda p, d: L.ga_gelu_and_mul_sparse_with_plan(  # noqa: E731
         IN, OUT, 0, d, BF16, Z, None, ctypes.byref(p), WS, WS_BYTES, None)

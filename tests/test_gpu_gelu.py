@@ -212,6 +212,48 @@ def test_realigning_path_headline_rows():
     run_offset(xb, BF16, Z95, 1, 1, rows_sample=list(np.linspace(0, 2047, 48).astype(int)), label="realign headline")
 
 
+def _packed_plans(d, dt):
+    per = 4 if dt == F32 else 8
+    nvec = d // per
+    for g in (4, 8, 16, 32):
+        for v in (1, 2, 4):
+            if g * v >= nvec and g * (v // 2 if v > 1 else 0) < nvec:
+                yield ga.Plan(path=3, lanes_per_row=g, per_lane=v, block=256)
+
+
+@pytest.mark.parametrize("dt", [BF16, F16, F32], ids=["bf16", "f16", "f32"])
+@pytest.mark.parametrize("d", [8, 64, 128, 256])
+def test_packed_rows_every_geometry(dt, d):
+    """Short aligned rows, several per wavefront: every packed geometry that
+    covers the row, with T leaving a ragged last workgroup, matches the
+    oracle; so does the planner's choice at a large T."""
+    if dt == F32 and d > 128:
+        pytest.skip("fp32 rows of more than 32 vectors are not packed")
+    T = 203
+    x = synth.gelu_offset_rows(T, d, seed=500 + d + dt, dtype=dt)
+    plans = list(_packed_plans(d, dt))
+    assert plans
+    for p in plans:
+        run_and_check(x, dt, Z95, plan=p, label=f"packed dt{dt} d{d} g{p.lanes_per_row} v{p.per_lane}")
+    big = synth.gelu_iid(9000, d, seed=d, dtype=dt)
+    assert ga.plan_gelu_and_mul_sparse(9000, d, dt).path == 3
+    run_and_check(big, dt, Z95, rows_sample=list(range(0, 9000, 97)) + [8999], label=f"packed big dt{dt} d{d}")
+
+
+@pytest.mark.parametrize("live", [0, 1, 63, 64, 65, 200, 203, 10 ** 6, -1])
+def test_packed_rows_live_bound(live):
+    """Live counts that end inside, at and past a workgroup's rows."""
+    x = synth.gelu_iid(203, 128, seed=17)
+    run_and_check(x, BF16, Z95, live=live, label=f"packed live {live}")
+
+
+def test_packed_rows_edge_and_constant_rows():
+    for dt in (BF16, F16):
+        x = synth.edge_rows(40, 256, dt, seed=8)
+        for z in (0.0, Z95, Z99):
+            run_and_check(x, dt, z, label=f"packed edge dt{dt} z{z}")
+
+
 def test_repeat_runs_are_bit_identical():
     x = to_device(synth.gelu_large(64, 16384), BF16)
     a = ga.gelu_and_mul_sparse(x, Z95)

@@ -152,6 +152,16 @@ def test_every_geometry(geom):
     run_rt(synth.gelu_offset_rows(32, 8192), BF16, Z95, plan=plan, label=f"rt geom {geom}")
 
 
+@pytest.mark.parametrize("dt", [BF16, F16], ids=["bf16", "f16"])
+def test_packed_rows(dt):
+    """Short rows, several per wavefront (the packed-rows kernels)."""
+    for d, g, v in ((64, 4, 2), (128, 8, 2), (256, 16, 2), (256, 32, 1)):
+        x = synth.gelu_offset_rows(203, d, seed=700 + d, dtype=dt)
+        plan = ga.Plan(path=3, lanes_per_row=g, per_lane=v, block=256)
+        res = run_rt(x, dt, Z95, plan=plan, label=f"rt packed dt{dt} d{d} g{g} v{v}")
+        assert res["bitexact_frac"] > 0.98
+
+
 def test_round_trip_differs_from_default_as_the_pages_describe():
     """On bf16 the rounded cutoff moves the threshold by up to half a bf16
     step of the cutoff, so the two forms disagree on some elements; both
