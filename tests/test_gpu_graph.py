@@ -71,3 +71,66 @@ def test_graph_replay_with_changing_live_counts():
         got_q = bits_of(out_q, BF16)
         compare(got_q[:n_q], ref_q[:n_q], BF16, gate=gate_q[:n_q], stats=st_q[:, :n_q], label=f"graph split {n_q}")
         assert np.all(got_q[n_q:] == synth.SENTINEL[BF16])
+
+
+def test_graph_replay_packed_realigned_and_round_trip():
+    """The packed-rows path (short rows), the realigning path (odd d), the
+    round-trip form and gelu_and_mul captured together, replayed under
+    changing live counts and checked on every replay."""
+    o = oracle.get()
+    cases = []
+    for T, d, rt in ((1000, 128, False), (300, 2047, False), (200, 4096, True)):
+        xb = synth.gelu_offset_rows(T, d, seed=T + d)
+        if rt:
+            ref, st = o.gelu_and_mul_sparse_rt(xb, BF16, Z95)
+        else:
+            ref, st = o.gelu_and_mul_sparse(xb, BF16, Z95, want_stats=True)
+        _, out = sentinel_buffer(T, d, BF16)
+        live = torch.tensor([T], dtype=torch.int32, device="cuda")
+        cases.append(dict(T=T, d=d, rt=rt, xb=xb, x=to_device(xb, BF16), ref=ref, st=st, out=out, live=live))
+    assert ga.plan_gelu_and_mul_sparse(1000, 128, ga.GA_BF16).path == 3
+    assert ga.plan_gelu_and_mul_sparse(300, 2047, ga.GA_BF16).path == 2
+    xm_b = synth.gelu_iid(500, 1536, seed=31)
+    ref_m = o.gelu_and_mul(xm_b, BF16, True)
+    xm = to_device(xm_b, BF16)
+    _, out_m = sentinel_buffer(500, 1536, BF16)
+    live_m = torch.tensor([500], dtype=torch.int32, device="cuda")
+    sentinel = int(synth.SENTINEL[BF16])
+
+    def launch():
+        for c in cases:
+            ga.gelu_and_mul_sparse(c["x"], Z95, out=c["out"], live_rows=c["live"], round_intermediates=c["rt"])
+        ga.gelu_and_mul(xm, "tanh", out=out_m, live_rows=live_m)
+
+    launch()
+    torch.cuda.synchronize()
+    eager = [bits_of(c["out"], BF16).copy() for c in cases]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        launch()
+    torch.cuda.synchronize()
+    for step, frac in enumerate((1.0, 0.0, 0.37, 1.5, 0.01)):
+        for c in cases:
+            c["out"].view(torch.int16).fill_(sentinel)
+            c["live"].fill_(int(c["T"] * frac))
+        out_m.view(torch.int16).fill_(sentinel)
+        live_m.fill_(int(500 * frac))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for c, eg in zip(cases, eager):
+            k = min(int(c["T"] * frac), c["T"])
+            got = bits_of(c["out"], BF16)
+            label = f"graph T{c['T']} d{c['d']} rt{c['rt']} step {step}"
+            # every replay reproduces the eager launch bit for bit ...
+            assert np.array_equal(got[:k], eg[:k]), label
+            # ... which matches the oracle (the round-trip form within its
+            # cutoff-candidate rule, checked in test_gpu_roundtrip.py)
+            if not c["rt"]:
+                gate = decode(c["xb"][:k, :c["d"]], BF16)
+                compare(got[:k], c["ref"][:k], BF16, gate=gate, stats=c["st"][:, :k], label=label)
+            assert np.all(got[k:] == synth.SENTINEL[BF16]), label
+        km = min(int(500 * frac), 500)
+        got_m = bits_of(out_m, BF16)
+        compare(got_m[:km], ref_m[:km], BF16, label=f"graph gelu_and_mul step {step}")
+        assert np.all(got_m[km:] == synth.SENTINEL[BF16])
