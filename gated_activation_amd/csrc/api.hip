@@ -109,17 +109,44 @@ ga_status current_cus(int *cus) {
 constexpr uint32_t kDefaultSpinLimit = 1u << 16;
 constexpr int64_t kSplitMaxRows = 65535;  // the grid's y limit
 
-// Vectors per lane and waves for `nvec` vectors of one workgroup: 1 vector
-// per lane up to 512 vectors, 2 up to 1024, else 4 (at most max_v); enough
-// waves (at most 16) to cover them.  Measured on MI355X: wide workgroups with
-// a few vectors per lane keep the most bytes in flight per compute unit.
-void pick_waves(int64_t nvec, int max_v, int *w_out, int *v_out) {
-    int target = nvec <= 512 ? 1 : nvec <= 1024 ? 2 : 4;
-    if (target > max_v) target = max_v;
+// Waves for `nvec` vectors of one workgroup at `target` vectors per lane
+// (at most 16 waves; the vectors per lane grow to cover the rest).
+void waves_for(int64_t nvec, int target, int *w_out, int *v_out) {
     int w = next_pow2((nvec + 64 * target - 1) / (64 * target));
     if (w > 16) w = 16;
     *w_out = w;
     *v_out = next_pow2((nvec + 64 * w - 1) / (64 * w));
+}
+
+// Split-row chunks: 1 vector per lane up to 512 vectors, 2 up to 1024, else 4
+// (at most max_v).
+void pick_waves(int64_t nvec, int max_v, int *w_out, int *v_out) {
+    int target = nvec <= 512 ? 1 : nvec <= 1024 ? 2 : 4;
+    if (target > max_v) target = max_v;
+    waves_for(nvec, target, w_out, v_out);
+}
+
+// One row per workgroup: waves, vectors per lane and when to load up, from a
+// sweep of every geometry over T in 256..8192 and 128..4096 vectors per row on
+// MI355X (bf16; the choice depends on bytes, so it serves every type).
+// Loading up after the statistics frees registers for more resident rows; it
+// pays once the gate alone is >= 2^20 vectors (16 MiB) and either there are
+// >= 1024 rows or the gate is >= 2^21 vectors, else the shorter dependency
+// chain of loading up with the gate wins.  Two vectors per lane suit rows of
+// 65..1024 vectors (one for up to 256 when up comes early), four longer rows;
+// 2048-vector rows take 16 waves of 2 once there are >= 4096 rows.
+void pick_row_geometry(int64_t nvec, int64_t T, int *w_out, int *v_out, int *late_out) {
+    const int64_t gate_vectors = T * nvec;
+    const bool late = gate_vectors >= ((int64_t)1 << 20) && (T >= 1024 || gate_vectors >= ((int64_t)1 << 21));
+    int target;
+    if (nvec <= 64) target = 1;
+    else if (nvec <= 128) target = 2;
+    else if (nvec <= 256) target = late ? 2 : 1;
+    else if (nvec <= 1024) target = 2;
+    else if (nvec <= 2048) target = T >= 4096 ? 2 : 4;
+    else target = 4;
+    waves_for(nvec, target, w_out, v_out);
+    *late_out = late ? 1 : 0;
 }
 
 ga_status check_gelu_plan(const ga_plan *p, int64_t T, int64_t d, int32_t dtype) {
@@ -339,15 +366,12 @@ ga_status ga_plan_gelu_and_mul_sparse(int64_t T, int64_t d, int32_t dtype, int32
         p.lanes_per_row = g;
         p.per_lane = next_pow2((int)((nvec + g - 1) / g));
     } else if (aligned && ((size_t)d * es) % 16 == 0 && nvec <= 16 * 64 * 8) {
-        int w, v;
-        pick_waves(nvec, 8, &w, &v);
+        int w, v, late;
+        pick_row_geometry(nvec, T, &w, &v, &late);
         p.path = 0;
         p.waves_per_row = w;
         p.per_lane = v;
-        // With at least ~4 rows per compute unit, loading up after the
-        // statistics frees registers for more resident rows; with fewer rows
-        // the shorter dependency chain of loading it early wins.
-        p.up_late = T >= 1024 ? 1 : 0;
+        p.up_late = late;
         // Few long rows: split each over several workgroups that exchange
         // partial statistics.  Measured on MI355X, the exchange costs about
         // a microsecond, which pays off once a row has >= 2048 vectors
