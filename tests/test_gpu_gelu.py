@@ -122,6 +122,27 @@ def test_every_vector_geometry_matches_oracle():
         run_and_check(x, BF16, Z95, plan=p, label=f"plan w{p.waves_per_row} v{p.per_lane} late{p.up_late}")
 
 
+# Shapes at which the planner's measured rule picks each of its row
+# geometries: (T, d) -> (waves, vectors per lane, up late).
+PLANNER_SHAPES = {(1024, 1024): (1, 2, 0), (8192, 1024): (1, 2, 1), (2048, 2048): (4, 1, 0),
+                  (4096, 2048): (2, 2, 1), (1024, 4096): (4, 2, 0), (2048, 4096): (4, 2, 1),
+                  (512, 16384): (8, 4, 0), (4096, 16384): (16, 2, 1), (512, 32768): (16, 4, 1),
+                  (256, 32768): (16, 4, 0)}
+
+
+@pytest.mark.parametrize("T,d", sorted(PLANNER_SHAPES), ids=[f"T{t}-d{d}" for t, d in sorted(PLANNER_SHAPES)])
+def test_planner_geometry_at_its_shapes(T, d):
+    """The default call at each shape where the planner picks a different row
+    geometry, on sampled rows (first, last and scattered) against the oracle."""
+    p = ga.plan_gelu_and_mul_sparse(T, d, BF16)
+    assert (p.path, p.splits) == (0, 1)
+    assert (p.waves_per_row, p.per_lane, p.up_late) == PLANNER_SHAPES[(T, d)]
+    x = synth.gelu_offset_rows(T, d, seed=T * 7 + d)
+    rng = np.random.default_rng(T + d)
+    sample = list(range(16)) + list(range(T - 16, T)) + list(rng.integers(0, T, 32))
+    run_and_check(x, BF16, Z95, rows_sample=sample, label=f"planner T{T} d{d}")
+
+
 def test_element_path_on_aligned_rows():
     x = synth.gelu_offset_rows(24, 4096, seed=78)
     for w, e in ((1, 64), (4, 16), (16, 4), (4, 64), (16, 16)):
