@@ -294,7 +294,8 @@ def sweep(dev, stream, num_cus):
 
 def siblings(dev, stream):
     """The other ops of the family, graph-replayed over rotating buffers:
-    gelu_and_mul (tanh and erf), the round-trip form of gelu_and_mul_sparse
+    gelu_and_mul (tanh and erf), gelu_and_mul_sparse in fp16 and fp32, the
+    round-trip form of gelu_and_mul_sparse
     and its realigning path (a base one element off 16-byte alignment, and
     d = 16383) on the headline shape, and the bounded
     squared ReLU (not gated: read d, write d per row) on an MoE buffer."""
@@ -316,6 +317,24 @@ def siblings(dev, stream):
         res[f"gelu_and_mul_{mode}_T{T}_d{D}"] = {
             "us_per_call": round(ms * 1e3, 3), "GBps": round(bytes_call / (ms * 1e-3) / 1e9, 1),
             "pct_of_peak": round(100 * bytes_call / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2)}
+
+    # The headline op in fp16 (same bytes as bf16) and fp32 (twice the bytes).
+    for name, dt, tdt in (("fp16", synth.F16, torch.float16), ("fp32", synth.F32, torch.float32)):
+        xt = synth.gelu_large(T, D, dtype=dt)
+        npdt = np.int16 if dt == synth.F16 else np.int32
+        t0 = torch.from_numpy(xt.view(npdt)).to(dev).view(tdt)
+        b = T * 3 * D * t0.element_size()
+        k_sets = max(2, math.ceil(ROTATE_BYTES / b))
+        ts = [t0] + [t0.clone() for _ in range(k_sets - 1)]
+        touts = [torch.empty(T, D, dtype=tdt, device=dev) for _ in range(k_sets)]
+
+        def call(i, ts=ts, touts=touts):
+            ga.gelu_and_mul_sparse(ts[i], Z, out=touts[i])
+        ms = time_graph(call, k_sets, 256, 10, stream)
+        res[f"gelu_and_mul_sparse_{name}_T{T}_d{D}"] = {
+            "us_per_call": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+            "pct_of_peak": round(100 * b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2), "bytes": b}
+        del ts, touts, t0
 
     # The round-trip form of the headline op (intermediates rounded to bf16).
     def call(i):
