@@ -104,19 +104,29 @@ def time_graph(fn, n_sets, steps, warmup, stream, per_graph=64):
     return start.elapsed_time(end) / (reps * per_graph)
 
 
-def time_calls(fn, n_sets, steps, warmup, stream):
+def time_calls(fn, n_sets, steps, warmup, stream, segments=1):
+    """ms per call over exactly `steps` calls launched back to back on the
+    stream, bracketed by synchronisations.  With segments > 1, events are also
+    recorded at segment boundaries inside the same timed region (no
+    synchronisation between them) and the per-segment ms per call are
+    returned as well."""
     import torch
     for i in range(warmup):
         fn(i % n_sets)
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(steps):
-        fn(i % n_sets)
-    end.record(stream)
+    bounds = [round(k * steps / segments) for k in range(segments + 1)]
+    events = [torch.cuda.Event(enable_timing=True) for _ in bounds]
+    events[0].record(stream)
+    for k in range(segments):
+        for i in range(bounds[k], bounds[k + 1]):
+            fn(i % n_sets)
+        events[k + 1].record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps      # ms per call
+    total = events[0].elapsed_time(events[-1]) / steps      # ms per call
+    if segments == 1:
+        return total
+    seg = [events[k].elapsed_time(events[k + 1]) / max(1, bounds[k + 1] - bounds[k]) for k in range(segments)]
+    return total, seg
 
 
 def main():
@@ -151,7 +161,7 @@ def main():
     def gelu(i):
         ga.gelu_and_mul_sparse(xs[i], Z, out=outs[i])
 
-    ms = time_calls(gelu, n_sets, args.steps, args.warmup, stream)
+    ms, seg_ms = time_calls(gelu, n_sets, args.steps, args.warmup, stream, segments=5)
     gbps = bytes_call / (ms * 1e-3) / 1e9
     gelu_out = outs[0].clone()      # kept for the parity check of the CPU leg
 
@@ -177,6 +187,8 @@ def main():
             "device": f"{props.name} ({getattr(props, 'gcnArchName', '?')}, {props.multi_processor_count} CUs)",
         },
         "us_per_call": round(ms * 1e3, 3),
+        # the same timed region in five consecutive segments (events only)
+        "segments_us_per_call": [round(x * 1e3, 3) for x in seg_ms],
         "pct_of_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
         "roofline": {
             "bound": "hbm",
