@@ -134,7 +134,9 @@ void pick_waves(int64_t nvec, int max_v, int *w_out, int *v_out) {
 // >= 1024 rows or the gate is >= 2^21 vectors, else the shorter dependency
 // chain of loading up with the gate wins.  Two vectors per lane suit rows of
 // 65..1024 vectors (one for up to 256 when up comes early), four longer rows;
-// 2048-vector rows take 16 waves of 2 once there are >= 4096 rows.
+// 2048-vector rows take 16 waves of 2 once there are >= 8192 rows (an
+// interleaved A/B at d = 16384 bf16: W=8 V=4 is 3.5 % faster at 4096 rows,
+// even at 6144, W=16 V=2 2.6 % faster at 8192).
 void pick_row_geometry(int64_t nvec, int64_t T, int *w_out, int *v_out, int *late_out) {
     const int64_t gate_vectors = T * nvec;
     const bool late = gate_vectors >= ((int64_t)1 << 20) && (T >= 1024 || gate_vectors >= ((int64_t)1 << 21));
@@ -143,7 +145,7 @@ void pick_row_geometry(int64_t nvec, int64_t T, int *w_out, int *v_out, int *lat
     else if (nvec <= 128) target = 2;
     else if (nvec <= 256) target = late ? 2 : 1;
     else if (nvec <= 1024) target = 2;
-    else if (nvec <= 2048) target = T >= 4096 ? 2 : 4;
+    else if (nvec <= 2048) target = T >= 8192 ? 2 : 4;
     else target = 4;
     waves_for(nvec, target, w_out, v_out);
     *late_out = late ? 1 : 0;
