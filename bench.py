@@ -308,7 +308,7 @@ def siblings(dev, stream):
     """The other ops of the family, graph-replayed over rotating buffers:
     gelu_and_mul (tanh and erf), gelu_and_mul_sparse in fp16 and fp32, the
     round-trip form of gelu_and_mul_sparse
-    and its realigning path (a base one element off 16-byte alignment, and
+    and its unaligned path (a base one element off 16-byte alignment, and
     d = 16383) on the headline shape, and the bounded
     squared ReLU (not gated: read d, write d per row) on an MoE buffer."""
     import numpy as np
@@ -356,7 +356,7 @@ def siblings(dev, stream):
         "us_per_call": round(ms * 1e3, 3), "GBps": round(bytes_call / (ms * 1e-3) / 1e9, 1),
         "pct_of_peak": round(100 * bytes_call / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2)}
 
-    # Rows off 16-byte alignment (the realigning path): the headline input
+    # Rows off 16-byte alignment (the unaligned path): the headline input
     # viewed one element past a 16-byte boundary, and an odd d.
     bases = [torch.empty(x0.numel() + 8, dtype=torch.bfloat16, device=dev) for _ in range(n_sets)]
     shifted = [b[1:1 + x0.numel()].view(T, 2 * D) for b in bases]

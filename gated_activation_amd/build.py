@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libga.so")
-SOURCES = ["api.hip", "gelu_sparse.hip", "gelu_sparse_split.hip", "gelu_sparse_realign.hip", "gelu_sparse_rows.hip",
+SOURCES = ["api.hip", "gelu_sparse.hip", "gelu_sparse_split.hip", "gelu_sparse_unaligned.hip", "gelu_sparse_rows.hip",
            "elementwise.hip"]
 ARCH = "gfx950"
 

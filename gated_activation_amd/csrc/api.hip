@@ -15,7 +15,6 @@
 
 #include "../../include/ga.h"
 #include "ga_internal.h"
-#include "ga_realign.h"
 
 namespace {
 
@@ -188,13 +187,13 @@ ga_status check_gelu_plan(const ga_plan *p, int64_t T, int64_t d, int32_t dtype)
         if ((int64_t)p->lanes_per_row * p->per_lane * per16 < d)
             return fail(GA_EUNSUPPORTED, "gelu plan: geometry covers fewer than d elements");
     } else if (p->path == 2) {
-        if (p->splits != 1) return fail(GA_EUNSUPPORTED, "gelu plan: the realigning path does not split rows");
-        if (!ga::gelu_realign_available(dtype, p->waves_per_row, p->per_lane, p->up_late))
-            return fail(GA_EUNSUPPORTED, "gelu plan: no realigning kernel for waves=%d per_lane=%d up_late=%d",
+        if (p->splits != 1) return fail(GA_EUNSUPPORTED, "gelu plan: the unaligned path does not split rows");
+        if (!ga::gelu_unaligned_available(dtype, p->waves_per_row, p->per_lane, p->up_late))
+            return fail(GA_EUNSUPPORTED, "gelu plan: no unaligned-path kernel for waves=%d per_lane=%d up_late=%d",
                         p->waves_per_row, p->per_lane, p->up_late);
-        const int32_t per = 16 / (int32_t)elem_size(dtype);
-        if ((int64_t)p->waves_per_row * 64 * p->per_lane < ga::realign_blocks_max((int32_t)d, per))
-            return fail(GA_EUNSUPPORTED, "gelu plan: geometry covers fewer than the row's 16-byte blocks");
+        const int64_t per16 = 16 / (int64_t)elem_size(dtype);
+        if ((int64_t)p->waves_per_row * 64 * p->per_lane < (d + per16 - 1) / per16)
+            return fail(GA_EUNSUPPORTED, "gelu plan: geometry covers fewer than the row's 16-byte vectors");
     } else if (p->path == 1) {
         if (p->splits != 1) return fail(GA_EUNSUPPORTED, "gelu plan: the element path does not split rows");
         if (!ga::gelu_elem_available(dtype, p->waves_per_row, p->per_lane))
@@ -242,8 +241,8 @@ ga_status launch_gelu(const void *in, void *out, int64_t T, int64_t d, int32_t d
                                                    (int32_t)d, nvec, z, live, s));
     }
     if (p.path == 2)
-        return launched(name, ga::launch_gelu_realign(dtype, p.waves_per_row, p.per_lane, p.up_late, rt, T, in, out,
-                                                      (int32_t)T, (int32_t)d, z, live, s));
+        return launched(name, ga::launch_gelu_unaligned(dtype, p.waves_per_row, p.per_lane, p.up_late, rt, T, in,
+                                                        out, (int32_t)T, (int32_t)d, z, live, s));
     return launched(name, ga::launch_gelu_elem(dtype, p.waves_per_row, p.per_lane, rt, T, in, out, (int32_t)T,
                                                (int32_t)d, z, live, s));
 }
@@ -393,25 +392,16 @@ ga_status ga_plan_gelu_and_mul_sparse(int64_t T, int64_t d, int32_t dtype, int32
                 p.splits = (int32_t)splits;
             }
         }
-    } else if (ga::realign_blocks_max((int32_t)d, (int32_t)(16 / es)) <= 16 * 64 * 8) {
-        // Rows that are not 16-byte aligned: 16-byte blocks in each stream's
-        // own alignment, realigned through LDS.  Measured on MI355X: with
-        // many rows (T >= 1024) the smallest workgroup (>= 2 waves) that
-        // needs at most 5 blocks per lane, with up loaded chunk by chunk,
-        // keeps the most rows resident; with fewer rows, wide workgroups
-        // with about 2 blocks per lane and up loaded with the gate.
-        const int64_t blocks = ga::realign_blocks_max((int32_t)d, (int32_t)(16 / es));
-        int w;
-        if (T >= 1024) {
-            w = 2;
-            while (w < 16 && (blocks + 64 * w - 1) / (64 * w) > 5) w *= 2;
-        } else {
-            w = std::min(16, next_pow2((blocks + 127) / 128));
-        }
+    } else if ((d * (int64_t)es + 15) / 16 <= 16 * 64 * 8) {
+        // Rows that are not 16-byte aligned: the same vectors, each one
+        // unaligned 16-byte access, with the geometry of the vector path.
+        const int64_t nv = (d * (int64_t)es + 15) / 16;
+        int w, v, late;
+        pick_row_geometry(nv, T, &w, &v, &late);
         p.path = 2;
         p.waves_per_row = w;
-        p.per_lane = (int32_t)((blocks + 64 * w - 1) / (64 * w));
-        p.up_late = T >= 1024 ? 1 : 0;
+        p.per_lane = v;
+        p.up_late = late;
     } else {
         // Element path: up to 16 elements per lane, 1, 4 or 16 waves.
         const int64_t lanes = (d + 15) / 16;

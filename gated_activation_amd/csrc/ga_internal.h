@@ -38,14 +38,14 @@ hipError_t launch_gelu_rows(int dtype, int lanes_per_row, int vec_per_lane, bool
                             const void *in, void *out, int32_t T, int32_t d, int32_t nvec, float z,
                             const int32_t *live, hipStream_t stream);
 
-// Realigning path for rows that are not 16-byte aligned: waves 1, 2, 4, 8,
-// 16; vectors per lane 1 .. 8 (16-byte blocks per lane, covering the most
-// blocks a row can touch); up_late 0 (up loaded with the gate) or 1 (chunk
-// by chunk after the statistics).
-bool gelu_realign_available(int dtype, int waves, int vec_per_lane, int up_late);
-hipError_t launch_gelu_realign(int dtype, int waves, int vec_per_lane, int up_late, bool round_trip, int64_t grid,
-                               const void *in, void *out, int32_t T, int32_t d, float z,
-                               const int32_t *live, hipStream_t stream);
+// Unaligned path for rows that are not 16-byte aligned: waves 1, 2, 4, 8, 16;
+// vectors per lane 1 .. 8 (vector j = elements [j * 16 / es, (j + 1) * 16 / es),
+// one unaligned 16-byte access); up_late 0 (up loaded with the gate) or 1
+// (one vector at a time after the statistics).
+bool gelu_unaligned_available(int dtype, int waves, int vec_per_lane, int up_late);
+hipError_t launch_gelu_unaligned(int dtype, int waves, int vec_per_lane, int up_late, bool round_trip,
+                                 int64_t grid, const void *in, void *out, int32_t T, int32_t d, float z,
+                                 const int32_t *live, hipStream_t stream);
 
 // round_trip selects the form that rounds each intermediate (mean, std, z,
 // z * std, cutoff, gate - cutoff, GELU output) to the element type.

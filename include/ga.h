@@ -37,9 +37,11 @@
  *     aligned (GA_EINVAL otherwise).
  *   - Any alignment natural to the element type is accepted; when in and out
  *     are 16-byte aligned and a row's bytes are a multiple of 16, 16-byte
- *     vector loads and stores are used.  Otherwise gelu_and_mul_sparse moves
- *     each stream in its own 16-byte blocks and realigns them through LDS
- *     (rows up to 8192 blocks), and the other ops take a per-element path.
+ *     vector loads and stores are used.  Otherwise gelu_and_mul_sparse still
+ *     moves each row as 16-byte vectors of consecutive elements, each one
+ *     unaligned 16-byte access (rows up to 8192 vectors; gfx950 runs global
+ *     memory in unaligned-access mode), and the other ops take a
+ *     per-element path.
  */
 #ifndef GA_H
 #define GA_H
@@ -70,16 +72,16 @@ typedef void *ga_stream;
  * specific geometry (a tuning sweep); see ga_gelu_and_mul_sparse_with_plan. */
 typedef struct {
     int32_t path;          /* 0: 16-byte vector path, 1: per-element path,
-                              2: gelu realigning path (rows off 16-byte alignment),
+                              2: gelu unaligned path (rows off 16-byte alignment),
                               3: gelu packed-rows path (short aligned rows, several
                               rows per wavefront) */
     int32_t waves_per_row; /* gelu: 64-lane wavefronts per workgroup (1,2,4,8,16) */
     int32_t per_lane;      /* gelu vector path: 16-byte gate vectors per lane (1,2,4,8;
                               split rows 1,2,4); gelu element path: gate elements per
-                              lane (4,16,64); gelu realigning path: 16-byte blocks per
+                              lane (4,16,64); gelu unaligned path: 16-byte vectors per
                               lane (1..8); gelu packed rows: vectors per lane (1,2,4);
                               silu: items per lane per step (1,2,4) */
-    int32_t up_late;       /* gelu vector and realigning paths: 0 = load the up row together
+    int32_t up_late;       /* gelu vector and unaligned paths: 0 = load the up row together
                               with the gate row (shortest latency), 1 = load it after the
                               statistics, a vector (a chunk) at a time (fewer registers, more
                               rows resident); split rows: 0 only */
@@ -223,10 +225,10 @@ ga_status ga_plan_silu_and_mul_bounded(int64_t M, int64_t d, int32_t dtype, int3
  * (the values listed in ga_plan) and cover the row: vector path
  * splits * waves_per_row * 64 * per_lane * (16 / element size) >= d, with
  * every split owning at least one vector; element path
- * waves_per_row * 64 * per_lane >= d; realigning path (any alignment)
- * waves_per_row * 64 * per_lane >= (d + 2 * e - 2) / e with e = 16 / element
- * size (the most 16-byte blocks a row can touch); packed rows (16-byte rows
- * and bases only) lanes_per_row * per_lane * e >= d; else GA_EUNSUPPORTED.
+ * waves_per_row * 64 * per_lane >= d; unaligned path (any alignment)
+ * waves_per_row * 64 * per_lane * e >= d with e = 16 / element size;
+ * packed rows (16-byte rows and bases only) lanes_per_row * per_lane * e >= d;
+ * else GA_EUNSUPPORTED.
  * `block` and
  * `grid` are derived for gelu; silu takes its grid from the plan.  A split
  * plan needs the workspace described above (else GA_EINVAL) and T <= 65535.

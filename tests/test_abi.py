@@ -136,17 +136,20 @@ def test_gelu_planner_known_shapes():
     # without a workspace the rows are never split
     p = ga.plan_gelu_and_mul_sparse(1, 32768, BF16, with_workspace=False)
     assert (p.splits, p.waves_per_row, p.per_lane) == (1, 16, 4)
-    p = ga.plan_gelu_and_mul_sparse(7, 8191, F16)            # odd d: realigning path
-    assert p.path == 2 and p.splits == 1 and p.waves_per_row * 64 * p.per_lane >= (8191 + 14) // 8
-    p = ga.plan_gelu_and_mul_sparse(7, 8192, F16, aligned=False)    # few rows: wide, 2 blocks per lane
-    assert (p.path, p.waves_per_row, p.per_lane, p.up_late) == (2, 16, 2, 0)
-    p = ga.plan_gelu_and_mul_sparse(2048, 8191, BF16)                 # many rows: narrow, up late
-    assert (p.path, p.waves_per_row, p.per_lane, p.up_late) == (2, 4, 5, 1)
+    # rows off 16-byte alignment: the unaligned path, with the vector path's geometry rule
+    p = ga.plan_gelu_and_mul_sparse(7, 8191, F16)            # odd d
+    assert p.path == 2 and p.splits == 1 and p.waves_per_row * 64 * p.per_lane >= (8191 + 7) // 8
+    p = ga.plan_gelu_and_mul_sparse(7, 8192, F16, aligned=False)
+    assert (p.path, p.waves_per_row, p.per_lane, p.up_late) == (2, 8, 2, 0)
+    p = ga.plan_gelu_and_mul_sparse(2048, 8191, BF16)
+    assert p.path == 2 and p.up_late == 1 and p.waves_per_row * 64 * p.per_lane >= 1024
     p = ga.plan_gelu_and_mul_sparse(2048, 511, BF16)
-    assert (p.path, p.waves_per_row, p.per_lane, p.up_late) == (2, 2, 1, 1)
+    assert (p.path, p.waves_per_row, p.per_lane, p.up_late) == (2, 1, 1, 0)
     p = ga.plan_gelu_and_mul_sparse(7, 65536, F32)           # beyond the vector reach
     assert p.path == 1 and p.waves_per_row * 64 * p.per_lane >= 65536
-    p = ga.plan_gelu_and_mul_sparse(7, 65536, BF16, aligned=False)   # 8193 blocks: element path
+    p = ga.plan_gelu_and_mul_sparse(7, 65536, BF16, aligned=False)   # 8192 vectors: still unaligned path
+    assert (p.path, p.waves_per_row, p.per_lane) == (2, 16, 8)
+    p = ga.plan_gelu_and_mul_sparse(7, 32769, F32, aligned=False)    # 8193 vectors: element path
     assert p.path == 1
 
 
@@ -235,11 +238,12 @@ def test_gelu_with_plan_rejects_bad_geometry():
     assert L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 2048, BF16, Z, None, ctypes.byref(
         ga.Plan(path=0, waves_per_row=4, per_lane=1, lanes_per_row=8)), WS, WS_BYTES, None) == EINVAL
     assert rows(16, 2, reserved=1) == EINVAL
-    # realigning path: must cover the most blocks a row can touch, 1..8 per lane
+    # unaligned path: must cover the row's 16-byte vectors, 1..8 per lane
     wp = lambda p, d: L.ga_gelu_and_mul_sparse_with_plan(  # noqa: E731
         IN, OUT, 0, d, BF16, Z, None, ctypes.byref(p), WS, WS_BYTES, None)
-    assert wp(ga.Plan(path=2, waves_per_row=8, per_lane=5, block=512), 16384) == OK     # 2049 blocks
-    assert wp(ga.Plan(path=2, waves_per_row=8, per_lane=4, block=512), 16384) == EUNSUP  # 2048 < 2049
+    assert wp(ga.Plan(path=2, waves_per_row=8, per_lane=4, block=512), 16384) == OK     # 2048 vectors
+    assert wp(ga.Plan(path=2, waves_per_row=8, per_lane=4, block=512), 16385) == EUNSUP  # 2049 > 2048
+    assert wp(ga.Plan(path=2, waves_per_row=8, per_lane=5, block=512), 16385) == OK
     assert wp(ga.Plan(path=2, waves_per_row=8, per_lane=9, block=512), 16384) == EUNSUP
     assert wp(ga.Plan(path=2, waves_per_row=3, per_lane=8, block=192), 64) == EUNSUP
     assert wp(ga.Plan(path=2, waves_per_row=8, per_lane=5, up_late=1, block=512), 16384) == OK

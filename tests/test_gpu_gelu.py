@@ -152,7 +152,7 @@ def test_element_path_on_aligned_rows():
 
 @pytest.mark.parametrize("shift", [1, 3, 7])
 def test_misaligned_base_pointers(shift):
-    """Bases off 16-byte alignment by `shift` elements (the realigning path)."""
+    """Bases off 16-byte alignment by `shift` elements (the unaligned path)."""
     T, d = 9, 2048
     xb = synth.gelu_iid(T, d, seed=shift)
     flat = torch.zeros(T * 2 * d + 16, dtype=torch.bfloat16, device="cuda")
@@ -175,8 +175,8 @@ def run_offset(xb, dt, z, in_shift, out_shift, plan=None, rows_sample=None, labe
     T, two_d = xb.shape
     d = two_d // 2
     tdt = TORCH_DTYPE[dt]
-    # NaN around the input view: an end block that reaches past the row
-    # reads these, and they must not reach the statistics or the output.
+    # NaN around the input view: a read past the view would bring NaN into
+    # the statistics or the output.
     flat = torch.full((T * two_d + 16,), float("nan"), dtype=tdt, device="cuda")
     x = flat[in_shift: in_shift + T * two_d].view(T, two_d)
     x.copy_(to_device(xb, dt))
@@ -195,10 +195,13 @@ def run_offset(xb, dt, z, in_shift, out_shift, plan=None, rows_sample=None, labe
 
 @pytest.mark.parametrize("dt", [BF16, F16, F32], ids=["bf16", "f16", "f32"])
 @pytest.mark.parametrize("d", [1, 5, 31, 1000, 8191, 16383, 16384])
-def test_realigning_path_every_phase_mix(dt, d):
+def test_unaligned_path_every_phase_mix(dt, d):
     """Rows off a 16-byte boundary (shifted bases, odd d: phases change from
-    row to row) take the realigning path; input and output shifts vary
-    independently."""
+    row to row) take the unaligned path; input and output shifts vary
+    independently.  With odd d every row but the last reads its partial last
+    up vector whole (into the next row) and the last row element by element;
+    tiny d (1, 5) also reads the gate's partial vector element by element near
+    the end of the buffer."""
     T = 37 if d <= 8191 else 9
     xb = synth.gelu_iid(T, d, seed=300 + d + dt, dtype=dt, gate_std=1.4)
     per = 4 if dt == F32 else 8
@@ -207,30 +210,30 @@ def test_realigning_path_every_phase_mix(dt, d):
             continue
         plan = ga.plan_gelu_and_mul_sparse(T, d, dt, aligned=False)
         assert plan.path == 2
-        run_offset(xb, dt, Z95, i_s, o_s, label=f"realign dt{dt} d{d} shifts {i_s},{o_s}")
+        run_offset(xb, dt, Z95, i_s, o_s, label=f"unaligned dt{dt} d{d} shifts {i_s},{o_s}")
 
 
-def test_realigning_path_every_geometry():
-    """Every realigning geometry that covers the row, with up loaded early or
-    late, on shifted and on aligned rows, matches the oracle."""
-    d = 8192
+def test_unaligned_path_every_geometry():
+    """Every unaligned-path geometry that covers the row, with up loaded
+    early or late, on shifted and on aligned rows, matches the oracle."""
+    d = 8191
     xb = synth.gelu_offset_rows(12, d, seed=79)
-    nblk = (d + 14) // 8
+    nvec = (d + 7) // 8
     for w in (1, 2, 4, 8, 16):
         for v in range(1, 9):
-            if w * 64 * v < nblk:
+            if w * 64 * v < nvec:
                 continue
             for late in (0, 1):
                 p = ga.Plan(path=2, waves_per_row=w, per_lane=v, up_late=late, block=64 * w)
                 for i_s, o_s in ((0, 0), (5, 2), (2, 5)):
                     run_offset(xb, BF16, Z95, i_s, o_s, plan=p,
-                               label=f"realign w{w} v{v} late{late} shifts {i_s},{o_s}")
+                               label=f"unaligned w{w} v{v} late{late} shifts {i_s},{o_s}")
 
 
-def test_realigning_path_headline_rows():
+def test_unaligned_path_headline_rows():
     """T = 2048, d = 16384 bf16 one element off alignment (sampled rows)."""
     xb = synth.gelu_large(2048, 16384)
-    run_offset(xb, BF16, Z95, 1, 1, rows_sample=list(np.linspace(0, 2047, 48).astype(int)), label="realign headline")
+    run_offset(xb, BF16, Z95, 1, 1, rows_sample=list(np.linspace(0, 2047, 48).astype(int)), label="unaligned headline")
 
 
 def _packed_plans(d, dt):

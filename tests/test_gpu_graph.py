@@ -73,8 +73,8 @@ def test_graph_replay_with_changing_live_counts():
         assert np.all(got_q[n_q:] == synth.SENTINEL[BF16])
 
 
-def test_graph_replay_packed_realigned_and_round_trip():
-    """The packed-rows path (short rows), the realigning path (odd d), the
+def test_graph_replay_packed_unaligned_and_round_trip():
+    """The packed-rows path (short rows), the unaligned path (odd d), the
     round-trip form and gelu_and_mul captured together, replayed under
     changing live counts and checked on every replay."""
     o = oracle.get()

@@ -120,7 +120,7 @@ def test_token_sweep_d8192(T):
 @pytest.mark.parametrize("dt", [BF16, F16, F32], ids=["bf16", "f16", "f32"])
 @pytest.mark.parametrize("d", [1, 31, 128, 4096, 16384])
 def test_dtypes_and_sizes(dt, d):
-    """The page's small d (1, 31, 128: element path for odd d) and larger rows."""
+    """The page's small d (1, 31, 128; odd d takes the unaligned path) and larger rows."""
     T = 64 if d <= 4096 else 16
     x = synth.gelu_iid(T, d, seed=d + 17 * dt, dtype=dt)
     res = run_rt(x, dt, Z95, label=f"rt {dt} d{d}")
@@ -143,7 +143,7 @@ def test_live_rows():
 
 
 @pytest.mark.parametrize("geom", [(0, 16, 1, 0), (0, 8, 2, 0), (0, 4, 4, 1), (0, 2, 8, 1), (1, 16, 16, 0),
-                                  (2, 8, 3, 0), (2, 4, 5, 0)],
+                                  (2, 8, 3, 0), (2, 4, 5, 0), (2, 8, 2, 1)],
                          ids=lambda g: f"path{g[0]}_w{g[1]}_pl{g[2]}_late{g[3]}")
 def test_every_geometry(geom):
     """The form is the same for any launch geometry of d = 8192 bf16."""
