@@ -151,6 +151,10 @@ def test_gelu_planner_known_shapes():
     assert (p.path, p.waves_per_row, p.per_lane) == (2, 16, 8)
     p = ga.plan_gelu_and_mul_sparse(7, 32769, F32, aligned=False)    # 8193 vectors: element path
     assert p.path == 1
+    p = ga.plan_gelu_and_mul_sparse(8192, 16383, BF16)     # 2048 vectors: 8 waves of 4 at any T
+    assert (p.path, p.waves_per_row, p.per_lane, p.up_late) == (2, 8, 4, 1)
+    p = ga.plan_gelu_and_mul_sparse(8192, 2047, BF16)      # 256 vectors: one per lane
+    assert (p.path, p.waves_per_row, p.per_lane, p.up_late) == (2, 4, 1, 1)
 
 
 def test_workspace_size_and_split_plan_checks():
