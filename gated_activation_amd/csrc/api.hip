@@ -271,10 +271,19 @@ constexpr int64_t kMaxItems = (int64_t)1 << 31;
 // beyond, and up to 32 workgroups per compute unit beyond 4M items.  The
 // grid-stride loop covers the rest.  The grid depends on the capacity, never
 // on a live count.
+// 16-byte items of a plan: whole-row vectors (path 0), elements (path 1), or
+// vectors numbered flat over the output region (path 2, the last one partial).
+int64_t act_items(int path, int64_t rows, int64_t d, size_t es) {
+    const int64_t per = 16 / (int64_t)es;
+    return path == 0 ? rows * (d / per) : path == 1 ? rows * d : (rows * d + per - 1) / per;
+}
+
 ga_plan plan_act(int64_t rows, int64_t d, size_t es, bool aligned, int num_cus) {
     ga_plan p{};
-    p.path = (aligned && ((size_t)d * es) % 16 == 0) ? 0 : 1;
-    const int64_t items = rows * (p.path == 0 ? d * (int64_t)es / 16 : d);
+    // Rows off 16-byte alignment take unaligned 16-byte vectors (measured on
+    // MI355X: 1.3-2x the per-element path, which stays for explicit plans).
+    p.path = (aligned && ((size_t)d * es) % 16 == 0) ? 0 : 2;
+    const int64_t items = act_items(p.path, rows, d, es);
     p.per_lane = items > ((int64_t)2 << 20) ? 2 : 1;
     p.waves_per_row = 0;
     p.splits = 1;
@@ -293,12 +302,12 @@ ga_status check_act_plan(const ga_plan *p, int op, int64_t rows, int64_t d, int3
     if (!ga::act_available(op, p->path, dtype, p->per_lane))
         return fail(GA_EUNSUPPORTED, "plan: no kernel for path=%d per_lane=%d", p->path, p->per_lane);
     if (p->grid < 1 || p->grid > INT32_MAX) return fail(GA_EINVAL, "plan: grid %lld", (long long)p->grid);
-    const int64_t items_row = p->path == 0 ? d * (int64_t)elem_size(dtype) / 16 : d;
     // The kernels step through items with 32-bit counters: both the region
-    // and one grid-wide step must stay below 2^31 so their sum cannot wrap.
+    // and one grid-wide step must stay below 2^31 so their sum cannot wrap;
+    // paths 1 and 2 also index elements of the region with 32 bits.
     if (p->grid * ga::SILU_BLOCK * p->per_lane > kMaxItems)
         return fail(GA_EUNSUPPORTED, "plan: grid too large for 32-bit item indices");
-    if (rows * items_row >= kMaxItems)
+    if (act_items(p->path, rows, d, elem_size(dtype)) >= kMaxItems || (p->path != 0 && rows * d >= kMaxItems))
         return fail(GA_EUNSUPPORTED, "plan: rows * d too large for 32-bit item indices");
     return GA_OK;
 }

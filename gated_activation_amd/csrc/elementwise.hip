@@ -119,6 +119,108 @@ __global__ __launch_bounds__(SILU_BLOCK) void act_elem_kernel(
     }
 }
 
+// Rows off 16-byte alignment (a shifted base, or d * element size not a
+// multiple of 16).  The live region of the output is contiguous, so its
+// 16-byte vectors are numbered flat over it and every one but the region's
+// last is written whole: vector j holds output elements [PER j, PER j + PER),
+// each vector one 16-byte access at the element's own alignment (gfx950 runs
+// global memory in unaligned-access mode).  A vector inside one row reads its
+// gate and up as one 16-byte access each, one that straddles a row boundary a
+// third for the next row's up; the region's partial last vector, and every
+// vector when d is below 16 bytes, go element by element.
+template <int DT, int PL, int OP>
+__global__ __launch_bounds__(SILU_BLOCK) void act_una_kernel(
+    const typename Elem<DT>::storage *__restrict__ in, typename Elem<DT>::storage *__restrict__ out,
+    int32_t M, uint32_t d, const int32_t *__restrict__ live) {
+    using E = Elem<DT>;
+    using S = typename E::storage;
+    typedef u32x4 u32x4_a2 __attribute__((aligned(2)));
+    constexpr int PER = E::PER16;
+    constexpr uint32_t CHUNK = SILU_BLOCK * PL;
+    constexpr bool GATED = op_gated(OP);
+    const uint32_t rows = live != nullptr ? (uint32_t)clamp_live(live, M) : (uint32_t)M;
+    const uint32_t total = rows * d;  // live output elements
+    const uint32_t nitems = (total + PER - 1) / PER;
+    const uint32_t step = gridDim.x * CHUNK;
+    for (uint32_t base = blockIdx.x * CHUNK + threadIdx.x; base < nitems; base += step) {
+#pragma unroll
+        for (int k = 0; k < PL; ++k) {
+            const uint32_t j = base + k * SILU_BLOCK;
+            if (j >= nitems) continue;
+            const uint32_t e0 = j * PER;
+            const bool full = e0 + PER <= total;
+            float g[PER], u[PER], y[PER];
+            if constexpr (GATED) {
+                const uint32_t row = e0 / d;
+                const uint32_t c0 = e0 - row * d;
+                if (full && d >= (uint32_t)PER) {
+                    // gate[row][c0..] and up[row][c0..]; a vector that runs
+                    // past the row (d >= PER: into the next row only) takes
+                    // its gate tail from the same 16 bytes as up (they run
+                    // on into the next row's gate) and its up tail from the
+                    // next row, at the same column.
+                    const size_t off = (size_t)row * 2 * d + c0;
+                    const u32x4 gw = __builtin_nontemporal_load(reinterpret_cast<const u32x4_a2 *>(in + off));
+                    const u32x4 mw = __builtin_nontemporal_load(reinterpret_cast<const u32x4_a2 *>(in + off + d));
+                    E::unpack(uint4{gw.x, gw.y, gw.z, gw.w}, g);
+                    E::unpack(uint4{mw.x, mw.y, mw.z, mw.w}, u);
+                    if (c0 + PER > d) {
+                        const u32x4 bw =
+                            __builtin_nontemporal_load(reinterpret_cast<const u32x4_a2 *>(in + off + 2 * (size_t)d));
+                        float m[PER], b[PER];
+                        E::unpack(uint4{mw.x, mw.y, mw.z, mw.w}, m);
+                        E::unpack(uint4{bw.x, bw.y, bw.z, bw.w}, b);
+                        const uint32_t k = d - c0;  // elements of the vector in this row
+#pragma unroll
+                        for (int e = 0; e < PER; ++e) {
+                            g[e] = (uint32_t)e < k ? g[e] : m[e];
+                            u[e] = (uint32_t)e < k ? u[e] : b[e];
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < PER; ++e) {
+                        const uint32_t i = e0 + e;
+                        g[e] = 0.0f;
+                        u[e] = 0.0f;
+                        if (i < total) {
+                            const uint32_t r = i / d;
+                            const size_t off = (size_t)r * 2 * d + (i - r * d);
+                            g[e] = E::to_f32(in[off]);
+                            u[e] = E::to_f32(in[off + d]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < PER; ++e) y[e] = activation<OP>(g[e]) * u[e];
+            } else {
+                if (full) {
+                    const u32x4 gw = __builtin_nontemporal_load(reinterpret_cast<const u32x4_a2 *>(in + e0));
+                    E::unpack(uint4{gw.x, gw.y, gw.z, gw.w}, g);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < PER; ++e) g[e] = e0 + e < total ? E::to_f32(in[e0 + e]) : 0.0f;
+                }
+#pragma unroll
+                for (int e = 0; e < PER; ++e) y[e] = activation<OP>(g[e]);
+            }
+            const uint4 o = E::pack(y);
+            if (full) {
+                __builtin_nontemporal_store(u32x4{o.x, o.y, o.z, o.w}, reinterpret_cast<u32x4_a2 *>(out + e0));
+            } else {
+                const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+                for (int e = 0; e < PER; ++e) {
+                    if (e0 + e < total) {
+                        if constexpr (PER == 4) out[e0 + e] = (S)w[e];
+                        else out[e0 + e] = (S)(w[e >> 1] >> ((e & 1) * 16));
+                    }
+                }
+            }
+        }
+    }
+}
+
 // Streaming ceiling with the same access pattern: read both halves of each
 // row 16 bytes at a time, write their XOR.
 template <bool NONTEMP = true>
@@ -151,20 +253,25 @@ __global__ __launch_bounds__(SILU_BLOCK) void xor_rows_kernel(const uint4 *__res
 
 namespace {
 
-// Index [op][path][dtype][per-lane index].
+// Index [op][path (vector, element, unaligned vector)][dtype][per-lane index].
 #define GA_AV(OP, DT) \
     { (const void *)&act_vec_kernel<DT, 1, OP>, (const void *)&act_vec_kernel<DT, 2, OP>, \
       (const void *)&act_vec_kernel<DT, 4, OP> }
 #define GA_AE(OP, DT) \
     { (const void *)&act_elem_kernel<DT, 1, OP>, (const void *)&act_elem_kernel<DT, 2, OP>, \
       (const void *)&act_elem_kernel<DT, 4, OP> }
+#define GA_AU(OP, DT) \
+    { (const void *)&act_una_kernel<DT, 1, OP>, (const void *)&act_una_kernel<DT, 2, OP>, \
+      (const void *)&act_una_kernel<DT, 4, OP> }
 #define GA_AOP(OP) \
     { {GA_AV(OP, DT_F32), GA_AV(OP, DT_F16), GA_AV(OP, DT_BF16)}, \
-      {GA_AE(OP, DT_F32), GA_AE(OP, DT_F16), GA_AE(OP, DT_BF16)} }
-const void *const kAct[OP_COUNT][2][3][3] = {GA_AOP(OP_SILU_MUL), GA_AOP(OP_GELU_TANH_MUL),
+      {GA_AE(OP, DT_F32), GA_AE(OP, DT_F16), GA_AE(OP, DT_BF16)}, \
+      {GA_AU(OP, DT_F32), GA_AU(OP, DT_F16), GA_AU(OP, DT_BF16)} }
+const void *const kAct[OP_COUNT][3][3][3] = {GA_AOP(OP_SILU_MUL), GA_AOP(OP_GELU_TANH_MUL),
                                              GA_AOP(OP_GELU_ERF_MUL), GA_AOP(OP_SQUARED_RELU)};
 #undef GA_AV
 #undef GA_AE
+#undef GA_AU
 #undef GA_AOP
 
 int pl_index(int pl) { return pl == 1 ? 0 : pl == 2 ? 1 : pl == 4 ? 2 : -1; }
@@ -172,7 +279,7 @@ int pl_index(int pl) { return pl == 1 ? 0 : pl == 2 ? 1 : pl == 4 ? 2 : -1; }
 }  // namespace
 
 bool act_available(int op, int path, int dtype, int per_lane) {
-    return op >= 0 && op < OP_COUNT && (path == 0 || path == 1) && dtype >= 0 && dtype <= 2 &&
+    return op >= 0 && op < OP_COUNT && path >= 0 && path <= 2 && dtype >= 0 && dtype <= 2 &&
            pl_index(per_lane) >= 0;
 }
 

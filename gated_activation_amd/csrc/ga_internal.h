@@ -58,7 +58,9 @@ hipError_t launch_gelu_elem(int dtype, int waves, int elem_per_lane, bool round_
                             float z, const int32_t *live, hipStream_t stream);
 
 // path 0: 16-byte items (nitems_row = d / elements per 16 bytes),
-// path 1: single elements (nitems_row = d).  live may be null (all M rows).
+// path 1: single elements (nitems_row = d), path 2: unaligned 16-byte vectors
+// numbered flat over the live output region (nitems_row = d).  live may be
+// null (all M rows).
 hipError_t launch_act(int op, int path, int dtype, int per_lane, int64_t grid, const void *in, void *out,
                       int32_t M, uint32_t nitems_row, const int32_t *live, hipStream_t stream);
 

@@ -37,11 +37,11 @@
  *     aligned (GA_EINVAL otherwise).
  *   - Any alignment natural to the element type is accepted; when in and out
  *     are 16-byte aligned and a row's bytes are a multiple of 16, 16-byte
- *     vector loads and stores are used.  Otherwise gelu_and_mul_sparse still
- *     moves each row as 16-byte vectors of consecutive elements, each one
- *     unaligned 16-byte access (rows up to 8192 vectors; gfx950 runs global
- *     memory in unaligned-access mode), and the other ops take a
- *     per-element path.
+ *     vector loads and stores are used.  Otherwise the data still moves as
+ *     16-byte vectors of consecutive elements, each one unaligned 16-byte
+ *     access (gfx950 runs global memory in unaligned-access mode):
+ *     gelu_and_mul_sparse per row (rows up to 8192 vectors), the other ops
+ *     flat over the output region.
  */
 #ifndef GA_H
 #define GA_H
@@ -72,7 +72,8 @@ typedef void *ga_stream;
  * specific geometry (a tuning sweep); see ga_gelu_and_mul_sparse_with_plan. */
 typedef struct {
     int32_t path;          /* 0: 16-byte vector path, 1: per-element path,
-                              2: gelu unaligned path (rows off 16-byte alignment),
+                              2: unaligned path (rows off 16-byte alignment; gelu: per
+                                 row, the elementwise ops: flat over the output),
                               3: gelu packed-rows path (short aligned rows, several
                               rows per wavefront) */
     int32_t waves_per_row; /* gelu: 64-lane wavefronts per workgroup (1,2,4,8,16) */

@@ -299,7 +299,8 @@ def test_silu_planner_depends_on_capacity_only():
     assert big.grid == 256 * 32 and big.per_lane == 2     # > 4M items: 2 per lane, 32 per CU
     mid = ga.plan_silu_and_mul_bounded(16384, 1536, BF16, num_cus=256)
     assert mid.per_lane == 2 and mid.grid == 256 * 16     # 3.1M items
-    assert ga.plan_silu_and_mul_bounded(100, 777, BF16).path == 1
+    assert ga.plan_silu_and_mul_bounded(100, 777, BF16).path == 2      # rows off 16 bytes: unaligned vectors
+    assert ga.plan_silu_and_mul_bounded(100, 768, BF16, aligned=False).path == 2
     for M in (1, 7, 64, 1000, 16384):
         for d in (1, 8, 768, 777, 4096):
             p = ga.plan_silu_and_mul_bounded(M, d, BF16)

@@ -79,3 +79,46 @@ def test_squared_relu_is_exact_on_bf16_squares():
     ref = oracle.get().squared_relu_bounded(xb, BF16, M)
     exact = np.abs(v) < 4.0
     assert np.array_equal(bits_of(out, BF16)[exact], ref[exact])
+
+
+@pytest.mark.parametrize("op", ["silu", "gelu_tanh", "gelu_erf", "sqrelu"])
+@pytest.mark.parametrize("dt", [F32, F16, BF16], ids=["f32", "f16", "bf16"])
+def test_shifted_views_take_the_unaligned_path(op, dt):
+    """Input and output views off a 16-byte boundary (and odd d): the
+    unaligned path, 16-byte vectors numbered flat over the output region.
+    Elements of the output buffer outside the live part of the view keep
+    their sentinel bits; the input view is surrounded by NaN."""
+    M = 300
+    o = oracle.get()
+    tdt = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}[dt]
+    for d in (768, 777, 5):
+        cols = 1 if op == "sqrelu" else 2
+        if op == "sqrelu":
+            xb = synth.to_bits(3.0 * synth.normal(synth.stream_key(d, 11), 0, M * d).reshape(M, d), dt)
+        else:
+            xb = synth.gelu_iid(M, d, seed=d + 3 * dt, dtype=dt, gate_std=2.0)
+        for i_s, o_s in ((1, 0), (0, 1), (3, 5)):
+            flat = torch.full((M * cols * d + 16,), float("nan"), dtype=tdt, device="cuda")
+            x = flat[i_s: i_s + M * cols * d].view(M, cols * d)
+            x.copy_(to_device(xb, dt))
+            buf, _ = sentinel_buffer(M * d + 16, 1, dt)
+            out = buf[o_s: o_s + M * d].view(tdt).view(M, d)
+            for live in (M, 123):
+                buf.fill_(int(synth.SENTINEL[dt]))      # below 2^15 / 2^31: the same bits as a signed fill
+                lt = _live(live)
+                if op == "silu":
+                    ga.silu_and_mul_bounded(x, lt, out=out)
+                    ref = o.silu_and_mul_bounded(xb, dt, live)
+                elif op == "sqrelu":
+                    ga.squared_relu_bounded(x, lt, out=out)
+                    ref = o.squared_relu_bounded(xb, dt, live)
+                else:
+                    tanh = op == "gelu_tanh"
+                    ga.gelu_and_mul(x, "tanh" if tanh else "none", out=out, live_rows=lt)
+                    ref = o.gelu_and_mul(xb, dt, tanh, live=live)
+                torch.cuda.synchronize()
+                everything = bits_of(buf, dt)
+                view = everything[o_s: o_s + M * d].reshape(M, d)
+                outside = np.concatenate([everything[:o_s], everything[o_s + M * d:], view[live:].ravel()])
+                assert np.all(outside == synth.SENTINEL[dt]), f"{op} d{d} shifts {i_s},{o_s} live {live}: wrote outside"
+                compare(view[:live], ref[:live], dt, label=f"{op} dt{dt} d{d} shifts {i_s},{o_s} live {live}")

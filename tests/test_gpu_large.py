@@ -114,15 +114,16 @@ def test_silu_bounded_near_2pow31_elements():
     compare(bits_of(out[torch.from_numpy(rows).cuda()], BF16), ref, BF16, label="silu near 2^31")
 
 
-def test_squared_relu_element_path_near_2pow31():
-    """M = 2^21 rows of d = 1023 fp16 (not 16-byte rows: element path),
-    2^21 * 1023 = 2.145e9 flat items, just under the 2^31 bound."""
+def test_squared_relu_unaligned_path_near_2pow31():
+    """M = 2^21 rows of d = 1023 fp16 (not 16-byte rows: the unaligned path,
+    vectors flat over the output), 2^21 * 1023 = 2.145e9 elements, just under
+    the 2^31 bound."""
     M, d, blk = 1 << 21, 1023, 4096
     rng_block = synth.gelu_iid(blk, d, seed=1023, dtype=F16)[:, :d]   # gate half: N(0,1)
     xb = np.ascontiguousarray(rng_block)
     x = _tiled(xb, F16, M // blk)
     plan = ga.plan_silu_and_mul_bounded(M, d, F16)
-    assert plan.path == 1
+    assert plan.path == 2
     out = _sentinel_out(M, d, F16)
     live = torch.tensor([M], dtype=torch.int32, device="cuda")
     ga.squared_relu_bounded(x, live, out=out)

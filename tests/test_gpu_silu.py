@@ -63,6 +63,10 @@ def test_every_geometry_is_byte_identical(moe):
     for pl in (1, 4):
         p = ga.Plan(path=1, waves_per_row=0, per_lane=pl, block=256, grid=512)
         assert np.array_equal(run(x, live, BF16, M, D, plan=p), base), ("elem", pl)
+    for pl in (1, 2, 4):
+        for grid in (1, 512, 4096):
+            p = ga.Plan(path=2, waves_per_row=0, per_lane=pl, block=256, grid=grid)
+            assert np.array_equal(run(x, live, BF16, M, D, plan=p), base), ("unaligned", pl, grid)
 
 
 @pytest.mark.parametrize("dt", [F32, F16, BF16], ids=["f32", "f16", "bf16"])
