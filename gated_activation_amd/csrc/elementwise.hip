@@ -134,7 +134,6 @@ __global__ __launch_bounds__(SILU_BLOCK) void act_una_kernel(
     int32_t M, uint32_t d, const int32_t *__restrict__ live) {
     using E = Elem<DT>;
     using S = typename E::storage;
-    typedef u32x4 u32x4_a2 __attribute__((aligned(2)));
     constexpr int PER = E::PER16;
     constexpr uint32_t CHUNK = SILU_BLOCK * PL;
     constexpr bool GATED = op_gated(OP);
@@ -160,16 +159,14 @@ __global__ __launch_bounds__(SILU_BLOCK) void act_una_kernel(
                     // on into the next row's gate) and its up tail from the
                     // next row, at the same column.
                     const size_t off = (size_t)row * 2 * d + c0;
-                    const u32x4 gw = __builtin_nontemporal_load(reinterpret_cast<const u32x4_a2 *>(in + off));
-                    const u32x4 mw = __builtin_nontemporal_load(reinterpret_cast<const u32x4_a2 *>(in + off + d));
-                    E::unpack(uint4{gw.x, gw.y, gw.z, gw.w}, g);
-                    E::unpack(uint4{mw.x, mw.y, mw.z, mw.w}, u);
+                    const uint4 gw = ldu16(in + off), mw = ldu16(in + off + d);
+                    E::unpack(gw, g);
+                    E::unpack(mw, u);
                     if (c0 + PER > d) {
-                        const u32x4 bw =
-                            __builtin_nontemporal_load(reinterpret_cast<const u32x4_a2 *>(in + off + 2 * (size_t)d));
+                        const uint4 bw = ldu16(in + off + 2 * (size_t)d);
                         float m[PER], b[PER];
-                        E::unpack(uint4{mw.x, mw.y, mw.z, mw.w}, m);
-                        E::unpack(uint4{bw.x, bw.y, bw.z, bw.w}, b);
+                        E::unpack(mw, m);
+                        E::unpack(bw, b);
                         const uint32_t k = d - c0;  // elements of the vector in this row
 #pragma unroll
                         for (int e = 0; e < PER; ++e) {
@@ -195,8 +192,7 @@ __global__ __launch_bounds__(SILU_BLOCK) void act_una_kernel(
                 for (int e = 0; e < PER; ++e) y[e] = activation<OP>(g[e]) * u[e];
             } else {
                 if (full) {
-                    const u32x4 gw = __builtin_nontemporal_load(reinterpret_cast<const u32x4_a2 *>(in + e0));
-                    E::unpack(uint4{gw.x, gw.y, gw.z, gw.w}, g);
+                    E::unpack(ldu16(in + e0), g);
                 } else {
 #pragma unroll
                     for (int e = 0; e < PER; ++e) g[e] = e0 + e < total ? E::to_f32(in[e0 + e]) : 0.0f;
@@ -206,7 +202,7 @@ __global__ __launch_bounds__(SILU_BLOCK) void act_una_kernel(
             }
             const uint4 o = E::pack(y);
             if (full) {
-                __builtin_nontemporal_store(u32x4{o.x, o.y, o.z, o.w}, reinterpret_cast<u32x4_a2 *>(out + e0));
+                stu16(out + e0, o);
             } else {
                 const uint32_t w[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll

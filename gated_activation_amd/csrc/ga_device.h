@@ -40,6 +40,22 @@ __device__ __forceinline__ void st16(uint4 *p, const uint4 &v) {
     }
 }
 
+// The same 16 bytes at any address aligned to the element size.  gfx950 runs
+// global memory in unaligned-access mode; the compiler emits one 16-byte
+// access for these (the type only lowers the alignment it may assume).
+typedef u32x4 u32x4_a2 __attribute__((aligned(2)));
+
+template <typename S>
+__device__ __forceinline__ uint4 ldu16(const S *p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_a2 *>(p));
+    return uint4{v.x, v.y, v.z, v.w};
+}
+
+template <typename S>
+__device__ __forceinline__ void stu16(S *p, const uint4 &v) {
+    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_a2 *>(p));
+}
+
 // ---------------------------------------------------------------------------
 // Element traits.  A 16-byte vector holds PER16 elements; unpack widens them
 // to fp32, pack rounds fp32 to the element type (ties to even; gfx950 has a

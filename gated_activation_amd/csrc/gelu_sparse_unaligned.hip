@@ -25,19 +25,6 @@ namespace ga {
 
 namespace {
 
-typedef u32x4 u32x4_a2 __attribute__((aligned(2)));
-
-template <typename S>
-__device__ __forceinline__ uint4 ldu16(const S *p) {
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_a2 *>(p));
-    return uint4{v.x, v.y, v.z, v.w};
-}
-
-template <typename S>
-__device__ __forceinline__ void stu16(S *p, const uint4 &v) {
-    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_a2 *>(p));
-}
-
 // The first n elements of a 16-byte vector, the rest zero.
 template <typename E>
 __device__ __forceinline__ uint4 keep_first(const uint4 &v, int32_t n) {
