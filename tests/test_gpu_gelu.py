@@ -230,6 +230,24 @@ def test_unaligned_path_every_geometry():
                                label=f"unaligned w{w} v{v} late{late} shifts {i_s},{o_s}")
 
 
+@pytest.mark.parametrize("dt,d", [(BF16, 16384), (F16, 8192), (F32, 4096)], ids=["bf16", "f16", "f32"])
+def test_unaligned_path_is_bit_identical_to_vector_path_on_aligned_rows(dt, d):
+    """On 16-byte rows the unaligned path holds the same vectors in the same
+    lanes as the vector path, so with the same geometry the bytes match."""
+    T = 64
+    xb = synth.gelu_iid(T, d, seed=d + dt, dtype=dt, gate_std=1.3)
+    x = to_device(xb, dt)
+    for w, v, late in ((8, (d * (4 if dt == F32 else 2)) // 16 // 512, 1), (16, 2 if dt != F32 else 1, 0)):
+        if w * 64 * v * (16 // (4 if dt == F32 else 2)) < d:
+            continue
+        outs = []
+        for path in (0, 2):
+            p = ga.Plan(path=path, waves_per_row=w, per_lane=v, up_late=late, block=64 * w)
+            outs.append(bits_of(ga.gelu_and_mul_sparse(x, Z95, plan=p), dt))
+        torch.cuda.synchronize()
+        assert np.array_equal(outs[0], outs[1]), (w, v, late)
+
+
 def test_unaligned_path_headline_rows():
     """T = 2048, d = 16384 bf16 one element off alignment (sampled rows)."""
     xb = synth.gelu_large(2048, 16384)
