@@ -246,9 +246,12 @@ ga_status launch_gelu(const void *in, void *out, int64_t T, int64_t d, int32_t d
                                                   (int32_t)T, (int32_t)d, nvec, z, live, s));
     }
     if (p.path == 3) {
-        const int32_t nvec = (int32_t)(d * (int64_t)elem_size(dtype) / 16);
+        // Rows' 16-byte vectors, a partial last one included; rows or bases
+        // off 16-byte alignment take the unaligned-vector kernel.
+        const int32_t nvec = (int32_t)((d * (int64_t)elem_size(dtype) + 15) / 16);
         const int64_t rows_per_block = ga::ROWS_BLOCK / p.lanes_per_row;
         return launched(name, ga::launch_gelu_rows(dtype, p.lanes_per_row, p.per_lane, rt,
+                                                   !vector_aligned(in, out, d, dtype),
                                                    (T + rows_per_block - 1) / rows_per_block, in, out, (int32_t)T,
                                                    (int32_t)d, nvec, z, live, s));
     }
@@ -378,15 +381,17 @@ ga_status ga_plan_gelu_and_mul_sparse(int64_t T, int64_t d, int32_t dtype, int32
     p.splits = 1;
     p.spin_limit = kDefaultSpinLimit;
     const int64_t nvec = (int64_t)d * (int64_t)es / 16;
-    if (aligned && ((size_t)d * es) % 16 == 0 && nvec <= 32) {
-        // Short rows: several rows per wavefront, a group of G lanes per row
-        // with one vector each (measured on MI355X at T = 65536: d = 64 bf16
-        // 14 % -> 52 % of peak, d = 128 29 % -> 62 %, d = 256 57 % -> 71 %).
-        int g = next_pow2((int)nvec);
+    const int64_t nvec_ceil = (d * (int64_t)es + 15) / 16;
+    if (nvec_ceil <= 32) {
+        // Short rows, aligned or not: several rows per wavefront, a group of
+        // G lanes per row with one vector each (measured on MI355X at
+        // T = 65536: d = 64 bf16 14 % -> 52 % of peak, d = 128 29 % -> 62 %,
+        // d = 256 57 % -> 71 %).
+        int g = next_pow2((int)nvec_ceil);
         g = g < 4 ? 4 : g > 32 ? 32 : g;
         p.path = 3;
         p.lanes_per_row = g;
-        p.per_lane = next_pow2((int)((nvec + g - 1) / g));
+        p.per_lane = next_pow2((int)((nvec_ceil + g - 1) / g));
     } else if (aligned && ((size_t)d * es) % 16 == 0 && nvec <= 16 * 64 * 8) {
         int w, v, late;
         pick_row_geometry(nvec, T, &w, &v, &late);
@@ -413,12 +418,11 @@ ga_status ga_plan_gelu_and_mul_sparse(int64_t T, int64_t d, int32_t dtype, int32
                 p.splits = (int32_t)splits;
             }
         }
-    } else if ((d * (int64_t)es + 15) / 16 <= 16 * 64 * 8) {
+    } else if (nvec_ceil <= 16 * 64 * 8) {
         // Rows that are not 16-byte aligned: the same vectors, each one
         // unaligned 16-byte access.
-        const int64_t nv = (d * (int64_t)es + 15) / 16;
         int w, v, late;
-        pick_unaligned_geometry(nv, T, &w, &v, &late);
+        pick_unaligned_geometry(nvec_ceil, T, &w, &v, &late);
         p.path = 2;
         p.waves_per_row = w;
         p.per_lane = v;
@@ -456,7 +460,7 @@ ga_status ga_gelu_and_mul_sparse_with_plan(const void *in, void *out, int64_t T,
     if (!std::isfinite(z)) return fail(GA_EINVAL, "ga_gelu_and_mul_sparse: z is not finite");
     if (plan == nullptr) return fail(GA_EINVAL, "ga_gelu_and_mul_sparse: null plan");
     if ((st = check_gelu_plan(plan, T, d, dtype)) != GA_OK) return st;
-    if ((plan->path == 0 || plan->path == 3) && !vector_aligned(in, out, d, dtype))
+    if (plan->path == 0 && !vector_aligned(in, out, d, dtype))
         return fail(GA_EUNSUPPORTED, "ga_gelu_and_mul_sparse: vector path needs 16-byte rows and bases");
     if ((st = check_workspace(*plan, T, workspace, workspace_bytes)) != GA_OK) return st;
     if (T == 0) return GA_OK;

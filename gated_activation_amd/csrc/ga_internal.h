@@ -29,13 +29,15 @@ hipError_t launch_gelu_split(int dtype, int waves, int vec_per_lane, int splits,
                              int32_t T, int32_t d, int32_t nvec, float z, const int32_t *live, void *workspace,
                              uint32_t spin_limit, hipStream_t stream);
 
-// Packed-rows path for short aligned rows: ROWS_BLOCK threads per workgroup,
+// Packed-rows path for short rows: ROWS_BLOCK threads per workgroup,
 // lanes_per_row in {4, 8, 16, 32} lanes per row, vec_per_lane in {1, 2, 4};
-// grid = ceil(T / (ROWS_BLOCK / lanes_per_row)).
+// grid = ceil(T / (ROWS_BLOCK / lanes_per_row)).  nvec: the row's 16-byte
+// vectors (a partial last one included); unaligned: rows or bases off 16-byte
+// alignment (unaligned 16-byte vectors).
 constexpr int ROWS_BLOCK = 256;
 bool gelu_rows_available(int dtype, int lanes_per_row, int vec_per_lane);
-hipError_t launch_gelu_rows(int dtype, int lanes_per_row, int vec_per_lane, bool round_trip, int64_t grid,
-                            const void *in, void *out, int32_t T, int32_t d, int32_t nvec, float z,
+hipError_t launch_gelu_rows(int dtype, int lanes_per_row, int vec_per_lane, bool round_trip, bool unaligned,
+                            int64_t grid, const void *in, void *out, int32_t T, int32_t d, int32_t nvec, float z,
                             const int32_t *live, hipStream_t stream);
 
 // Unaligned path for rows that are not 16-byte aligned: waves 1, 2, 4, 8, 16;

@@ -9,11 +9,13 @@
 // the group with DPP moves (quad permutes, half-row and row mirrors, and one
 // cross-row exchange for 32 lanes), and store their own vectors.  A 256-lane
 // workgroup covers 256 / G consecutive rows, so the loads of neighbouring
-// rows form one contiguous stream.  Rows are aligned 16-byte vector rows
-// (d * element size a multiple of 16, aligned bases); the up row is loaded
-// with the gate.
+// rows form one contiguous stream.  The up row is loaded with the gate.
+// Rows off 16-byte alignment (UNA) keep the same layout with unaligned
+// 16-byte vectors (ga_unaligned.h): only a row's last vector can be partial,
+// and only its lane tests elements in the statistics.
 #include "ga_device.h"
 #include "ga_internal.h"
+#include "ga_unaligned.h"
 
 namespace ga {
 
@@ -36,12 +38,14 @@ __device__ __forceinline__ float group_sum(float v) {
 
 }  // namespace
 
-// G lanes per row, VPL 16-byte vectors per lane (G * VPL >= nvec).
-template <int DT, int G, int VPL, bool RT = false>
+// G lanes per row, VPL 16-byte vectors per lane (G * VPL >= nvec, the row's
+// vectors including a partial last one).  UNA: rows off 16-byte alignment.
+template <int DT, int G, int VPL, bool RT = false, bool UNA = false>
 __global__ __launch_bounds__(ROWS_BLOCK) void gelu_sparse_rows_kernel(
-    const uint4 *__restrict__ in, uint4 *__restrict__ out, int32_t T, int32_t d, int32_t nvec, float z,
+    const void *__restrict__ in_, void *__restrict__ out_, int32_t T, int32_t d, int32_t nvec, float z,
     const int32_t *__restrict__ live) {
     using E = Elem<DT>;
+    using S = typename E::storage;
     constexpr int PER = E::PER16;
     constexpr int RPB = ROWS_BLOCK / G;
 
@@ -54,21 +58,42 @@ __global__ __launch_bounds__(ROWS_BLOCK) void gelu_sparse_rows_kernel(
     // A group past the last row runs the reductions on zeros (its lanes
     // only exchange values among themselves) and stores nothing.
     const bool valid = r < n;
+    const int32_t nfull = UNA ? d / PER : nvec, tail = UNA ? d - nfull * PER : 0;
 
-    const uint4 *grow = in + (size_t)r * 2 * (size_t)nvec;
-    const uint4 *urow = grow + nvec;
-    uint4 *orow = out + (size_t)r * (size_t)nvec;
+    // Aligned rows: 16-byte vector pointers.  Unaligned rows: element
+    // pointers, and whether the 16 bytes of a partial last vector lie inside
+    // the input buffer.
+    const uint4 *grow = nullptr, *urow = nullptr;
+    uint4 *orow = nullptr;
+    const S *gs = nullptr, *us = nullptr;
+    S *os = nullptr;
+    bool gspill = false, uspill = false;
+    if constexpr (UNA) {
+        const size_t row0 = (size_t)r * 2 * (size_t)d, total = (size_t)T * 2 * (size_t)d;
+        const size_t last = (size_t)nfull * PER + PER;
+        gs = static_cast<const S *>(in_) + row0;
+        us = gs + d;
+        os = static_cast<S *>(out_) + (size_t)r * (size_t)d;
+        gspill = row0 + last <= total;
+        uspill = row0 + (size_t)d + last <= total;
+    } else {
+        grow = static_cast<const uint4 *>(in_) + (size_t)r * 2 * (size_t)nvec;
+        urow = grow + nvec;
+        orow = static_cast<uint4 *>(out_) + (size_t)r * (size_t)nvec;
+    }
 
     uint4 gv[VPL], uv[VPL];
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
         const int32_t j = k * G + l;
-        gv[k] = (valid && j < nvec) ? ld16<true>(grow + j) : uint4{0u, 0u, 0u, 0u};
+        if constexpr (UNA) gv[k] = valid ? load_vec<E>(gs, j, nfull, tail, gspill) : uint4{0u, 0u, 0u, 0u};
+        else gv[k] = (valid && j < nvec) ? ld16<true>(grow + j) : uint4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
         const int32_t j = k * G + l;
-        uv[k] = (valid && j < nvec) ? ld16<true>(urow + j) : uint4{0u, 0u, 0u, 0u};
+        if constexpr (UNA) uv[k] = valid ? load_vec<E>(us, j, nfull, tail, uspill) : uint4{0u, 0u, 0u, 0u};
+        else uv[k] = (valid && j < nvec) ? ld16<true>(urow + j) : uint4{0u, 0u, 0u, 0u};
     }
 
     float s = 0.0f;
@@ -84,12 +109,19 @@ __global__ __launch_bounds__(ROWS_BLOCK) void gelu_sparse_rows_kernel(
     float q = 0.0f;
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-        if (k * G + l < nvec) {
-            float g[PER];
-            E::unpack(gv[k], g);
+        const int32_t j = k * G + l;
+        float g[PER];
+        E::unpack(gv[k], g);
+        if (j < nfull) {
 #pragma unroll
             for (int e = 0; e < PER; ++e) {
                 const float dv = g[e] - mean;
+                q = __builtin_fmaf(dv, dv, q);
+            }
+        } else if (UNA && j == nfull) {
+#pragma unroll
+            for (int e = 0; e < PER; ++e) {
+                const float dv = e < tail ? g[e] - mean : 0.0f;
                 q = __builtin_fmaf(dv, dv, q);
             }
         }
@@ -107,24 +139,31 @@ __global__ __launch_bounds__(ROWS_BLOCK) void gelu_sparse_rows_kernel(
             E::unpack(uv[k], u);
 #pragma unroll
             for (int e = 0; e < PER; ++e) y[e] = sparse_apply<E, RT>(g[e], cut, u[e]);
-            st16<true>(orow + j, E::pack(y));
+            if constexpr (UNA) store_vec<E>(os, j, nfull, tail, E::pack(y));
+            else st16<true>(orow + j, E::pack(y));
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Launch table: [round trip][dtype][log2 G - 2][log2 VPL].
+// Launch table.
 // ---------------------------------------------------------------------------
 namespace {
 
-#define GA_RW(RT, DT, G)                                                                               \
-    { (const void *)&gelu_sparse_rows_kernel<DT, G, 1, RT>, (const void *)&gelu_sparse_rows_kernel<DT, G, 2, RT>, \
-      (const void *)&gelu_sparse_rows_kernel<DT, G, 4, RT> }
-#define GA_RWD(RT, DT) { GA_RW(RT, DT, 4), GA_RW(RT, DT, 8), GA_RW(RT, DT, 16), GA_RW(RT, DT, 32) }
-const void *const kGeluRows[2][3][4][3] = {{GA_RWD(false, DT_F32), GA_RWD(false, DT_F16), GA_RWD(false, DT_BF16)},
-                                           {GA_RWD(true, DT_F32), GA_RWD(true, DT_F16), GA_RWD(true, DT_BF16)}};
+#define GA_RW(UNA, RT, DT, G)                                                                 \
+    { (const void *)&gelu_sparse_rows_kernel<DT, G, 1, RT, UNA>,                            \
+      (const void *)&gelu_sparse_rows_kernel<DT, G, 2, RT, UNA>,                            \
+      (const void *)&gelu_sparse_rows_kernel<DT, G, 4, RT, UNA> }
+#define GA_RWD(UNA, RT, DT) \
+    { GA_RW(UNA, RT, DT, 4), GA_RW(UNA, RT, DT, 8), GA_RW(UNA, RT, DT, 16), GA_RW(UNA, RT, DT, 32) }
+#define GA_RWU(UNA) \
+    { {GA_RWD(UNA, false, DT_F32), GA_RWD(UNA, false, DT_F16), GA_RWD(UNA, false, DT_BF16)}, \
+      {GA_RWD(UNA, true, DT_F32), GA_RWD(UNA, true, DT_F16), GA_RWD(UNA, true, DT_BF16)} }
+// [unaligned rows][round trip][dtype][log2 G - 2][log2 VPL]
+const void *const kGeluRows[2][2][3][4][3] = {GA_RWU(false), GA_RWU(true)};
 #undef GA_RW
 #undef GA_RWD
+#undef GA_RWU
 
 int group_index(int g) { return g == 4 ? 0 : g == 8 ? 1 : g == 16 ? 2 : g == 32 ? 3 : -1; }
 int vpl_index(int v) { return v == 1 ? 0 : v == 2 ? 1 : v == 4 ? 2 : -1; }
@@ -135,13 +174,14 @@ bool gelu_rows_available(int dtype, int lanes_per_row, int vpl) {
     return dtype >= 0 && dtype <= 2 && group_index(lanes_per_row) >= 0 && vpl_index(vpl) >= 0;
 }
 
-hipError_t launch_gelu_rows(int dtype, int lanes_per_row, int vpl, bool round_trip, int64_t grid, const void *in,
-                            void *out, int32_t T, int32_t d, int32_t nvec, float z, const int32_t *live,
-                            hipStream_t stream) {
+hipError_t launch_gelu_rows(int dtype, int lanes_per_row, int vpl, bool round_trip, bool unaligned, int64_t grid,
+                            const void *in, void *out, int32_t T, int32_t d, int32_t nvec, float z,
+                            const int32_t *live, hipStream_t stream) {
     if (!gelu_rows_available(dtype, lanes_per_row, vpl)) return hipErrorInvalidValue;
-    const void *fn = kGeluRows[round_trip ? 1 : 0][dtype][group_index(lanes_per_row)][vpl_index(vpl)];
-    const uint4 *a_in = static_cast<const uint4 *>(in);
-    uint4 *a_out = static_cast<uint4 *>(out);
+    const void *fn =
+        kGeluRows[unaligned ? 1 : 0][round_trip ? 1 : 0][dtype][group_index(lanes_per_row)][vpl_index(vpl)];
+    const void *a_in = in;
+    void *a_out = out;
     void *args[] = {&a_in, &a_out, &T, &d, &nvec, &z, &live};
     return hipLaunchKernel(fn, dim3((uint32_t)grid), dim3(ROWS_BLOCK), args, 0, stream);
 }

@@ -40,8 +40,9 @@
  *     vector loads and stores are used.  Otherwise the data still moves as
  *     16-byte vectors of consecutive elements, each one unaligned 16-byte
  *     access (gfx950 runs global memory in unaligned-access mode):
- *     gelu_and_mul_sparse per row (rows up to 8192 vectors), the other ops
- *     flat over the output region.
+ *     gelu_and_mul_sparse per row (rows up to 8192 vectors; rows of up to 32
+ *     vectors packed several to a wavefront, as aligned ones are), the other
+ *     ops flat over the output region.
  */
 #ifndef GA_H
 #define GA_H
@@ -74,8 +75,8 @@ typedef struct {
     int32_t path;          /* 0: 16-byte vector path, 1: per-element path,
                               2: unaligned path (rows off 16-byte alignment; gelu: per
                                  row, the elementwise ops: flat over the output),
-                              3: gelu packed-rows path (short aligned rows, several
-                              rows per wavefront) */
+                              3: gelu packed-rows path (short rows of any alignment,
+                              several rows per wavefront) */
     int32_t waves_per_row; /* gelu: 64-lane wavefronts per workgroup (1,2,4,8,16) */
     int32_t per_lane;      /* gelu vector path: 16-byte gate vectors per lane (1,2,4,8;
                               split rows 1,2,4); gelu element path: gate elements per
@@ -228,7 +229,7 @@ ga_status ga_plan_silu_and_mul_bounded(int64_t M, int64_t d, int32_t dtype, int3
  * every split owning at least one vector; element path
  * waves_per_row * 64 * per_lane >= d; unaligned path (any alignment)
  * waves_per_row * 64 * per_lane * e >= d with e = 16 / element size;
- * packed rows (16-byte rows and bases only) lanes_per_row * per_lane * e >= d;
+ * packed rows (any alignment) lanes_per_row * per_lane * e >= d;
  * else GA_EUNSUPPORTED.
  * `block` and
  * `grid` are derived for gelu; silu takes its grid from the plan.  A split

@@ -133,6 +133,13 @@ def test_gelu_planner_known_shapes():
         p = ga.plan_gelu_and_mul_sparse(4096, d, BF16)
         assert (p.path, p.lanes_per_row, p.per_lane, p.block, p.grid) == (3, g, v, 256, 4096 * g // 256), (d, p.as_dict())
     assert ga.plan_gelu_and_mul_sparse(4096, 264, BF16).path == 0      # 33 vectors: one row per workgroup
+    # short rows off 16-byte alignment are packed too (unaligned 16-byte vectors, a partial last one)
+    for d, aligned, g, v in ((7, True, 4, 1), (1, True, 4, 1), (255, True, 32, 1), (64, False, 8, 1),
+                             (129, True, 32, 1), (33, False, 8, 1)):
+        p = ga.plan_gelu_and_mul_sparse(4096, d, BF16, aligned=aligned)
+        assert (p.path, p.lanes_per_row, p.per_lane) == (3, g, v), (d, aligned, p.as_dict())
+    assert ga.plan_gelu_and_mul_sparse(4096, 257, BF16).path == 2      # 33 vectors: unaligned path
+    assert ga.plan_gelu_and_mul_sparse(4096, 127, F32).path == 3       # 32 vectors of fp32
     # without a workspace the rows are never split
     p = ga.plan_gelu_and_mul_sparse(1, 32768, BF16, with_workspace=False)
     assert (p.splits, p.waves_per_row, p.per_lane) == (1, 16, 4)
@@ -200,8 +207,9 @@ def test_gelu_planner_covers_every_d(dt):
             p = ga.plan_gelu_and_mul_sparse(3, d, dt, aligned=aligned)
             if p.path == 3:   # packed rows: 256 lanes, 256 / lanes_per_row rows per workgroup
                 assert p.block == 256 and p.grid == -(-3 // (256 // p.lanes_per_row))
-                assert aligned and (d * es) % 16 == 0 and d * es <= 32 * 16
+                assert d * es <= 32 * 16
             else:
+                assert d * es > 32 * 16
                 assert p.block == p.waves_per_row * 64 and p.grid == 3 * p.splits
             if p.path == 0:
                 assert aligned and (d * es) % 16 == 0 and d * es > 32 * 16
@@ -237,7 +245,8 @@ def test_gelu_with_plan_rejects_bad_geometry():
     assert rows(16, 2, up_late=1) == EUNSUP
     assert L.ga_gelu_and_mul_sparse_with_plan(ctypes.c_void_p(0x7F0000000002), OUT, 0, 256, BF16, Z, None,
                                               ctypes.byref(ga.Plan(path=3, lanes_per_row=16, per_lane=2)),
-                                              WS, WS_BYTES, None) == EUNSUP   # needs 16-byte bases
+                                              WS, WS_BYTES, None) == OK       # any alignment
+    assert rows(32, 1, d=257) == EUNSUP and rows(16, 4, d=257) == OK   # 257 elements: 33 vectors
     # lanes_per_row belongs to the packed-rows path; reserved must be zero
     assert L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 2048, BF16, Z, None, ctypes.byref(
         ga.Plan(path=0, waves_per_row=4, per_lane=1, lanes_per_row=8)), WS, WS_BYTES, None) == EINVAL
@@ -254,8 +263,9 @@ def test_gelu_with_plan_rejects_bad_geometry():
     assert wp(ga.Plan(path=2, waves_per_row=8, per_lane=5, up_late=2, block=512), 16384) == EUNSUP
     assert wp(ga.Plan(path=2, waves_per_row=1, per_lane=1, block=64), 1) == OK
     # vector path on a base that is not 16-byte aligned
-    p = ga.plan_gelu_and_mul_sparse(1, 64, BF16)
-    st = L.ga_gelu_and_mul_sparse_with_plan(ctypes.c_void_p(0x7F0000000002), OUT, 0, 64, BF16, Z, None,
+    p = ga.plan_gelu_and_mul_sparse(1, 2048, BF16)
+    assert p.path == 0
+    st = L.ga_gelu_and_mul_sparse_with_plan(ctypes.c_void_p(0x7F0000000002), OUT, 0, 2048, BF16, Z, None,
                                             ctypes.byref(p), WS, WS_BYTES, None)
     assert st == EUNSUP
 

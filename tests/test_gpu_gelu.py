@@ -209,7 +209,7 @@ def test_unaligned_path_every_phase_mix(dt, d):
         if d % per == 0 and i_s == 0 and o_s == 0:
             continue
         plan = ga.plan_gelu_and_mul_sparse(T, d, dt, aligned=False)
-        assert plan.path == 2
+        assert plan.path == (3 if d * (16 // per) <= 512 else 2)    # short rows are packed
         run_offset(xb, dt, Z95, i_s, o_s, label=f"unaligned dt{dt} d{d} shifts {i_s},{o_s}")
 
 
@@ -256,7 +256,7 @@ def test_unaligned_path_headline_rows():
 
 def _packed_plans(d, dt):
     per = 4 if dt == F32 else 8
-    nvec = d // per
+    nvec = -(-d // per)
     for g in (4, 8, 16, 32):
         for v in (1, 2, 4):
             if g * v >= nvec and g * (v // 2 if v > 1 else 0) < nvec:
@@ -294,6 +294,61 @@ def test_packed_rows_edge_and_constant_rows():
         x = synth.edge_rows(40, 256, dt, seed=8)
         for z in (0.0, Z95, Z99):
             run_and_check(x, dt, z, label=f"packed edge dt{dt} z{z}")
+
+
+@pytest.mark.parametrize("dt", [BF16, F16, F32], ids=["bf16", "f16", "f32"])
+@pytest.mark.parametrize("d", [1, 3, 7, 9, 31, 64, 100, 127, 255, 256])
+def test_packed_rows_unaligned(dt, d):
+    """Short rows off 16-byte alignment (shifted views, odd d) packed several
+    per wavefront: every covering geometry, input and output shifts varied
+    independently, NaN around the input view.  Rows of 1 and 3 elements read
+    their last gate vector element by element near the end of the buffer."""
+    es = 4 if dt == F32 else 2
+    if d * es > 512:
+        pytest.skip("more than 32 vectors: not packed")
+    per = 16 // es
+    T = 203
+    xb = synth.gelu_offset_rows(T, d, seed=700 + d + dt, dtype=dt)
+    plans = list(_packed_plans(d, dt))
+    assert plans
+    for p in plans:
+        for i_s, o_s in ((0, 1), (1, 0), (per - 1, per - 1), (3, 2 % per), (0, 0)):
+            if d % per == 0 and i_s == 0 and o_s == 0:
+                continue
+            run_offset(xb, dt, Z95, i_s, o_s, plan=p,
+                       label=f"packed unaligned dt{dt} d{d} g{p.lanes_per_row} v{p.per_lane} shifts {i_s},{o_s}")
+
+
+@pytest.mark.parametrize("dt", [BF16, F16])
+def test_packed_rows_unaligned_planner_and_edge_rows(dt):
+    """The planner's packed choice on shifted views at a large T (sampled
+    rows), and the edge mix (cancellation, constant rows, heavy tails) on an
+    odd d."""
+    big = synth.gelu_iid(9000, 255, seed=41 + dt, dtype=dt)
+    assert ga.plan_gelu_and_mul_sparse(9000, 255, dt).path == 3
+    run_offset(big, dt, Z95, 3, 5, rows_sample=list(range(0, 9000, 89)) + [8999], label=f"packed big dt{dt}")
+    x = synth.edge_rows(40, 255, dt, seed=9)
+    for z in (0.0, Z95, Z99):
+        run_offset(x, dt, z, 1, 2, label=f"packed edge unaligned dt{dt} z{z}")
+
+
+@pytest.mark.parametrize("dt,d", [(BF16, 128), (F16, 256), (F32, 64)], ids=["bf16", "f16", "f32"])
+def test_packed_rows_unaligned_is_bit_identical_to_aligned(dt, d):
+    """On rows of whole 16-byte vectors, shifted bases give the same vectors
+    in the same lanes as aligned ones, so the bytes match."""
+    T = 300
+    xb = synth.gelu_iid(T, d, seed=d + 3 * dt, dtype=dt, gate_std=1.3)
+    tdt = TORCH_DTYPE[dt]
+    for p in _packed_plans(d, dt):
+        ref = bits_of(ga.gelu_and_mul_sparse(to_device(xb, dt), Z95, plan=p), dt)
+        flat = torch.zeros(T * 2 * d + 8, dtype=tdt, device="cuda")
+        x = flat[3: 3 + T * 2 * d].view(T, 2 * d)
+        x.copy_(to_device(xb, dt))
+        obuf = torch.zeros(T * d + 8, dtype=tdt, device="cuda")
+        out = obuf[1: 1 + T * d].view(T, d)
+        ga.gelu_and_mul_sparse(x, Z95, out=out, plan=p)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_of(out, dt), ref), (p.lanes_per_row, p.per_lane)
 
 
 def test_repeat_runs_are_bit_identical():
