@@ -44,9 +44,9 @@ __device__ __forceinline__ uint4 load_vec(const typename E::storage *row, int32_
     if (j < nfull) return ldu16(row + (size_t)PER * j);
     uint4 v{0u, 0u, 0u, 0u};
     if (j == nfull && tail > 0) {
-        // Only one lane gets here, at an address the compiler could prove
-        // uniform and turn into a scalar load, which would drop the low bits
-        // of a 2-byte-aligned address; the empty asm keeps j per lane.
+        // Few lanes get here (one per row), at an address the compiler could
+        // prove uniform and turn into a scalar load, which would drop the low
+        // bits of a 2-byte-aligned address; the empty asm keeps j per lane.
         int32_t jv = j;
         asm volatile("" : "+v"(jv));
         if (spill) {
@@ -75,6 +75,7 @@ __device__ __forceinline__ void store_vec(typename E::storage *row, int32_t j, i
         stu16(row + (size_t)PER * j, v);
         return;
     }
+    if (j != nfull) return;  // past the row
 #pragma unroll
     for (int e = 0; e < PER; ++e)
         if (e < tail) row[(size_t)PER * j + e] = elem_of<E>(v, e);
