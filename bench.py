@@ -9,8 +9,9 @@ Cache; timing uses HIP events on the stream the kernels are launched on.
 
 Also measured in the same run: a streaming kernel with the same access
 pattern (the ceiling), silu_and_mul_bounded on the MoE decode buffer
-(M = 16384, d = 768, live 16384 and 2048), and the fp64 CPU oracle on a
-bounded sample of the same workload (the CPU baseline).
+(M = 16384, d = 768, live 16384, 2048 and 64; its own roofline object, and
+the fp64 oracle's silu timed on the host beside it), and the fp64 CPU oracle
+on a bounded sample of the headline workload (the CPU baseline).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 
@@ -36,9 +37,11 @@ SILU_M, SILU_D = 16384, 768
 # Calls moving less than this finish in about the launch latency: % of peak is
 # not meaningful for them.
 LATENCY_BOUND_BYTES = 16 << 20
+CSRC = os.path.join(ROOT, "gated_activation_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gelu_and_mul_sparse_T2048_d16384_bf16.traffic.txt")
-KERNEL_SOURCES = [os.path.join(ROOT, "gated_activation_amd", "csrc", f)
-                  for f in ("gelu_sparse.hip", "ga_device.h")]
+KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("gelu_sparse.hip", "ga_device.h")]
+SILU_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "silu_and_mul_bounded_M16384_d768_bf16.traffic.txt")
+SILU_SOURCES = [os.path.join(CSRC, f) for f in ("elementwise.hip", "ga_device.h")]
 
 
 def parse():
@@ -53,27 +56,27 @@ def parse():
     return p.parse_args()
 
 
-def kernel_source_digest():
+def kernel_source_digest(sources=KERNEL_SOURCES):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         h.update(open(f, "rb").read())
     return h.hexdigest()
 
 
-def recorded_traffic():
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel source; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+def recorded_traffic(path=TRAFFIC_FILE, sources=KERNEL_SOURCES, key="hbm_bytes_per_launch"):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    if not os.path.exists(path):
         return None
     fields = {}
-    for ln in open(TRAFFIC_FILE):
+    for ln in open(path):
         if "=" in ln and not ln.lstrip().startswith("#"):
             k, v = ln.split("=", 1)
-            fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_sha256") != kernel_source_digest():
+            fields[k.strip()] = v.split()[0] if v.split() else ""
+    if fields.get("kernel_source_sha256") != kernel_source_digest(sources):
         return None
     try:
-        return int(float(fields["hbm_bytes_per_launch"]))
+        return int(float(fields[key]))
     except (KeyError, ValueError):
         return None
 
@@ -234,6 +237,19 @@ def main():
                                          "GBps": round(b / (ms_s * 1e-3) / 1e9, 1),
                                          "pct_of_peak": round(100 * b / (ms_s * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
                                          "bytes": b, "timing": "graph replay"}
+        # The full buffer (live = M) moves 75 MB per call: the HBM-bound case.
+        full = silu_res[f"live{SILU_M}"]
+        silu_res["roofline"] = {
+            "bound": "hbm", "achieved": full["GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(full["GBps"] / PEAK_HBM_GBPS, 4),
+            "traffic": recorded_traffic(SILU_TRAFFIC_FILE, SILU_SOURCES, f"live{SILU_M}_hbm_bytes_per_launch"),
+            "kernel": "act_vec_kernel<bf16, 1 item per lane, silu>", "live": SILU_M}
+        if args.cpu_seconds > 0:
+            live.fill_(2048)
+            souts[0].zero_()
+            ga.silu_and_mul_bounded(sxs[0], live, out=souts[0])
+            silu_res["cpu_baseline"], silu_res["parity_sample"] = silu_cpu_baseline(
+                sb, souts[0], min(3.0, args.cpu_seconds / 4))
         result["silu_and_mul_bounded"] = silu_res
         # The headline kernel replayed from a graph as well, for comparison
         # with the stream-launched figure above.
@@ -400,6 +416,43 @@ def siblings(dev, stream):
             "us_per_call": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
             "pct_of_peak": round(100 * b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2)}
     return res
+
+
+def silu_cpu_baseline(sb, gpu_out, seconds):
+    """The fp64 oracle's silu_and_mul_bounded, as it stands, on one thread,
+    over 2048-row blocks of the MoE buffer (each call with all 2048 rows
+    live) for about `seconds`; its first block is compared with the GPU's
+    output at live = 2048."""
+    import numpy as np
+    import torch
+    import oracle
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from parity import BF16, bits_of, compare
+    o = oracle.get()
+    block = 2048
+    ref = o.silu_and_mul_bounded(sb[:block], oracle.BF16, block)
+    got = bits_of(gpu_out, BF16)
+    torch.cuda.synchronize()
+    parity = compare(got[:block], ref, BF16, label="bench silu sample")
+    parity["rows"] = f"0..{block - 1} (live {block})"
+    assert not got[block:].any(), "silu wrote rows beyond the live count"
+    done, b, t0 = 0, 0, time.perf_counter()
+    n_blocks = sb.shape[0] // block
+    while True:
+        r0 = (b % n_blocks) * block
+        o.silu_and_mul_bounded(sb[r0:r0 + block], oracle.BF16, block)
+        done += block
+        b += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    row_bytes = 3 * SILU_D * 2
+    del np
+    return ({"value": round(done * row_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+             "sample": f"{done} live rows of the M=16384 d=768 bf16 buffer (2048-row blocks, 1 thread, "
+                       f"{el:.1f} s, fp64)",
+             "us_per_call_equiv_live2048": round(el / done * block * 1e6, 1)},
+            parity)
 
 
 def cpu_baseline(xb, gpu_out, seconds):
