@@ -319,6 +319,32 @@ def test_packed_rows_unaligned(dt, d):
                        label=f"packed unaligned dt{dt} d{d} g{p.lanes_per_row} v{p.per_lane} shifts {i_s},{o_s}")
 
 
+@pytest.mark.parametrize("live", [0, 1, 31, 32, 33, 200, 203, 10 ** 6, -1])
+def test_packed_rows_unaligned_live_bound(live):
+    """Odd d on a shifted view, packed: live counts that end inside, at and
+    past a workgroup's rows (16 rows of 16 lanes per workgroup); rows past
+    the count keep their sentinel bits."""
+    T, d = 203, 127
+    xb = synth.gelu_iid(T, d, seed=23)
+    flat = torch.full((T * 2 * d + 8,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    x = flat[5: 5 + T * 2 * d].view(T, 2 * d)
+    x.copy_(to_device(xb, BF16))
+    buf, _ = sentinel_buffer(T * d + 8, 1, BF16)
+    out = buf[3: 3 + T * d].view(torch.bfloat16).view(T, d)
+    assert ga.plan_gelu_and_mul_sparse(T, d, BF16).path == 3
+    live_t = torch.tensor([live], dtype=torch.int32, device="cuda")
+    ga.gelu_and_mul_sparse(x, Z95, out=out, live_rows=live_t)
+    torch.cuda.synchronize()
+    everything = bits_of(buf, BF16)
+    n = max(0, min(live, T))
+    got = everything[3: 3 + T * d].reshape(T, d)
+    assert np.all(everything[:3] == synth.SENTINEL[BF16]) and np.all(everything[3 + T * d:] == synth.SENTINEL[BF16])
+    assert np.all(got[n:] == synth.SENTINEL[BF16]), "rows past the live count were written"
+    if n:
+        ref, st = oracle.get().gelu_and_mul_sparse(xb[:n], BF16, Z95, want_stats=True)
+        compare(got[:n], ref, BF16, gate=decode(xb[:n, :d], BF16), stats=st, label=f"packed unaligned live {live}")
+
+
 @pytest.mark.parametrize("dt", [BF16, F16])
 def test_packed_rows_unaligned_planner_and_edge_rows(dt):
     """The planner's packed choice on shifted views at a large T (sampled

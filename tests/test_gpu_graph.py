@@ -74,12 +74,12 @@ def test_graph_replay_with_changing_live_counts():
 
 
 def test_graph_replay_packed_unaligned_and_round_trip():
-    """The packed-rows path (short rows), the unaligned path (odd d), the
-    round-trip form and gelu_and_mul captured together, replayed under
-    changing live counts and checked on every replay."""
+    """The packed-rows path (short rows, aligned and odd d), the unaligned
+    path (odd d), the round-trip form and gelu_and_mul captured together,
+    replayed under changing live counts and checked on every replay."""
     o = oracle.get()
     cases = []
-    for T, d, rt in ((1000, 128, False), (300, 2047, False), (200, 4096, True)):
+    for T, d, rt in ((1000, 128, False), (700, 101, False), (300, 2047, False), (200, 4096, True)):
         xb = synth.gelu_offset_rows(T, d, seed=T + d)
         if rt:
             ref, st = o.gelu_and_mul_sparse_rt(xb, BF16, Z95)
@@ -89,6 +89,7 @@ def test_graph_replay_packed_unaligned_and_round_trip():
         live = torch.tensor([T], dtype=torch.int32, device="cuda")
         cases.append(dict(T=T, d=d, rt=rt, xb=xb, x=to_device(xb, BF16), ref=ref, st=st, out=out, live=live))
     assert ga.plan_gelu_and_mul_sparse(1000, 128, ga.GA_BF16).path == 3
+    assert ga.plan_gelu_and_mul_sparse(700, 101, ga.GA_BF16).path == 3
     assert ga.plan_gelu_and_mul_sparse(300, 2047, ga.GA_BF16).path == 2
     xm_b = synth.gelu_iid(500, 1536, seed=31)
     ref_m = o.gelu_and_mul(xm_b, BF16, True)
