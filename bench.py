@@ -276,7 +276,9 @@ def sweep(dev, stream, num_cus):
     T = 65536 (gate N(0,2); the packed-rows path), bf16, each timed
     by replaying a graph of 64 launches over distinct buffers (a split-row
     workspace passed explicitly so few-row shapes take the split path), and
-    by the same launches issued one by one on the stream.  Shapes under
+    by the same launches issued one by one on the stream; the same-pattern
+    streaming kernel is graph-replayed on the same buffers beside each
+    shape (ceiling_us_per_call, pct_of_ceiling).  Shapes under
     ~256 MB in total may be served from the Infinity Cache; shapes that move
     under 16 MiB are bound by launch latency (about 2 us per call), not by
     HBM, and are marked latency_bound: their % of peak is not meaningful."""
@@ -304,6 +306,12 @@ def sweep(dev, stream, num_cus):
         # than the host's launch cost this avoids the per-node cost of graph
         # replay; for short ones it measures the host instead.
         ms_s = time_calls(call, n_sets, reps * per_graph, 10, stream)
+
+        def ceiling(i):
+            ga.stream_xor_rows(xs[i], out=outs[i])
+        # The same-pattern streaming kernel on the same buffers, replayed the
+        # same way: what the shape allows without statistics or arithmetic.
+        ms_c = time_graph(ceiling, n_sets, reps * per_graph, 10, stream, per_graph=per_graph)
         plan = ga.plan_gelu_and_mul_sparse(T, d, ga.GA_BF16, True, num_cus, True)
         gbps = bytes_call / (ms * 1e-3) / 1e9
         gbps_s = bytes_call / (ms_s * 1e-3) / 1e9
@@ -313,6 +321,8 @@ def sweep(dev, stream, num_cus):
                     "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
                     "us_per_call_stream": round(ms_s * 1e3, 3),
                     "pct_of_peak_stream": round(100 * gbps_s / PEAK_HBM_GBPS, 2),
+                    "ceiling_us_per_call": round(ms_c * 1e3, 3),
+                    "pct_of_ceiling": round(100 * ms_c / ms, 2),
                     "latency_bound": bytes_call < LATENCY_BOUND_BYTES,
                     "bytes": bytes_call,
                     "working_set_MB": round(n_sets * bytes_call / 1e6, 1), "plan": geom})
