@@ -122,3 +122,35 @@ def test_shifted_views_take_the_unaligned_path(op, dt):
                 outside = np.concatenate([everything[:o_s], everything[o_s + M * d:], view[live:].ravel()])
                 assert np.all(outside == synth.SENTINEL[dt]), f"{op} d{d} shifts {i_s},{o_s} live {live}: wrote outside"
                 compare(view[:live], ref[:live], dt, label=f"{op} dt{dt} d{d} shifts {i_s},{o_s} live {live}")
+
+
+@pytest.mark.parametrize("dt", [F32, F16, BF16], ids=["f32", "f16", "bf16"])
+def test_unaligned_small_d_around_the_vector_width(dt):
+    """d from 1 to 17 elements on shifted views: output vectors numbered flat
+    over the region straddle several rows (d below a vector), exactly one
+    row boundary, or none, and the region's last vector is partial; every
+    per-lane count and a grid small enough to loop."""
+    M = 37
+    o = oracle.get()
+    tdt = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}[dt]
+    for d in range(1, 18):
+        xb = synth.gelu_iid(M, d, seed=900 + d + 7 * dt, dtype=dt, gate_std=2.0)
+        ref = o.silu_and_mul_bounded(xb, dt, M)
+        for i_s, o_s in ((1, 2), (3, 0)):
+            flat = torch.full((M * 2 * d + 16,), float("nan"), dtype=tdt, device="cuda")
+            x = flat[i_s: i_s + M * 2 * d].view(M, 2 * d)
+            x.copy_(to_device(xb, dt))
+            buf, _ = sentinel_buffer(M * d + 16, 1, dt)
+            out = buf[o_s: o_s + M * d].view(tdt).view(M, d)
+            for plan in (None, ga.Plan(path=2, per_lane=1, block=256, grid=1),
+                         ga.Plan(path=2, per_lane=4, block=256, grid=1)):
+                for live in (M, 20):
+                    buf.fill_(int(synth.SENTINEL[dt]))
+                    ga.silu_and_mul_bounded(x, _live(live), out=out, plan=plan)
+                    torch.cuda.synchronize()
+                    everything = bits_of(buf, dt)
+                    view = everything[o_s: o_s + M * d].reshape(M, d)
+                    outside = np.concatenate([everything[:o_s], everything[o_s + M * d:], view[live:].ravel()])
+                    label = f"silu dt{dt} d{d} shifts {i_s},{o_s} live {live} plan {plan and plan.per_lane}"
+                    assert np.all(outside == synth.SENTINEL[dt]), label + ": wrote outside"
+                    compare(view[:live], ref[:live], dt, label=label)
