@@ -135,7 +135,10 @@ void pick_waves(int64_t nvec, int max_v, int *w_out, int *v_out) {
 // 65..1024 vectors (one for up to 256 when up comes early), four longer rows;
 // 2048-vector rows take 16 waves of 2 once there are >= 8192 rows (an
 // interleaved A/B at d = 16384 bf16: W=8 V=4 is 3.5 % faster at 4096 rows,
-// even at 6144, W=16 V=2 2.6 % faster at 8192).
+// even at 6144, W=16 V=2 2.6 % faster at 8192).  Rows of 1664..2047 vectors
+// (d = 13312 .. 16376 bf16, e.g. 14336) take 16 waves of 2 from 2048 rows,
+// and rows of 1536..1663 from 4096 rows (A/B over T = 1024..6144: 1.1-4.9 %
+// faster there, slower below).
 void pick_row_geometry(int64_t nvec, int64_t T, int *w_out, int *v_out, int *late_out) {
     const int64_t gate_vectors = T * nvec;
     const bool late = gate_vectors >= ((int64_t)1 << 20) && (T >= 1024 || gate_vectors >= ((int64_t)1 << 21));
@@ -144,7 +147,8 @@ void pick_row_geometry(int64_t nvec, int64_t T, int *w_out, int *v_out, int *lat
     else if (nvec <= 128) target = 2;
     else if (nvec <= 256) target = late ? 2 : 1;
     else if (nvec <= 1024) target = 2;
-    else if (nvec <= 2048) target = T >= 8192 ? 2 : 4;
+    else if (nvec < 2048) target = (T >= 2048 && nvec >= 1664) || (T >= 4096 && nvec >= 1536) ? 2 : 4;
+    else if (nvec == 2048) target = T >= 8192 ? 2 : 4;
     else target = 4;
     waves_for(nvec, target, w_out, v_out);
     *late_out = late ? 1 : 0;

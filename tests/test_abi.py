@@ -123,7 +123,10 @@ def test_gelu_planner_known_shapes():
             (2048, 4096): (0, 4, 2, 1, 1), (1024, 4096): (0, 4, 2, 0, 1), (512, 32768): (0, 16, 4, 1, 1),
             (256, 32768): (0, 16, 4, 0, 1), (512, 16384): (0, 8, 4, 0, 1), (4096, 2048): (0, 2, 2, 1, 1),
             (2048, 2048): (0, 4, 1, 0, 1), (1024, 1024): (0, 1, 2, 0, 1), (8192, 1024): (0, 1, 2, 1, 1),
-            (8192, 16384): (0, 16, 2, 1, 1), (4096, 16384): (0, 8, 4, 1, 1), (4096, 65536): (0, 16, 8, 1, 1)}
+            (8192, 16384): (0, 16, 2, 1, 1), (4096, 16384): (0, 8, 4, 1, 1), (4096, 65536): (0, 16, 8, 1, 1),
+            # 1664..2047-vector rows: 16 waves of 2 from 2048 rows; 1536..1663 from 4096 rows
+            (2048, 14336): (0, 16, 2, 1, 1), (1536, 14336): (0, 8, 4, 1, 1), (2048, 13312): (0, 16, 2, 1, 1),
+            (2048, 12800): (0, 8, 4, 1, 1), (4096, 12288): (0, 16, 2, 1, 1), (4096, 11264): (0, 8, 4, 1, 1)}
     for (T, d), w in want.items():
         p = ga.plan_gelu_and_mul_sparse(T, d, BF16)
         assert (p.path, p.waves_per_row, p.per_lane, p.up_late, p.splits) == w, (T, d, p.as_dict())

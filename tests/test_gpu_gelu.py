@@ -127,7 +127,7 @@ def test_every_vector_geometry_matches_oracle():
 PLANNER_SHAPES = {(1024, 1024): (1, 2, 0), (8192, 1024): (1, 2, 1), (2048, 2048): (4, 1, 0),
                   (4096, 2048): (2, 2, 1), (1024, 4096): (4, 2, 0), (2048, 4096): (4, 2, 1),
                   (512, 16384): (8, 4, 0), (4096, 16384): (8, 4, 1), (512, 32768): (16, 4, 1),
-                  (256, 32768): (16, 4, 0)}
+                  (256, 32768): (16, 4, 0), (2048, 14336): (16, 2, 1), (4096, 12288): (16, 2, 1)}
 
 
 @pytest.mark.parametrize("T,d", sorted(PLANNER_SHAPES), ids=[f"T{t}-d{d}" for t, d in sorted(PLANNER_SHAPES)])
