@@ -125,43 +125,109 @@ void pick_waves(int64_t nvec, int max_v, int *w_out, int *v_out) {
     waves_for(nvec, target, w_out, v_out);
 }
 
-// One row per workgroup: waves, vectors per lane and when to load up, from a
-// sweep of every geometry over T in 256..8192 and 128..4096 vectors per row on
-// MI355X (bf16; the choice depends on bytes, so it serves every type).
-// Loading up after the statistics frees registers for more resident rows; it
-// pays once the gate alone is >= 2^20 vectors (16 MiB) and either there are
-// >= 1024 rows or the gate is >= 2^21 vectors, else the shorter dependency
-// chain of loading up with the gate wins.  Two vectors per lane suit rows of
-// 65..1024 vectors (one for up to 256 when up comes early), four longer rows;
-// 2048-vector rows take 16 waves of 2 once there are >= 8192 rows (an
-// interleaved A/B at d = 16384 bf16: W=8 V=4 is 3.5 % faster at 4096 rows,
-// even at 6144, W=16 V=2 2.6 % faster at 8192).  Rows of 1664..2047 vectors
-// (d = 13312 .. 16376 bf16, e.g. 14336) take 16 waves of 2 from 2048 rows,
-// and rows of 1536..1663 from 4096 rows (A/B over T = 1024..6144: 1.1-4.9 %
-// faster there, slower below).
-void pick_row_geometry(int64_t nvec, int64_t T, int *w_out, int *v_out, int *late_out) {
+// The analytic row rule, from a first sweep of power-of-two shapes (T in
+// 256..8192, 128..4096 vectors per row, bf16): loading up after the
+// statistics frees registers for more resident rows; it pays once the gate
+// alone is >= 2^20 vectors (16 MiB) and either there are >= 1024 rows or the
+// gate is >= 2^21 vectors.  Two vectors per lane suit rows of 65..1024
+// vectors (one for up to 256 when up comes early), four longer rows.  The
+// vector path now takes its geometry from the measured table below; this rule
+// remains for the unaligned path's choice of when to load up and as the
+// fallback where the table has no data.
+bool late_by_size(int64_t nvec, int64_t T) {
     const int64_t gate_vectors = T * nvec;
-    const bool late = gate_vectors >= ((int64_t)1 << 20) && (T >= 1024 || gate_vectors >= ((int64_t)1 << 21));
+    return gate_vectors >= ((int64_t)1 << 20) && (T >= 1024 || gate_vectors >= ((int64_t)1 << 21));
+}
+
+void analytic_row_geometry(int64_t nvec, int64_t T, int *w_out, int *v_out, int *late_out) {
+    const bool late = late_by_size(nvec, T);
     int target;
     if (nvec <= 64) target = 1;
     else if (nvec <= 128) target = 2;
     else if (nvec <= 256) target = late ? 2 : 1;
-    else if (nvec <= 1024) target = 2;
-    else if (nvec < 2048) target = (T >= 2048 && nvec >= 1664) || (T >= 4096 && nvec >= 1536) ? 2 : 4;
-    else if (nvec == 2048) target = T >= 8192 ? 2 : 4;
-    else target = 4;
+    else target = nvec <= 1024 ? 2 : 4;
     waves_for(nvec, target, w_out, v_out);
     *late_out = late ? 1 : 0;
 }
 
-// Unaligned path (rows off 16-byte alignment), from the same kind of sweep on
-// shifted and odd-d bf16 rows: up early or late as on the vector path; one
-// vector per lane for 129..256-vector rows (3.7 % faster at T = 8192), and
-// 2048-vector rows stay at 8 waves of 4 for every T (16 waves of 2 is 7-13 %
-// slower at T = 8192 here).
+// The measured geometry table: kPlanLoss[t][n][g] is how much slower geometry
+// g ran than the best geometry at kPlanT[t] rows of kPlanN[n] vectors (in
+// 1/400 steps; 255 = not run), from sweeps of every compiled geometry of the
+// vector kernel on MI355X (gated_activation_amd/tune; bf16 rows: the choice
+// depends on bytes per row, so it serves every type).
+#include "planner_table.inc"
+
+constexpr int kPlanWaves[5] = {1, 2, 4, 8, 16};
+constexpr int kPlanPerLane[4] = {1, 2, 4, 8};
+
+// Grid interval around x: indices lo <= hi and the weight of lo, linear in
+// log2 x; outside the grid both indices are the end point.
+void plan_bracket(const int *grid, int n, double x, int *lo, int *hi, double *wlo) {
+    *lo = *hi = x <= grid[0] ? 0 : n - 1;
+    *wlo = 1.0;
+    if (x <= grid[0] || x >= grid[n - 1]) return;
+    for (int i = 0; i + 1 < n; ++i) {
+        if (grid[i] <= x && x <= grid[i + 1]) {
+            *lo = i;
+            *hi = i + 1;
+            const double l0 = std::log2((double)grid[i]), l1 = std::log2((double)grid[i + 1]);
+            *wlo = (l1 - std::log2(x)) / (l1 - l0);
+            return;
+        }
+    }
+}
+
+// One workgroup per row: the compiled geometry that covers nvec with the least
+// loss interpolated over the four grid points around (T, nvec) (weights
+// linear in log2 T and log2 nvec), scored as half the weighted mean plus half
+// the largest loss over the points where it was run (at least half of the
+// weight); ties go to the first geometry in table order.  On 153 shapes off
+// the grid this choice ran at 1.007x the best geometry on average, 1.013x at
+// the 90th percentile (the analytic rule: 1.027x and 1.080x, up to 1.28x).
+void pick_row_geometry(int64_t nvec, int64_t T, int *w_out, int *v_out, int *late_out) {
+    int t0, t1, n0, n1;
+    double wt, wn;
+    plan_bracket(kPlanT, kPlanNT, (double)T, &t0, &t1, &wt);
+    plan_bracket(kPlanN, kPlanNN, (double)nvec, &n0, &n1, &wn);
+    const int ti[4] = {t0, t0, t1, t1}, ni[4] = {n0, n1, n0, n1};
+    const double pw[4] = {wt * wn, wt * (1.0 - wn), (1.0 - wt) * wn, (1.0 - wt) * (1.0 - wn)};
+    int best = -1;
+    double best_score = 0.0;
+    for (int g = 0; g < kPlanNG; ++g) {
+        const int w = kPlanWaves[g / 8], v = kPlanPerLane[(g / 2) % 4];
+        if ((int64_t)w * 64 * v < nvec) continue;
+        double sum = 0.0, wsum = 0.0, mx = 0.0;
+        for (int c = 0; c < 4; ++c) {
+            if (pw[c] <= 0.0) continue;
+            const int l = kPlanLoss[ti[c]][ni[c]][g];
+            if (l == 255) continue;
+            sum += pw[c] * l;
+            wsum += pw[c];
+            mx = std::max(mx, (double)l);
+        }
+        if (wsum < 0.5) continue;
+        const double score = 0.5 * sum / wsum + 0.5 * mx;
+        if (best < 0 || score < best_score) {
+            best = g;
+            best_score = score;
+        }
+    }
+    if (best < 0) {
+        analytic_row_geometry(nvec, T, w_out, v_out, late_out);
+        return;
+    }
+    *w_out = kPlanWaves[best / 8];
+    *v_out = kPlanPerLane[(best / 2) % 4];
+    *late_out = best % 2;
+}
+
+// Unaligned path (rows off 16-byte alignment), from a sweep of the analytic
+// rule's kind on shifted and odd-d bf16 rows: up early or late by the analytic
+// rule; one vector per lane for 129..256-vector rows (3.7 % faster at
+// T = 8192), and 2048-vector rows stay at 8 waves of 4 for every T (16 waves
+// of 2 is 7-13 % slower at T = 8192 here).
 void pick_unaligned_geometry(int64_t nvec, int64_t T, int *w_out, int *v_out, int *late_out) {
-    int w, v;
-    pick_row_geometry(nvec, T, &w, &v, late_out);
+    *late_out = late_by_size(nvec, T) ? 1 : 0;
     const int target = nvec <= 64 ? 1 : nvec <= 128 ? 2 : nvec <= 256 ? 1 : nvec <= 1024 ? 2 : 4;
     waves_for(nvec, target, w_out, v_out);
 }

@@ -1,0 +1,146 @@
+// Geometry sweep for the gelu_and_mul_sparse planner (a tuning tool, not part
+// of the library).  For each (rows T, 16-byte vectors per row nvec) of a grid,
+// every compiled one-row-per-workgroup geometry of the vector kernel (waves
+// 1..16, vectors per lane 1, 2, 4, 8, the up row loaded with the gate or after
+// the statistics) is launched through the public entry point
+// ga_gelu_and_mul_sparse_with_plan on bf16 rows (d = 8 nvec), back to back on
+// the null stream over buffer sets rotated past the 256 MB Infinity Cache, and
+// timed with HIP events; each geometry's time is the best of 3 interleaved
+// passes.  Output, one CSV line per geometry: T,d,nvec,waves,per_lane,up_late,us
+//
+//   sweep <T values> -- <nvec values>      (pool size from GA_SWEEP_POOL_GB, default 16)
+//
+// gated_activation_amd/tune/make_table.py turns one or more such files into
+// the planner's table (csrc/planner_table.inc).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <functional>
+#include <vector>
+
+#include "ga.h"
+
+#define CK(x)                                                                              \
+    do {                                                                                   \
+        hipError_t e_ = (x);                                                               \
+        if (e_ != hipSuccess) {                                                            \
+            std::printf("HIP error %s at line %d\n", hipGetErrorString(e_), __LINE__);    \
+            std::exit(1);                                                                  \
+        }                                                                                  \
+    } while (0)
+
+// Finite bf16 values in [-2, 2) from a hash of the index (the kernels' speed
+// does not depend on the values).
+__global__ void fill_bf16(uint16_t *p, size_t n, uint32_t seed) {
+    size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (; i < n; i += stride) {
+        uint32_t h = (uint32_t)i * 2654435761u ^ seed;
+        h ^= h >> 13;
+        h *= 0x5bd1e995u;
+        h ^= h >> 15;
+        const float f = ((h & 0xFFFFu) / 65536.0f - 0.5f) * 4.0f;
+        p[i] = (uint16_t)(__builtin_bit_cast(uint32_t, f) >> 16);
+    }
+}
+
+static float time_pass(int sets, int iters, const std::function<void(int)> &launch) {
+    hipEvent_t a, b;
+    CK(hipEventCreate(&a));
+    CK(hipEventCreate(&b));
+    CK(hipEventRecord(a, nullptr));
+    for (int i = 0; i < iters; ++i) launch(i % sets);
+    CK(hipEventRecord(b, nullptr));
+    CK(hipEventSynchronize(b));
+    float ms = 0.0f;
+    CK(hipEventElapsedTime(&ms, a, b));
+    CK(hipEventDestroy(a));
+    CK(hipEventDestroy(b));
+    return ms * 1000.0f / (float)iters;
+}
+
+int main(int argc, char **argv) {
+    std::vector<int> Ts, NVs;
+    int a = 1;
+    for (; a < argc && std::strcmp(argv[a], "--") != 0; ++a) Ts.push_back(std::atoi(argv[a]));
+    for (++a; a < argc; ++a) NVs.push_back(std::atoi(argv[a]));
+    if (Ts.empty() || NVs.empty()) {
+        std::fprintf(stderr, "usage: sweep <T values> -- <nvec values>\n");
+        return 2;
+    }
+    const char *gb = std::getenv("GA_SWEEP_POOL_GB");
+    const size_t pool_bytes = (size_t)(gb ? std::atof(gb) : 16.0) * ((size_t)1 << 30);
+    uint16_t *pool = nullptr;
+    CK(hipMalloc(&pool, pool_bytes));
+    fill_bf16<<<8192, 256>>>(pool, pool_bytes / 2, 99u);
+    CK(hipDeviceSynchronize());
+    // Clocks up before the first measurement.
+    for (int i = 0; i < 6000; ++i)
+        ga_stream_xor_rows(pool, (char *)pool + ((size_t)512 << 20), 2048, 32768, nullptr);
+    CK(hipDeviceSynchronize());
+
+    for (int T : Ts) {
+        for (int nvec : NVs) {
+            const int d = nvec * 8;
+            const size_t in_b = (size_t)T * 2 * d * 2, out_b = (size_t)T * d * 2;
+            const size_t per = (in_b + out_b + 4095) / 4096 * 4096;
+            // At least two sets, and sets enough to span 1 GiB.
+            if (2 * per > pool_bytes) continue;
+            int sets = (int)std::min<size_t>(64, std::max<size_t>(2, ((size_t)1 << 30) / per + 1));
+            if ((size_t)sets * per > pool_bytes) sets = (int)(pool_bytes / per);
+            std::vector<void *> vin(sets), vout(sets);
+            for (int s = 0; s < sets; ++s) {
+                vin[s] = (char *)pool + (size_t)s * per;
+                vout[s] = (char *)pool + (size_t)s * per + in_b;
+            }
+            const double bytes = (double)(in_b + out_b);
+            const int iters = std::max(30, std::min(800, (int)(1.5e5 / (bytes / 5e3 + 3.0))));
+            std::vector<ga_plan> plans;
+            for (int w : {1, 2, 4, 8, 16})
+                for (int v : {1, 2, 4, 8}) {
+                    const long slots = (long)w * 64 * v;
+                    if (slots < nvec || slots >= 8L * nvec) continue;
+                    for (int late : {0, 1}) {
+                        ga_plan p;
+                        std::memset(&p, 0, sizeof p);
+                        p.path = 0;
+                        p.waves_per_row = w;
+                        p.per_lane = v;
+                        p.up_late = late;
+                        p.splits = 1;
+                        p.block = w * 64;
+                        p.grid = T;
+                        // Zero rows: the library validates the plan and launches nothing.
+                        if (ga_gelu_and_mul_sparse_with_plan(vin[0], vout[0], 0, d, GA_BF16, 1.6448536f, nullptr, &p,
+                                                             nullptr, 0, nullptr) == GA_OK)
+                            plans.push_back(p);
+                    }
+                }
+            std::vector<float> best(plans.size(), 1e30f);
+            for (size_t i = 0; i < plans.size(); ++i)
+                for (int k = 0; k < 3; ++k)
+                    ga_gelu_and_mul_sparse_with_plan(vin[k % sets], vout[k % sets], T, d, GA_BF16, 1.6448536f,
+                                                     nullptr, &plans[i], nullptr, 0, nullptr);
+            CK(hipDeviceSynchronize());
+            for (int pass = 0; pass < 3; ++pass)
+                for (size_t i = 0; i < plans.size(); ++i) {
+                    const ga_plan &p = plans[i];
+                    best[i] = std::min(best[i], time_pass(sets, iters, [&](int s) {
+                        ga_gelu_and_mul_sparse_with_plan(vin[s], vout[s], T, d, GA_BF16, 1.6448536f, nullptr, &p,
+                                                         nullptr, 0, nullptr);
+                    }));
+                }
+            CK(hipGetLastError());
+            for (size_t i = 0; i < plans.size(); ++i)
+                std::printf("%d,%d,%d,%d,%d,%d,%.3f\n", T, d, nvec, plans[i].waves_per_row, plans[i].per_lane,
+                            plans[i].up_late, best[i]);
+            std::fflush(stdout);
+        }
+    }
+    CK(hipFree(pool));
+    std::printf("done\n");
+    return 0;
+}

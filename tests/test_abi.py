@@ -113,24 +113,49 @@ def test_stream_xor_rows_checks():
 
 def test_gelu_planner_known_shapes():
     # (T, d) -> (path, waves per workgroup, vectors per lane, up loaded late, splits)
-    want = {(2048, 16384): (0, 8, 4, 1, 1), (512, 8192): (0, 8, 2, 0, 1), (2048, 8192): (0, 8, 2, 1, 1),
-            (4, 2048): (0, 4, 1, 0, 1), (2048, 32768): (0, 16, 4, 1, 1), (1, 8192): (0, 8, 2, 0, 1),
+    want = {(2048, 16384): (0, 8, 4, 1, 1), (2048, 32768): (0, 16, 4, 1, 1), (4096, 65536): (0, 16, 8, 1, 1),
             # few long rows split over workgroups (with a workspace)
             (1, 32768): (0, 8, 1, 0, 8), (64, 16384): (0, 8, 1, 0, 4), (64, 32768): (0, 8, 2, 0, 4),
-            (128, 32768): (0, 8, 4, 0, 2), (65, 16384): (0, 8, 4, 0, 1), (64, 65536): (0, 8, 4, 0, 4),
-            # measured geometry choices: 2 vectors per lane for 65..1024-vector rows, up late
-            # from 2^20 gate vectors (with >= 1024 rows or >= 2^21 vectors)
-            (2048, 4096): (0, 4, 2, 1, 1), (1024, 4096): (0, 4, 2, 0, 1), (512, 32768): (0, 16, 4, 1, 1),
-            (256, 32768): (0, 16, 4, 0, 1), (512, 16384): (0, 8, 4, 0, 1), (4096, 2048): (0, 2, 2, 1, 1),
-            (2048, 2048): (0, 4, 1, 0, 1), (1024, 1024): (0, 1, 2, 0, 1), (8192, 1024): (0, 1, 2, 1, 1),
-            (8192, 16384): (0, 16, 2, 1, 1), (4096, 16384): (0, 8, 4, 1, 1), (4096, 65536): (0, 16, 8, 1, 1),
-            # 1664..2047-vector rows: 16 waves of 2 from 2048 rows; 1536..1663 from 4096 rows
-            (2048, 14336): (0, 16, 2, 1, 1), (1536, 14336): (0, 8, 4, 1, 1), (2048, 13312): (0, 16, 2, 1, 1),
-            (2048, 12800): (0, 8, 4, 1, 1), (4096, 12288): (0, 16, 2, 1, 1), (4096, 11264): (0, 8, 4, 1, 1)}
+            (128, 32768): (0, 8, 4, 0, 2), (64, 65536): (0, 8, 4, 0, 4)}
     for (T, d), w in want.items():
         p = ga.plan_gelu_and_mul_sparse(T, d, BF16)
         assert (p.path, p.waves_per_row, p.per_lane, p.up_late, p.splits) == w, (T, d, p.as_dict())
         assert p.block == 64 * p.waves_per_row and p.grid == T * p.splits
+
+
+def test_row_geometry_follows_the_measured_table():
+    """One workgroup per row: the planner's geometry is the one the measured
+    table's interpolation rule picks, checked against the independent Python
+    statement of that rule in tune/make_table.py over on- and off-grid
+    shapes; every choice is a compiled geometry covering the row."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "make_table", os.path.join(ROOT, "gated_activation_amd", "tune", "make_table.py"))
+    mt = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mt)
+    table = mt.read_inc(os.path.join(ROOT, "gated_activation_amd", "csrc", "planner_table.inc"))
+    Ts = sorted(set(table[0]) | {1, 7, 33, 100, 300, 700, 900, 1800, 2500, 3500, 5000, 10000, 20000, 65535})
+    Ns = sorted(set(table[1]) | {33, 63, 65, 72, 88, 140, 200, 300, 420, 600, 700, 1100, 1376, 1664, 1792,
+                                 2368, 2752, 3200, 3800, 4500, 8191})
+    for T in Ts:
+        for n in Ns:
+            p = ga.plan_gelu_and_mul_sparse(T, n * 8, BF16, with_workspace=False)
+            assert p.path == 0 and p.splits == 1
+            got = (p.waves_per_row, p.per_lane, p.up_late)
+            assert p.waves_per_row * 64 * p.per_lane >= n
+            want = mt.choose(table, T, n)
+            if got != want:
+                # only a floating-point tie may differ
+                sc = mt.scores(table, T, n)
+                gi = mt.GEOS.index(got)
+                wi = mt.GEOS.index(want)
+                assert sc[gi] is not None and abs(sc[gi] - sc[wi]) < 1e-9, (T, n, got, want)
+    # the headline shape keeps 8 waves of 4 vectors with up loaded late
+    p = ga.plan_gelu_and_mul_sparse(2048, 16384, BF16)
+    assert (p.waves_per_row, p.per_lane, p.up_late) == (8, 4, 1)
+
+
+def test_planner_paths_by_row_size():
     # short rows: packed, several rows per wavefront
     for d, g, v in ((8, 4, 1), (24, 4, 1), (64, 8, 1), (128, 16, 1), (256, 32, 1), (200, 32, 1)):
         p = ga.plan_gelu_and_mul_sparse(4096, d, BF16)

@@ -18,8 +18,18 @@ HIPCC = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
 
 
 def _copy_sources(dst):
-    keep = (".py", ".hip", ".h", ".c", ".cpp")
-    for top in ("gated_activation_amd", "oracle", "synth", "include"):
+    """The tracked files of a fresh clone (git ls-files), else the sources by
+    extension."""
+    tops = ("gated_activation_amd", "oracle", "synth", "include")
+    r = subprocess.run(["git", "ls-files", *tops], cwd=ROOT, capture_output=True, text=True)
+    if r.returncode == 0 and r.stdout.strip():
+        for rel in r.stdout.split():
+            os.makedirs(os.path.join(dst, os.path.dirname(rel)), exist_ok=True)
+            shutil.copy2(os.path.join(ROOT, rel), os.path.join(dst, rel))
+        shutil.copy2(os.path.join(ROOT, "__graft_entry__.py"), dst)
+        return
+    keep = (".py", ".hip", ".h", ".inc", ".c", ".cpp")
+    for top in tops:
         for dirpath, dirnames, filenames in os.walk(os.path.join(ROOT, top)):
             dirnames[:] = [d for d in dirnames if d != "__pycache__"]
             rel = os.path.relpath(dirpath, ROOT)

@@ -1,0 +1,60 @@
+"""The planner's tuning tool (gated_activation_amd/tune): the sweep program
+compiles against the public header, and the table builder turns sweep lines
+into a table whose interpolation rule picks the measured best geometry at
+the grid points and respects coverage between them."""
+import importlib.util
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+TUNE = os.path.join(ROOT, "gated_activation_amd", "tune")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+def _make_table():
+    spec = importlib.util.spec_from_file_location("make_table", os.path.join(TUNE, "make_table.py"))
+    mt = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mt)
+    return mt
+
+
+@pytest.mark.skipif(not os.path.exists(os.path.join(ROCM, "bin", "hipcc")), reason="no hipcc")
+def test_sweep_tool_compiles():
+    subprocess.run([os.path.join(ROCM, "bin", "hipcc"), "--offload-arch=gfx950", "-std=c++17", "-fsyntax-only",
+                    "-I", os.path.join(ROOT, "include"), os.path.join(TUNE, "sweep.hip")],
+                   check=True, capture_output=True, text=True)
+
+
+def test_table_builder_round_trip(tmp_path):
+    mt = _make_table()
+    # A synthetic sweep on a 2 x 2 grid: at every point one geometry is
+    # fastest; a second one is 10 % slower everywhere.
+    lines = []
+    fast = {(100, 128): (1, 2, 0), (100, 512): (8, 1, 1), (400, 128): (2, 1, 1), (400, 512): (4, 2, 0)}
+    for (T, n), g in fast.items():
+        for geo in mt.GEOS:
+            w, v, late = geo
+            if w * 64 * v < n or w * 64 * v >= 8 * n:
+                continue
+            us = 10.0 if geo == g else 11.0 + 0.01 * mt.GEOS.index(geo)
+            lines.append(f"{T},{n * 8},{n},{w},{v},{late},{us}")
+    csv = tmp_path / "s.csv"
+    csv.write_text("\n".join(lines) + "\ndone\n")
+    inc = tmp_path / "t.inc"
+    mt.main(["make_table.py", str(inc), str(csv)])
+    table = mt.read_inc(str(inc))
+    assert table[0] == [100, 400] and table[1] == [128, 512]
+    for (T, n), g in fast.items():
+        assert mt.choose(table, T, n) == g
+        i = mt.GEOS.index(g)
+        assert table[2][(T, n)][i] == 0
+    # between grid points every choice still covers the row
+    for T in (50, 150, 250, 1000):
+        for n in (100, 200, 300, 511):
+            w, v, late = mt.choose(table, T, n)
+            assert w * 64 * v >= n
+    # a geometry not run at a point is marked, not guessed
+    assert table[2][(100, 128)][mt.GEOS.index((16, 8, 0))] == mt.NOT_RUN
