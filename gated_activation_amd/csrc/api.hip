@@ -150,15 +150,28 @@ void analytic_row_geometry(int64_t nvec, int64_t T, int *w_out, int *v_out, int 
     *late_out = late ? 1 : 0;
 }
 
-// The measured geometry table: kPlanLoss[t][n][g] is how much slower geometry
-// g ran than the best geometry at kPlanT[t] rows of kPlanN[n] vectors (in
-// 1/400 steps; 255 = not run), from sweeps of every compiled geometry of the
-// vector kernel on MI355X (gated_activation_amd/tune; bf16 rows: the choice
-// depends on bytes per row, so it serves every type).
+// The measured geometry tables: Loss[t][n][g] is how much slower geometry g
+// ran than the best geometry at T[t] rows of N[n] vectors (in 1/400 steps;
+// 255 = not run), from sweeps of every compiled geometry on MI355X
+// (gated_activation_amd/tune; bf16 rows: the choice depends on bytes per
+// row, so it serves every type).  kPlan*: the vector kernel; kUna*: the
+// unaligned kernel on rows one element off 16-byte alignment.
 #include "planner_table.inc"
+#include "planner_table_una.inc"
 
 constexpr int kPlanWaves[5] = {1, 2, 4, 8, 16};
 constexpr int kPlanPerLane[4] = {1, 2, 4, 8};
+static_assert(kPlanNG == 40 && kUnaNG == 40, "geometry tables: 5 wave counts x 4 per-lane counts x 2 up modes");
+
+struct GeoTable {
+    const int *T;
+    int nT;
+    const int *N;
+    int nN;
+    const unsigned char *loss;  // [nT][nN][40]
+};
+const GeoTable kVecTable{kPlanT, kPlanNT, kPlanN, kPlanNN, &kPlanLoss[0][0][0]};
+const GeoTable kUnaTable{kUnaT, kUnaNT, kUnaN, kUnaNN, &kUnaLoss[0][0][0]};
 
 // Grid interval around x: indices lo <= hi and the weight of lo, linear in
 // log2 x; outside the grid both indices are the end point.
@@ -177,29 +190,27 @@ void plan_bracket(const int *grid, int n, double x, int *lo, int *hi, double *wl
     }
 }
 
-// One workgroup per row: the compiled geometry that covers nvec with the least
-// loss interpolated over the four grid points around (T, nvec) (weights
-// linear in log2 T and log2 nvec), scored as half the weighted mean plus half
-// the largest loss over the points where it was run (at least half of the
-// weight); ties go to the first geometry in table order.  On 153 shapes off
-// the grid this choice ran at 1.007x the best geometry on average, 1.013x at
-// the 90th percentile (the analytic rule: 1.027x and 1.080x, up to 1.28x).
-void pick_row_geometry(int64_t nvec, int64_t T, int *w_out, int *v_out, int *late_out) {
+// The tabled geometry that covers nvec with the least loss interpolated over
+// the four grid points around (T, nvec) (weights linear in log2 T and log2
+// nvec), scored as half the weighted mean plus half the largest loss over the
+// points where it was run (at least half of the weight); ties go to the
+// first geometry in table order.  False if no geometry qualifies.
+bool table_geometry(const GeoTable &tb, int64_t nvec, int64_t T, int *w_out, int *v_out, int *late_out) {
     int t0, t1, n0, n1;
     double wt, wn;
-    plan_bracket(kPlanT, kPlanNT, (double)T, &t0, &t1, &wt);
-    plan_bracket(kPlanN, kPlanNN, (double)nvec, &n0, &n1, &wn);
+    plan_bracket(tb.T, tb.nT, (double)T, &t0, &t1, &wt);
+    plan_bracket(tb.N, tb.nN, (double)nvec, &n0, &n1, &wn);
     const int ti[4] = {t0, t0, t1, t1}, ni[4] = {n0, n1, n0, n1};
     const double pw[4] = {wt * wn, wt * (1.0 - wn), (1.0 - wt) * wn, (1.0 - wt) * (1.0 - wn)};
     int best = -1;
     double best_score = 0.0;
-    for (int g = 0; g < kPlanNG; ++g) {
+    for (int g = 0; g < 40; ++g) {
         const int w = kPlanWaves[g / 8], v = kPlanPerLane[(g / 2) % 4];
         if ((int64_t)w * 64 * v < nvec) continue;
         double sum = 0.0, wsum = 0.0, mx = 0.0;
         for (int c = 0; c < 4; ++c) {
             if (pw[c] <= 0.0) continue;
-            const int l = kPlanLoss[ti[c]][ni[c]][g];
+            const int l = tb.loss[((size_t)ti[c] * tb.nN + ni[c]) * 40 + g];
             if (l == 255) continue;
             sum += pw[c] * l;
             wsum += pw[c];
@@ -212,21 +223,29 @@ void pick_row_geometry(int64_t nvec, int64_t T, int *w_out, int *v_out, int *lat
             best_score = score;
         }
     }
-    if (best < 0) {
-        analytic_row_geometry(nvec, T, w_out, v_out, late_out);
-        return;
-    }
+    if (best < 0) return false;
     *w_out = kPlanWaves[best / 8];
     *v_out = kPlanPerLane[(best / 2) % 4];
     *late_out = best % 2;
+    return true;
 }
 
-// Unaligned path (rows off 16-byte alignment), from a sweep of the analytic
-// rule's kind on shifted and odd-d bf16 rows: up early or late by the analytic
-// rule; one vector per lane for 129..256-vector rows (3.7 % faster at
-// T = 8192), and 2048-vector rows stay at 8 waves of 4 for every T (16 waves
-// of 2 is 7-13 % slower at T = 8192 here).
+// One workgroup per row, vector path.  On 153 shapes off the grid the tabled
+// choice ran at 1.007x the best geometry on average, 1.013x at the 90th
+// percentile (the analytic rule: 1.027x and 1.080x, up to 1.28x).
+void pick_row_geometry(int64_t nvec, int64_t T, int *w_out, int *v_out, int *late_out) {
+    if (!table_geometry(kVecTable, nvec, T, w_out, v_out, late_out))
+        analytic_row_geometry(nvec, T, w_out, v_out, late_out);
+}
+
+// Unaligned path (rows off 16-byte alignment).  On the same 153 shapes, one
+// element off alignment, the tabled choice ran at 1.012x the best geometry on
+// average, 1.037x at the 90th percentile; the earlier rule (below, the
+// fallback) at 1.045x and 1.103x, up to 1.39x.  That rule: up early or late
+// by the analytic rule; one vector per lane for 129..256-vector rows, else the
+// analytic rule's vectors per lane.
 void pick_unaligned_geometry(int64_t nvec, int64_t T, int *w_out, int *v_out, int *late_out) {
+    if (table_geometry(kUnaTable, nvec, T, w_out, v_out, late_out)) return;
     *late_out = late_by_size(nvec, T) ? 1 : 0;
     const int target = nvec <= 64 ? 1 : nvec <= 128 ? 2 : nvec <= 256 ? 1 : nvec <= 1024 ? 2 : 4;
     waves_for(nvec, target, w_out, v_out);

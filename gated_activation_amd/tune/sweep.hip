@@ -10,6 +10,9 @@
 //
 //   sweep <T values> -- <nvec values>      (pool size from GA_SWEEP_POOL_GB, default 16)
 //
+// GA_SWEEP_PATH=2 sweeps the unaligned path instead (vectors per lane 1..8):
+// the input view starts one element past a 16-byte boundary.
+//
 // gated_activation_amd/tune/make_table.py turns one or more such files into
 // the planner's table (csrc/planner_table.inc).
 #include <hip/hip_runtime.h>
@@ -71,6 +74,9 @@ int main(int argc, char **argv) {
         std::fprintf(stderr, "usage: sweep <T values> -- <nvec values>\n");
         return 2;
     }
+    const char *path_env = std::getenv("GA_SWEEP_PATH");
+    const int path = path_env && std::atoi(path_env) == 2 ? 2 : 0;
+    const size_t shift = path == 2 ? 2 : 0;  // bytes: one bf16 element
     const char *gb = std::getenv("GA_SWEEP_POOL_GB");
     const size_t pool_bytes = (size_t)(gb ? std::atof(gb) : 16.0) * ((size_t)1 << 30);
     uint16_t *pool = nullptr;
@@ -86,27 +92,29 @@ int main(int argc, char **argv) {
         for (int nvec : NVs) {
             const int d = nvec * 8;
             const size_t in_b = (size_t)T * 2 * d * 2, out_b = (size_t)T * d * 2;
-            const size_t per = (in_b + out_b + 4095) / 4096 * 4096;
+            // the output starts 256 bytes past the input's end (room for the shift)
+            const size_t per = (in_b + 256 + out_b + 4095) / 4096 * 4096;
             // At least two sets, and sets enough to span 1 GiB.
             if (2 * per > pool_bytes) continue;
             int sets = (int)std::min<size_t>(64, std::max<size_t>(2, ((size_t)1 << 30) / per + 1));
             if ((size_t)sets * per > pool_bytes) sets = (int)(pool_bytes / per);
             std::vector<void *> vin(sets), vout(sets);
             for (int s = 0; s < sets; ++s) {
-                vin[s] = (char *)pool + (size_t)s * per;
-                vout[s] = (char *)pool + (size_t)s * per + in_b;
+                vin[s] = (char *)pool + (size_t)s * per + shift;
+                vout[s] = (char *)pool + (size_t)s * per + in_b + 256;
             }
             const double bytes = (double)(in_b + out_b);
             const int iters = std::max(30, std::min(800, (int)(1.5e5 / (bytes / 5e3 + 3.0))));
             std::vector<ga_plan> plans;
             for (int w : {1, 2, 4, 8, 16})
-                for (int v : {1, 2, 4, 8}) {
+                for (int v = 1; v <= 8; ++v) {
+                    if (path == 0 && (v & (v - 1)) != 0) continue;
                     const long slots = (long)w * 64 * v;
                     if (slots < nvec || slots >= 8L * nvec) continue;
                     for (int late : {0, 1}) {
                         ga_plan p;
                         std::memset(&p, 0, sizeof p);
-                        p.path = 0;
+                        p.path = path;
                         p.waves_per_row = w;
                         p.per_lane = v;
                         p.up_late = late;
