@@ -117,14 +117,6 @@ void waves_for(int64_t nvec, int target, int *w_out, int *v_out) {
     *v_out = next_pow2((nvec + 64 * w - 1) / (64 * w));
 }
 
-// Split-row chunks: 1 vector per lane up to 512 vectors, 2 up to 1024, else 4
-// (at most max_v).
-void pick_waves(int64_t nvec, int max_v, int *w_out, int *v_out) {
-    int target = nvec <= 512 ? 1 : nvec <= 1024 ? 2 : 4;
-    if (target > max_v) target = max_v;
-    waves_for(nvec, target, w_out, v_out);
-}
-
 // The analytic row rule, from a first sweep of power-of-two shapes (T in
 // 256..8192, 128..4096 vectors per row, bf16): loading up after the
 // statistics frees registers for more resident rows; it pays once the gate
@@ -158,6 +150,7 @@ void analytic_row_geometry(int64_t nvec, int64_t T, int *w_out, int *v_out, int 
 // unaligned kernel on rows one element off 16-byte alignment.
 #include "planner_table.inc"
 #include "planner_table_una.inc"
+#include "planner_table_split.inc"
 
 constexpr int kPlanWaves[5] = {1, 2, 4, 8, 16};
 constexpr int kPlanPerLane[4] = {1, 2, 4, 8};
@@ -190,39 +183,49 @@ void plan_bracket(const int *grid, int n, double x, int *lo, int *hi, double *wl
     }
 }
 
-// The tabled geometry that covers nvec with the least loss interpolated over
-// the four grid points around (T, nvec) (weights linear in log2 T and log2
-// nvec), scored as half the weighted mean plus half the largest loss over the
-// points where it was run (at least half of the weight); ties go to the
-// first geometry in table order.  False if no geometry qualifies.
-bool table_geometry(const GeoTable &tb, int64_t nvec, int64_t T, int *w_out, int *v_out, int *late_out) {
+// The valid candidate with the least loss interpolated over the four grid
+// points around (T, nvec) (weights linear in log2 T and log2 nvec), scored as
+// half the weighted mean plus half the largest loss over the points where it
+// was run (at least half of the weight); ties go to the first candidate in
+// table order.  loss: [nT][nN][nc].  -1 if no candidate qualifies.
+template <typename Valid>
+int table_argmin(const int *Tg, int nT, const int *Ng, int nN, const unsigned char *loss, int nc, int64_t T,
+                 int64_t nvec, Valid valid) {
     int t0, t1, n0, n1;
     double wt, wn;
-    plan_bracket(tb.T, tb.nT, (double)T, &t0, &t1, &wt);
-    plan_bracket(tb.N, tb.nN, (double)nvec, &n0, &n1, &wn);
+    plan_bracket(Tg, nT, (double)T, &t0, &t1, &wt);
+    plan_bracket(Ng, nN, (double)nvec, &n0, &n1, &wn);
     const int ti[4] = {t0, t0, t1, t1}, ni[4] = {n0, n1, n0, n1};
     const double pw[4] = {wt * wn, wt * (1.0 - wn), (1.0 - wt) * wn, (1.0 - wt) * (1.0 - wn)};
     int best = -1;
     double best_score = 0.0;
-    for (int g = 0; g < 40; ++g) {
-        const int w = kPlanWaves[g / 8], v = kPlanPerLane[(g / 2) % 4];
-        if ((int64_t)w * 64 * v < nvec) continue;
+    for (int c = 0; c < nc; ++c) {
+        if (!valid(c)) continue;
         double sum = 0.0, wsum = 0.0, mx = 0.0;
-        for (int c = 0; c < 4; ++c) {
-            if (pw[c] <= 0.0) continue;
-            const int l = tb.loss[((size_t)ti[c] * tb.nN + ni[c]) * 40 + g];
+        for (int k = 0; k < 4; ++k) {
+            if (pw[k] <= 0.0) continue;
+            const int l = loss[((size_t)ti[k] * nN + ni[k]) * nc + c];
             if (l == 255) continue;
-            sum += pw[c] * l;
-            wsum += pw[c];
+            sum += pw[k] * l;
+            wsum += pw[k];
             mx = std::max(mx, (double)l);
         }
         if (wsum < 0.5) continue;
         const double score = 0.5 * sum / wsum + 0.5 * mx;
         if (best < 0 || score < best_score) {
-            best = g;
+            best = c;
             best_score = score;
         }
     }
+    return best;
+}
+
+// The tabled row geometry (40 candidates: waves x vectors per lane x up mode)
+// that covers nvec.  False if no geometry qualifies.
+bool table_geometry(const GeoTable &tb, int64_t nvec, int64_t T, int *w_out, int *v_out, int *late_out) {
+    const int best = table_argmin(tb.T, tb.nT, tb.N, tb.nN, tb.loss, 40, T, nvec, [&](int g) {
+        return (int64_t)kPlanWaves[g / 8] * 64 * kPlanPerLane[(g / 2) % 4] >= nvec;
+    });
     if (best < 0) return false;
     *w_out = kPlanWaves[best / 8];
     *v_out = kPlanPerLane[(best / 2) % 4];
@@ -249,6 +252,31 @@ void pick_unaligned_geometry(int64_t nvec, int64_t T, int *w_out, int *v_out, in
     *late_out = late_by_size(nvec, T) ? 1 : 0;
     const int target = nvec <= 64 ? 1 : nvec <= 128 ? 2 : nvec <= 256 ? 1 : nvec <= 1024 ? 2 : 4;
     waves_for(nvec, target, w_out, v_out);
+}
+
+// Few long rows, with a workspace: whether to split each row over several
+// workgroups, and into which chunks, from the measured split table
+// (kSplitLoss: 15 chunk geometries of the split kernel, waves 1..16 times
+// vectors per lane 1, 2, 4, each row taking ceil(nvec / chunk) splits in
+// 2..16, and not splitting as the last candidate; 1 <= T <= 256, 2048 ..
+// 8192 vectors per row).  On 36 shapes off the grid the tabled choice ran at
+// 1.0085x the best plan on average (the earlier rule, about 512-vector chunks
+// for about 256 workgroups: 1.04x, up to 1.26x).  False: do not split.
+bool pick_split(int64_t nvec, int64_t T, int *w_out, int *v_out, int *splits_out) {
+    static_assert(kSplitNG == 16, "split table: 15 chunk geometries and the row path");
+    if (T < 1 || T > kSplitT[kSplitNT - 1] || nvec < kSplitN[0] || nvec > kSplitN[kSplitNN - 1]) return false;
+    auto chunk_of = [](int c) { return (int64_t)kPlanWaves[c / 3] * 64 * (1 << (c % 3)); };
+    const int best = table_argmin(kSplitT, kSplitNT, kSplitN, kSplitNN, &kSplitLoss[0][0][0], kSplitNG, T, nvec,
+                                  [&](int c) {
+                                      if (c == 15) return true;
+                                      const int64_t splits = (nvec + chunk_of(c) - 1) / chunk_of(c);
+                                      return splits >= 2 && splits <= ga::SPLIT_MAX;
+                                  });
+    if (best < 0 || best == 15) return false;
+    *w_out = kPlanWaves[best / 3];
+    *v_out = 1 << (best % 3);
+    *splits_out = (int)((nvec + chunk_of(best) - 1) / chunk_of(best));
+    return true;
 }
 
 ga_status check_gelu_plan(const ga_plan *p, int64_t T, int64_t d, int32_t dtype) {
@@ -489,23 +517,14 @@ ga_status ga_plan_gelu_and_mul_sparse(int64_t T, int64_t d, int32_t dtype, int32
         p.per_lane = v;
         p.up_late = late;
         // Few long rows: split each over several workgroups that exchange
-        // partial statistics.  Measured on MI355X, the exchange costs about
-        // a microsecond, which pays off once a row has >= 2048 vectors
-        // (32 KB of bf16 gate) and there are at most 64 rows per 2048
-        // vectors; splits aim at ~512-vector chunks and ~256 workgroups.
-        if (with_workspace && T >= 1 && T <= kSplitMaxRows && nvec >= 2048 && T * 2048 <= 64 * nvec) {
-            int64_t splits = std::min<int64_t>(nvec / 512, std::max<int64_t>(2, 256 / T));
-            if (splits > ga::SPLIT_MAX) splits = ga::SPLIT_MAX;
-            int sw, sv;
-            pick_waves((nvec + splits - 1) / splits, 4, &sw, &sv);
-            const int64_t chunk = (int64_t)sw * 64 * sv;
-            splits = (nvec + chunk - 1) / chunk;  // every split owns >= 1 vector
-            if (splits >= 2 && splits <= ga::SPLIT_MAX) {
-                p.waves_per_row = sw;
-                p.per_lane = sv;
-                p.up_late = 0;
-                p.splits = (int32_t)splits;
-            }
+        // partial statistics (about a microsecond, so only where the measured
+        // split table says it pays).
+        int sw, sv, ss;
+        if (with_workspace && pick_split(nvec, T, &sw, &sv, &ss)) {
+            p.waves_per_row = sw;
+            p.per_lane = sv;
+            p.up_late = 0;
+            p.splits = ss;
         }
     } else if (nvec_ceil <= 16 * 64 * 8) {
         // Rows that are not 16-byte aligned: the same vectors, each one

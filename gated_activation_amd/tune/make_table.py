@@ -1,7 +1,7 @@
 """Turn geometry sweeps (tune/sweep.hip output) into the planner's table.
 
-    python make_table.py [--prefix kUna] OUT.inc SWEEP.csv [SWEEP.csv ...]
-    python make_table.py --check [--prefix kUna] TABLE.inc OFFGRID.csv
+    python make_table.py [--prefix kUna | --split] OUT.inc SWEEP.csv [SWEEP.csv ...]
+    python make_table.py --check [--prefix kUna | --split] TABLE.inc OFFGRID.csv
 
 The prefix names the table's symbols: kPlan (default) for the vector path,
 kUna for the unaligned path (sweeps run with GA_SWEEP_PATH=2; its kernel also
@@ -33,6 +33,11 @@ WAVES = (1, 2, 4, 8, 16)
 PER_LANE = (1, 2, 4, 8)
 GEOS = [(w, v, late) for w in WAVES for v in PER_LANE for late in (0, 1)]
 NOT_RUN = 255
+# Split table (--split, sweeps run with GA_SWEEP_PATH=split): chunk geometries
+# (waves, vectors per lane) of the split kernel, then the row path (no split)
+# as the last candidate; a row takes ceil(nvec / chunk) splits, 2..16.
+SPLIT_CHUNKS = [(w, v) for w in WAVES for v in (1, 2, 4)]
+ROW = len(SPLIT_CHUNKS)
 
 
 def read_sweeps(paths):
@@ -47,6 +52,63 @@ def read_sweeps(paths):
     for (T, nvec, geo), ts in acc.items():
         times[(T, nvec)][geo] = sum(ts) / len(ts)
     return times
+
+
+def read_split_sweeps(paths):
+    """(T, nvec) -> {candidate index: mean time}: chunk candidates from the
+    split plans, ROW from the fastest one-row-per-workgroup plan."""
+    acc = collections.defaultdict(list)
+    for path in paths:
+        for line in open(path):
+            if not line[:1].isdigit():
+                continue
+            f = line.strip().split(",")
+            T, nvec, w, v, us, splits = int(f[0]), int(f[2]), int(f[3]), int(f[4]), float(f[6]), int(f[7])
+            key = ROW if splits == 1 else SPLIT_CHUNKS.index((w, v))
+            acc[(T, nvec, key, w, v, int(f[5]))].append(us)
+    times = collections.defaultdict(dict)
+    for (T, nvec, key, w, v, late), ts in acc.items():
+        t = sum(ts) / len(ts)
+        if key not in times[(T, nvec)] or t < times[(T, nvec)][key]:
+            times[(T, nvec)][key] = t
+    return times
+
+
+def build_split(times):
+    Ts = sorted({k[0] for k in times})
+    Ns = sorted({k[1] for k in times})
+    loss = {}
+    for T in Ts:
+        for n in Ns:
+            g = times.get((T, n), {})
+            row = [NOT_RUN] * (ROW + 1)
+            if g:
+                best = min(g.values())
+                for c, t in g.items():
+                    row[c] = min(254, int(round((t / best - 1.0) * 400.0)))
+            loss[(T, n)] = row
+    return Ts, Ns, loss
+
+
+def split_valid(c, nvec):
+    if c == ROW:
+        return True
+    w, v = SPLIT_CHUNKS[c]
+    splits = -(-nvec // (w * 64 * v))
+    return 2 <= splits <= 16
+
+
+def choose_split(table, T, nvec):
+    """None (do not split) or (waves, vectors per lane, splits)."""
+    sc = scores(table, T, nvec, [c for c in range(ROW + 1) if split_valid(c, nvec)])
+    best = None
+    for c, x in enumerate(sc):
+        if x is not None and (best is None or x < sc[best]):
+            best = c
+    if best is None or best == ROW:
+        return None
+    w, v = SPLIT_CHUNKS[best]
+    return (w, v, -(-nvec // (w * 64 * v)))
 
 
 def build(times):
@@ -68,17 +130,24 @@ def build(times):
 
 def write_inc(path, Ts, Ns, loss, sources, prefix="kPlan"):
     P = prefix
-    kind = "the unaligned path" if P == "kUna" else "the vector path"
+    kind = {"kUna": "the unaligned path", "kSplit": "few-row shapes (the split path)"}.get(P, "the vector path")
+    if P == "kSplit":
+        cand = ["// candidate c < 15: split-kernel chunks of waves 1, 2, 4, 8, 16 (index c / 3) times",
+                "// vectors per lane 1, 2, 4 (index c % 3), ceil(nvec / chunk) splits; c = 15: no split",
+                "// (the fastest one-row-per-workgroup geometry)."]
+        ng = ROW + 1
+    else:
+        cand = ["// Geometry g = ((waves index * 4 + vectors-per-lane index) * 2 + up_late), waves",
+                "// 1, 2, 4, 8, 16, vectors per lane 1, 2, 4, 8."]
+        ng = len(GEOS)
     out = ["// Generated by gated_activation_amd/tune/make_table.py from geometry sweeps of " + kind,
            "// (gated_activation_amd/tune/sweep.hip, bf16 rows, one MI355X): " + ", ".join(sources) + ".",
-           f"// {P}Loss[t][n][g]: time of geometry g over the best geometry's time at",
+           f"// {P}Loss[t][n][g]: time of candidate g over the best candidate's time at",
            f"// ({P}T[t] rows, {P}N[n] vectors per row), as round((ratio - 1) * 400),",
-           "// capped at 254; 255 = not run there.  Geometry g = ((waves index * 4 +",
-           "// vectors-per-lane index) * 2 + up_late), waves 1, 2, 4, 8, 16, vectors per lane",
-           "// 1, 2, 4, 8.",
+           "// capped at 254; 255 = not run there."] + cand + [
            f"constexpr int {P}NT = {len(Ts)};",
            f"constexpr int {P}NN = {len(Ns)};",
-           f"constexpr int {P}NG = {len(GEOS)};",
+           f"constexpr int {P}NG = {ng};",
            f"constexpr int {P}T[{P}NT] = {{" + ", ".join(map(str, Ts)) + "};",
            f"constexpr int {P}N[{P}NN] = {{" + ", ".join(map(str, Ns)) + "};",
            f"constexpr unsigned char {P}Loss[{P}NT][{P}NN][{P}NG] = {{"]
@@ -112,15 +181,18 @@ def _bracket(grid, x):
     raise AssertionError
 
 
-def scores(table, T, nvec):
-    """Score of every geometry that covers nvec (None where not enough data)."""
+def scores(table, T, nvec, valid=None):
+    """Score of every candidate (None where not valid or not enough data).
+    valid: candidate indices to score; default: the geometries covering nvec."""
     Ts, Ns, loss = table
     t0, t1, wt = _bracket(Ts, T)
     n0, n1, wn = _bracket(Ns, nvec)
     pts = [((t0, n0), wt * wn), ((t0, n1), wt * (1 - wn)), ((t1, n0), (1 - wt) * wn), ((t1, n1), (1 - wt) * (1 - wn))]
+    if valid is None:
+        valid = [i for i, (w, v, late) in enumerate(GEOS) if w * 64 * v >= nvec]
     out = []
-    for i, (w, v, late) in enumerate(GEOS):
-        if w * 64 * v < nvec:
+    for i in range(len(next(iter(loss.values())))):
+        if i not in valid:
             out.append(None)
             continue
         s = ws = mx = 0.0
@@ -156,6 +228,31 @@ def main(argv):
         i = argv.index("--prefix")
         prefix = argv[i + 1]
         del argv[i:i + 2]
+    split = "--split" in argv
+    if split:
+        argv.remove("--split")
+        prefix = "kSplit"
+    if check and split:
+        table = read_inc(argv[1], prefix)
+        times = read_split_sweeps(argv[2:])
+        ratios = []
+        for (T, n), g in sorted(times.items()):
+            c = choose_split(table, T, n)
+            key = ROW if c is None else SPLIT_CHUNKS.index((c[0], c[1]))
+            ratios.append(g[key] / min(g.values()) if key in g else float("nan"))
+            print(f"T={T:4d} nvec={n:5d} choice {'no split' if c is None else 'S%d W%d V%d' % (c[2], c[0], c[1])}:"
+                  f" {ratios[-1]:.3f} of the best")
+        ok = sorted(x for x in ratios if x == x)
+        print(f"{len(ok)} shapes: median {ok[len(ok) // 2]:.4f}, mean {sum(ok) / len(ok):.4f}, "
+              f"90th percentile {ok[int(0.9 * len(ok))]:.4f}, worst {ok[-1]:.4f}, "
+              f"> 3 % slower: {sum(x > 1.03 for x in ok)}, not measured: {len(ratios) - len(ok)}")
+        return 0
+    if split:
+        out, sources = argv[1], argv[2:]
+        Ts, Ns, loss = build_split(read_split_sweeps(sources))
+        write_inc(out, Ts, Ns, loss, [p.split("/")[-1] for p in sources], prefix)
+        print(f"{out}: {len(Ts)} row counts x {len(Ns)} row sizes x {ROW + 1} candidates")
+        return 0
     if check:
         table = read_inc(argv[1], prefix)
         times = read_sweeps(argv[2:])

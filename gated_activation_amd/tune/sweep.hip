@@ -12,6 +12,11 @@
 //
 // GA_SWEEP_PATH=2 sweeps the unaligned path instead (vectors per lane 1..8):
 // the input view starts one element past a 16-byte boundary.
+// GA_SWEEP_PATH=split sweeps few-row shapes for the split path: every row
+// geometry as above (splits = 1) and every split plan (chunks of waves 1..16
+// times vectors per lane 1, 2, 4; splits = the chunks a row needs, 2..16),
+// with a zero-filled workspace, each timed by replaying a graph of 64 launches
+// (the calls are a few microseconds); an eighth column holds the splits.
 //
 // gated_activation_amd/tune/make_table.py turns one or more such files into
 // the planner's table (csrc/planner_table.inc).
@@ -50,6 +55,23 @@ __global__ void fill_bf16(uint16_t *p, size_t n, uint32_t seed) {
     }
 }
 
+// Per-call time from a graph of 64 launches replayed 8 times.
+static float time_graph(hipGraphExec_t exec) {
+    hipEvent_t a, b;
+    CK(hipEventCreate(&a));
+    CK(hipEventCreate(&b));
+    CK(hipGraphLaunch(exec, nullptr));
+    CK(hipEventRecord(a, nullptr));
+    for (int i = 0; i < 8; ++i) CK(hipGraphLaunch(exec, nullptr));
+    CK(hipEventRecord(b, nullptr));
+    CK(hipEventSynchronize(b));
+    float ms = 0.0f;
+    CK(hipEventElapsedTime(&ms, a, b));
+    CK(hipEventDestroy(a));
+    CK(hipEventDestroy(b));
+    return ms * 1000.0f / (8.0f * 64.0f);
+}
+
 static float time_pass(int sets, int iters, const std::function<void(int)> &launch) {
     hipEvent_t a, b;
     CK(hipEventCreate(&a));
@@ -75,12 +97,23 @@ int main(int argc, char **argv) {
         return 2;
     }
     const char *path_env = std::getenv("GA_SWEEP_PATH");
-    const int path = path_env && std::atoi(path_env) == 2 ? 2 : 0;
+    const bool split_mode = path_env && std::strcmp(path_env, "split") == 0;
+    const int path = path_env && std::strcmp(path_env, "2") == 0 ? 2 : 0;
     const size_t shift = path == 2 ? 2 : 0;  // bytes: one bf16 element
     const char *gb = std::getenv("GA_SWEEP_POOL_GB");
     const size_t pool_bytes = (size_t)(gb ? std::atof(gb) : 16.0) * ((size_t)1 << 30);
     uint16_t *pool = nullptr;
     CK(hipMalloc(&pool, pool_bytes));
+    // Split plans: one zero-filled workspace for the largest T (the kernels
+    // keep it consistent across calls).
+    int tmax = 1;
+    for (int T : Ts) tmax = std::max(tmax, T);
+    const size_t ws_bytes = split_mode ? ga_gelu_and_mul_sparse_workspace_bytes(tmax) : 0;
+    void *ws = nullptr;
+    if (split_mode) {
+        CK(hipMalloc(&ws, ws_bytes));
+        CK(hipMemset(ws, 0, ws_bytes));
+    }
     fill_bf16<<<8192, 256>>>(pool, pool_bytes / 2, 99u);
     CK(hipDeviceSynchronize());
     // Clocks up before the first measurement.
@@ -127,27 +160,67 @@ int main(int argc, char **argv) {
                             plans.push_back(p);
                     }
                 }
+            if (split_mode) {
+                for (int w : {1, 2, 4, 8, 16})
+                    for (int v : {1, 2, 4}) {
+                        const int chunk = w * 64 * v;
+                        const int splits = (nvec + chunk - 1) / chunk;
+                        if (splits < 2 || splits > 16) continue;
+                        ga_plan p;
+                        std::memset(&p, 0, sizeof p);
+                        p.path = 0;
+                        p.waves_per_row = w;
+                        p.per_lane = v;
+                        p.splits = splits;
+                        p.spin_limit = 1u << 16;
+                        p.block = w * 64;
+                        p.grid = (int64_t)T * splits;
+                        if (ga_gelu_and_mul_sparse_with_plan(vin[0], vout[0], 0, d, GA_BF16, 1.6448536f, nullptr, &p,
+                                                             ws, ws_bytes, nullptr) == GA_OK)
+                            plans.push_back(p);
+                    }
+            }
+            auto call = [&](const ga_plan &p, int s, hipStream_t st) {
+                ga_gelu_and_mul_sparse_with_plan(vin[s], vout[s], T, d, GA_BF16, 1.6448536f, nullptr, &p, ws,
+                                                 ws_bytes, st);
+            };
             std::vector<float> best(plans.size(), 1e30f);
             for (size_t i = 0; i < plans.size(); ++i)
-                for (int k = 0; k < 3; ++k)
-                    ga_gelu_and_mul_sparse_with_plan(vin[k % sets], vout[k % sets], T, d, GA_BF16, 1.6448536f,
-                                                     nullptr, &plans[i], nullptr, 0, nullptr);
+                for (int k = 0; k < 3; ++k) call(plans[i], k % sets, nullptr);
             CK(hipDeviceSynchronize());
-            for (int pass = 0; pass < 3; ++pass)
+            if (split_mode) {
+                // one graph of 64 launches per plan, replayed in 3 interleaved passes
+                std::vector<hipGraphExec_t> execs(plans.size());
+                hipStream_t st;
+                CK(hipStreamCreate(&st));
                 for (size_t i = 0; i < plans.size(); ++i) {
-                    const ga_plan &p = plans[i];
-                    best[i] = std::min(best[i], time_pass(sets, iters, [&](int s) {
-                        ga_gelu_and_mul_sparse_with_plan(vin[s], vout[s], T, d, GA_BF16, 1.6448536f, nullptr, &p,
-                                                         nullptr, 0, nullptr);
-                    }));
+                    hipGraph_t g;
+                    CK(hipStreamBeginCapture(st, hipStreamCaptureModeGlobal));
+                    for (int k = 0; k < 64; ++k) call(plans[i], k % sets, st);
+                    CK(hipStreamEndCapture(st, &g));
+                    CK(hipGraphInstantiate(&execs[i], g, nullptr, nullptr, 0));
+                    CK(hipGraphDestroy(g));
                 }
+                CK(hipStreamDestroy(st));
+                for (int pass = 0; pass < 3; ++pass)
+                    for (size_t i = 0; i < plans.size(); ++i) best[i] = std::min(best[i], time_graph(execs[i]));
+                for (hipGraphExec_t e : execs) CK(hipGraphExecDestroy(e));
+            } else {
+                for (int pass = 0; pass < 3; ++pass)
+                    for (size_t i = 0; i < plans.size(); ++i)
+                        best[i] = std::min(best[i], time_pass(sets, iters, [&](int s) { call(plans[i], s, nullptr); }));
+            }
             CK(hipGetLastError());
-            for (size_t i = 0; i < plans.size(); ++i)
-                std::printf("%d,%d,%d,%d,%d,%d,%.3f\n", T, d, nvec, plans[i].waves_per_row, plans[i].per_lane,
+            for (size_t i = 0; i < plans.size(); ++i) {
+                std::printf("%d,%d,%d,%d,%d,%d,%.3f", T, d, nvec, plans[i].waves_per_row, plans[i].per_lane,
                             plans[i].up_late, best[i]);
+                if (split_mode) std::printf(",%d", plans[i].splits);
+                std::printf("\n");
+            }
             std::fflush(stdout);
         }
     }
+    if (ws) CK(hipFree(ws));
     CK(hipFree(pool));
     std::printf("done\n");
     return 0;

@@ -115,8 +115,8 @@ def test_gelu_planner_known_shapes():
     # (T, d) -> (path, waves per workgroup, vectors per lane, up loaded late, splits)
     want = {(2048, 16384): (0, 8, 4, 1, 1), (2048, 32768): (0, 16, 4, 1, 1), (4096, 65536): (0, 16, 8, 1, 1),
             # few long rows split over workgroups (with a workspace)
-            (1, 32768): (0, 8, 1, 0, 8), (64, 16384): (0, 8, 1, 0, 4), (64, 32768): (0, 8, 2, 0, 4),
-            (128, 32768): (0, 8, 4, 0, 2), (64, 65536): (0, 8, 4, 0, 4)}
+            (1, 32768): (0, 4, 2, 0, 8), (64, 16384): (0, 4, 2, 0, 4), (64, 32768): (0, 8, 2, 0, 4),
+            (128, 32768): (0, 8, 2, 0, 4), (64, 65536): (0, 8, 4, 0, 4)}
     for (T, d), w in want.items():
         p = ga.plan_gelu_and_mul_sparse(T, d, BF16)
         assert (p.path, p.waves_per_row, p.per_lane, p.up_late, p.splits) == w, (T, d, p.as_dict())
@@ -167,6 +167,39 @@ def test_row_geometry_follows_the_measured_table():
                 if got != want:
                     sc = mt.scores(una, T, nv)
                     assert abs(sc[mt.GEOS.index(got)] - sc[mt.GEOS.index(want)]) < 1e-9, (T, d, got, want)
+
+
+def test_split_choice_follows_the_measured_table():
+    """Few long rows with a workspace: whether and how the planner splits rows
+    is the split table's choice under the interpolation rule, checked against
+    the independent Python statement in tune/make_table.py on and off the
+    grid; outside the table (more rows, shorter rows) nothing is split."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "make_table", os.path.join(ROOT, "gated_activation_amd", "tune", "make_table.py"))
+    mt = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mt)
+    table = mt.read_inc(os.path.join(ROOT, "gated_activation_amd", "csrc", "planner_table_split.inc"), "kSplit")
+    Ts = sorted(set(table[0]) | {3, 5, 12, 40, 72, 100, 112, 200, 224})
+    Ns = sorted(set(table[1]) | {2049, 2200, 2816, 3328, 4608, 5632, 7680, 8191})
+    for T in Ts:
+        for n in Ns:
+            p = ga.plan_gelu_and_mul_sparse(T, n * 8, BF16, with_workspace=True)
+            want = mt.choose_split(table, T, n)
+            if want is None:
+                assert p.splits == 1, (T, n, p.as_dict())
+                continue
+            got = (p.waves_per_row, p.per_lane, p.splits)
+            if got != want:
+                sc = mt.scores(table, T, n, [c for c in range(mt.ROW + 1) if mt.split_valid(c, n)])
+                gi = mt.ROW if p.splits == 1 else mt.SPLIT_CHUNKS.index(got[:2])
+                wi = mt.SPLIT_CHUNKS.index(want[:2])
+                assert sc[gi] is not None and abs(sc[gi] - sc[wi]) < 1e-9, (T, n, got, want)
+            assert p.up_late == 0 and p.grid == T * p.splits
+            chunk = p.waves_per_row * 64 * p.per_lane
+            assert chunk * p.splits >= n > chunk * (p.splits - 1)
+    for T, n in ((257, 8192), (4096, 8192), (8, 2047), (1, 1024)):
+        assert ga.plan_gelu_and_mul_sparse(T, n * 8, BF16, with_workspace=True).splits == 1
 
 
 def test_planner_paths_by_row_size():

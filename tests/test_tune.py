@@ -58,3 +58,30 @@ def test_table_builder_round_trip(tmp_path):
             assert w * 64 * v >= n
     # a geometry not run at a point is marked, not guessed
     assert table[2][(100, 128)][mt.GEOS.index((16, 8, 0))] == mt.NOT_RUN
+
+
+def test_split_table_builder_round_trip(tmp_path):
+    mt = _make_table()
+    # Two row sizes x two row counts: at three points a chunk geometry wins,
+    # at one the row path (no split) does.
+    win = {(1, 4096): (8, 1), (1, 8192): (8, 2), (64, 4096): (4, 2), (64, 8192): None}
+    lines = []
+    for (T, n), g in win.items():
+        for w, v in mt.SPLIT_CHUNKS:
+            splits = -(-n // (w * 64 * v))
+            if 2 <= splits <= 16:
+                us = 5.0 if g == (w, v) else 6.0
+                lines.append(f"{T},{n * 8},{n},{w},{v},0,{us},{splits}")
+        lines.append(f"{T},{n * 8},{n},16,4,1,{5.0 if g is None else 7.0},1")
+        lines.append(f"{T},{n * 8},{n},8,8,0,{9.0},1")
+    csv = tmp_path / "split.csv"
+    csv.write_text("\n".join(lines) + "\ndone\n")
+    inc = tmp_path / "split.inc"
+    mt.main(["make_table.py", "--split", str(inc), str(csv)])
+    table = mt.read_inc(str(inc), "kSplit")
+    for (T, n), g in win.items():
+        c = mt.choose_split(table, T, n)
+        if g is None:
+            assert c is None
+        else:
+            assert c == (g[0], g[1], -(-n // (g[0] * 64 * g[1])))
