@@ -19,10 +19,10 @@ bool act_available(int op, int path, int dtype, int per_lane);
 constexpr int SILU_BLOCK = 256;
 
 // Split-row gelu workspace: one record per row, the same layout for every T
-// and split count: a 16-byte header (uint32 arrival counter, padding) and
-// SPLIT_MAX 8-byte partials (fp32 mean, fp32 M2).
+// and split count: SPLIT_MAX 16-byte slots of two 64-bit words,
+// {uint32 tag, fp32 mean} and {uint32 tag, fp32 M2}.
 constexpr int SPLIT_MAX = 16;
-constexpr size_t SPLIT_RECORD_BYTES = 16 + SPLIT_MAX * 8;
+constexpr size_t SPLIT_RECORD_BYTES = SPLIT_MAX * 16;
 inline size_t split_workspace_bytes(int64_t T) { return (size_t)T * SPLIT_RECORD_BYTES; }
 bool gelu_split_available(int dtype, int waves, int vec_per_lane, int splits);
 hipError_t launch_gelu_split(int dtype, int waves, int vec_per_lane, int splits, const void *in, void *out,

@@ -4,28 +4,38 @@
 // Same op as gelu_sparse.hip (vLLM PR 48498, "[Performance] Add Triton kernel
 // for Gemma3n sparse GELU", section Purpose).  Workgroup (s, r) of the grid
 // (splits, T) owns vectors [s*CHUNK, (s+1)*CHUNK) of row r:
-//   1. load its gate chunk (and, early mode, its up chunk) into registers;
+//   1. read the tag in its own slot of the row's record (the previous call's)
+//      while loading its gate chunk (and, early mode, its up chunk) into
+//      registers; this call's tag is 16 more;
 //   2. reduce the chunk's mean m_s and M2_s = sum (g - m_s)^2 (two passes over
 //      the registers);
-//   3. publish (m_s, M2_s) in the workspace and add this workgroup's share of
-//      16 to the row's arrival counter;
-//   4. poll the counter until this call's 16 have arrived, then combine the
-//      partials of s = 0..splits-1 in that order with Chan's parallel-variance
-//      formula, so every workgroup of the row derives the same mean, M2 and
-//      cutoff;
+//   3. publish (m_s, M2_s) as two tagged 64-bit words, {tag, m_s} and
+//      {tag, M2_s}, in its slot;
+//   4. read the row's other slots, one lane per slot, all at once, until each
+//      holds this call's tag, then combine the partials of s = 0..splits-1 in
+//      that order with Chan's parallel-variance formula, so every workgroup
+//      of the row derives the same mean, M2 and cutoff;
 //   5. apply to its chunk and store.
-// The partials and the counter are only ever touched by device-scope atomic
-// operations, which are coherent across the XCDs without cache maintenance;
-// the partial's store is waited for (vmcnt) before the counter add that
-// announces it.  Release/acquire fences would instead write back and
-// invalidate the whole L2 of every participating workgroup, which measured
-// several microseconds per call.
-// The counter only ever grows by 16 per row per call, so a call finds it at
-// a multiple of 16 and waits for the next one: the workspace is zero-filled
-// once and then serves any sequence of calls and graph replays.  The poll is
-// bounded (spin_limit polls); a workgroup that gives up computes the whole
-// row's statistics from global memory itself, so the kernel always finishes
-// and stays correct even if the row's workgroups are not co-resident.
+// A tagged word carries its own proof of arrival, so a poll that succeeds
+// has also read the data: once the row's workgroups have all published, the
+// exchange costs one round of parallel loads, with no wait on a store, no
+// read-modify-write and no second read.  The words are only ever touched by
+// device-scope atomic loads and stores, which are coherent across the XCDs
+// without cache maintenance (release/acquire fences would instead write back
+// and invalidate the whole L2 of every participating workgroup, which
+// measured several microseconds per call).
+// Tags: a call writes its tag into all SPLIT_MAX slots of each row it
+// processes (slots no workgroup owns at this split count get a zero
+// payload), and within a call only workgroup s writes the slots
+// l = s mod splits.  So when a call starts, every slot of the row holds the
+// previous call's tag, each workgroup derives the same new tag from its own
+// slot, and no slot holds the new tag before its owner writes it (tags step
+// by 16 mod 2^32, so a slot never repeats the tag of the call before).  The
+// workspace is zero-filled once and then serves any sequence of calls, split
+// counts and graph replays.  The poll is bounded (spin_limit rounds); a
+// workgroup that gives up computes the whole row's statistics from global
+// memory itself, so the kernel always finishes and stays correct even if the
+// row's workgroups are not co-resident.
 #include "ga_device.h"
 #include "ga_internal.h"
 
@@ -56,6 +66,7 @@ __global__ __launch_bounds__(WAVES * 64) void gelu_sparse_split_kernel(
     constexpr int CHUNK = NT * VPL;
     constexpr int PER = E::PER16;
     __shared__ float red[4][WAVES];
+    __shared__ float row_stats[2];
     __shared__ int flag;
 
     const int32_t s = (int32_t)blockIdx.x;
@@ -69,6 +80,19 @@ __global__ __launch_bounds__(WAVES * 64) void gelu_sparse_split_kernel(
     const int t = (int)threadIdx.x;
     const int v0 = s * CHUNK;
     const int nhere = nvec - v0 < CHUNK ? nvec - v0 : CHUNK;  // >= 1 (host guarantees)
+
+    // Row r's record: SPLIT_MAX slots of two words, {tag, mean} and
+    // {tag, M2}.  Every call writes all of them with one tag, so the tag in
+    // this workgroup's own slot (which no other workgroup writes) is the
+    // previous call's, and this call's is 16 more.  Lane 0 reads it, at an
+    // address kept per lane by the empty asm so that it stays a vector load.
+    uint64_t *slots = reinterpret_cast<uint64_t *>(workspace + (size_t)r * SPLIT_RECORD_BYTES);
+    uint32_t prev = 0;
+    if (t == 0) {
+        int32_t lane_off = 2 * s;
+        asm volatile("" : "+v"(lane_off));
+        prev = (uint32_t)__hip_atomic_load(slots + lane_off, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 
     uint4 gv[VPL], uv[VPL];
 #pragma unroll
@@ -110,55 +134,73 @@ __global__ __launch_bounds__(WAVES * 64) void gelu_sparse_split_kernel(
     }
     const float m2_here = block_sum<WAVES>(q, red[1]);
 
-    // Publish, then wait for the other workgroups of the row.  Row r's
-    // record: a 16-byte header holding the counter, then SPLIT_MAX partials.
-    uint32_t *counter = reinterpret_cast<uint32_t *>(workspace + (size_t)r * SPLIT_RECORD_BYTES);
-    uint64_t *partials = reinterpret_cast<uint64_t *>(workspace + (size_t)r * SPLIT_RECORD_BYTES + 16);
-    if (t == 0) {
-        const uint64_t packed = (uint64_t)__builtin_bit_cast(uint32_t, m_here) |
-                                ((uint64_t)__builtin_bit_cast(uint32_t, m2_here) << 32);
-        __hip_atomic_store(partials + s, packed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the partial has landed
-        // The row's workgroups add exactly 16 in total (16 / splits each, one
-        // more for the first 16 % splits of them), whatever the split count.
-        const uint32_t inc = 16u / (uint32_t)splits + ((uint32_t)s < 16u % (uint32_t)splits ? 1u : 0u);
-        const uint32_t old = __hip_atomic_fetch_add(counter, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t base = old - (old % 16u);
+    // Publish and gather, in the first wavefront: lane l < SPLIT_MAX writes
+    // slot l when l % splits == s (its own partial at l == s, a zero payload
+    // elsewhere), and lane l < splits gathers slot l.
+    if (t < 64) {
+        const uint32_t tag = (uint32_t)__builtin_amdgcn_readlane(prev, 0) + 16u;
+        if (t < SPLIT_MAX && t % splits == s) {
+            const bool own = t == s;
+            const uint64_t w0 = (uint64_t)tag | ((uint64_t)__builtin_bit_cast(uint32_t, own ? m_here : 0.0f) << 32);
+            const uint64_t w1 = (uint64_t)tag | ((uint64_t)__builtin_bit_cast(uint32_t, own ? m2_here : 0.0f) << 32);
+            __hip_atomic_store(slots + 2 * t, w0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(slots + 2 * t + 1, w1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // Lanes that gather nothing count as arrived; lane s has its own.
+        bool have = t >= splits || t == s;
+        float pm = t == s ? m_here : 0.0f, pq = t == s ? m2_here : 0.0f;
         uint32_t polls = 0;
-        int ok = 0;
+        bool ok;
         while (true) {
-            const uint32_t now = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (now - base >= 16u) {
-                ok = 1;
+            if (!have) {
+                const uint64_t a = __hip_atomic_load(slots + 2 * t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const uint64_t b = __hip_atomic_load(slots + 2 * t + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if ((uint32_t)a == tag && (uint32_t)b == tag) {
+                    have = true;
+                    pm = __builtin_bit_cast(float, (uint32_t)(a >> 32));
+                    pq = __builtin_bit_cast(float, (uint32_t)(b >> 32));
+                }
+            }
+            if (__builtin_amdgcn_ballot_w64(!have) == 0) {
+                ok = true;
                 break;
             }
-            if (++polls > spin_limit) break;
+            if (++polls > spin_limit) {
+                ok = false;
+                break;
+            }
             __builtin_amdgcn_s_sleep(1);
         }
-        flag = ok;
+        if (ok) {
+            // Every lane combines the same scalars in slot order.
+            float n_acc = 0.0f, mean = 0.0f, m2 = 0.0f;
+            for (int i = 0; i < splits; ++i) {
+                const float im = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pm), i));
+                const float iq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pq), i));
+                const int pv0 = i * CHUNK;
+                const float pn = (float)((nvec - pv0 < CHUNK ? nvec - pv0 : CHUNK) * PER);
+                if (i == 0) {
+                    n_acc = pn;
+                    mean = im;
+                    m2 = iq;
+                } else {
+                    chan_combine(n_acc, mean, m2, pn, im, iq);
+                }
+            }
+            if (t == 0) {
+                row_stats[0] = mean;
+                row_stats[1] = m2;
+            }
+        }
+        if (t == 0) flag = ok ? 1 : 0;
     }
     __syncthreads();
     const bool ok = flag != 0;
 
     float mean, m2;
     if (ok) {
-        float n_acc = 0.0f;
-        mean = 0.0f;
-        m2 = 0.0f;
-        for (int i = 0; i < splits; ++i) {
-            const uint64_t raw = __hip_atomic_load(partials + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const float pm = __builtin_bit_cast(float, (uint32_t)raw);
-            const float pq = __builtin_bit_cast(float, (uint32_t)(raw >> 32));
-            const int pv0 = i * CHUNK;
-            const float pn = (float)((nvec - pv0 < CHUNK ? nvec - pv0 : CHUNK) * PER);
-            if (i == 0) {
-                n_acc = pn;
-                mean = pm;
-                m2 = pq;
-            } else {
-                chan_combine(n_acc, mean, m2, pn, pm, pq);
-            }
-        }
+        mean = row_stats[0];
+        m2 = row_stats[1];
     } else {
         // Bounded wait expired: the whole row's statistics from global
         // memory, two passes, by this workgroup alone.

@@ -91,7 +91,7 @@ typedef struct {
     int32_t splits;        /* gelu vector path: workgroups sharing one row; 1, or 2, 4, 8,
                               16 (needs a workspace, see ga_gelu_and_mul_sparse_ws) */
     int64_t grid;          /* workgroups launched (silu: from the capacity M only) */
-    uint32_t spin_limit;   /* split rows: polls of a row's arrival counter before a
+    uint32_t spin_limit;   /* split rows: rounds of polls of the row's partials before a
                               workgroup computes the whole row's statistics itself */
     int32_t flags;         /* gelu_and_mul_sparse: 0 or GA_ROUND_INTERMEDIATES (not
                               with split rows); silu: zero */
@@ -156,8 +156,9 @@ ga_status ga_silu_and_mul_bounded(const void *in, void *out, int64_t M, int64_t 
  *   workspace        device memory of at least
  *                    ga_gelu_and_mul_sparse_workspace_bytes(T) bytes, 256-byte
  *                    aligned, zero-filled before its first use; the kernels keep
- *                    it valid for every later call (its counters only grow), so
- *                    it is zeroed once, not per call, and survives graph replay.
+ *                    it valid for every later call (each call tags its partials
+ *                    with the previous call's tag plus 16), so it is zeroed
+ *                    once, not per call, and survives graph replay.
  *   Calls that share a workspace must not run concurrently (the same stream
  *   serialises them).  A row's workgroups wait for each other for a bounded
  *   number of polls; past it a workgroup computes the row's statistics on

@@ -233,14 +233,14 @@ def test_planner_paths_by_row_size():
 
 def test_workspace_size_and_split_plan_checks():
     assert L.ga_gelu_and_mul_sparse_workspace_bytes(0) == 0
-    assert L.ga_gelu_and_mul_sparse_workspace_bytes(1) == 144
-    assert L.ga_gelu_and_mul_sparse_workspace_bytes(64) == 64 * 144
+    assert L.ga_gelu_and_mul_sparse_workspace_bytes(1) == 256
+    assert L.ga_gelu_and_mul_sparse_workspace_bytes(64) == 64 * 256
     split = ga.plan_gelu_and_mul_sparse(8, 16384, BF16)
     assert split.splits == 4
     call = lambda p, T=8, ws=WS, nb=WS_BYTES, d=16384: L.ga_gelu_and_mul_sparse_with_plan(  # noqa: E731
         IN, OUT, T, d, BF16, Z, None, ctypes.byref(p), ws, nb, None)
     assert call(split, ws=None) == EINVAL                                # needs a workspace
-    assert call(split, nb=8 * 144 - 1) == EINVAL                          # too small
+    assert call(split, nb=8 * 256 - 1) == EINVAL                          # too small
     assert call(split, ws=ctypes.c_void_p(0x7F3000000010)) == EINVAL     # not 256-byte aligned
     assert call(split, T=0) == OK
     bad = ga.Plan(path=0, waves_per_row=8, per_lane=1, block=512, splits=5)   # 5 x 512 > 2048 + 512

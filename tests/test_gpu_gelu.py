@@ -460,11 +460,13 @@ def test_split_rows_forced_fallback():
 
 def test_split_workspace_reused_across_shapes():
     """One workspace serves calls of different T and split counts in any
-    order (each call adds exactly 16 to a row's counter)."""
+    order (each call tags all of a row's slots with the previous call's tag
+    plus 16)."""
     ws = torch.zeros(ga.lib.ga_gelu_and_mul_sparse_workspace_bytes(128), dtype=torch.uint8, device="cuda")
     o = oracle.get()
-    for T, d, S in ((8, 16384, 4), (2, 8800, 3), (128, 32768, 2), (8, 12800, 7), (64, 16384, 16),
-                    (1, 32768, 8), (3, 8800, 9)):
+    shapes = ((8, 16384, 4), (2, 8800, 3), (128, 32768, 2), (8, 12800, 7), (64, 16384, 16),
+              (1, 32768, 8), (3, 8800, 9))
+    for T, d, S in shapes:
         xb = synth.gelu_iid(T, d, seed=T * 7 + S, gate_std=1.3)
         nvec = d // 8
         plan = next(p for p in _tiling_plans(nvec) if p.splits == S)
@@ -472,8 +474,15 @@ def test_split_workspace_reused_across_shapes():
         torch.cuda.synchronize()
         ref, st = o.gelu_and_mul_sparse(xb, BF16, Z95, want_stats=True)
         compare(bits_of(out, BF16), ref, BF16, gate=decode(xb[:, :d], BF16), stats=st, label=f"reuse T{T} S{S}")
-    counters = ws.view(torch.int32).cpu().numpy()[::36][:128]
-    assert np.all(counters % 16 == 0) and counters.max() > 0
+    # Each row's record: 16 slots of two 64-bit words {tag, value}.  After any
+    # sequence of calls all 32 tags of a row are equal (the tag of the row's
+    # last call, a multiple of 16; 0 for rows never processed).
+    tags = ws.view(torch.int32).cpu().numpy().reshape(128, 32, 2)[:, :, 0]
+    assert np.all(tags == tags[:, :1])
+    # Row r was processed by every call with T > r, each adding 16.
+    calls = np.array([T for T, _, _ in shapes])
+    want = 16 * (calls[None, :] > np.arange(128)[:, None]).sum(axis=1)
+    assert np.array_equal(tags[:, 0], want), (tags[:, 0], want)
 
 
 @pytest.mark.parametrize("live", [0, 3, 8, 20])
