@@ -2,6 +2,11 @@
 
     python make_table.py [--prefix kUna | --split] OUT.inc SWEEP.csv [SWEEP.csv ...]
     python make_table.py --check [--prefix kUna | --split] TABLE.inc OFFGRID.csv
+    python make_table.py --packed PACKED.csv [PACKED.csv ...]
+
+--packed checks the short-row planner (a rule, no table) against sweeps run
+with GA_SWEEP_PATH=packed: for every shape, the library's own choice (from
+ga_plan_gelu_and_mul_sparse, host-only) against the fastest measured plan.
 
 The prefix names the table's symbols: kPlan (default) for the vector path,
 kUna for the unaligned path (sweeps run with GA_SWEEP_PATH=2; its kernel also
@@ -26,6 +31,7 @@ independently of the C code so that a test can compare the two.
 """
 import collections
 import math
+import os
 import re
 import sys
 
@@ -218,8 +224,53 @@ def choose(table, T, nvec):
     return None if best is None else GEOS[best]
 
 
+def read_packed_sweeps(paths):
+    """(T, nvec) -> {plan name: mean time}; packed plans are ('packed', lanes
+    per row, vectors per lane), the row plan ('row', up_late)."""
+    acc = collections.defaultdict(list)
+    for path in paths:
+        for line in open(path):
+            if not line[:1].isdigit():
+                continue
+            f = line.strip().split(",")
+            T, nvec, v, late, us, g = int(f[0]), int(f[2]), int(f[4]), int(f[5]), float(f[6]), int(f[7])
+            acc[(T, nvec, ("packed", g, v) if g else ("row", late))].append(us)
+    times = collections.defaultdict(dict)
+    for (T, nvec, key), ts in acc.items():
+        times[(T, nvec)][key] = sum(ts) / len(ts)
+    return times
+
+
+def plan_name(key):
+    return "G%d V%d" % key[1:] if key[0] == "packed" else "row W1 V1%s" % (" late" if key[1] else "")
+
+
+def check_packed(paths):
+    # The repository root (this file is gated_activation_amd/tune/make_table.py).
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__)))))
+    import gated_activation_amd as ga
+    times = read_packed_sweeps(paths)
+    ratios = []
+    for (T, n), g in sorted(times.items()):
+        p = ga.plan_gelu_and_mul_sparse(T, 8 * n, ga.GA_BF16, aligned=True, with_workspace=False)
+        key = ("packed", p.lanes_per_row, p.per_lane)
+        best = min(g, key=g.get)
+        r = g[key] / g[best] if key in g else float("nan")
+        ratios.append(r)
+        print(f"T={T:7d} nvec={n:3d} planner {plan_name(key):9s} {g.get(key, float('nan')):7.2f} us: {r:.3f} of the"
+              f" best ({plan_name(best)}, {g[best]:.2f} us)")
+    ok = sorted(x for x in ratios if x == x)
+    print(f"{len(ok)} shapes: median {ok[len(ok) // 2]:.4f}, mean {sum(ok) / len(ok):.4f}, "
+          f"90th percentile {ok[int(0.9 * len(ok))]:.4f}, worst {ok[-1]:.4f}, "
+          f"> 3 % slower: {sum(x > 1.03 for x in ok)}, not measured: {len(ratios) - len(ok)}")
+    return 0
+
+
 def main(argv):
     argv = list(argv)
+    if "--packed" in argv:
+        argv.remove("--packed")
+        return check_packed(argv[1:])
     check = "--check" in argv
     if check:
         argv.remove("--check")

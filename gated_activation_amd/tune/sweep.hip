@@ -17,6 +17,10 @@
 // times vectors per lane 1, 2, 4; splits = the chunks a row needs, 2..16),
 // with a zero-filled workspace, each timed by replaying a graph of 64 launches
 // (the calls are a few microseconds); an eighth column holds the splits.
+// GA_SWEEP_PATH=packed sweeps short rows (nvec <= 32): every packed-rows
+// geometry (lanes per row 4..32 times vectors per lane 1, 2, 4, covering the
+// row without a spare half) and the one-wave row geometry, timed by graph
+// replay; an eighth column holds the lanes per row (0 for the row geometry).
 //
 // gated_activation_amd/tune/make_table.py turns one or more such files into
 // the planner's table (csrc/planner_table.inc).
@@ -98,6 +102,7 @@ int main(int argc, char **argv) {
     }
     const char *path_env = std::getenv("GA_SWEEP_PATH");
     const bool split_mode = path_env && std::strcmp(path_env, "split") == 0;
+    const bool packed_mode = path_env && std::strcmp(path_env, "packed") == 0;
     const int path = path_env && std::strcmp(path_env, "2") == 0 ? 2 : 0;
     const size_t shift = path == 2 ? 2 : 0;  // bytes: one bf16 element
     const char *gb = std::getenv("GA_SWEEP_POOL_GB");
@@ -139,11 +144,27 @@ int main(int argc, char **argv) {
             const double bytes = (double)(in_b + out_b);
             const int iters = std::max(30, std::min(800, (int)(1.5e5 / (bytes / 5e3 + 3.0))));
             std::vector<ga_plan> plans;
+            if (packed_mode) {
+                for (int g : {4, 8, 16, 32})
+                    for (int v : {1, 2, 4}) {
+                        if (g * v < nvec || (v > 1 && g * (v / 2) >= nvec)) continue;
+                        ga_plan p;
+                        std::memset(&p, 0, sizeof p);
+                        p.path = 3;
+                        p.lanes_per_row = g;
+                        p.per_lane = v;
+                        p.splits = 1;
+                        if (ga_gelu_and_mul_sparse_with_plan(vin[0], vout[0], 0, d, GA_BF16, 1.6448536f, nullptr, &p,
+                                                             nullptr, 0, nullptr) == GA_OK)
+                            plans.push_back(p);
+                    }
+            }
             for (int w : {1, 2, 4, 8, 16})
                 for (int v = 1; v <= 8; ++v) {
                     if (path == 0 && (v & (v - 1)) != 0) continue;
                     const long slots = (long)w * 64 * v;
-                    if (slots < nvec || slots >= 8L * nvec) continue;
+                    if (slots < nvec || (slots >= 8L * nvec && !(packed_mode && w == 1 && v == 1))) continue;
+                    if (packed_mode && (w != 1 || v != 1)) continue;
                     for (int late : {0, 1}) {
                         ga_plan p;
                         std::memset(&p, 0, sizeof p);
@@ -188,7 +209,7 @@ int main(int argc, char **argv) {
             for (size_t i = 0; i < plans.size(); ++i)
                 for (int k = 0; k < 3; ++k) call(plans[i], k % sets, nullptr);
             CK(hipDeviceSynchronize());
-            if (split_mode) {
+            if (split_mode || packed_mode) {
                 // one graph of 64 launches per plan, replayed in 3 interleaved passes
                 std::vector<hipGraphExec_t> execs(plans.size());
                 hipStream_t st;
@@ -215,6 +236,7 @@ int main(int argc, char **argv) {
                 std::printf("%d,%d,%d,%d,%d,%d,%.3f", T, d, nvec, plans[i].waves_per_row, plans[i].per_lane,
                             plans[i].up_late, best[i]);
                 if (split_mode) std::printf(",%d", plans[i].splits);
+                if (packed_mode) std::printf(",%d", plans[i].lanes_per_row);
                 std::printf("\n");
             }
             std::fflush(stdout);

@@ -85,3 +85,29 @@ def test_split_table_builder_round_trip(tmp_path):
             assert c is None
         else:
             assert c == (g[0], g[1], -(-n // (g[0] * 64 * g[1])))
+
+
+def test_packed_check_reads_sweeps_and_asks_the_library(tmp_path, capsys):
+    """The short-row check parses packed-mode sweep lines (eighth column:
+    lanes per row, 0 for the row geometry) and rates the library's own
+    choice (G = 8 lanes, one vector, for a row of 6 vectors; G = 32 for 24)
+    against the fastest line of each shape."""
+    mt = _make_table()
+    csv = tmp_path / "packed.csv"
+    csv.write_text("\n".join([
+        "4096,48,6,0,1,0,2.00,8",      # the planner's G8 V1: the fastest
+        "4096,48,6,0,1,0,2.20,4",      # G4 V2 would not be offered (spare half) but parses
+        "4096,48,6,1,1,0,2.50,0",      # row geometry, up early
+        "4096,192,24,0,1,0,3.15,32",   # the planner's G32 V1
+        "4096,192,24,0,2,0,3.00,16",   # G16 V2: 5 % faster
+        "4096,192,24,1,1,1,3.30,0",    # row geometry, up late
+        "done",
+    ]) + "\n")
+    times = mt.read_packed_sweeps([str(csv)])
+    assert times[(4096, 6)][("packed", 8, 1)] == 2.0
+    assert times[(4096, 24)][("row", 1)] == 3.3
+    assert mt.main(["make_table.py", "--packed", str(csv)]) == 0
+    out = capsys.readouterr().out
+    assert "nvec=  6 planner G8 V1" in out and "1.000 of the best (G8 V1" in out
+    assert "nvec= 24 planner G32 V1" in out and "1.050 of the best (G16 V2" in out
+    assert "2 shapes:" in out and "worst 1.0500" in out
