@@ -163,8 +163,9 @@ int main(int argc, char **argv) {
                 for (int v = 1; v <= 8; ++v) {
                     if (path == 0 && (v & (v - 1)) != 0) continue;
                     const long slots = (long)w * 64 * v;
-                    if (slots < nvec || (slots >= 8L * nvec && !(packed_mode && w == 1 && v == 1))) continue;
-                    if (packed_mode && (w != 1 || v != 1)) continue;
+                    // Packed mode: the one-wave geometry only (the library rejects it
+                    // if it does not cover the row).
+                    if (packed_mode ? (w != 1 || v != 1) : (slots < nvec || slots >= 8L * nvec)) continue;
                     for (int late : {0, 1}) {
                         ga_plan p;
                         std::memset(&p, 0, sizeof p);
