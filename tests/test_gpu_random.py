@@ -80,3 +80,70 @@ def test_random_case(i):
     if n:
         ref, st = oracle.get().gelu_and_mul_sparse(xb[:n], dt, c["z"], want_stats=True)
         compare(got[:n], ref, dt, gate=decode(xb[:n, :d], dt), stats=st, label=label)
+
+
+N_ELEM_CASES = 96
+ELEM_OPS = ("silu", "gelu_tanh", "gelu_erf", "squared_relu")
+
+
+def draw_elementwise(i):
+    rng = np.random.default_rng(104729 * (i + 1))
+    op = ELEM_OPS[rng.integers(len(ELEM_OPS))]
+    dt = (BF16, F16, F32)[rng.integers(3)]
+    d = int(rng.integers(1, 64) if rng.random() < 0.3 else rng.integers(64, 20000))
+    if rng.random() < 0.5:
+        d = max(8, d // 8 * 8)
+    M = max(1, min(int(np.exp(rng.uniform(0.0, np.log(20000.0)))), MAX_ELEMS // d))
+    shifted = rng.random() < 0.3
+    in_shift = int(rng.integers(0, 4)) if shifted else 0
+    out_shift = int(rng.integers(0, 4)) if shifted else 0
+    live = int(rng.integers(-2, M + 3)) if (op in ("silu", "squared_relu") or rng.random() < 0.5) else None
+    gate_std = float(np.exp(rng.uniform(np.log(0.1), np.log(10.0))))
+    return dict(op=op, dt=dt, d=d, M=M, in_shift=in_shift, out_shift=out_shift, live=live, gate_std=gate_std,
+                seed=5000 + i)
+
+
+@pytest.mark.parametrize("i", range(N_ELEM_CASES))
+def test_random_elementwise_case(i):
+    """silu_and_mul_bounded, gelu_and_mul (tanh and erf) and squared ReLU on
+    random shapes, types, shifted views and live counts (negative and past the
+    capacity included), planned by the library, against the oracle."""
+    c = draw_elementwise(i)
+    op, dt, d, M = c["op"], c["dt"], c["d"], c["M"]
+    label = "random elementwise %d: %s" % (i, {k: (round(v, 4) if isinstance(v, float) else v)
+                                               for k, v in c.items()})
+    print(label, flush=True)
+    gated = op != "squared_relu"
+    xb = synth.gelu_iid(M, d, seed=c["seed"], dtype=dt, gate_std=c["gate_std"])
+    if not gated:
+        xb = np.ascontiguousarray(xb[:, :d])
+    width = xb.shape[1]
+    tdt = TORCH_DTYPE[dt]
+    flat = torch.full((M * width + 16,), float("nan"), dtype=tdt, device="cuda")
+    x = flat[c["in_shift"]: c["in_shift"] + M * width].view(M, width)
+    x.copy_(to_device(xb, dt))
+    buf, _ = sentinel_buffer(M * d + 16, 1, dt)
+    out = buf[c["out_shift"]: c["out_shift"] + M * d].view(tdt).view(M, d)
+    live_t = None if c["live"] is None else torch.tensor([c["live"]], dtype=torch.int32, device="cuda")
+    o = oracle.get()
+    n = M if c["live"] is None else max(0, min(c["live"], M))
+    if op == "silu":
+        ga.silu_and_mul_bounded(x, live_t, out=out)
+        ref = o.silu_and_mul_bounded(xb, dt, n)
+    elif op == "squared_relu":
+        ga.squared_relu_bounded(x, live_t, out=out)
+        ref = o.squared_relu_bounded(xb, dt, n)
+    else:
+        approx = op == "gelu_tanh"
+        ga.gelu_and_mul(x, "tanh" if approx else "none", out=out, live_rows=live_t)
+        ref = o.gelu_and_mul(xb, dt, approx, live=n)
+    torch.cuda.synchronize()
+
+    everything = bits_of(buf, dt)
+    o0 = c["out_shift"]
+    outside = np.concatenate([everything[:o0], everything[o0 + M * d:]])
+    assert np.all(outside == synth.SENTINEL[dt]), f"{label}: wrote outside the output view"
+    got = everything[o0: o0 + M * d].reshape(M, d)
+    assert np.all(got[n:] == synth.SENTINEL[dt]), f"{label}: rows beyond the live count were written"
+    if n:
+        compare(got[:n], ref[:n], dt, label=label)
