@@ -173,3 +173,20 @@ def test_round_trip_differs_from_default_as_the_pages_describe():
     torch.cuda.synchronize()
     diff = (bits_of(a, BF16) != bits_of(b, BF16)).mean()
     assert 0.0 < diff < 0.5
+
+
+@pytest.mark.parametrize("i", range(64))
+def test_random_cases(i):
+    """Seeded random shapes, types, z, gate scales and live counts through the
+    planner's own choice, against the round-trip oracle as above."""
+    rng = np.random.default_rng(15485863 * (i + 1))
+    dt = (BF16, F16, F32)[rng.integers(3)]
+    d = int(rng.integers(1, 300) if rng.random() < 0.3 else rng.integers(300, 20000))
+    if rng.random() < 0.5:
+        d = max(8, d // 8 * 8)
+    T = max(1, min(int(np.exp(rng.uniform(0.0, np.log(2000.0)))), 500_000 // d))
+    z = float((0.0, Z95, Z99, rng.uniform(-1.0, 3.0))[rng.integers(4)])
+    live = None if rng.random() < 0.6 else int(rng.integers(0, T + 3))
+    gate_std = float(np.exp(rng.uniform(np.log(0.1), np.log(10.0))))
+    xb = synth.gelu_iid(T, d, seed=9000 + i, dtype=dt, gate_std=gate_std)
+    run_rt(xb, dt, z, live=live, label=f"rt random {i}: dt{dt} T{T} d{d} z{z:.4f} live{live} std{gate_std:.3f}")
