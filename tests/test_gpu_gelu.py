@@ -264,14 +264,16 @@ def _packed_plans(d, dt):
                 yield ga.Plan(path=3, lanes_per_row=g, per_lane=v, block=256)
 
 
-@pytest.mark.parametrize("dt", [BF16, F16, F32], ids=["bf16", "f16", "f32"])
-@pytest.mark.parametrize("d", [8, 64, 128, 256])
+# Rows of at most 32 16-byte vectors (fp32: d <= 128) are the packed path's.
+PACKED_CASES = [(d, dt) for dt in (BF16, F16, F32) for d in (8, 64, 128, 256) if d * (4 if dt == F32 else 2) <= 512]
+PACKED_IDS = [f"{d}-{ {BF16: 'bf16', F16: 'f16', F32: 'f32'}[dt]}" for d, dt in PACKED_CASES]
+
+
+@pytest.mark.parametrize("d,dt", PACKED_CASES, ids=PACKED_IDS)
 def test_packed_rows_every_geometry(dt, d):
     """Short aligned rows, several per wavefront: every packed geometry that
     covers the row, with T leaving a ragged last workgroup, matches the
     oracle; so does the planner's choice at a large T."""
-    if dt == F32 and d > 128:
-        pytest.skip("fp32 rows of more than 32 vectors are not packed")
     T = 203
     x = synth.gelu_offset_rows(T, d, seed=500 + d + dt, dtype=dt)
     plans = list(_packed_plans(d, dt))
@@ -297,16 +299,18 @@ def test_packed_rows_edge_and_constant_rows():
             run_and_check(x, dt, z, label=f"packed edge dt{dt} z{z}")
 
 
-@pytest.mark.parametrize("dt", [BF16, F16, F32], ids=["bf16", "f16", "f32"])
-@pytest.mark.parametrize("d", [1, 3, 7, 9, 31, 64, 100, 127, 255, 256])
+PACKED_UNA_CASES = [(d, dt) for dt in (BF16, F16, F32) for d in (1, 3, 7, 9, 31, 64, 100, 127, 255, 256)
+                    if d * (4 if dt == F32 else 2) <= 512]
+PACKED_UNA_IDS = [f"{d}-{ {BF16: 'bf16', F16: 'f16', F32: 'f32'}[dt]}" for d, dt in PACKED_UNA_CASES]
+
+
+@pytest.mark.parametrize("d,dt", PACKED_UNA_CASES, ids=PACKED_UNA_IDS)
 def test_packed_rows_unaligned(dt, d):
     """Short rows off 16-byte alignment (shifted views, odd d) packed several
     per wavefront: every covering geometry, input and output shifts varied
     independently, NaN around the input view.  Rows of 1 and 3 elements read
     their last gate vector element by element near the end of the buffer."""
     es = 4 if dt == F32 else 2
-    if d * es > 512:
-        pytest.skip("more than 32 vectors: not packed")
     per = 16 // es
     T = 203
     xb = synth.gelu_offset_rows(T, d, seed=700 + d + dt, dtype=dt)
