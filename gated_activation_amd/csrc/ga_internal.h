@@ -22,7 +22,8 @@ constexpr int SILU_BLOCK = 256;
 // and split count: SPLIT_MAX 16-byte slots of two 64-bit words,
 // {uint32 tag, fp32 mean} and {uint32 tag, fp32 M2}.
 constexpr int SPLIT_MAX = 16;
-constexpr size_t SPLIT_RECORD_BYTES = SPLIT_MAX * 16;
+constexpr int SPLIT_SLOT_BYTES = 16;  // slot stride: the two words, packed (one slot per cache line measured slower)
+constexpr size_t SPLIT_RECORD_BYTES = (size_t)SPLIT_MAX * SPLIT_SLOT_BYTES;
 inline size_t split_workspace_bytes(int64_t T) { return (size_t)T * SPLIT_RECORD_BYTES; }
 bool gelu_split_available(int dtype, int waves, int vec_per_lane, int splits);
 hipError_t launch_gelu_split(int dtype, int waves, int vec_per_lane, int splits, const void *in, void *out,

@@ -87,9 +87,10 @@ __global__ __launch_bounds__(WAVES * 64) void gelu_sparse_split_kernel(
     // previous call's, and this call's is 16 more.  Lane 0 reads it, at an
     // address kept per lane by the empty asm so that it stays a vector load.
     uint64_t *slots = reinterpret_cast<uint64_t *>(workspace + (size_t)r * SPLIT_RECORD_BYTES);
+    constexpr int SW = SPLIT_SLOT_BYTES / 8;  // 64-bit words from one slot to the next
     uint32_t prev = 0;
     if (t == 0) {
-        int32_t lane_off = 2 * s;
+        int32_t lane_off = SW * s;
         asm volatile("" : "+v"(lane_off));
         prev = (uint32_t)__hip_atomic_load(slots + lane_off, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -143,8 +144,8 @@ __global__ __launch_bounds__(WAVES * 64) void gelu_sparse_split_kernel(
             const bool own = t == s;
             const uint64_t w0 = (uint64_t)tag | ((uint64_t)__builtin_bit_cast(uint32_t, own ? m_here : 0.0f) << 32);
             const uint64_t w1 = (uint64_t)tag | ((uint64_t)__builtin_bit_cast(uint32_t, own ? m2_here : 0.0f) << 32);
-            __hip_atomic_store(slots + 2 * t, w0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(slots + 2 * t + 1, w1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(slots + SW * t, w0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(slots + SW * t + 1, w1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         // Lanes that gather nothing count as arrived; lane s has its own.
         bool have = t >= splits || t == s;
@@ -153,8 +154,8 @@ __global__ __launch_bounds__(WAVES * 64) void gelu_sparse_split_kernel(
         bool ok;
         while (true) {
             if (!have) {
-                const uint64_t a = __hip_atomic_load(slots + 2 * t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const uint64_t b = __hip_atomic_load(slots + 2 * t + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const uint64_t a = __hip_atomic_load(slots + SW * t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const uint64_t b = __hip_atomic_load(slots + SW * t + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if ((uint32_t)a == tag && (uint32_t)b == tag) {
                     have = true;
                     pm = __builtin_bit_cast(float, (uint32_t)(a >> 32));
