@@ -23,7 +23,7 @@ from parity import BF16, F16, F32, TORCH_DTYPE, Z95, Z99, bits_of, compare, deco
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 160
+N_CASES = 400
 MAX_ELEMS = 1_000_000  # T * d per case: the oracle stays within milliseconds
 
 
@@ -82,7 +82,7 @@ def test_random_case(i):
         compare(got[:n], ref, dt, gate=decode(xb[:n, :d], dt), stats=st, label=label)
 
 
-N_ELEM_CASES = 96
+N_ELEM_CASES = 200
 ELEM_OPS = ("silu", "gelu_tanh", "gelu_erf", "squared_relu")
 
 

@@ -175,7 +175,7 @@ def test_round_trip_differs_from_default_as_the_pages_describe():
     assert 0.0 < diff < 0.5
 
 
-@pytest.mark.parametrize("i", range(64))
+@pytest.mark.parametrize("i", range(128))
 def test_random_cases(i):
     """Seeded random shapes, types, z, gate scales and live counts through the
     planner's own choice, against the round-trip oracle as above."""
