@@ -19,4 +19,5 @@ from ._lib import (  # noqa: F401
     gelu_and_mul_sparse, silu_and_mul_bounded, stream_xor_rows,
     gelu_and_mul, squared_relu_bounded, z_from_sparsity,
     plan_gelu_and_mul_sparse, plan_silu_and_mul_bounded, workspace_for,
+    reserve_workspace, held_workspaces, GA_SPLIT_PLAN_ROWS, WORKSPACE_BYTES,
 )

@@ -80,6 +80,10 @@ def _load():
 
 
 lib = _load()
+# Calls of more rows than this are never split over workgroups, so a workspace
+# of WORKSPACE_BYTES serves every call.
+GA_SPLIT_PLAN_ROWS = 256
+WORKSPACE_BYTES = int(lib.ga_gelu_and_mul_sparse_workspace_bytes(GA_SPLIT_PLAN_ROWS))
 
 
 def _check(status):
@@ -119,22 +123,57 @@ def _live_ptr(live_rows, x, name):
     return ctypes.c_void_p(live_rows.data_ptr())
 
 
+# Split-row workspaces: one per (device index, stream handle), of a fixed size
+# that covers every call the planner splits (it splits only calls of at most
+# GA_SPLIT_PLAN_ROWS rows), zero-filled once and then kept for the life of the
+# process.  A workspace is never replaced or released, so a graph captured
+# with one keeps a valid pointer for as long as it can be replayed.  Calls
+# that share a workspace must not overlap in time: calls on one stream are
+# serialised by the stream, and each stream has its own workspace.
 _WORKSPACES = {}
 
 
-def workspace_for(x, T):
-    """The zero-filled split-row workspace for x's device and current stream
-    (allocated once, grown when a call needs more; never created during
-    graph capture, where the call then runs without one)."""
-    need = int(lib.ga_gelu_and_mul_sparse_workspace_bytes(T))
-    key = (x.device.index, torch.cuda.current_stream(x.device).cuda_stream)
+def _workspace_key(device, stream):
+    return (device.index, stream.cuda_stream)
+
+
+def reserve_workspace(device=None, stream=None):
+    """Create the split-row workspace of `stream` (default: the current stream
+    of `device`) now, if it does not exist yet, and return it.  Call this
+    before capturing a graph on a stream that has not run a call yet, so the
+    workspace is allocated (and zeroed) outside the graph; otherwise the first
+    call inside the capture allocates it from the graph's memory pool and
+    records its zero fill into the graph, which then re-zeroes it on every
+    replay."""
+    device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    if device.index is None:
+        device = torch.device("cuda", torch.cuda.current_device())
+    stream = torch.cuda.current_stream(device) if stream is None else stream
+    key = _workspace_key(device, stream)
     ws = _WORKSPACES.get(key)
-    if ws is None or ws.numel() < need:
-        if torch.cuda.is_current_stream_capturing():
-            return None
-        ws = torch.zeros(max(need, 1 << 16), dtype=torch.uint8, device=x.device)
+    if ws is None:
+        with torch.cuda.device(device), torch.cuda.stream(stream):
+            ws = torch.zeros(WORKSPACE_BYTES, dtype=torch.uint8, device=device)
         _WORKSPACES[key] = ws
     return ws
+
+
+def workspace_for(x, T):
+    """The split-row workspace for x's device and current stream, or None when
+    a call of T rows is never split (T > GA_SPLIT_PLAN_ROWS) and the stream
+    has none yet.  Created on first use (see reserve_workspace for graph
+    capture) and kept for the life of the process."""
+    stream = torch.cuda.current_stream(x.device)
+    ws = _WORKSPACES.get(_workspace_key(x.device, stream))
+    if ws is None and 0 < T <= GA_SPLIT_PLAN_ROWS:
+        ws = reserve_workspace(x.device, stream)
+    return ws
+
+
+def held_workspaces():
+    """{(device index, stream handle): data_ptr} of every workspace the
+    binding holds."""
+    return {k: v.data_ptr() for k, v in _WORKSPACES.items()}
 
 
 def gelu_and_mul_sparse(x, z=Z_SPARSITY_095, out=None, live_rows=None, plan=None, workspace=None,
@@ -142,9 +181,10 @@ def gelu_and_mul_sparse(x, z=Z_SPARSITY_095, out=None, live_rows=None, plan=None
     """Sparse GELU-and-multiply of x = [gate | up] ([T, 2d]) -> [T, d].
     z = Phi^-1(target sparsity); live_rows (optional int32 device tensor)
     limits the rows written; plan (optional Plan) forces a launch geometry
-    (its `flags` then select the form).  workspace: None = the cached
-    per-stream workspace (lets few rows split over several workgroups),
-    False = none, or a zero-filled uint8 tensor.  round_intermediates: the
+    (its `flags` then select the form).  workspace: None = the binding's
+    workspace of the current stream (lets few rows split over several
+    workgroups; see reserve_workspace), False = none, or a zero-filled uint8
+    tensor owned by the caller.  round_intermediates: the
     round-trip form, which rounds each intermediate to the input dtype as an
     eager PyTorch composition does (never split, no workspace)."""
     T, d, out = _prep(x, out, "gelu_and_mul_sparse")

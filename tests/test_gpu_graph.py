@@ -135,3 +135,81 @@ def test_graph_replay_packed_unaligned_and_round_trip():
         got_m = bits_of(out_m, BF16)
         compare(got_m[:km], ref_m[:km], BF16, label=f"graph gelu_and_mul step {step}")
         assert np.all(got_m[km:] == synth.SENTINEL[BF16])
+
+
+def test_default_workspace_survives_capture_and_later_calls():
+    """A few-row call captured with the binding's own workspace (no
+    workspace= argument) takes the split path; an eager call of 2048 rows on
+    the same stream afterwards must not replace or free that workspace, so
+    every replay still finds it and matches the oracle (Megatron-LM PR 6328,
+    What changed and why: the buffers a graph captures stay fixed while the
+    per-step data changes)."""
+    Tq, dq, Tb, db = 8, 32768, 2048, 16384
+    o = oracle.get()
+    xq_b = synth.gelu_large(Tq, dq)
+    ref_q, st_q = o.gelu_and_mul_sparse(xq_b, BF16, Z95, want_stats=True)
+    xb_b = synth.gelu_large(Tb, db)
+    assert ga.plan_gelu_and_mul_sparse(Tq, dq, ga.GA_BF16).splits > 1
+    assert ga.plan_gelu_and_mul_sparse(Tb, db, ga.GA_BF16).splits == 1
+    s = torch.cuda.Stream()
+    key = (torch.cuda.current_device(), s.cuda_stream)
+    assert key not in ga.held_workspaces()       # a fresh stream: nothing reserved yet
+    xq, xb = to_device(xq_b, BF16), to_device(xb_b, BF16)
+    _, out_q = sentinel_buffer(Tq, dq, BF16)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        ga.gelu_and_mul_sparse(xq, Z95, out=out_q)
+    torch.cuda.synchronize()
+    # the captured call allocated the stream's workspace (inside the capture)
+    captured_ptr = ga.held_workspaces()[key]
+    # an eager call with many rows on the same stream, then eager few-row calls
+    with torch.cuda.stream(s):
+        out_b = ga.gelu_and_mul_sparse(xb, Z95)
+        ga.gelu_and_mul_sparse(xq, Z95)
+    torch.cuda.synchronize()
+    assert ga.held_workspaces()[key] == captured_ptr
+    ref_b, st_b = o.gelu_and_mul_sparse(xb_b[:64], BF16, Z95, want_stats=True)
+    compare(bits_of(out_b[:64], BF16), ref_b, BF16, gate=decode(xb_b[:64, :db], BF16), stats=st_b,
+            label="eager T2048 beside the graph")
+    gate_q = decode(xq_b[:, :dq], BF16)
+    sentinel = int(synth.SENTINEL[BF16])
+    for step in range(4):
+        out_q.view(torch.int16).fill_(sentinel)
+        with torch.cuda.stream(s):
+            ga.gelu_and_mul_sparse(xq, Z95)      # eager use of the workspace between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        compare(bits_of(out_q, BF16), ref_q, BF16, gate=gate_q, stats=st_q, label=f"captured split, replay {step}")
+    assert ga.held_workspaces()[key] == captured_ptr
+
+
+def test_reserved_workspace_is_the_one_a_capture_uses():
+    """reserve_workspace(stream=s) before capture: the captured few-row call
+    uses that workspace (zeroed outside the graph) and splits its rows."""
+    Tq, dq = 4, 16384
+    o = oracle.get()
+    xq_b = synth.gelu_large(Tq, dq)
+    ref_q, st_q = o.gelu_and_mul_sparse(xq_b, BF16, Z95, want_stats=True)
+    assert ga.plan_gelu_and_mul_sparse(Tq, dq, ga.GA_BF16).splits > 1
+    s = torch.cuda.Stream()
+    ws = ga.reserve_workspace(stream=s)
+    assert ws.numel() == ga.WORKSPACE_BYTES
+    key = (torch.cuda.current_device(), s.cuda_stream)
+    assert ga.held_workspaces()[key] == ws.data_ptr()
+    xq = to_device(xq_b, BF16)
+    _, out_q = sentinel_buffer(Tq, dq, BF16)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        ga.gelu_and_mul_sparse(xq, Z95, out=out_q)
+    torch.cuda.synchronize()
+    assert ga.held_workspaces()[key] == ws.data_ptr()
+    for step in range(3):
+        out_q.view(torch.int16).fill_(int(synth.SENTINEL[BF16]))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        compare(bits_of(out_q, BF16), ref_q, BF16, gate=decode(xq_b[:, :dq], BF16), stats=st_q,
+                label=f"reserved workspace, replay {step}")
