@@ -264,7 +264,8 @@ void pick_unaligned_geometry(int64_t nvec, int64_t T, int *w_out, int *v_out, in
 // for about 256 workgroups: 1.04x, up to 1.26x).  False: do not split.
 bool pick_split(int64_t nvec, int64_t T, int *w_out, int *v_out, int *splits_out) {
     static_assert(kSplitNG == 16, "split table: 15 chunk geometries and the row path");
-    if (T < 1 || T > kSplitT[kSplitNT - 1] || nvec < kSplitN[0] || nvec > kSplitN[kSplitNN - 1]) return false;
+    static_assert(kSplitT[kSplitNT - 1] <= GA_SPLIT_PLAN_ROWS, "the planner splits calls of <= GA_SPLIT_PLAN_ROWS rows");
+    if (T < 1 || T > kSplitT[kSplitNT - 1] || T > GA_SPLIT_PLAN_ROWS || nvec < kSplitN[0] || nvec > kSplitN[kSplitNN - 1]) return false;
     auto chunk_of = [](int c) { return (int64_t)kPlanWaves[c / 3] * 64 * (1 << (c % 3)); };
     const int best = table_argmin(kSplitT, kSplitNT, kSplitN, kSplitNN, &kSplitLoss[0][0][0], kSplitNG, T, nvec,
                                   [&](int c) {
@@ -336,6 +337,28 @@ ga_status check_gelu_plan(const ga_plan *p, int64_t T, int64_t d, int32_t dtype)
     return GA_OK;
 }
 
+// One launch dimension holds fewer than 2^32 work-items (grid * block): the
+// dispatch packet's grid size is a 32-bit count of work-items.
+constexpr int64_t kMaxWorkItems = (int64_t)1 << 32;
+
+// Work-items of a gelu launch with this plan over T rows.
+int64_t gelu_work_items(const ga_plan &p, int64_t T) {
+    if (p.path == 3) {
+        const int64_t rows_per_block = ga::ROWS_BLOCK / p.lanes_per_row;
+        return (T + rows_per_block - 1) / rows_per_block * ga::ROWS_BLOCK;
+    }
+    return T * (int64_t)p.splits * (int64_t)p.waves_per_row * 64;
+}
+
+ga_status check_work_items(const ga_plan &p, int64_t T) {
+    if (gelu_work_items(p, T) >= kMaxWorkItems)
+        return fail(GA_EUNSUPPORTED,
+                    "ga_gelu_and_mul_sparse: %lld rows need %lld work-items in one launch (limit 2^32); "
+                    "split the rows over several calls",
+                    (long long)T, (long long)gelu_work_items(p, T));
+    return GA_OK;
+}
+
 ga_status check_workspace(const ga_plan &p, int64_t T, const void *workspace, size_t workspace_bytes) {
     if (p.path != 0 || p.splits <= 1) return GA_OK;
     if (workspace == nullptr) return fail(GA_EINVAL, "ga_gelu_and_mul_sparse: a split plan needs a workspace");
@@ -351,6 +374,8 @@ ga_status launch_gelu(const void *in, void *out, int64_t T, int64_t d, int32_t d
                       const int32_t *live, const ga_plan &p, void *workspace, ga_stream stream) {
     const char *name = "ga_gelu_and_mul_sparse";
     if ((uintptr_t)live % 4 != 0) return fail(GA_EINVAL, "%s: live_rows is not 4-byte aligned", name);
+    ga_status st = check_work_items(p, T);
+    if (st != GA_OK) return st;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const bool rt = (p.flags & GA_ROUND_INTERMEDIATES) != 0;
     if (p.path == 0) {
@@ -552,6 +577,8 @@ ga_status ga_plan_gelu_and_mul_sparse(int64_t T, int64_t d, int32_t dtype, int32
         p.block = p.waves_per_row * 64;
         p.grid = T * p.splits;
     }
+    const ga_status st = check_work_items(p, T);
+    if (st != GA_OK) return st;
     *plan = p;
     return GA_OK;
 }

@@ -125,7 +125,11 @@ typedef struct {
  *   z         cutoff multiplier Phi^-1(target sparsity); must be finite.
  *   live_rows NULL: all T rows.  Else a device int32; rows r with
  *             r >= clamp(*live_rows, 0, T) are left untouched.
- * Returns GA_OK once the launch is enqueued.
+ * Returns GA_OK once the launch is enqueued.  A launch is one workgroup per
+ * row (rows of up to 32 16-byte vectors: several rows per workgroup); where
+ * its work-items would reach 2^32 (T >= 2^26 / waves per row, e.g. T = 2^26
+ * rows of d = 512 bf16), the call returns GA_EUNSUPPORTED before any HIP call
+ * (split the rows over several calls).
  */
 ga_status ga_gelu_and_mul_sparse(const void *in, void *out, int64_t T, int64_t d,
                                  int32_t dtype, float z, const int32_t *live_rows,
@@ -165,6 +169,10 @@ ga_status ga_silu_and_mul_bounded(const void *in, void *out, int64_t M, int64_t 
  *   its own, so a launch always completes with a correct result.
  */
 size_t ga_gelu_and_mul_sparse_workspace_bytes(int64_t T);
+/* The planner splits rows only in calls of at most this many rows, so a
+ * workspace of ga_gelu_and_mul_sparse_workspace_bytes(GA_SPLIT_PLAN_ROWS)
+ * bytes (64 KiB) lets every call that the planner would split do so. */
+#define GA_SPLIT_PLAN_ROWS 256
 ga_status ga_gelu_and_mul_sparse_ws(const void *in, void *out, int64_t T, int64_t d,
                                     int32_t dtype, float z, const int32_t *live_rows,
                                     void *workspace, size_t workspace_bytes, ga_stream stream);

@@ -126,13 +126,9 @@ def test_gelu_planner_known_shapes():
 def test_row_geometry_follows_the_measured_table():
     """One workgroup per row: the planner's geometry is the one the measured
     table's interpolation rule picks, checked against the independent Python
-    statement of that rule in tune/make_table.py over on- and off-grid
+    statement of that rule in tests/planner_rule.py over on- and off-grid
     shapes; every choice is a compiled geometry covering the row."""
-    import importlib.util
-    spec = importlib.util.spec_from_file_location(
-        "make_table", os.path.join(ROOT, "gated_activation_amd", "tune", "make_table.py"))
-    mt = importlib.util.module_from_spec(spec)
-    spec.loader.exec_module(mt)
+    import planner_rule as mt
     table = mt.read_inc(os.path.join(ROOT, "gated_activation_amd", "csrc", "planner_table.inc"))
     Ts = sorted(set(table[0]) | {1, 7, 33, 100, 300, 700, 900, 1800, 2500, 3500, 5000, 10000, 20000, 65535})
     Ns = sorted(set(table[1]) | {33, 63, 65, 72, 88, 140, 200, 300, 420, 600, 700, 1100, 1376, 1664, 1792,
@@ -172,13 +168,9 @@ def test_row_geometry_follows_the_measured_table():
 def test_split_choice_follows_the_measured_table():
     """Few long rows with a workspace: whether and how the planner splits rows
     is the split table's choice under the interpolation rule, checked against
-    the independent Python statement in tune/make_table.py on and off the
+    the independent Python statement in tests/planner_rule.py on and off the
     grid; outside the table (more rows, shorter rows) nothing is split."""
-    import importlib.util
-    spec = importlib.util.spec_from_file_location(
-        "make_table", os.path.join(ROOT, "gated_activation_amd", "tune", "make_table.py"))
-    mt = importlib.util.module_from_spec(spec)
-    spec.loader.exec_module(mt)
+    import planner_rule as mt
     table = mt.read_inc(os.path.join(ROOT, "gated_activation_amd", "csrc", "planner_table_split.inc"), "kSplit")
     Ts = sorted(set(table[0]) | {3, 5, 12, 40, 72, 100, 112, 200, 224})
     Ns = sorted(set(table[1]) | {2049, 2200, 2816, 3328, 4608, 5632, 7680, 8191})
@@ -258,6 +250,48 @@ def test_workspace_size_and_split_plan_checks():
     # the workspace entry point validates like the others
     assert L.ga_gelu_and_mul_sparse_ws(None, OUT, 4, 64, BF16, Z, None, WS, WS_BYTES, None) == EINVAL
     assert L.ga_gelu_and_mul_sparse_ws(IN, OUT, 0, 64, BF16, Z, None, WS, WS_BYTES, None) == OK
+
+
+def test_launches_of_2pow32_work_items_are_unsupported():
+    """One launch holds fewer than 2^32 work-items (grid x block).  One
+    workgroup per row reaches that at T = 2^26 rows of d = 512 bf16 (one
+    64-lane wave per row); the packed short rows (32 lanes per row) at
+    T = 2^27 rows of d = 256.  Both inputs fit in HBM, so the planner and the
+    entry points return GA_EUNSUPPORTED, before any HIP call."""
+    far_in = ctypes.c_void_p(0x100000000000)      # 128 GiB inputs: no overlap with far_out
+    far_out = ctypes.c_void_p(0x700000000000)
+    p = ga.Plan()
+    for T, d in ((1 << 26, 512), (1 << 27, 256), ((1 << 31) - 1, 8), ((1 << 31) - 1, 65536)):
+        assert L.ga_plan_gelu_and_mul_sparse(T, d, BF16, 1, 256, 0, ctypes.byref(p)) == EUNSUP, (T, d)
+        assert b"2^32" in L.ga_last_error()
+        if T * 3 * d * 2 < 0x600000000000:      # buffers that fit between far_in and far_out
+            assert L.ga_gelu_and_mul_sparse(far_in, far_out, T, d, BF16, Z, None, None) == EUNSUP, (T, d)
+    # just below: the plan is returned, and its launch stays under 2^32
+    for T, d in (((1 << 26) - 1, 512), ((1 << 27) - 8, 256), (1 << 20, 65536)):
+        assert L.ga_plan_gelu_and_mul_sparse(T, d, BF16, 1, 256, 0, ctypes.byref(p)) == OK, (T, d)
+        assert p.grid * p.block < 1 << 32
+    # an explicit plan is held to the same bound (rejected before a launch)
+    one_wave = ga.Plan(path=0, waves_per_row=1, per_lane=1, block=64)
+    st = L.ga_gelu_and_mul_sparse_with_plan(far_in, far_out, 1 << 26, 512, BF16, Z, None, ctypes.byref(one_wave),
+                                            None, 0, None)
+    assert st == EUNSUP
+    sixteen = ga.Plan(path=0, waves_per_row=16, per_lane=1, block=1024)
+    st = L.ga_gelu_and_mul_sparse_with_plan(far_in, far_out, 1 << 22, 512, BF16, Z, None, ctypes.byref(sixteen),
+                                            None, 0, None)
+    assert st == EUNSUP
+
+
+def test_split_rows_only_in_calls_of_few_rows():
+    """The planner splits rows only in calls of at most GA_SPLIT_PLAN_ROWS
+    rows (the header's constant, mirrored by the binding), so the binding's
+    fixed workspace of workspace_bytes(GA_SPLIT_PLAN_ROWS) serves every call."""
+    m = re.search(r"#define GA_SPLIT_PLAN_ROWS (\d+)", open(HEADER).read())
+    assert m and int(m.group(1)) == ga.GA_SPLIT_PLAN_ROWS == 256
+    assert ga.WORKSPACE_BYTES == L.ga_gelu_and_mul_sparse_workspace_bytes(ga.GA_SPLIT_PLAN_ROWS) == 256 * 256
+    assert ga.plan_gelu_and_mul_sparse(224, 65536, BF16).splits > 1
+    for d in (8192, 12288, 16384, 24576, 32768, 49152, 65536):
+        for T in (257, 300, 1000, 65535):
+            assert ga.plan_gelu_and_mul_sparse(T, d, BF16, with_workspace=True).splits == 1, (T, d)
 
 
 @pytest.mark.parametrize("dt", [BF16, F16, F32])
