@@ -1,17 +1,30 @@
-"""Turn geometry sweeps (tune/sweep.hip output) into the planner's table.
+"""The planner's measured tables: an independent statement of the rule that
+reads them, and the writer that turns geometry sweeps into them.
 
-    python make_table.py [--prefix kUna | --split] OUT.inc SWEEP.csv [SWEEP.csv ...]
-    python make_table.py --check [--prefix kUna | --split] TABLE.inc OFFGRID.csv
-    python make_table.py --packed PACKED.csv [PACKED.csv ...]
+    python tests/planner_rule.py [--prefix kUna | --split] OUT.inc SWEEP.csv [SWEEP.csv ...]
+    python tests/planner_rule.py --check [--prefix kUna | --split] TABLE.inc OFFGRID.csv
+    python tests/planner_rule.py --packed PACKED.csv [PACKED.csv ...]
+    python tests/planner_rule.py --summarize OUT.csv SWEEP.csv [SWEEP.csv ...]
 
---packed checks the short-row planner (a rule, no table) against sweeps run
-with GA_SWEEP_PATH=packed: for every shape, the library's own choice (from
+A sweep line is "T,d,nvec,waves,vectors per lane,up_late,us[,splits | lanes
+per row]": one MI355X's time per call of gelu_and_mul_sparse on T bf16 rows of
+nvec 16-byte vectors with that geometry, forced through the library's
+ga_gelu_and_mul_sparse_with_plan entry point (each geometry's best of 3
+interleaved passes of back-to-back launches over buffer sets past 1 GiB).
+The sweeps behind the committed tables are summarised under profiles/ as
+planner_sweep_*.csv (--summarize: the runs averaged, one line per geometry
+and shape), which the table writer reads like the raw sweeps, so
+        python tests/planner_rule.py gated_activation_amd/csrc/planner_table.inc \
+            profiles/planner_sweep_vector_bf16.csv
+regenerates a table.
+
+--packed checks the short-row planner (a rule, no table) against sweeps of
+the packed-rows path: for every shape, the library's own choice (from
 ga_plan_gelu_and_mul_sparse, host-only) against the fastest measured plan.
 
 The prefix names the table's symbols: kPlan (default) for the vector path,
-kUna for the unaligned path (sweeps run with GA_SWEEP_PATH=2; its kernel also
-takes 3, 5, 6 or 7 vectors per lane, but the table, and so the planner, keeps
-to 1, 2, 4, 8).
+kUna for the unaligned path (its kernel also takes 3, 5, 6 or 7 vectors per
+lane, but the table, and so the planner, keeps to 1, 2, 4, 8).
 
 The table holds, for every (rows T, 16-byte vectors per row nvec) point of the
 sweep's grid and every compiled geometry of the vector kernel (waves 1..16,
@@ -146,8 +159,8 @@ def write_inc(path, Ts, Ns, loss, sources, prefix="kPlan"):
         cand = ["// Geometry g = ((waves index * 4 + vectors-per-lane index) * 2 + up_late), waves",
                 "// 1, 2, 4, 8, 16, vectors per lane 1, 2, 4, 8."]
         ng = len(GEOS)
-    out = ["// Generated by gated_activation_amd/tune/make_table.py from geometry sweeps of " + kind,
-           "// (gated_activation_amd/tune/sweep.hip, bf16 rows, one MI355X): " + ", ".join(sources) + ".",
+    out = ["// Generated by tests/planner_rule.py from geometry sweeps of " + kind,
+           "// (bf16 rows, one MI355X): " + ", ".join(sources) + ".",
            f"// {P}Loss[t][n][g]: time of candidate g over the best candidate's time at",
            f"// ({P}T[t] rows, {P}N[n] vectors per row), as round((ratio - 1) * 400),",
            "// capped at 254; 255 = not run there."] + cand + [
@@ -246,8 +259,8 @@ def plan_name(key):
 
 
 def check_packed(paths):
-    # The repository root (this file is gated_activation_amd/tune/make_table.py).
-    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__)))))
+    # The repository root (this file is tests/planner_rule.py).
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     import gated_activation_amd as ga
     times = read_packed_sweeps(paths)
     ratios = []
@@ -266,8 +279,33 @@ def check_packed(paths):
     return 0
 
 
+def summarize(out, paths):
+    """Average the runs of the given sweeps per (T, d, nvec, geometry[, extra
+    column]) and write one line each, in the sweeps' own line format."""
+    acc = collections.defaultdict(list)
+    for path in paths:
+        for line in open(path):
+            if not line[:1].isdigit():
+                continue
+            f = line.strip().split(",")
+            acc[tuple(f[:6]) + tuple(f[7:])].append(float(f[6]))
+    lines = []
+    for key in sorted(acc, key=lambda k: tuple(int(x) for x in k)):
+        us = sum(acc[key]) / len(acc[key])
+        lines.append(",".join(list(key[:6]) + [repr(us)] + list(key[6:])))
+    head = ["# Geometry sweep summary (tests/planner_rule.py --summarize): " + ", ".join(
+        os.path.basename(p) for p in paths) + " averaged.",
+        "# T,d,nvec,waves,vectors per lane,up_late,us per call[,splits | lanes per row]"]
+    open(out, "w").write("\n".join(head + lines) + "\n")
+    return len(lines)
+
+
 def main(argv):
     argv = list(argv)
+    if "--summarize" in argv:
+        argv.remove("--summarize")
+        print(f"{argv[1]}: {summarize(argv[1], argv[2:])} lines")
+        return 0
     if "--packed" in argv:
         argv.remove("--packed")
         return check_packed(argv[1:])

@@ -1,35 +1,30 @@
-"""The planner's tuning tool (gated_activation_amd/tune): the sweep program
-compiles against the public header, and the table builder turns sweep lines
-into a table whose interpolation rule picks the measured best geometry at
-the grid points and respects coverage between them."""
-import importlib.util
+"""The planner's measured tables (tests/planner_rule.py): the table writer
+turns sweep lines into a table whose interpolation rule picks the measured
+best geometry at the grid points and respects coverage between them, and the
+committed tables are exactly what the committed sweep summaries give."""
 import os
-import shutil
-import subprocess
 
-import pytest
+import planner_rule as mt
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-TUNE = os.path.join(ROOT, "gated_activation_amd", "tune")
-ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+CSRC = os.path.join(ROOT, "gated_activation_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
-def _make_table():
-    spec = importlib.util.spec_from_file_location("make_table", os.path.join(TUNE, "make_table.py"))
-    mt = importlib.util.module_from_spec(spec)
-    spec.loader.exec_module(mt)
-    return mt
+def _body(path):
+    return [ln for ln in open(path) if not ln.startswith("//")]
 
 
-@pytest.mark.skipif(not os.path.exists(os.path.join(ROCM, "bin", "hipcc")), reason="no hipcc")
-def test_sweep_tool_compiles():
-    subprocess.run([os.path.join(ROCM, "bin", "hipcc"), "--offload-arch=gfx950", "-std=c++17", "-fsyntax-only",
-                    "-I", os.path.join(ROOT, "include"), os.path.join(TUNE, "sweep.hip")],
-                   check=True, capture_output=True, text=True)
+def test_committed_tables_regenerate_from_the_sweep_summaries(tmp_path):
+    for inc, summary, flags in (("planner_table.inc", "planner_sweep_vector_bf16.csv", []),
+                                ("planner_table_una.inc", "planner_sweep_unaligned_bf16.csv", ["--prefix", "kUna"]),
+                                ("planner_table_split.inc", "planner_sweep_split_bf16.csv", ["--split"])):
+        out = tmp_path / inc
+        assert mt.main(["planner_rule.py"] + flags + [str(out), os.path.join(PROFILES, summary)]) == 0
+        assert _body(str(out)) == _body(os.path.join(CSRC, inc)), inc
 
 
 def test_table_builder_round_trip(tmp_path):
-    mt = _make_table()
     # A synthetic sweep on a 2 x 2 grid: at every point one geometry is
     # fastest; a second one is 10 % slower everywhere.
     lines = []
@@ -44,7 +39,7 @@ def test_table_builder_round_trip(tmp_path):
     csv = tmp_path / "s.csv"
     csv.write_text("\n".join(lines) + "\ndone\n")
     inc = tmp_path / "t.inc"
-    mt.main(["make_table.py", str(inc), str(csv)])
+    mt.main(["planner_rule.py", str(inc), str(csv)])
     table = mt.read_inc(str(inc))
     assert table[0] == [100, 400] and table[1] == [128, 512]
     for (T, n), g in fast.items():
@@ -61,7 +56,6 @@ def test_table_builder_round_trip(tmp_path):
 
 
 def test_split_table_builder_round_trip(tmp_path):
-    mt = _make_table()
     # Two row sizes x two row counts: at three points a chunk geometry wins,
     # at one the row path (no split) does.
     win = {(1, 4096): (8, 1), (1, 8192): (8, 2), (64, 4096): (4, 2), (64, 8192): None}
@@ -77,7 +71,7 @@ def test_split_table_builder_round_trip(tmp_path):
     csv = tmp_path / "split.csv"
     csv.write_text("\n".join(lines) + "\ndone\n")
     inc = tmp_path / "split.inc"
-    mt.main(["make_table.py", "--split", str(inc), str(csv)])
+    mt.main(["planner_rule.py", "--split", str(inc), str(csv)])
     table = mt.read_inc(str(inc), "kSplit")
     for (T, n), g in win.items():
         c = mt.choose_split(table, T, n)
@@ -92,7 +86,6 @@ def test_packed_check_reads_sweeps_and_asks_the_library(tmp_path, capsys):
     lanes per row, 0 for the row geometry) and rates the library's own
     choice (G = 8 lanes, one vector, for a row of 6 vectors; G = 32 for 24)
     against the fastest line of each shape."""
-    mt = _make_table()
     csv = tmp_path / "packed.csv"
     csv.write_text("\n".join([
         "4096,48,6,0,1,0,2.00,8",      # the planner's G8 V1: the fastest
@@ -106,7 +99,7 @@ def test_packed_check_reads_sweeps_and_asks_the_library(tmp_path, capsys):
     times = mt.read_packed_sweeps([str(csv)])
     assert times[(4096, 6)][("packed", 8, 1)] == 2.0
     assert times[(4096, 24)][("row", 1)] == 3.3
-    assert mt.main(["make_table.py", "--packed", str(csv)]) == 0
+    assert mt.main(["planner_rule.py", "--packed", str(csv)]) == 0
     out = capsys.readouterr().out
     assert "nvec=  6 planner G8 V1" in out and "1.000 of the best (G8 V1" in out
     assert "nvec= 24 planner G32 V1" in out and "1.050 of the best (G16 V2" in out
