@@ -8,6 +8,8 @@ is not built, importing this package raises: there is no fallback.
 
     gelu_and_mul_sparse(x, z)           x: [T, 2d] -> [T, d] (round_intermediates=True:
                                         the round-trip form)
+    gelu_and_mul_sparse_noalloc(x, z)   the same for T <= 256 rows, no workspace
+                                        (the library's own static array)
     silu_and_mul_bounded(x, live_rows)  x: [M, 2d] -> [M, d] (live rows only)
     gelu_and_mul(x, approximate)        x: [T, 2d] -> [T, d] (tanh or erf GELU)
     squared_relu_bounded(x, live_rows)  x: [M, d]  -> [M, d] (live rows only)
@@ -16,7 +18,7 @@ is not built, importing this package raises: there is no fallback.
 from ._lib import (  # noqa: F401
     GA_BF16, GA_F16, GA_F32, GA_OK, GA_EINVAL, GA_EUNSUPPORTED, GA_EHIP, GA_MAX_D, GA_ROUND_INTERMEDIATES,
     GaError, Plan, Z_SPARSITY_095, lib, library_path,
-    gelu_and_mul_sparse, silu_and_mul_bounded, stream_xor_rows,
+    gelu_and_mul_sparse, gelu_and_mul_sparse_noalloc, silu_and_mul_bounded, stream_xor_rows,
     gelu_and_mul, squared_relu_bounded, z_from_sparsity,
     plan_gelu_and_mul_sparse, plan_silu_and_mul_bounded, workspace_for,
     reserve_workspace, held_workspaces, GA_SPLIT_PLAN_ROWS, WORKSPACE_BYTES,

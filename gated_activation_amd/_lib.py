@@ -55,6 +55,7 @@ def _load():
                                              ctypes.c_size_t, vp],
         "ga_gelu_and_mul_sparse_ws": [vp, vp, i64, i64, i32, ctypes.c_float, vp, vp, ctypes.c_size_t, vp],
         "ga_gelu_and_mul_sparse_ex": [vp, vp, i64, i64, i32, ctypes.c_float, vp, i32, vp, ctypes.c_size_t, vp],
+        "ga_gelu_and_mul_sparse_noalloc": [vp, vp, i64, i64, i32, ctypes.c_float, vp, vp],
         "ga_silu_and_mul_bounded_with_plan": [vp, vp, i64, i64, i32, vp, pplan, vp],
         "ga_plan_gelu_and_mul_sparse": [i64, i64, i32, i32, i32, i32, pplan],
         "ga_plan_silu_and_mul_bounded": [i64, i64, i32, i32, i32, pplan],
@@ -213,6 +214,20 @@ def gelu_and_mul_sparse(x, z=Z_SPARSITY_095, out=None, live_rows=None, plan=None
             _check(lib.ga_gelu_and_mul_sparse_ws(*args, ws_ptr, ws_bytes, _stream_of(x)))
         else:
             _check(lib.ga_gelu_and_mul_sparse(*args, _stream_of(x)))
+    return out
+
+
+def gelu_and_mul_sparse_noalloc(x, z=Z_SPARSITY_095, out=None, live_rows=None):
+    """gelu_and_mul_sparse for at most GA_SPLIT_PLAN_ROWS rows that uses the
+    library's own static split-row array instead of a workspace, for code
+    that must not allocate (pass `out` too).  Calls on one device share that
+    array: they must not overlap in time."""
+    T, d, out = _prep(x, out, "gelu_and_mul_sparse_noalloc")
+    live = _live_ptr(live_rows, x, "gelu_and_mul_sparse_noalloc")
+    with torch.cuda.device(x.device):
+        _check(lib.ga_gelu_and_mul_sparse_noalloc(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                                  T, d, _TORCH_DTYPE[x.dtype], ctypes.c_float(z), live,
+                                                  _stream_of(x)))
     return out
 
 

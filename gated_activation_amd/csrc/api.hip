@@ -12,6 +12,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/ga.h"
 #include "ga_internal.h"
@@ -504,6 +505,64 @@ double normal_quantile_lower(double p) {
     return z;
 }
 
+// ---------------------------------------------------------------------------
+// The library's own split-row workspace, for ga_gelu_and_mul_sparse_noalloc:
+// callers that cannot allocate device memory (stream capture, serving loops).
+// One copy per device, holding the records of GA_SPLIT_PLAN_ROWS rows (64 KiB),
+// kept until the process ends.  Host code never uses the array's name as an
+// address: its per-device address comes from hipGetSymbolAddress.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)GA_SPLIT_PLAN_ROWS * ga::SPLIT_RECORD_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Zero fill by a kernel (a memset node recorded into a graph is avoided).
+__global__ __launch_bounds__(256) void zero_scratch_kernel(uint4 *p, int32_t n) {
+    const int32_t i = (int32_t)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (i < n) p[i] = uint4{0u, 0u, 0u, 0u};
+}
+
+struct DeviceScratch {
+    void *ptr = nullptr;   // device address of `scratch` on this device
+    bool zeroed = false;   // a zero fill has been enqueued outside stream capture
+};
+std::mutex g_scratch_mu;
+DeviceScratch g_scratch[64];
+
+// The current device's scratch: its address is resolved once per device; the
+// first call on a device also enqueues a zero fill on the caller's stream
+// (the split kernels need every record zeroed before first use).  A fill made
+// while the stream is being captured lands in the graph, and the next call
+// fills again, so the memory is zeroed before any launch that runs eagerly.
+ga_status device_scratch(ga_stream stream, void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(GA_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(GA_EUNSUPPORTED, "device %d: at most 64 devices", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    DeviceScratch &ds = g_scratch[dev];
+    if (ds.ptr == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(GA_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        ds.ptr = p;
+    }
+    if (!ds.zeroed) {
+        const hipStream_t s = static_cast<hipStream_t>(stream);
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        e = hipStreamIsCapturing(s, &cap);
+        if (e != hipSuccess) return fail(GA_EHIP, "hipStreamIsCapturing: %s", hipGetErrorString(e));
+        const int32_t n = (int32_t)(kScratchBytes / 16);
+        uint4 *a = static_cast<uint4 *>(ds.ptr);
+        void *args[] = {&a, (void *)&n};
+        e = hipLaunchKernel((const void *)&zero_scratch_kernel, dim3((n + 255) / 256), dim3(256), args, 0, s);
+        if (e != hipSuccess) return fail(GA_EHIP, "scratch zero fill: %s", hipGetErrorString(e));
+        if (cap == hipStreamCaptureStatusNone) ds.zeroed = true;
+    }
+    *ptr = ds.ptr;
+    return GA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -643,6 +702,24 @@ ga_status ga_gelu_and_mul_sparse(const void *in, void *out, int64_t T, int64_t d
     if ((st = ga_plan_gelu_and_mul_sparse(T, d, dtype, vector_aligned(in, out, d, dtype), 256, 0, &p)) != GA_OK)
         return st;
     return launch_gelu(in, out, T, d, dtype, z, live_rows, p, nullptr, stream);
+}
+
+ga_status ga_gelu_and_mul_sparse_noalloc(const void *in, void *out, int64_t T, int64_t d, int32_t dtype, float z,
+                                         const int32_t *live_rows, ga_stream stream) {
+    const char *name = "ga_gelu_and_mul_sparse_noalloc";
+    ga_status st = check_rows(name, in, out, T, d, dtype);
+    if (st != GA_OK) return st;
+    if (!std::isfinite(z)) return fail(GA_EINVAL, "%s: z is not finite", name);
+    if ((uintptr_t)live_rows % 4 != 0) return fail(GA_EINVAL, "%s: live_rows is not 4-byte aligned", name);
+    if (T > GA_SPLIT_PLAN_ROWS)
+        return fail(GA_EUNSUPPORTED,
+                    "%s: %lld rows; its scratch holds the split records of at most %d rows (calls of more "
+                    "rows never split: ga_gelu_and_mul_sparse serves them and needs no memory either)",
+                    name, (long long)T, GA_SPLIT_PLAN_ROWS);
+    if (T == 0) return GA_OK;
+    void *ws = nullptr;
+    if ((st = device_scratch(stream, &ws)) != GA_OK) return st;
+    return ga_gelu_and_mul_sparse_ex(in, out, T, d, dtype, z, live_rows, 0, ws, kScratchBytes, stream);
 }
 
 double ga_z_from_sparsity(double target_sparsity) {

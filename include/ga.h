@@ -178,6 +178,26 @@ ga_status ga_gelu_and_mul_sparse_ws(const void *in, void *out, int64_t T, int64_
                                     void *workspace, size_t workspace_bytes, ga_stream stream);
 
 /*
+ * ga_gelu_and_mul_sparse_ws without a caller workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the split records live in the
+ * library's own static device array (64 KiB per device, held until the
+ * process ends).  It allocates nothing and calls no allocating routine.
+ *   Same arguments and checks as ga_gelu_and_mul_sparse, and
+ *   T <= GA_SPLIT_PLAN_ROWS (larger T: GA_EUNSUPPORTED; such calls never
+ *   split rows, and ga_gelu_and_mul_sparse serves them with no memory).
+ * The first call on a device also enqueues a zero fill of that device's
+ * array on `stream` (recorded into the graph when `stream` is capturing,
+ * and then repeated by the next call).  Every call on one device shares its
+ * array: calls that overlap in time on one device (other streams, other
+ * threads, concurrent graph replays) race and may compute wrong cutoffs;
+ * serialise them, e.g. on one stream.
+ */
+ga_status ga_gelu_and_mul_sparse_noalloc(const void *in, void *out, int64_t T, int64_t d,
+                                         int32_t dtype, float z, const int32_t *live_rows,
+                                         ga_stream stream);
+
+/*
  * ga_gelu_and_mul_sparse_ws with flags: 0 (the same as _ws) or
  * GA_ROUND_INTERMEDIATES (the round-trip form above; it never splits rows,
  * so the workspace may then be NULL).  Unknown flag bits: GA_EINVAL.

@@ -252,6 +252,30 @@ def test_workspace_size_and_split_plan_checks():
     assert L.ga_gelu_and_mul_sparse_ws(IN, OUT, 0, 64, BF16, Z, None, WS, WS_BYTES, None) == OK
 
 
+def test_noalloc_entry_point_host_checks():
+    """The no-allocation entry point checks its arguments like the others
+    and serves at most GA_SPLIT_PLAN_ROWS rows; every rejection happens
+    before any HIP call."""
+    f = L.ga_gelu_and_mul_sparse_noalloc
+    assert f(IN, OUT, 257, 32768, BF16, Z, None, None) == EUNSUP
+    assert b"at most 256 rows" in L.ga_last_error()
+    assert f(IN, OUT, 1 << 20, 64, BF16, Z, None, None) == EUNSUP
+    assert f(None, OUT, 4, 2048, BF16, Z, None, None) == EINVAL
+    assert f(IN, IN, 4, 2048, BF16, Z, None, None) == EINVAL
+    assert f(IN, OUT, 4, 0, BF16, Z, None, None) == EINVAL
+    assert f(IN, OUT, 4, 65537, BF16, Z, None, None) == EUNSUP
+    assert f(IN, OUT, 4, 2048, 7, Z, None, None) == EINVAL
+    assert f(IN, OUT, 4, 2048, BF16, ctypes.c_float(float("nan")), None, None) == EINVAL
+    assert f(IN, OUT, 4, 2048, BF16, Z, ctypes.c_void_p(0x7F2000000002), None) == EINVAL
+    assert f(IN, OUT, -1, 2048, BF16, Z, None, None) == EINVAL
+    assert f(IN, OUT, 0, 2048, BF16, Z, None, None) == OK          # no rows: nothing launched
+    # its source resolves the array's device address and never names the array
+    # in a kernel argument or copy
+    src = open(os.path.join(ROOT, "gated_activation_amd", "csrc", "api.hip")).read()
+    assert "hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))" in src
+    assert "hipMalloc" not in src and "hipFree" not in src
+
+
 def test_launches_of_2pow32_work_items_are_unsupported():
     """One launch holds fewer than 2^32 work-items (grid x block).  One
     workgroup per row reaches that at T = 2^26 rows of d = 512 bf16 (one
