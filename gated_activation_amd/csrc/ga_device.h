@@ -234,6 +234,43 @@ __device__ __forceinline__ float silu(float x) {
     return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// ---------------------------------------------------------------------------
+// Row mean and variance from the workgroup sums.
+//
+// The default form avoids IEEE division: r = 1/n from the hardware reciprocal
+// (within 1 ulp), q0 = sum * r is then within 1.5 ulp of sum / n, so the
+// residual sum - q0 * n is exact in one fma, and q0 + residual * r lands on
+// sum / n itself whenever that quotient is a float.  A row of one repeated
+// value therefore gets exactly that value as its mean, hence a variance of
+// exactly 0; any other mean is within about half an ulp.  The variance is
+// the sum times r (within 1.5 ulp) and the std the hardware square root
+// (within 1 ulp): both far inside the error of the fp32 sums themselves.
+// The round-trip form keeps IEEE division and square root, as the tensor
+// composition it reproduces does.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float div_count(float sum, float n, float r) {
+    const float q0 = sum * r;
+    return __builtin_fmaf(__builtin_fmaf(-q0, n, sum), r, q0);
+}
+
+template <bool RT>
+__device__ __forceinline__ float row_mean(float sum, float n) {
+    if constexpr (RT) {
+        return sum / n;
+    } else {
+        return div_count(sum, n, __builtin_amdgcn_rcpf(n));
+    }
+}
+
+template <bool RT>
+__device__ __forceinline__ float row_var(float sq_sum, float n) {
+    if constexpr (RT) {
+        return sq_sum / n;
+    } else {
+        return sq_sum * __builtin_amdgcn_rcpf(n);
+    }
+}
+
 // The cutoff from the row's fp32 mean and variance.  RT (round-trip form):
 // every intermediate is rounded to the element type as a tensor of that type
 // would hold it -- mean, std, z, z * std, mean + z * std.  Contraction is off
@@ -246,7 +283,7 @@ __device__ __forceinline__ float sparse_cutoff(float mean, float var, float z) {
         const float zs = E::round(E::round(z) * E::round(__builtin_sqrtf(var)));
         return E::round(E::round(mean) + zs);
     } else {
-        return __builtin_fmaf(z, __builtin_sqrtf(var), mean);
+        return __builtin_fmaf(z, __builtin_amdgcn_sqrtf(var), mean);
     }
 }
 

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(WAVES * 64) void gelu_sparse_vec_kernel(
 #pragma unroll
         for (int e = 0; e < PER; ++e) s += f[e];
     }
-    const float mean = block_sum<WAVES>(s, red[0]) / (float)d;
+    const float mean = row_mean<RT>(block_sum<WAVES>(s, red[0]), (float)d);
 
     // Population variance from the staged row.
     float q = 0.0f;
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(WAVES * 64) void gelu_sparse_vec_kernel(
             }
         }
     }
-    const float var = block_sum<WAVES>(q, red[1]) / (float)d;
+    const float var = row_var<RT>(block_sum<WAVES>(q, red[1]), (float)d);
     const float cut = sparse_cutoff<E, RT>(mean, var, z);
 
     if constexpr (UP == 1) {
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(WAVES * 64) void gelu_sparse_elem_kernel(
         g[k] = i < d ? E::to_f32(grow[i]) : 0.0f;
         s += g[k];
     }
-    const float mean = block_sum<WAVES>(s, red[0]) / (float)d;
+    const float mean = row_mean<RT>(block_sum<WAVES>(s, red[0]), (float)d);
 
     float q = 0.0f;
 #pragma unroll
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(WAVES * 64) void gelu_sparse_elem_kernel(
             q = __builtin_fmaf(dv, dv, q);
         }
     }
-    const float var = block_sum<WAVES>(q, red[1]) / (float)d;
+    const float var = row_var<RT>(block_sum<WAVES>(q, red[1]), (float)d);
     const float cut = sparse_cutoff<E, RT>(mean, var, z);
 
 #pragma unroll

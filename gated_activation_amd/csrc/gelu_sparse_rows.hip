@@ -104,7 +104,7 @@ __global__ __launch_bounds__(ROWS_BLOCK) void gelu_sparse_rows_kernel(
 #pragma unroll
         for (int e = 0; e < PER; ++e) s += g[e];
     }
-    const float mean = group_sum<G>(s) / (float)d;
+    const float mean = row_mean<RT>(group_sum<G>(s), (float)d);
 
     float q = 0.0f;
 #pragma unroll
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(ROWS_BLOCK) void gelu_sparse_rows_kernel(
             }
         }
     }
-    const float var = group_sum<G>(q) / (float)d;
+    const float var = row_var<RT>(group_sum<G>(q), (float)d);
     const float cut = sparse_cutoff<E, RT>(mean, var, z);
 
     if (!valid) return;

@@ -48,7 +48,7 @@ __device__ __forceinline__ void chan_combine(float &n_a, float &mean_a, float &m
                                              float mean_b, float m2_b) {
     const float n = n_a + n_b;
     const float delta = mean_b - mean_a;
-    const float w = n_b / n;
+    const float w = n_b * __builtin_amdgcn_rcpf(n);
     mean_a = __builtin_fmaf(delta, w, mean_a);
     m2_a = m2_a + m2_b + delta * delta * n_a * w;
     n_a = n;
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(WAVES * 64) void gelu_sparse_split_kernel(
 #pragma unroll
         for (int e = 0; e < PER; ++e) acc += f[e];
     }
-    const float m_here = block_sum<WAVES>(acc, red[0]) / n_here;
+    const float m_here = row_mean<false>(block_sum<WAVES>(acc, red[0]), n_here);
     float q = 0.0f;
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(WAVES * 64) void gelu_sparse_split_kernel(
 #pragma unroll
             for (int e = 0; e < PER; ++e) a += f[e];
         }
-        mean = block_sum<WAVES>(a, red[2]) / (float)d;
+        mean = row_mean<false>(block_sum<WAVES>(a, red[2]), (float)d);
         float b = 0.0f;
         for (int j = t; j < nvec; j += NT) {
             float f[PER];
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(WAVES * 64) void gelu_sparse_split_kernel(
         }
         m2 = block_sum<WAVES>(b, red[3]);
     }
-    const float cut = __builtin_fmaf(z, __builtin_sqrtf(m2 / (float)d), mean);
+    const float cut = sparse_cutoff<E, false>(mean, row_var<false>(m2, (float)d), z);
 
     if constexpr (UP == 1) {
 #pragma unroll

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(WAVES * 64) void gelu_sparse_unaligned_kernel(
 #pragma unroll
         for (int e = 0; e < PER; ++e) s += f[e];
     }
-    const float mean = block_sum<WAVES>(s, red[0]) / (float)d;
+    const float mean = row_mean<RT>(block_sum<WAVES>(s, red[0]), (float)d);
 
     // Population variance from the staged row; only the lane holding the
     // partial last vector tests elements.
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(WAVES * 64) void gelu_sparse_unaligned_kernel(
             }
         }
     }
-    const float var = block_sum<WAVES>(q, red[1]) / (float)d;
+    const float var = row_var<RT>(block_sum<WAVES>(q, red[1]), (float)d);
     const float cut = sparse_cutoff<E, RT>(mean, var, z);
 
     // Apply and store.
