@@ -173,7 +173,7 @@ def test_split_choice_follows_the_measured_table():
     import planner_rule as mt
     table = mt.read_inc(os.path.join(ROOT, "gated_activation_amd", "csrc", "planner_table_split.inc"), "kSplit")
     Ts = sorted(set(table[0]) | {3, 5, 12, 40, 72, 100, 112, 200, 224})
-    Ns = sorted(set(table[1]) | {2049, 2200, 2816, 3328, 4608, 5632, 7680, 8191})
+    Ns = sorted(set(table[1]) | {1100, 1400, 1700, 2047, 2049, 2200, 2816, 3328, 4608, 5632, 7680, 8191})
     for T in Ts:
         for n in Ns:
             p = ga.plan_gelu_and_mul_sparse(T, n * 8, BF16, with_workspace=True)
@@ -190,7 +190,7 @@ def test_split_choice_follows_the_measured_table():
             assert p.up_late == 0 and p.grid == T * p.splits
             chunk = p.waves_per_row * 64 * p.per_lane
             assert chunk * p.splits >= n > chunk * (p.splits - 1)
-    for T, n in ((257, 8192), (4096, 8192), (8, 2047), (1, 1024)):
+    for T, n in ((257, 8192), (4096, 8192), (8, 1023), (1, 1024), (64, 1024)):
         assert ga.plan_gelu_and_mul_sparse(T, n * 8, BF16, with_workspace=True).splits == 1
 
 
