@@ -152,6 +152,7 @@ void analytic_row_geometry(int64_t nvec, int64_t T, int *w_out, int *v_out, int 
 #include "planner_table.inc"
 #include "planner_table_una.inc"
 #include "planner_table_split.inc"
+#include "planner_table_rep.inc"
 
 constexpr int kPlanWaves[5] = {1, 2, 4, 8, 16};
 constexpr int kPlanPerLane[4] = {1, 2, 4, 8};
@@ -281,6 +282,29 @@ bool pick_split(int64_t nvec, int64_t T, int *w_out, int *v_out, int *splits_out
     return true;
 }
 
+// Few rows: whether the replicated-statistics path (each of REP workgroups
+// per row reduces the whole gate row and applies its share; no workspace)
+// beats the row path and, with a workspace, the split path, and with which
+// geometry, from the measured table kRepLoss (60 replicated geometries,
+// waves 1..16 times vectors per lane 1, 2, 4, 8 times REP 2, 4, 8; then the
+// fastest row geometry and the fastest split plan; 1 <= T <= 256 rows of
+// 256 .. 8192 vectors).  False: not replicated (the row and split tables
+// decide).
+bool pick_rep(int64_t nvec, int64_t T, bool with_workspace, int *w_out, int *v_out, int *rep_out) {
+    static_assert(kRepNG == 62, "replicated table: 60 geometries, the row path and the split path");
+    if (T < 1 || T > kRepT[kRepNT - 1] || nvec < kRepN[0] || nvec > kRepN[kRepNN - 1]) return false;
+    const int best = table_argmin(kRepT, kRepNT, kRepN, kRepNN, &kRepLoss[0][0][0], kRepNG, T, nvec, [&](int c) {
+        if (c == 60) return true;
+        if (c == 61) return with_workspace;
+        return (int64_t)kPlanWaves[c / 12] * 64 * kPlanPerLane[(c / 3) % 4] >= nvec;
+    });
+    if (best < 0 || best >= 60) return false;
+    *w_out = kPlanWaves[best / 12];
+    *v_out = kPlanPerLane[(best / 3) % 4];
+    *rep_out = 2 << (best % 3);
+    return true;
+}
+
 ga_status check_gelu_plan(const ga_plan *p, int64_t T, int64_t d, int32_t dtype) {
     if ((p->flags & ~GA_ROUND_INTERMEDIATES) != 0)
         return fail(GA_EINVAL, "gelu plan: unknown flag bits 0x%x", (unsigned)p->flags);
@@ -308,6 +332,16 @@ ga_status check_gelu_plan(const ga_plan *p, int64_t T, int64_t d, int32_t dtype)
             if (T > kSplitMaxRows)
                 return fail(GA_EUNSUPPORTED, "gelu plan: split rows need T <= %lld", (long long)kSplitMaxRows);
         }
+    } else if (p->path == 4) {
+        if ((p->flags & GA_ROUND_INTERMEDIATES) != 0)
+            return fail(GA_EUNSUPPORTED, "gelu plan: the round-trip form has no replicated-statistics kernel");
+        if (p->up_late != 0 || !ga::gelu_rep_available(dtype, p->waves_per_row, p->per_lane, p->splits))
+            return fail(GA_EUNSUPPORTED,
+                        "gelu plan: no replicated-statistics kernel for waves=%d per_lane=%d splits=%d up_late=%d",
+                        p->waves_per_row, p->per_lane, p->splits, p->up_late);
+        const int64_t per16 = 16 / (int64_t)elem_size(dtype);
+        if ((int64_t)p->waves_per_row * 64 * p->per_lane < (d + per16 - 1) / per16)
+            return fail(GA_EUNSUPPORTED, "gelu plan: geometry covers fewer than d elements");
     } else if (p->path == 3) {
         if (p->splits != 1 || p->up_late != 0)
             return fail(GA_EUNSUPPORTED, "gelu plan: the packed-rows path takes splits=1, up_late=0");
@@ -344,6 +378,7 @@ constexpr int64_t kMaxWorkItems = (int64_t)1 << 32;
 
 // Work-items of a gelu launch with this plan over T rows.
 int64_t gelu_work_items(const ga_plan &p, int64_t T) {
+    if (p.path == 4) return ga::gelu_rep_grid(T, p.splits) * (int64_t)p.waves_per_row * 64;
     if (p.path == 3) {
         const int64_t rows_per_block = ga::ROWS_BLOCK / p.lanes_per_row;
         return (T + rows_per_block - 1) / rows_per_block * ga::ROWS_BLOCK;
@@ -387,6 +422,12 @@ ga_status launch_gelu(const void *in, void *out, int64_t T, int64_t d, int32_t d
                                                         p.spin_limit, s));
         return launched(name, ga::launch_gelu_vec(dtype, p.waves_per_row, p.per_lane, p.up_late, rt, T, in, out,
                                                   (int32_t)T, (int32_t)d, nvec, z, live, s));
+    }
+    if (p.path == 4) {
+        if (rt) return fail(GA_EUNSUPPORTED, "%s: the round-trip form has no replicated-statistics kernel", name);
+        const int32_t nvec = (int32_t)(d * (int64_t)elem_size(dtype) / 16);
+        return launched(name, ga::launch_gelu_rep(dtype, p.waves_per_row, p.per_lane, p.splits, in, out, (int32_t)T,
+                                                  (int32_t)d, nvec, z, live, s));
     }
     if (p.path == 3) {
         // Rows' 16-byte vectors, a partial last one included; rows or bases
@@ -565,13 +606,10 @@ ga_status device_scratch(ga_stream stream, void **ptr) {
 
 }  // namespace
 
-extern "C" {
-
-// ---------------------------------------------------------------------------
-// gelu_and_mul_sparse
-// ---------------------------------------------------------------------------
-ga_status ga_plan_gelu_and_mul_sparse(int64_t T, int64_t d, int32_t dtype, int32_t aligned,
-                                      int32_t num_cus, int32_t with_workspace, ga_plan *plan) {
+// The planner.  allow_rep: the replicated-statistics path may be chosen (it
+// has no round-trip form, so calls in that form pass false).
+static ga_status plan_gelu(int64_t T, int64_t d, int32_t dtype, int32_t aligned, int32_t num_cus,
+                           int32_t with_workspace, bool allow_rep, ga_plan *plan) {
     if (plan == nullptr) return fail(GA_EINVAL, "plan: null output");
     if (T < 0 || T > INT32_MAX || d < 1) return fail(GA_EINVAL, "plan: bad sizes");
     const size_t es = elem_size(dtype);
@@ -600,11 +638,18 @@ ga_status ga_plan_gelu_and_mul_sparse(int64_t T, int64_t d, int32_t dtype, int32
         p.waves_per_row = w;
         p.per_lane = v;
         p.up_late = late;
-        // Few long rows: split each over several workgroups that exchange
-        // partial statistics (about a microsecond, so only where the measured
-        // split table says it pays).
+        // Few rows: share each row among several workgroups, either each
+        // reducing the whole gate row itself (replicated statistics) or
+        // exchanging partial statistics through the workspace (split rows;
+        // about a microsecond), where the measured tables say it pays.
         int sw, sv, ss;
-        if (with_workspace && pick_split(nvec, T, &sw, &sv, &ss)) {
+        if (allow_rep && pick_rep(nvec, T, with_workspace != 0, &sw, &sv, &ss)) {
+            p.path = 4;
+            p.waves_per_row = sw;
+            p.per_lane = sv;
+            p.up_late = 0;
+            p.splits = ss;
+        } else if (with_workspace && pick_split(nvec, T, &sw, &sv, &ss)) {
             p.waves_per_row = sw;
             p.per_lane = sv;
             p.up_late = 0;
@@ -632,6 +677,9 @@ ga_status ga_plan_gelu_and_mul_sparse(int64_t T, int64_t d, int32_t dtype, int32
         const int64_t rows_per_block = ga::ROWS_BLOCK / p.lanes_per_row;
         p.block = ga::ROWS_BLOCK;
         p.grid = (T + rows_per_block - 1) / rows_per_block;
+    } else if (p.path == 4) {
+        p.block = p.waves_per_row * 64;
+        p.grid = ga::gelu_rep_grid(T, p.splits);
     } else {
         p.block = p.waves_per_row * 64;
         p.grid = T * p.splits;
@@ -640,6 +688,16 @@ ga_status ga_plan_gelu_and_mul_sparse(int64_t T, int64_t d, int32_t dtype, int32
     if (st != GA_OK) return st;
     *plan = p;
     return GA_OK;
+}
+
+extern "C" {
+
+// ---------------------------------------------------------------------------
+// gelu_and_mul_sparse
+// ---------------------------------------------------------------------------
+ga_status ga_plan_gelu_and_mul_sparse(int64_t T, int64_t d, int32_t dtype, int32_t aligned,
+                                      int32_t num_cus, int32_t with_workspace, ga_plan *plan) {
+    return plan_gelu(T, d, dtype, aligned, num_cus, with_workspace, true, plan);
 }
 
 size_t ga_gelu_and_mul_sparse_workspace_bytes(int64_t T) {
@@ -654,7 +712,7 @@ ga_status ga_gelu_and_mul_sparse_with_plan(const void *in, void *out, int64_t T,
     if (!std::isfinite(z)) return fail(GA_EINVAL, "ga_gelu_and_mul_sparse: z is not finite");
     if (plan == nullptr) return fail(GA_EINVAL, "ga_gelu_and_mul_sparse: null plan");
     if ((st = check_gelu_plan(plan, T, d, dtype)) != GA_OK) return st;
-    if (plan->path == 0 && !vector_aligned(in, out, d, dtype))
+    if ((plan->path == 0 || plan->path == 4) && !vector_aligned(in, out, d, dtype))
         return fail(GA_EUNSUPPORTED, "ga_gelu_and_mul_sparse: vector path needs 16-byte rows and bases");
     if ((st = check_workspace(*plan, T, workspace, workspace_bytes)) != GA_OK) return st;
     if (T == 0) return GA_OK;
@@ -679,8 +737,8 @@ ga_status ga_gelu_and_mul_sparse_ex(const void *in, void *out, int64_t T, int64_
     int cus = 256;
     if (have_ws && (st = current_cus(&cus)) != GA_OK) return st;
     ga_plan p;
-    if ((st = ga_plan_gelu_and_mul_sparse(T, d, dtype, vector_aligned(in, out, d, dtype), cus, have_ws, &p)) !=
-        GA_OK)
+    if ((st = plan_gelu(T, d, dtype, vector_aligned(in, out, d, dtype), cus, have_ws,
+                        !(flags & GA_ROUND_INTERMEDIATES), &p)) != GA_OK)
         return st;
     p.flags = flags;
     return launch_gelu(in, out, T, d, dtype, z, live_rows, p, workspace, stream);

@@ -30,6 +30,14 @@ hipError_t launch_gelu_split(int dtype, int waves, int vec_per_lane, int splits,
                              int32_t T, int32_t d, int32_t nvec, float z, const int32_t *live, void *workspace,
                              uint32_t spin_limit, hipStream_t stream);
 
+// Replicated-statistics path for few rows: REP (2, 4, 8) workgroups per row,
+// each reducing the whole gate row itself and applying its REP-th share;
+// grid = gelu_rep_grid(T, REP) (rows rounded up to groups of 8).
+bool gelu_rep_available(int dtype, int waves, int vec_per_lane, int rep);
+int64_t gelu_rep_grid(int64_t T, int rep);
+hipError_t launch_gelu_rep(int dtype, int waves, int vec_per_lane, int rep, const void *in, void *out, int32_t T,
+                           int32_t d, int32_t nvec, float z, const int32_t *live, hipStream_t stream);
+
 // Packed-rows path for short rows: ROWS_BLOCK threads per workgroup,
 // lanes_per_row in {4, 8, 16, 32} lanes per row, vec_per_lane in {1, 2, 4};
 // grid = ceil(T / (ROWS_BLOCK / lanes_per_row)).  nvec: the row's 16-byte

@@ -76,7 +76,10 @@ typedef struct {
                               2: unaligned path (rows off 16-byte alignment; gelu: per
                                  row, the elementwise ops: flat over the output),
                               3: gelu packed-rows path (short rows of any alignment,
-                              several rows per wavefront) */
+                              several rows per wavefront),
+                              4: gelu replicated-statistics path (few rows: `splits`
+                                 workgroups per row each reduce the whole gate row and
+                                 apply their share; 16-byte rows, no workspace) */
     int32_t waves_per_row; /* gelu: 64-lane wavefronts per workgroup (1,2,4,8,16) */
     int32_t per_lane;      /* gelu vector path: 16-byte gate vectors per lane (1,2,4,8;
                               split rows 1,2,4); gelu element path: gate elements per
@@ -88,8 +91,9 @@ typedef struct {
                               statistics, a vector (a chunk) at a time (fewer registers, more
                               rows resident); split rows: 0 only */
     int32_t block;         /* threads per workgroup */
-    int32_t splits;        /* gelu vector path: workgroups sharing one row; 1, or 2, 4, 8,
-                              16 (needs a workspace, see ga_gelu_and_mul_sparse_ws) */
+    int32_t splits;        /* gelu vector path: workgroups sharing one row; 1, or 2 .. 16
+                              (needs a workspace, see ga_gelu_and_mul_sparse_ws); gelu
+                              replicated-statistics path: 2, 4 or 8 */
     int64_t grid;          /* workgroups launched (silu: from the capacity M only) */
     uint32_t spin_limit;   /* split rows: rounds of polls of the row's partials before a
                               workgroup computes the whole row's statistics itself */

@@ -130,6 +130,81 @@ def choose_split(table, T, nvec):
     return (w, v, -(-nvec // (w * 64 * v)))
 
 
+# Replicated-statistics table (--rep, sweeps run in the few-rows mode: every
+# row geometry, every split plan and every replicated plan of a shape):
+# candidates c < 60 are replicated geometries, c = (waves index * 4 +
+# vectors-per-lane index) * 3 + (log2 REP - 1) with REP 2, 4, 8; c = 60 is the
+# fastest row geometry (no split), c = 61 the fastest split plan.
+REP_FACTORS = (2, 4, 8)
+REP_GEOS = [(w, v, r) for w in WAVES for v in PER_LANE for r in REP_FACTORS]
+REP_ROW, REP_SPLIT = len(REP_GEOS), len(REP_GEOS) + 1
+
+
+def read_fewrows_sweeps(paths):
+    """(T, nvec) -> {candidate: time}; each plan's runs averaged first, then
+    the row and split plans reduced to their fastest."""
+    acc = collections.defaultdict(list)
+    for path in paths:
+        for line in open(path):
+            if not line[:1].isdigit():
+                continue
+            f = line.strip().split(",")
+            T, nvec, w, v, late, us, splits, kind = (int(f[0]), int(f[2]), int(f[3]), int(f[4]), int(f[5]),
+                                                     float(f[6]), int(f[7]), int(f[8]))
+            acc[(T, nvec, kind, w, v, late, splits)].append(us)
+    times = collections.defaultdict(dict)
+    for (T, nvec, kind, w, v, late, splits), ts in acc.items():
+        t = sum(ts) / len(ts)
+        if kind == 4:
+            key = REP_GEOS.index((w, v, splits))
+        else:
+            key = REP_ROW if splits == 1 else REP_SPLIT
+        if key not in times[(T, nvec)] or t < times[(T, nvec)][key]:
+            times[(T, nvec)][key] = t
+    return times
+
+
+def build_rep(times):
+    Ts = sorted({k[0] for k in times})
+    Ns = sorted({k[1] for k in times})
+    loss = {}
+    for T in Ts:
+        for n in Ns:
+            g = times.get((T, n), {})
+            row = [NOT_RUN] * (REP_SPLIT + 1)
+            if g:
+                best = min(g.values())
+                for c, t in g.items():
+                    row[c] = min(254, int(round((t / best - 1.0) * 400.0)))
+            loss[(T, n)] = row
+    return Ts, Ns, loss
+
+
+def rep_valid(c, nvec, with_workspace=True):
+    if c == REP_ROW:
+        return True
+    if c == REP_SPLIT:
+        return with_workspace
+    w, v, r = REP_GEOS[c]
+    return w * 64 * v >= nvec
+
+
+def choose_rep(table, T, nvec, with_workspace=True):
+    """None (not a replicated plan) or (waves, vectors per lane, REP); outside
+    the table's grid, None."""
+    Ts, Ns = table[0], table[1]
+    if T < 1 or T > Ts[-1] or nvec < Ns[0] or nvec > Ns[-1]:
+        return None
+    sc = scores(table, T, nvec, [c for c in range(REP_SPLIT + 1) if rep_valid(c, nvec, with_workspace)])
+    best = None
+    for c, x in enumerate(sc):
+        if x is not None and (best is None or x < sc[best]):
+            best = c
+    if best is None or best >= REP_ROW:
+        return None
+    return REP_GEOS[best]
+
+
 def build(times):
     Ts = sorted({k[0] for k in times})
     Ns = sorted({k[1] for k in times})
@@ -149,8 +224,14 @@ def build(times):
 
 def write_inc(path, Ts, Ns, loss, sources, prefix="kPlan"):
     P = prefix
-    kind = {"kUna": "the unaligned path", "kSplit": "few-row shapes (the split path)"}.get(P, "the vector path")
-    if P == "kSplit":
+    kind = {"kUna": "the unaligned path", "kSplit": "few-row shapes (the split path)",
+            "kRep": "few-row shapes (row, split and replicated-statistics plans)"}.get(P, "the vector path")
+    if P == "kRep":
+        cand = ["// candidate c < 60: replicated-statistics geometries, c = (waves index * 4 + vectors-per-lane",
+                "// index) * 3 + (log2 REP - 1), waves 1, 2, 4, 8, 16, vectors per lane 1, 2, 4, 8, REP 2, 4, 8;",
+                "// c = 60: the fastest one-row-per-workgroup geometry; c = 61: the fastest split plan."]
+        ng = REP_SPLIT + 1
+    elif P == "kSplit":
         cand = ["// candidate c < 15: split-kernel chunks of waves 1, 2, 4, 8, 16 (index c / 3) times",
                 "// vectors per lane 1, 2, 4 (index c % 3), ceil(nvec / chunk) splits; c = 15: no split",
                 "// (the fastest one-row-per-workgroup geometry)."]
@@ -317,6 +398,35 @@ def main(argv):
         i = argv.index("--prefix")
         prefix = argv[i + 1]
         del argv[i:i + 2]
+    rep = "--rep" in argv
+    if rep:
+        argv.remove("--rep")
+        prefix = "kRep"
+        if check:
+            table = read_inc(argv[1], prefix)
+            times = read_fewrows_sweeps(argv[2:])
+            ratios = []
+            for (T, n), g in sorted(times.items()):
+                c = choose_rep(table, T, n)
+                key = REP_GEOS.index(c) if c is not None else None
+                if key is None:
+                    # not replicated: the row or split choice (the other tables'); rated by the better of the two
+                    t = min(g.get(REP_ROW, float("inf")), g.get(REP_SPLIT, float("inf")))
+                else:
+                    t = g.get(key, float("nan"))
+                ratios.append(t / min(g.values()))
+                print(f"T={T:4d} nvec={n:5d} choice {'row/split' if c is None else 'W%d V%d REP%d' % c}:"
+                      f" {ratios[-1]:.3f} of the best")
+            ok = sorted(x for x in ratios if x == x)
+            print(f"{len(ok)} shapes: median {ok[len(ok) // 2]:.4f}, mean {sum(ok) / len(ok):.4f}, "
+                  f"90th percentile {ok[int(0.9 * len(ok))]:.4f}, worst {ok[-1]:.4f}, "
+                  f"> 3 % slower: {sum(x > 1.03 for x in ok)}, not measured: {len(ratios) - len(ok)}")
+            return 0
+        out, sources = argv[1], argv[2:]
+        Ts, Ns, loss = build_rep(read_fewrows_sweeps(sources))
+        write_inc(out, Ts, Ns, loss, [p.split("/")[-1] for p in sources], prefix)
+        print(f"{out}: {len(Ts)} row counts x {len(Ns)} row sizes x {REP_SPLIT + 1} candidates")
+        return 0
     split = "--split" in argv
     if split:
         argv.remove("--split")

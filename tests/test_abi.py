@@ -114,13 +114,15 @@ def test_stream_xor_rows_checks():
 def test_gelu_planner_known_shapes():
     # (T, d) -> (path, waves per workgroup, vectors per lane, up loaded late, splits)
     want = {(2048, 16384): (0, 8, 4, 1, 1), (2048, 32768): (0, 16, 4, 1, 1), (4096, 65536): (0, 16, 8, 1, 1),
-            # few long rows split over workgroups (with a workspace)
-            (1, 32768): (0, 4, 2, 0, 8), (64, 16384): (0, 4, 2, 0, 4), (64, 32768): (0, 8, 2, 0, 4),
-            (128, 32768): (0, 8, 2, 0, 4), (64, 65536): (0, 8, 4, 0, 4)}
+            # few rows: replicated statistics (path 4) or split rows (path 0, with a workspace)
+            (1, 32768): (4, 16, 4, 0, 8), (64, 16384): (4, 8, 4, 0, 4), (64, 32768): (4, 8, 8, 0, 4),
+            (128, 32768): (4, 16, 4, 0, 2), (1, 8192): (4, 8, 2, 0, 8), (8, 32768): (0, 4, 2, 0, 8),
+            (64, 65536): (0, 8, 4, 0, 4)}
     for (T, d), w in want.items():
         p = ga.plan_gelu_and_mul_sparse(T, d, BF16)
         assert (p.path, p.waves_per_row, p.per_lane, p.up_late, p.splits) == w, (T, d, p.as_dict())
-        assert p.block == 64 * p.waves_per_row and p.grid == T * p.splits
+        grid = (T + 7) // 8 * 8 * p.splits if p.path == 4 else T * p.splits
+        assert p.block == 64 * p.waves_per_row and p.grid == grid
 
 
 def test_row_geometry_follows_the_measured_table():
@@ -130,12 +132,17 @@ def test_row_geometry_follows_the_measured_table():
     shapes; every choice is a compiled geometry covering the row."""
     import planner_rule as mt
     table = mt.read_inc(os.path.join(ROOT, "gated_activation_amd", "csrc", "planner_table.inc"))
+    rep = mt.read_inc(os.path.join(ROOT, "gated_activation_amd", "csrc", "planner_table_rep.inc"), "kRep")
     Ts = sorted(set(table[0]) | {1, 7, 33, 100, 300, 700, 900, 1800, 2500, 3500, 5000, 10000, 20000, 65535})
     Ns = sorted(set(table[1]) | {33, 63, 65, 72, 88, 140, 200, 300, 420, 600, 700, 1100, 1376, 1664, 1792,
                                  2368, 2752, 3200, 3800, 4500, 8191})
     for T in Ts:
         for n in Ns:
             p = ga.plan_gelu_and_mul_sparse(T, n * 8, BF16, with_workspace=False)
+            r = mt.choose_rep(rep, T, n, with_workspace=False)
+            if r is not None:     # few rows: replicated statistics (checked in the test below)
+                assert p.path == 4, (T, n, p.as_dict())
+                continue
             assert p.path == 0 and p.splits == 1
             got = (p.waves_per_row, p.per_lane, p.up_late)
             assert p.waves_per_row * 64 * p.per_lane >= n
@@ -172,11 +179,15 @@ def test_split_choice_follows_the_measured_table():
     grid; outside the table (more rows, shorter rows) nothing is split."""
     import planner_rule as mt
     table = mt.read_inc(os.path.join(ROOT, "gated_activation_amd", "csrc", "planner_table_split.inc"), "kSplit")
+    rep = mt.read_inc(os.path.join(ROOT, "gated_activation_amd", "csrc", "planner_table_rep.inc"), "kRep")
     Ts = sorted(set(table[0]) | {3, 5, 12, 40, 72, 100, 112, 200, 224})
     Ns = sorted(set(table[1]) | {1100, 1400, 1700, 2047, 2049, 2200, 2816, 3328, 4608, 5632, 7680, 8191})
     for T in Ts:
         for n in Ns:
             p = ga.plan_gelu_and_mul_sparse(T, n * 8, BF16, with_workspace=True)
+            if mt.choose_rep(rep, T, n, with_workspace=True) is not None:
+                assert p.path == 4, (T, n, p.as_dict())
+                continue
             want = mt.choose_split(table, T, n)
             if want is None:
                 assert p.splits == 1, (T, n, p.as_dict())
@@ -191,7 +202,43 @@ def test_split_choice_follows_the_measured_table():
             chunk = p.waves_per_row * 64 * p.per_lane
             assert chunk * p.splits >= n > chunk * (p.splits - 1)
     for T, n in ((257, 8192), (4096, 8192), (8, 1023), (1, 1024), (64, 1024)):
-        assert ga.plan_gelu_and_mul_sparse(T, n * 8, BF16, with_workspace=True).splits == 1
+        p = ga.plan_gelu_and_mul_sparse(T, n * 8, BF16, with_workspace=True)
+        assert p.path == 4 or p.splits == 1, (T, n, p.as_dict())     # no split rows here
+
+
+def test_rep_choice_follows_the_measured_table():
+    """Few rows: whether and how the planner replicates the statistics is the
+    replicated table's choice under the interpolation rule, checked against
+    the independent Python statement in tests/planner_rule.py on and off the
+    grid, with and without a workspace (without one the split plans are not
+    candidates); every replicated geometry covers the row."""
+    import planner_rule as mt
+    rep = mt.read_inc(os.path.join(ROOT, "gated_activation_amd", "csrc", "planner_table_rep.inc"), "kRep")
+    Ts = sorted(set(rep[0]) | {3, 5, 12, 40, 80, 112, 160, 224, 257, 300})
+    Ns = sorted(set(rep[1]) | {255, 300, 640, 900, 1280, 2500, 3584, 5120, 7000})
+    n_rep = 0
+    for T in Ts:
+        for n in Ns:
+            for ws in (True, False):
+                p = ga.plan_gelu_and_mul_sparse(T, n * 8, BF16, with_workspace=ws)
+                want = mt.choose_rep(rep, T, n, with_workspace=ws)
+                if p.path == 4:
+                    n_rep += 1
+                    got = (p.waves_per_row, p.per_lane, p.splits)
+                    assert p.waves_per_row * 64 * p.per_lane >= n and p.up_late == 0
+                    assert p.grid == (T + 7) // 8 * 8 * p.splits and p.block == 64 * p.waves_per_row
+                    if got != want:
+                        valid = [c for c in range(mt.REP_SPLIT + 1) if mt.rep_valid(c, n, ws)]
+                        sc = mt.scores(rep, T, n, valid)
+                        assert want is not None and abs(sc[mt.REP_GEOS.index(got)] - sc[mt.REP_GEOS.index(want)]) < 1e-9, \
+                            (T, n, ws, got, want)
+                else:
+                    assert want is None, (T, n, ws, p.as_dict(), want)
+    assert n_rep > 50
+    # beyond 256 rows, beyond the table's row sizes and off 16-byte alignment: never replicated
+    for T, d, aligned in ((257, 8192, True), (1, 2040, True), (1, 65544, True), (4, 8192, False)):
+        if d <= 65536:
+            assert ga.plan_gelu_and_mul_sparse(T, d, BF16, aligned=aligned).path != 4
 
 
 def test_planner_paths_by_row_size():
@@ -207,9 +254,11 @@ def test_planner_paths_by_row_size():
         assert (p.path, p.lanes_per_row, p.per_lane) == (3, g, v), (d, aligned, p.as_dict())
     assert ga.plan_gelu_and_mul_sparse(4096, 257, BF16).path == 2      # 33 vectors: unaligned path
     assert ga.plan_gelu_and_mul_sparse(4096, 127, F32).path == 3       # 32 vectors of fp32
-    # without a workspace the rows are never split
+    # without a workspace the rows are never split (few rows may still replicate the statistics)
     p = ga.plan_gelu_and_mul_sparse(1, 32768, BF16, with_workspace=False)
-    assert (p.splits, p.waves_per_row, p.per_lane) == (1, 16, 4)
+    assert (p.path, p.splits, p.waves_per_row, p.per_lane) == (4, 8, 16, 4)
+    p = ga.plan_gelu_and_mul_sparse(300, 32768, BF16, with_workspace=False)
+    assert (p.path, p.splits) == (0, 1)
     # rows off 16-byte alignment: the unaligned path (its geometry: see the table test)
     p = ga.plan_gelu_and_mul_sparse(7, 8191, F16)            # odd d
     assert p.path == 2 and p.splits == 1 and p.waves_per_row * 64 * p.per_lane >= (8191 + 7) // 8
@@ -227,8 +276,7 @@ def test_workspace_size_and_split_plan_checks():
     assert L.ga_gelu_and_mul_sparse_workspace_bytes(0) == 0
     assert L.ga_gelu_and_mul_sparse_workspace_bytes(1) == 256
     assert L.ga_gelu_and_mul_sparse_workspace_bytes(64) == 64 * 256
-    split = ga.plan_gelu_and_mul_sparse(8, 16384, BF16)
-    assert split.splits == 4
+    split = ga.Plan(path=0, waves_per_row=4, per_lane=2, splits=4, block=256)
     call = lambda p, T=8, ws=WS, nb=WS_BYTES, d=16384: L.ga_gelu_and_mul_sparse_with_plan(  # noqa: E731
         IN, OUT, T, d, BF16, Z, None, ctypes.byref(p), ws, nb, None)
     assert call(split, ws=None) == EINVAL                                # needs a workspace
@@ -333,6 +381,8 @@ def test_gelu_planner_covers_every_d(dt):
             if p.path == 3:   # packed rows: 256 lanes, 256 / lanes_per_row rows per workgroup
                 assert p.block == 256 and p.grid == -(-3 // (256 // p.lanes_per_row))
                 assert d * es <= 32 * 16
+            elif p.path == 4:  # replicated statistics: rows rounded up to a group of 8
+                assert aligned and p.block == p.waves_per_row * 64 and p.grid == 8 * p.splits
             else:
                 assert d * es > 32 * 16
                 assert p.block == p.waves_per_row * 64 and p.grid == 3 * p.splits
@@ -358,8 +408,21 @@ def test_gelu_with_plan_rejects_bad_geometry():
     assert L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 64, BF16, Z, None, ctypes.byref(p), WS, WS_BYTES, None) == EUNSUP
     p = ga.Plan(path=1, waves_per_row=16, per_lane=2, block=1024, grid=1)
     assert L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 64, BF16, Z, None, ctypes.byref(p), WS, WS_BYTES, None) == EUNSUP
-    p = ga.Plan(path=4, waves_per_row=1, per_lane=4, block=64, grid=1)
+    p = ga.Plan(path=5, waves_per_row=1, per_lane=4, block=64, grid=1)
     assert L.ga_gelu_and_mul_sparse_with_plan(IN, OUT, 0, 64, BF16, Z, None, ctypes.byref(p), WS, WS_BYTES, None) == EINVAL
+    # replicated statistics: REP 2, 4 or 8, up with the gate, no round-trip form, covering the row; no workspace
+    rep = lambda d=64, **kw: L.ga_gelu_and_mul_sparse_with_plan(  # noqa: E731
+        IN, OUT, 0, d, BF16, Z, None, ctypes.byref(ga.Plan(path=4, block=64 * kw.get("waves_per_row", 1), **kw)),
+        None, 0, None)
+    assert rep(waves_per_row=1, per_lane=1, splits=2) == OK and rep(waves_per_row=16, per_lane=8, splits=8, d=65536) == OK
+    assert rep(waves_per_row=1, per_lane=1, splits=1) == EUNSUP and rep(waves_per_row=1, per_lane=1, splits=3) == EUNSUP
+    assert rep(waves_per_row=1, per_lane=1, splits=16) == EUNSUP
+    assert rep(waves_per_row=1, per_lane=1, splits=2, up_late=1) == EUNSUP
+    assert rep(waves_per_row=1, per_lane=1, splits=2, flags=ga.GA_ROUND_INTERMEDIATES) == EUNSUP
+    assert rep(waves_per_row=1, per_lane=1, splits=2, d=1024) == EUNSUP          # covers 64 < 128 vectors
+    assert L.ga_gelu_and_mul_sparse_with_plan(ctypes.c_void_p(0x7F0000000002), OUT, 0, 64, BF16, Z, None,
+                                              ctypes.byref(ga.Plan(path=4, waves_per_row=1, per_lane=1, splits=2)),
+                                              None, 0, None) == EUNSUP       # 16-byte rows and bases only
     # packed rows: lanes_per_row in {4, 8, 16, 32}, 1, 2 or 4 vectors per lane, covering d
     rows = lambda g, v, d=256, **kw: L.ga_gelu_and_mul_sparse_with_plan(  # noqa: E731
         IN, OUT, 0, d, BF16, Z, None, ctypes.byref(ga.Plan(path=3, lanes_per_row=g, per_lane=v, **kw)),

@@ -136,8 +136,9 @@ def test_planner_geometry_at_its_shapes(T, d):
     """The default call at shapes across the planner's geometry choices, on
     sampled rows (first, last and scattered) against the oracle."""
     p = ga.plan_gelu_and_mul_sparse(T, d, BF16)
-    assert (p.path, p.splits) == (0, 1)
-    print(f"T={T} d={d}: waves {p.waves_per_row}, vectors per lane {p.per_lane}, up late {p.up_late}", flush=True)
+    assert (p.path, p.splits) == (0, 1) or p.path == 4
+    print(f"T={T} d={d}: path {p.path}, waves {p.waves_per_row}, vectors per lane {p.per_lane}, "
+          f"up late {p.up_late}, splits {p.splits}", flush=True)
     x = synth.gelu_offset_rows(T, d, seed=T * 7 + d)
     rng = np.random.default_rng(T + d)
     sample = list(range(16)) + list(range(T - 16, T)) + list(rng.integers(0, T, 32))
@@ -419,15 +420,18 @@ def test_subnormal_outputs_are_rounded_not_flushed(dt, tiny):
 
 
 # ---------------------------------------------------------------------------
-# Few long rows split over several workgroups (workspace entry point).
+# Few long rows shared by several workgroups: split rows (partial statistics
+# exchanged through the workspace) or replicated statistics, as planned.
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("T,d", [(1, 16384), (8, 16384), (64, 16384), (1, 32768), (64, 32768),
-                                 (128, 32768), (3, 65536)])
-def test_split_rows_default_plan(T, d):
-    assert ga.plan_gelu_and_mul_sparse(T, d, ga.GA_BF16).splits > 1
+                                 (128, 32768), (3, 65536), (8, 32768), (16, 32768), (4, 65536)])
+def test_few_rows_default_plan(T, d):
+    p = ga.plan_gelu_and_mul_sparse(T, d, ga.GA_BF16)
+    assert p.splits > 1
+    print(f"T={T} d={d}: path {p.path} splits {p.splits}", flush=True)
     x = synth.gelu_large(T, d)
-    run_and_check(x, BF16, Z95, label=f"split T{T} d{d}")
+    run_and_check(x, BF16, Z95, label=f"few rows T{T} d{d} path{p.path}")
 
 
 def _tiling_plans(nvec):
@@ -456,10 +460,13 @@ def test_split_rows_every_split_count():
 def test_split_rows_forced_fallback():
     """With a poll bound of zero every workgroup computes the whole row's
     statistics itself: the result must still match the oracle."""
-    x = synth.gelu_large(8, 16384)
-    p = ga.plan_gelu_and_mul_sparse(8, 16384, ga.GA_BF16)
+    x = synth.gelu_large(8, 32768)
+    p = ga.plan_gelu_and_mul_sparse(8, 32768, ga.GA_BF16)
+    assert p.path == 0 and p.splits > 1
     p.spin_limit = 0
     run_and_check(x, BF16, Z95, plan=p, label="fallback")
+    q = ga.Plan(path=0, waves_per_row=4, per_lane=2, splits=4, block=256, spin_limit=0)
+    run_and_check(synth.gelu_large(8, 16384), BF16, Z95, plan=q, label="fallback 4 splits")
 
 
 def test_split_workspace_reused_across_shapes():
@@ -495,21 +502,24 @@ def test_split_rows_live_bound(live):
     run_and_check(x, BF16, Z95, live=live, label=f"split live {live}")
 
 
-@pytest.mark.parametrize("dt", [F16, F32], ids=["f16", "f32"])
-def test_split_rows_other_dtypes(dt):
-    x = synth.gelu_iid(4, 16384, seed=123, dtype=dt, gate_std=2.0)
-    assert ga.plan_gelu_and_mul_sparse(4, 16384, dt).splits > 1
-    run_and_check(x, dt, Z95, label=f"split dt{dt}")
+@pytest.mark.parametrize("dt,d", [(F16, 32768), (F32, 16384), (F16, 16384)], ids=["f16", "f32", "f16-rep"])
+def test_split_rows_other_dtypes(dt, d):
+    x = synth.gelu_iid(4, d, seed=123, dtype=dt, gate_std=2.0)
+    p = ga.plan_gelu_and_mul_sparse(4, d, dt)
+    assert p.splits > 1 and p.path == (4 if d * (4 if dt == F32 else 2) == 32768 else 0)
+    run_and_check(x, dt, Z95, label=f"few rows dt{dt} d{d} path{p.path}")
 
 
 def test_split_rows_constant_and_edge_rows():
     """Constant rows still give exact zeros through the partial combine;
     near-constant N(100, 0.01) and Student-t rows match the oracle."""
+    split = ga.Plan(path=0, waves_per_row=4, per_lane=2, splits=4, block=256)
     for dt in (F16, BF16):
         x = synth.edge_rows(10, 16384, dt, seed=5)
         assert ga.plan_gelu_and_mul_sparse(10, 16384, dt).splits > 1
         for z in (0.0, Z95):
-            run_and_check(x, dt, z, label=f"split edge dt{dt} z{z}")
+            run_and_check(x, dt, z, label=f"few rows edge dt{dt} z{z}")
+            run_and_check(x, dt, z, plan=split, label=f"split edge dt{dt} z{z}")
     T, d = 5, 32768
     vals = np.array([0.0, 100.0, -3.5, 7.25, -250.0])
     xb = np.concatenate([synth.to_bits(np.repeat(vals[:, None], d, 1), BF16),
@@ -517,3 +527,45 @@ def test_split_rows_constant_and_edge_rows():
     out = ga.gelu_and_mul_sparse(to_device(xb, BF16), 0.0)
     torch.cuda.synchronize()
     assert np.all(decode(bits_of(out, BF16), BF16) == 0.0)
+
+
+# Few rows, statistics replicated: `splits` workgroups per row, each reducing
+# the whole gate row and applying its share (no workspace).
+def _rep_plans(d, dt):
+    per16 = 4 if dt == F32 else 8
+    nvec = d // per16
+    for w in (1, 2, 4, 8, 16):
+        for v in (1, 2, 4, 8):
+            if nvec <= w * 64 * v < 8 * nvec:
+                for rep in (2, 4, 8):
+                    yield ga.Plan(path=4, waves_per_row=w, per_lane=v, splits=rep, block=64 * w)
+
+
+@pytest.mark.parametrize("dt,d", [(BF16, 8192), (BF16, 2048), (F16, 8192), (F32, 4096), (BF16, 16384)],
+                         ids=["bf16-8192", "bf16-2048", "f16-8192", "f32-4096", "bf16-16384"])
+def test_replicated_statistics_every_geometry(dt, d):
+    """Every replicated-statistics geometry matches the oracle, writes only
+    its rows (T = 13: a ragged group of 8 rows), and is bit-identical to the
+    one-row kernel with the same waves and vectors (the same reduction), so
+    all shares of a row used the same cutoff."""
+    T = 13
+    x = synth.gelu_offset_rows(T, d, seed=900 + d + dt, dtype=dt)
+    xd = to_device(x, dt)
+    plans = list(_rep_plans(d, dt))
+    assert plans
+    for p in plans:
+        run_and_check(x, dt, Z95, plan=p, label=f"rep dt{dt} d{d} w{p.waves_per_row} v{p.per_lane} s{p.splits}")
+        one = ga.Plan(path=0, waves_per_row=p.waves_per_row, per_lane=p.per_lane, up_late=0, block=p.block)
+        a = bits_of(ga.gelu_and_mul_sparse(xd, Z95, plan=p), dt)
+        b = bits_of(ga.gelu_and_mul_sparse(xd, Z95, plan=one), dt)
+        torch.cuda.synchronize()
+        assert np.array_equal(a, b), (p.waves_per_row, p.per_lane, p.splits)
+
+
+@pytest.mark.parametrize("live", [0, 1, 5, 8, 9, 13, 100, -2])
+def test_replicated_statistics_live_rows(live):
+    """Live counts inside, at and past a group of 8 rows leave the other rows
+    untouched."""
+    x = synth.gelu_offset_rows(13, 8192, seed=31)
+    p = ga.Plan(path=4, waves_per_row=8, per_lane=2, splits=4, block=512)
+    run_and_check(x, BF16, Z95, plan=p, live=live, label=f"rep live {live}")

@@ -149,7 +149,8 @@ def test_default_workspace_survives_capture_and_later_calls():
     xq_b = synth.gelu_large(Tq, dq)
     ref_q, st_q = o.gelu_and_mul_sparse(xq_b, BF16, Z95, want_stats=True)
     xb_b = synth.gelu_large(Tb, db)
-    assert ga.plan_gelu_and_mul_sparse(Tq, dq, ga.GA_BF16).splits > 1
+    pq = ga.plan_gelu_and_mul_sparse(Tq, dq, ga.GA_BF16)
+    assert pq.path == 0 and pq.splits > 1                 # split rows: the workspace is used
     assert ga.plan_gelu_and_mul_sparse(Tb, db, ga.GA_BF16).splits == 1
     s = torch.cuda.Stream()
     key = (torch.cuda.current_device(), s.cuda_stream)
@@ -188,11 +189,12 @@ def test_default_workspace_survives_capture_and_later_calls():
 def test_reserved_workspace_is_the_one_a_capture_uses():
     """reserve_workspace(stream=s) before capture: the captured few-row call
     uses that workspace (zeroed outside the graph) and splits its rows."""
-    Tq, dq = 4, 16384
+    Tq, dq = 4, 32768
     o = oracle.get()
     xq_b = synth.gelu_large(Tq, dq)
     ref_q, st_q = o.gelu_and_mul_sparse(xq_b, BF16, Z95, want_stats=True)
-    assert ga.plan_gelu_and_mul_sparse(Tq, dq, ga.GA_BF16).splits > 1
+    pq = ga.plan_gelu_and_mul_sparse(Tq, dq, ga.GA_BF16)
+    assert pq.path == 0 and pq.splits > 1
     s = torch.cuda.Stream()
     ws = ga.reserve_workspace(stream=s)
     assert ws.numel() == ga.WORKSPACE_BYTES

@@ -18,7 +18,8 @@ def _body(path):
 def test_committed_tables_regenerate_from_the_sweep_summaries(tmp_path):
     for inc, summary, flags in (("planner_table.inc", "planner_sweep_vector_bf16.csv", []),
                                 ("planner_table_una.inc", "planner_sweep_unaligned_bf16.csv", ["--prefix", "kUna"]),
-                                ("planner_table_split.inc", "planner_sweep_split_bf16.csv", ["--split"])):
+                                ("planner_table_split.inc", "planner_sweep_split_bf16.csv", ["--split"]),
+                                ("planner_table_rep.inc", "planner_sweep_fewrows_bf16.csv", ["--rep"])):
         out = tmp_path / inc
         assert mt.main(["planner_rule.py"] + flags + [str(out), os.path.join(PROFILES, summary)]) == 0
         assert _body(str(out)) == _body(os.path.join(CSRC, inc)), inc
@@ -104,3 +105,33 @@ def test_packed_check_reads_sweeps_and_asks_the_library(tmp_path, capsys):
     assert "nvec=  6 planner G8 V1" in out and "1.000 of the best (G8 V1" in out
     assert "nvec= 24 planner G32 V1" in out and "1.050 of the best (G16 V2" in out
     assert "2 shapes:" in out and "worst 1.0500" in out
+
+
+def test_rep_table_builder_round_trip(tmp_path):
+    """Few-rows sweep lines (ninth column: the path, 4 for replicated plans)
+    become a table whose rule picks the fastest replicated geometry, or none
+    where a row or split plan is faster; without a workspace a split plan is
+    not a candidate."""
+    lines = []
+    # (T, nvec): (fastest replicated geometry or None, time of the best row plan, of the best split plan)
+    cases = {(1, 1024): ((8, 2, 8), 3.0, 3.5), (1, 4096): (None, 7.0, 6.5), (64, 1024): ((8, 2, 4), 3.5, 4.0),
+             (64, 4096): (None, 5.0, 6.0)}
+    for (T, n), (g, row_us, split_us) in cases.items():
+        lines.append(f"{T},{n * 8},{n},16,4,1,{row_us},1,0")
+        lines.append(f"{T},{n * 8},{n},8,8,0,{row_us + 1},1,0")
+        lines.append(f"{T},{n * 8},{n},4,2,0,{split_us},{-(-n // 512)},0")
+        for w, v, r in mt.REP_GEOS:
+            if n <= w * 64 * v < 8 * n:
+                us = 2.5 if (w, v, r) == g else max(row_us, split_us) + 0.5
+                lines.append(f"{T},{n * 8},{n},{w},{v},0,{us},{r},4")
+    csv = tmp_path / "fewrows.csv"
+    csv.write_text("\n".join(lines) + "\ndone\n")
+    inc = tmp_path / "rep.inc"
+    assert mt.main(["planner_rule.py", "--rep", str(inc), str(csv)]) == 0
+    table = mt.read_inc(str(inc), "kRep")
+    for (T, n), (g, row_us, split_us) in cases.items():
+        assert mt.choose_rep(table, T, n) == g, (T, n)
+    # (1, 4096): the split plan wins with a workspace; without one the row plan is
+    # still faster than every replicated geometry there
+    assert mt.choose_rep(table, 1, 4096, with_workspace=False) is None
+    assert table[2][(1, 1024)][mt.REP_ROW] > 0 and table[2][(1, 4096)][mt.REP_SPLIT] == 0
