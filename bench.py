@@ -53,7 +53,66 @@ def parse():
                    help="approximate CPU time spent on the oracle baseline, half on one thread "
                         "and half over the host cores (0 = skip)")
     p.add_argument("--no-side", action="store_true", help="skip the ceiling, silu and sweep measurements")
+    p.add_argument("--clock-warm-ms", type=float, default=300.0,
+                   help="untimed headline launches for about this long before the warmup steps, so the "
+                        "timed steps run at steady-state clocks (0 = none)")
+    p.add_argument("--markers", action="store_true",
+                   help="wrap each measured item in a roctx range (for a rocprofv3 --marker-trace run)")
+    p.add_argument("--no-sweep", action="store_true", help="skip the sweep and the sibling ops")
+    p.add_argument("--profile-cases", type=int, default=0, metavar="N",
+                   help="instead of the benchmark: launch each of the counter cases N times (and the "
+                        "same-pattern streaming kernel N times where it applies), printing one 'D <label>' "
+                        "line per launch, for rocprofv3 counter runs joined by dispatch order")
     return p.parse_args()
+
+
+class Markers:
+    """roctx ranges around the measured items, so a rocprofv3 kernel trace
+    taken with --marker-trace can be split per item; no-ops unless enabled."""
+
+    def __init__(self, enabled):
+        self.lib = None
+        if not enabled:
+            return
+        import ctypes
+        path = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib", "librocprofiler-sdk-roctx.so")
+        self.lib = ctypes.CDLL(path)
+        self.lib.roctxRangePushA.argtypes = [ctypes.c_char_p]
+        self.lib.roctxRangePushA.restype = ctypes.c_int
+        self.lib.roctxRangePop.argtypes = []
+        self.lib.roctxRangePop.restype = ctypes.c_int
+
+    def push(self, label):
+        if self.lib is not None:
+            self.lib.roctxRangePushA(label.encode())
+
+    def pop(self):
+        if self.lib is not None:
+            self.lib.roctxRangePop()
+
+
+# The pages' own figures, quoted beside the measurement for context; none of
+# them is a target (another machine, another workload).
+CONTEXT = {
+    "note": "figures printed on the source pages, for context only: not targets",
+    "megatron_silu_and_mul_bounded_gb200": {
+        "source": "Megatron-LM PR 6328, What changed and why / Measured gain / Where the time went",
+        "bytes_per_layer_MB": 9.44,
+        "us_per_layer_old_grid": 15.8,
+        "us_per_launch_old_to_new": [17.158, 7.644],
+        "bandwidth_floor_us_as_printed": 1.57,
+        "bandwidth_floor_us_recomputed": 1.552,
+        "measured_streaming_ceiling_TBps": 6.081,
+        "peer_elementwise_kernels_us": [1.26, 2.60],
+        "final_multiple_of_floor": 4.9,
+        "here": "silu_and_mul_bounded at live=2048 (9.44 MB) below",
+    },
+    "vllm_gelu_and_mul_sparse": {
+        "source": "vLLM PR 48498, Test Result (BF16 kernel performance)",
+        "published": "speed-ups over the compiled native path only (A100 geomean 2.59x over 42 shapes, "
+                     "B200 1.11-4.06x); no microseconds or GB/s",
+    },
+}
 
 
 def kernel_source_digest(sources=KERNEL_SOURCES):
@@ -107,6 +166,33 @@ def time_graph(fn, n_sets, steps, warmup, stream, per_graph=64):
     return start.elapsed_time(end) / (reps * per_graph)
 
 
+def time_graph_steps(fn, n_sets, steps, warmup, stream):
+    """ms per step over exactly `steps` calls recorded into one HIP graph and
+    replayed once between events, after `warmup` eager calls and one untimed
+    replay; synchronised on both sides."""
+    import torch
+    for i in range(warmup):
+        fn(i % n_sets)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(steps):
+            fn(i % n_sets)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        graph.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        graph.replay()
+        end.record(stream)
+    torch.cuda.synchronize()
+    del graph
+    return start.elapsed_time(end) / steps
+
+
 def time_calls(fn, n_sets, steps, warmup, stream, segments=1):
     """ms per call over exactly `steps` calls launched back to back on the
     stream, bracketed by synchronisations.  With segments > 1, events are also
@@ -146,6 +232,9 @@ def main():
     import synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.profile_cases > 0:
+        profile_cases(args.profile_cases)
+        return
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
@@ -164,7 +253,42 @@ def main():
     def gelu(i):
         ga.gelu_and_mul_sparse(xs[i], Z, out=outs[i])
 
-    ms, seg_ms = time_calls(gelu, n_sets, args.steps, args.warmup, stream, segments=5)
+    # The timed calls go straight to the C entry point with their arguments
+    # marshalled once, so the host issues a launch in about 2 us and the
+    # stream never waits for it (the binding's checks cost about 10 us per
+    # call, which a short timed region would see at its start).
+    # They run on a stream of their own (default priority), which the graph
+    # capture below needs (the device's default stream cannot be captured).
+    import ctypes
+    hs = torch.cuda.Stream(device=dev)
+    c_args = [(ctypes.c_void_p(xs[i].data_ptr()), ctypes.c_void_p(outs[i].data_ptr()), T, D, ga.GA_BF16,
+               ctypes.c_float(Z), None, ctypes.c_void_p(hs.cuda_stream)) for i in range(n_sets)]
+    statuses = []
+
+    def gelu_c(i):
+        statuses.append(ga.lib.ga_gelu_and_mul_sparse(*c_args[i]))
+
+    markers = Markers(args.markers)
+    # Steady-state clocks: the device ramps its clocks under load, and a short
+    # timed region would otherwise include the ramp.
+    warm_calls = 0
+    if args.clock_warm_ms > 0:
+        t_end = time.perf_counter() + args.clock_warm_ms * 1e-3
+        while time.perf_counter() < t_end:
+            for i in range(16):
+                gelu_c((warm_calls + i) % n_sets)
+            warm_calls += 16
+            torch.cuda.synchronize()
+    # The timed region: the K steps launched back to back on the stream,
+    # bracketed by synchronisations.  The same K steps recorded into a HIP
+    # graph and replayed once (after one untimed replay) are timed as well
+    # (graph_steps_us_per_call).
+    markers.push(f"headline T={T} d={D}")
+    with torch.cuda.stream(hs):
+        ms, seg_ms = time_calls(gelu_c, n_sets, args.steps, args.warmup, hs, segments=5)
+        ms_graph_steps = time_graph_steps(gelu_c, n_sets, args.steps, args.warmup, hs)
+    markers.pop()
+    assert statuses and all(st == ga.GA_OK for st in statuses), "gelu_and_mul_sparse returned an error"
     gbps = bytes_call / (ms * 1e-3) / 1e9
     gelu_out = outs[0].clone()      # kept for the parity check of the CPU leg
 
@@ -190,8 +314,12 @@ def main():
             "device": f"{props.name} ({getattr(props, 'gcnArchName', '?')}, {props.multi_processor_count} CUs)",
         },
         "us_per_call": round(ms * 1e3, 3),
-        # the same timed region in five consecutive segments (events only)
+        "timing": "HIP events on the launch stream around the K steps launched back to back, after W "
+                  "warmup steps",
+        "clock_warm": {"ms": args.clock_warm_ms, "untimed_calls": warm_calls},
+        # the timed K steps in five consecutive segments (events only)
         "segments_us_per_call": [round(x * 1e3, 3) for x in seg_ms],
+        "graph_steps_us_per_call": round(ms_graph_steps * 1e3, 3),
         "pct_of_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
         "roofline": {
             "bound": "hbm",
@@ -202,13 +330,16 @@ def main():
             "traffic": recorded_traffic(),
             "kernel": "gelu_sparse_vec_kernel<bf16, %d, %d>" % (plan.waves_per_row, plan.per_lane),
         },
+        "context": CONTEXT,
     }
 
     if not args.no_side:
         # ---- streaming ceiling: same access pattern, no arithmetic ----
         def xor(i):
             ga.stream_xor_rows(xs[i], out=outs[i])
+        markers.push(f"ceiling T={T} d={D}")
         ms_c = time_calls(xor, n_sets, args.steps, args.warmup, stream)
+        markers.pop()
         ceil_gbps = bytes_call / (ms_c * 1e-3) / 1e9
         result["copy_ceiling"] = {"GBps": round(ceil_gbps, 1), "us_per_call": round(ms_c * 1e3, 3),
                                   "pct_of_peak": round(100 * ceil_gbps / PEAK_HBM_GBPS, 2)}
@@ -231,12 +362,25 @@ def main():
                 ga.silu_and_mul_bounded(sxs[i], live, out=souts[i])
             # Short kernels: replayed from a graph (the decode setting the
             # op is built for), so Python launch cost is not measured.
+            markers.push(f"silu live={n_live}")
             ms_s = time_graph(silu, s_sets, args.steps, args.warmup, stream)
+            markers.pop()
             b = n_live * 3 * SILU_D * 2 + 4
             silu_res[f"live{n_live}"] = {"us_per_call": round(ms_s * 1e3, 3),
                                          "GBps": round(b / (ms_s * 1e-3) / 1e9, 1),
                                          "pct_of_peak": round(100 * b / (ms_s * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
                                          "bytes": b, "timing": "graph replay"}
+        # The same-pattern streaming kernel over only the live rows, replayed
+        # the same way: what a decode-size call allows at its size.
+        for n_live in (2048, 64):
+            def live_ceiling(i, n_live=n_live):
+                ga.stream_xor_rows(sxs[i][:n_live], out=souts[i][:n_live])
+            markers.push(f"silu ceiling live={n_live}")
+            ms_c = time_graph(live_ceiling, s_sets, args.steps, args.warmup, stream)
+            markers.pop()
+            rec = silu_res[f"live{n_live}"]
+            rec["ceiling_us_per_call"] = round(ms_c * 1e3, 3)
+            rec["pct_of_ceiling"] = round(100.0 * ms_c / (rec["us_per_call"] * 1e-3), 2)
         # The full buffer (live = M) moves 75 MB per call: the HBM-bound case.
         full = silu_res[f"live{SILU_M}"]
 
@@ -244,7 +388,9 @@ def main():
         # the same buffers, replayed the same way: what this shape allows.
         def silu_ceiling(i):
             ga.stream_xor_rows(sxs[i], out=souts[i])
+        markers.push(f"silu ceiling live={SILU_M}")
         ms_c = time_graph(silu_ceiling, s_sets, args.steps, args.warmup, stream)
+        markers.pop()
         full["ceiling_us_per_call"] = round(ms_c * 1e3, 3)
         full["pct_of_ceiling"] = round(100.0 * ms_c / (full["us_per_call"] * 1e-3), 2)
         silu_res["roofline"] = {
@@ -261,11 +407,16 @@ def main():
         result["silu_and_mul_bounded"] = silu_res
         # The headline kernel replayed from a graph as well, for comparison
         # with the stream-launched figure above.
+        markers.push(f"headline graph T={T} d={D}")
         ms_g = time_graph(gelu, n_sets, min(args.steps, 640), 10, stream)
+        markers.pop()
         result["graph_replay_us_per_call"] = round(ms_g * 1e3, 3)
 
-        result["sweep"] = sweep(dev, stream, props.multi_processor_count)
-        result["siblings"] = siblings(dev, stream)
+        if not args.no_sweep:
+            result["sweep"] = sweep(dev, stream, props.multi_processor_count, markers)
+            markers.push("siblings")
+            result["siblings"] = siblings(dev, stream)
+            markers.pop()
 
     if args.cpu_seconds > 0:
         result["cpu_baseline"], result["parity_sample"] = cpu_baseline(xb, gelu_out, args.cpu_seconds)
@@ -273,12 +424,15 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-SWEEP = [(T, 8192) for T in (1, 2, 8, 32, 128, 512, 2048)] + \
-        [(T, d) for d in (16384, 32768) for T in (1, 64, 2048)] + \
+# The token sweep (d = 8192), the large rows (d = 16384, 32768) and, within
+# them, the whole target region T in {512, 1024, 2048, 4096} x d in {8192,
+# 16384, 32768}; then short rows at T = 65536 (the packed-rows path).
+SWEEP = [(T, 8192) for T in (1, 2, 8, 32, 128, 512, 1024, 2048, 4096)] + \
+        [(T, d) for d in (16384, 32768) for T in (1, 64, 512, 1024, 2048, 4096)] + \
         [(65536, d) for d in (64, 128, 256)]
 
 
-def sweep(dev, stream, num_cus):
+def sweep(dev, stream, num_cus, markers):
     """gelu_and_mul_sparse over the token sweep (d = 8192, gate N(0,1) plus a
     per-row offset), the large-row shapes (gate N(0,2)) and short rows at
     T = 65536 (gate N(0,2); the packed-rows path), bf16, each timed
@@ -309,22 +463,32 @@ def sweep(dev, stream, num_cus):
         def call(i):
             ga.gelu_and_mul_sparse(xs[i], Z, out=outs[i], workspace=ws)
         reps = 4 if bytes_call > (64 << 20) else 16
+        markers.push(f"sweep gelu T={T} d={d}")
         ms = time_graph(call, n_sets, reps * per_graph, 10, stream, per_graph=per_graph)
         # The same calls launched one by one on the stream: for kernels longer
         # than the host's launch cost this avoids the per-node cost of graph
         # replay; for short ones it measures the host instead.
         ms_s = time_calls(call, n_sets, reps * per_graph, 10, stream)
+        markers.pop()
 
         def ceiling(i):
             ga.stream_xor_rows(xs[i], out=outs[i])
         # The same-pattern streaming kernel on the same buffers, replayed the
         # same way: what the shape allows without statistics or arithmetic.
+        markers.push(f"sweep ceiling T={T} d={d}")
         ms_c = time_graph(ceiling, n_sets, reps * per_graph, 10, stream, per_graph=per_graph)
+        markers.pop()
         plan = ga.plan_gelu_and_mul_sparse(T, d, ga.GA_BF16, True, num_cus, True)
         gbps = bytes_call / (ms * 1e-3) / 1e9
         gbps_s = bytes_call / (ms_s * 1e-3) / 1e9
-        geom = (f"packed lanes_per_row={plan.lanes_per_row} per_lane={plan.per_lane}" if plan.path == 3 else
-                f"splits={plan.splits} waves={plan.waves_per_row} per_lane={plan.per_lane} up_late={plan.up_late}")
+        if plan.path == 3:
+            geom = f"packed lanes_per_row={plan.lanes_per_row} per_lane={plan.per_lane}"
+        elif plan.path == 4:
+            geom = f"replicated statistics rep={plan.splits} waves={plan.waves_per_row} per_lane={plan.per_lane}"
+        elif plan.splits > 1:
+            geom = f"split rows splits={plan.splits} waves={plan.waves_per_row} per_lane={plan.per_lane}"
+        else:
+            geom = f"row waves={plan.waves_per_row} per_lane={plan.per_lane} up_late={plan.up_late}"
         out.append({"T": T, "d": d, "us_per_call": round(ms * 1e3, 3), "GBps": round(gbps, 1),
                     "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
                     "us_per_call_stream": round(ms_s * 1e3, 3),
@@ -436,6 +600,78 @@ def siblings(dev, stream):
     return res
 
 
+# Counter cases: (label, T, d, input shift, output shift, explicit plan or None
+# for the planner's, with the streaming kernel beside it).
+PROFILE_CASES = [
+    ("headline", 2048, 16384, 0, 0, None, True),
+    ("2048x32768 planner", 2048, 32768, 0, 0, None, True),
+    ("2048x32768 W8V8 early", 2048, 32768, 0, 0, (8, 8, 0, 0), False),
+    ("2048x32768 W16V4 early", 2048, 32768, 0, 0, (16, 4, 0, 0), False),
+    ("4096x32768 planner", 4096, 32768, 0, 0, None, True),
+    ("1024x32768 planner", 1024, 32768, 0, 0, None, True),
+    ("512x32768 planner", 512, 32768, 0, 0, None, True),
+    ("512x8192 planner", 512, 8192, 0, 0, None, True),
+    ("1024x8192 planner", 1024, 8192, 0, 0, None, True),
+    ("2048x8192 planner", 2048, 8192, 0, 0, None, True),
+    ("4096x8192 planner", 4096, 8192, 0, 0, None, True),
+    ("512x16384 planner", 512, 16384, 0, 0, None, True),
+    ("1024x16384 planner", 1024, 16384, 0, 0, None, True),
+    ("4096x16384 planner", 4096, 16384, 0, 0, None, True),
+    ("unaligned in+1 out+1", 2048, 16384, 1, 1, None, False),
+    ("unaligned in+1", 2048, 16384, 1, 0, None, False),
+    ("unaligned out+1", 2048, 16384, 0, 1, None, False),
+    ("unaligned kernel aligned rows", 2048, 16384, 0, 0, (8, 4, 1, 2), False),
+    ("d=16383", 2048, 16383, 0, 0, None, False),
+    ("T1 d8192", 1, 8192, 0, 0, None, True),
+    ("T64 d8192", 64, 8192, 0, 0, None, True),
+    ("T128 d8192", 128, 8192, 0, 0, None, True),
+    ("T1 d32768 split", 1, 32768, 0, 0, None, True),
+    ("T64 d32768 split", 64, 32768, 0, 0, None, True),
+]
+
+
+def profile_cases(reps):
+    """Each counter case `reps` times (distinct buffer sets, gate N(0,2) and
+    up N(0,1) rows tiled from a seeded block), then the same-pattern streaming
+    kernel `reps` times where the rows are 16-byte aligned; one 'D <label>'
+    line per launch, in launch order."""
+    import numpy as np
+    import torch
+    import gated_activation_amd as ga
+    import synth
+    dev = torch.device("cuda", 0)
+    block = synth.gelu_large(64, 32768)
+    for label, T, d, ish, osh, plan, ceiling in PROFILE_CASES:
+        rows = np.concatenate([block[:, :d], block[:, 32768:32768 + d]], axis=1)
+        x0 = torch.from_numpy(rows.view(np.int16)).to(dev).view(torch.bfloat16)
+        x0 = x0.repeat((T + 63) // 64, 1)[:T].contiguous()
+        sets = []
+        for _ in range(min(reps, 4)):
+            xbuf = torch.empty(T * 2 * d + 8, dtype=torch.bfloat16, device=dev)
+            x = xbuf[ish:ish + T * 2 * d].view(T, 2 * d)
+            x.copy_(x0)
+            obuf = torch.empty(T * d + 8, dtype=torch.bfloat16, device=dev)
+            sets.append((x, obuf[osh:osh + T * d].view(T, d)))
+        p = None
+        if plan is not None:
+            w, v, late, path = plan
+            p = ga.Plan(path=path, waves_per_row=w, per_lane=v, up_late=late, block=64 * w)
+        torch.cuda.synchronize()
+        for k in range(reps):
+            x, out = sets[k % len(sets)]
+            ga.gelu_and_mul_sparse(x, Z, out=out, plan=p)
+            torch.cuda.synchronize()
+            print(f"D gelu {label}", flush=True)
+        if ceiling:
+            for k in range(reps):
+                x, out = sets[k % len(sets)]
+                ga.stream_xor_rows(x, out=out)
+                torch.cuda.synchronize()
+                print(f"D ceiling {label}", flush=True)
+        del sets, x0
+    print("done", flush=True)
+
+
 def silu_cpu_baseline(sb, gpu_out, seconds):
     """The fp64 oracle's silu_and_mul_bounded, as it stands, on one thread,
     over 2048-row blocks of the MoE buffer (each call with all 2048 rows
@@ -479,8 +715,8 @@ def cpu_baseline(xb, gpu_out, seconds):
     then on every host core the process may use (at most 16, the host share
     of one GPU), one thread per core, for about seconds / 2 of CPU time in
     total.  The oracle's C routine runs without Python's lock, so the threads
-    run in parallel.  Its first block is also compared with the GPU's output
-    rows."""
+    run in parallel.  Every row of the GPU's output is also compared with
+    the oracle."""
     import concurrent.futures
     import numpy as np
     import torch
@@ -492,13 +728,12 @@ def cpu_baseline(xb, gpu_out, seconds):
     block = 64
     row_bytes = 3 * D * 2
 
-    # parity of the GPU's output against the oracle on the first block
-    rows = xb[:block]
-    ref, st = o.gelu_and_mul_sparse(rows, oracle.BF16, Z, want_stats=True)
-    got = bits_of(gpu_out[:block], BF16)
+    # parity of the GPU's output against the oracle on every row
+    ref, st = o.gelu_and_mul_sparse(xb, oracle.BF16, Z, want_stats=True)
+    got = bits_of(gpu_out, BF16)
     torch.cuda.synchronize()
-    parity = compare(got, ref, BF16, gate=decode(rows[:, :D], BF16), stats=st, label="bench sample")
-    parity["rows"] = f"0..{block - 1}"
+    parity = compare(got, ref, BF16, gate=decode(xb[:, :D], BF16), stats=st, label="bench output")
+    parity["rows"] = f"0..{T - 1} (all)"
 
     def run(first_block, stride, budget):
         done, b, t0 = 0, first_block, time.perf_counter()
