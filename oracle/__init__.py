@@ -46,6 +46,9 @@ def _load(path=None):
                                                vp, vp, vp, vp]
     lib.gao_gelu_and_mul.restype = ctypes.c_int
     lib.gao_gelu_and_mul.argtypes = [vp, vp, i64, i64, ctypes.c_int, ctypes.c_int, i64, vp]
+    lib.gao_gelu_and_mul_sparse_down.restype = ctypes.c_int
+    lib.gao_gelu_and_mul_sparse_down.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_float,
+                                                 i64, vp, vp]
     lib.gao_squared_relu_bounded.restype = ctypes.c_int
     lib.gao_squared_relu_bounded.argtypes = [vp, vp, i64, i64, ctypes.c_int, i64, vp]
     for name in ("gao_gelu_tanh_array", "gao_silu_array", "gao_gelu_erf_array", "gao_squared_relu_array"):
@@ -181,6 +184,29 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle rejected the arguments")
         return (y, f64) if want_f64 else y
+
+    def gelu_and_mul_sparse_down(self, x_bits, w_bits, dtype, z, live=None, out=None, want_f64=False):
+        """Sparse GELU-and-multiply of x[T, 2d], then the down projection
+        y[T, H] = a . w^T with w[H, d] (rows of weights per output feature).
+        Returns y bits (rows >= live keep `out`'s contents if given, else
+        zeros), plus (unrounded sums, sums of |a w|) when want_f64."""
+        x = np.ascontiguousarray(x_bits, dtype=BITS_DTYPE[dtype])
+        w = np.ascontiguousarray(w_bits, dtype=BITS_DTYPE[dtype])
+        T, two_d = x.shape
+        d = two_d // 2
+        H = w.shape[0]
+        assert two_d == 2 * d and d >= 1 and w.shape == (H, d) and H >= 1
+        live = T if live is None else int(live)
+        y = np.zeros((T, H), BITS_DTYPE[dtype]) if out is None else np.array(out, copy=True)
+        assert y.shape == (T, H)
+        f64 = np.full((T, H), np.nan) if want_f64 else None
+        mag = np.full((T, H), np.nan) if want_f64 else None
+        rc = self.lib.gao_gelu_and_mul_sparse_down(
+            x.ctypes.data, w.ctypes.data, y.ctypes.data, T, d, H, dtype, float(z), live,
+            None if f64 is None else f64.ctypes.data, None if mag is None else mag.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return (y, f64, mag) if want_f64 else y
 
     def squared_relu_bounded(self, x_bits, dtype, live, out=None, want_f64=False):
         """Bounded squared ReLU of x[M, d] (not gated)."""

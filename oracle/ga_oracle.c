@@ -19,6 +19,9 @@
  *     "approximation mode", so plain GELU-and-multiply exists in a tanh and
  *     an exact (erf) form; Megatron-LM PR 6328, section Scope and risks:
  *     the squared-ReLU activation kernel shares the bounded-row pattern.
+ *   - the vLLM page, Test Result, Correctness: the activation's output feeds
+ *     the layer's downstream projection, which a fused build keeps in order;
+ *     here the product with the projection's weights, in double.
  *
  * Readings taken where the pages are silent (each also listed in the design
  * notes): the std is the population std (divide by d); the cutoff is
@@ -32,7 +35,9 @@
  * codec against numpy / exhaustive search, GELU and SiLU against torch's fp64
  * routines and closed forms, row statistics against numpy and exact rational
  * arithmetic, the whole op against an fp64 torch composition, survival
- * fractions against 1 - Phi(z), and planted-mistake (mutant) runs.
+ * fractions against 1 - Phi(z), the down projection against exact rational
+ * sums, numpy's fp64 product and weights that pick out single elements, and
+ * planted-mistake (mutant) runs.
  */
 #include <math.h>
 #include <stdint.h>
@@ -306,6 +311,55 @@ int gao_gelu_and_mul(const void *in, void *out, int64_t T, int64_t d, int dtype,
         }
     }
     return 0;
+}
+
+/* Sparse GELU-and-multiply followed by the layer's down projection: the
+ * matrix product that consumes the activation (the vLLM page, Test Result,
+ * Correctness: the standalone regression keeps the upstream projection, the
+ * activation's write and the downstream projection in that order).  For each
+ * live row r < clamp(live, 0, T) and output feature h < H:
+ *     a[r, k] = gelu_and_mul_sparse(gu)[r, k]   as stored: rounded once
+ *     y[r, h] = sum over k of a[r, k] * w[h, k]  in double, rounded once
+ * gu is [T, 2d], w is [H, d] row-major (one row of d weights per output
+ * feature, a linear layer's layout), y is [T, H].  y_f64 (may be NULL) gets
+ * the unrounded sums and abs_f64 (may be NULL) the sums of |a[r,k] w[h,k]|
+ * (the scale of any rounding error in the sum).  Rows beyond the live count
+ * are not written. */
+int gao_gelu_and_mul_sparse_down(const void *gu, const void *w, void *y, int64_t T, int64_t d,
+                                 int64_t H, int dtype, float z, int64_t live, double *y_f64,
+                                 double *abs_f64)
+{
+    if (!gu || !w || !y || T < 0 || d < 1 || H < 1 || !gao_elem_size(dtype)) return -1;
+    const int64_t n = clamp_live(live, T);
+    if (n == 0) return 0;
+    const size_t es = gao_elem_size(dtype);
+    void *a_bits = malloc(es * (size_t)(n * d));
+    double *a = (double *)malloc(sizeof(double) * (size_t)(n * d));
+    double *wrow = (double *)malloc(sizeof(double) * (size_t)d);
+    int rc = -1;
+    if (!a_bits || !a || !wrow) goto done;
+    /* the activation, exactly as its own op stores it */
+    if (gao_gelu_and_mul_sparse(gu, a_bits, n, d, dtype, z, n, NULL, NULL, NULL, NULL)) goto done;
+    for (int64_t i = 0; i < n * d; ++i) a[i] = load_elem(a_bits, i, dtype);
+    for (int64_t h = 0; h < H; ++h) {
+        for (int64_t k = 0; k < d; ++k) wrow[k] = load_elem(w, h * d + k, dtype);
+        for (int64_t r = 0; r < n; ++r) {
+            double s = 0.0, m = 0.0;
+            for (int64_t k = 0; k < d; ++k) {
+                s += a[r * d + k] * wrow[k];
+                m += fabs(a[r * d + k] * wrow[k]);
+            }
+            if (y_f64) y_f64[r * H + h] = s;
+            if (abs_f64) abs_f64[r * H + h] = m;
+            store_elem(y, r * H + h, dtype, s);
+        }
+    }
+    rc = 0;
+done:
+    free(a_bits);
+    free(a);
+    free(wrow);
+    return rc;
 }
 
 /* Bounded squared ReLU (not gated): in[M, d] -> out[M, d] = max(x, 0)^2 on

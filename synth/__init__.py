@@ -31,7 +31,7 @@ _M2 = np.uint64(0x94D049BB133111EB)
 _THREADS = max(1, min(16, os.cpu_count() or 1))
 
 # stream identifiers inside one seed
-S_GATE, S_UP, S_OFFSET, S_KIND = 1, 2, 3, 4
+S_GATE, S_UP, S_OFFSET, S_KIND, S_WEIGHT = 1, 2, 3, 4, 5
 
 
 def _core():
@@ -212,6 +212,15 @@ def moe_buffer(M: int = 16384, d: int = 768, seed: int = 7,
                dtype: int = BF16) -> np.ndarray:
     """Capture-sized MoE activation buffer [M, 2d], gate and up N(0, 1)."""
     return gelu_iid(M, d, seed=seed, dtype=dtype, gate_std=1.0)
+
+
+def down_weight(H: int, d: int, seed: int = 0, dtype: int = BF16) -> np.ndarray:
+    """Weights of the down projection that follows the activation: [H, d],
+    one row of d weights per output feature, i.i.d. N(0, 1/d) (a linear
+    layer's usual initial scale, so outputs stay of order one)."""
+    w = np.empty((H, d), np.uint32 if dtype == F32 else np.uint16)
+    normal_rows_into(w, stream_key(seed, S_WEIGHT), scale=1.0 / np.sqrt(d), dtype=dtype)
+    return w
 
 
 # Sentinel bits written to rows beyond the live count and to canary tails: a

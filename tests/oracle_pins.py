@@ -486,9 +486,78 @@ def pin_gelu_sparse_roundtrip(o):
     assert np.array_equal(y1, y2) and np.array_equal(st1[2], st2[2])
 
 
+
+# ---------------------------------------------------------------------------
+# the activation followed by the down projection
+# ---------------------------------------------------------------------------
+
+def pin_down_projection(o):
+    """y = a . w^T with a the stored activation: exact rational sums on tiny
+    inputs (nearest bf16 by exhaustive search), numpy's fp64 product at a
+    moderate size, single-weight and permutation weights that pick out one
+    activation element exactly (a transposed operand or output fails), and
+    rows beyond the live count untouched."""
+    # exact sums, rounded by the exhaustive search
+    for seed, (T, d, H) in enumerate([(3, 24, 5), (2, 40, 7), (4, 16, 3)]):
+        x = synth.gelu_iid(T, d, seed=90 + seed)
+        w = synth.down_weight(H, d, seed=90 + seed)
+        a = o.decode(o.gelu_and_mul_sparse(x, BF16, Z95), BF16)
+        wv = o.decode(w, BF16)
+        exact = np.array([[float(sum(Fraction(float(a[r, k])) * Fraction(float(wv[h, k])) for k in range(d)))
+                           for h in range(H)] for r in range(T)])
+        y, f64, mag = o.gelu_and_mul_sparse_down(x, w, BF16, Z95, want_f64=True)
+        assert np.array_equal(y, _nearest_bf16_bits(exact)), (T, d, H)
+        assert np.all(np.abs(f64 - exact) <= d * 2.0 ** -52 * mag)
+    # numpy's fp64 product and absolute sums
+    T, d, H = 8, 512, 48
+    for dt in (BF16, F16):
+        x = synth.gelu_iid(T, d, seed=95, dtype=dt, gate_std=1.5)
+        w = synth.down_weight(H, d, seed=95, dtype=dt)
+        a = o.decode(o.gelu_and_mul_sparse(x, dt, Z95), dt)
+        wv = o.decode(w, dt)
+        y, f64, mag = o.gelu_and_mul_sparse_down(x, w, dt, Z95, want_f64=True)
+        assert np.all(np.abs(f64 - a @ wv.T) <= 1e-12 * (np.abs(a) @ np.abs(wv).T))
+        assert np.allclose(mag, np.abs(a) @ np.abs(wv).T, rtol=1e-12, atol=0)
+        assert np.array_equal(y, o.encode(f64, dt))
+    # one weight: y[:, h0] = a[:, k0] exactly, every other output 0 (H != d)
+    T, d, H = 5, 96, 40
+    x = synth.gelu_iid(T, d, seed=97, gate_std=1.0)
+    a_bits = o.gelu_and_mul_sparse(x, BF16, 0.0)
+    for h0, k0 in ((3, 71), (39, 0), (0, 95)):
+        w = np.zeros((H, d), np.uint16)
+        w[h0, k0] = 0x3F80                                     # 1.0
+        y = o.gelu_and_mul_sparse_down(x, w, BF16, 0.0)
+        # the same value (a -0 activation sums to +0)
+        assert np.array_equal(o.decode(y[:, h0], BF16), o.decode(a_bits[:, k0], BF16))
+        nz = o.decode(a_bits[:, k0], BF16) != 0
+        assert nz.any() and np.array_equal(y[nz, h0], a_bits[nz, k0])
+        rest = np.delete(y, h0, axis=1)
+        assert np.all(o.decode(rest, BF16) == 0)
+    # scaled permutation: y[r, h] = a[r, p(h)] * 2^e(h), exactly
+    T, d = 6, 64
+    x = synth.gelu_iid(T, d, seed=98)
+    a = o.decode(o.gelu_and_mul_sparse(x, BF16, Z95), BF16)
+    rng = _rng(98)
+    perm, e = rng.permutation(d), rng.integers(-3, 4, d)
+    wv = np.zeros((d, d))
+    wv[np.arange(d), perm] = 2.0 ** e
+    y = o.decode(o.gelu_and_mul_sparse_down(x, synth.to_bits(wv, BF16), BF16, Z95), BF16)
+    assert np.array_equal(y, a[:, perm] * 2.0 ** e[None, :])
+    # live rows only
+    T, d, H = 7, 48, 9
+    x = synth.gelu_iid(T, d, seed=99)
+    w = synth.down_weight(H, d, seed=99)
+    sentinel = np.full((T, H), synth.SENTINEL[BF16], np.uint16)
+    full = o.gelu_and_mul_sparse_down(x, w, BF16, Z95)
+    for live in (0, 3, 7, 12, -1):
+        y = o.gelu_and_mul_sparse_down(x, w, BF16, Z95, live=live, out=sentinel)
+        n = min(max(live, 0), T)
+        assert np.array_equal(y[:n], full[:n]) and np.all(y[n:] == synth.SENTINEL[BF16])
+
+
 ALL_PINS = [pin_decode, pin_encode_fp32, pin_encode_fp16, pin_encode_bf16,
             pin_roundtrip, pin_gelu, pin_silu, pin_row_stats,
             pin_gelu_sparse_composition, pin_gelu_sparse_invariants,
             pin_survival_fraction, pin_brute_force_1x8, pin_silu_bounded,
             pin_gelu_erf, pin_squared_relu, pin_gelu_and_mul, pin_squared_relu_bounded,
-            pin_gelu_sparse_roundtrip]
+            pin_gelu_sparse_roundtrip, pin_down_projection]

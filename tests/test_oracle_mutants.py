@@ -64,6 +64,17 @@ MUTANTS = {
                                   "            const double act",
                                   "const double up = load_elem(in, r * 2 * d + i, dtype);\n"
                                   "            const double act"),
+    "down_weight_transposed": ("wrow[k] = load_elem(w, h * d + k, dtype);",
+                               "wrow[k] = load_elem(w, k * H + h, dtype);"),
+    "down_output_transposed": ("store_elem(y, r * H + h, dtype, s);", "store_elem(y, h * T + r, dtype, s);"),
+    "down_ignores_live": ("const int64_t n = clamp_live(live, T);\n    if (n == 0) return 0;",
+                          "const int64_t n = T;\n    if (n == 0) return 0;"),
+    "down_drops_first_term": ("for (int64_t k = 0; k < d; ++k) {\n                s += ",
+                              "for (int64_t k = 1; k < d; ++k) {\n                s += "),
+    "down_activation_unrounded": ("NULL, NULL, NULL, NULL)) goto done;\n"
+                                  "    for (int64_t i = 0; i < n * d; ++i) a[i] = load_elem(a_bits, i, dtype);",
+                                  "a, NULL, NULL, NULL)) goto done;"),
+    "down_abs_signed": ("m += fabs(a[r * d + k] * wrow[k]);", "m += a[r * d + k] * wrow[k];"),
 }
 
 

@@ -90,3 +90,16 @@ def test_c_core_matches_numpy_rederivation():
     assert np.array_equal(u, synth.uniform(k, 0, 1000))
     z = np.sqrt(-2 * np.log(u[0::2])) * np.cos(2 * np.pi * u[1::2])
     assert np.abs(z - synth.normal(k, 0, 500)).max() < 1e-14
+
+
+def test_down_weight_recipe():
+    w = synth.down_weight(64, 2048, seed=3)
+    assert w.shape == (64, 2048) and w.dtype == np.uint16
+    assert np.array_equal(w, synth.down_weight(64, 2048, seed=3))
+    v = synth.bits_to_float(w, synth.BF16)
+    assert abs(v.mean()) < 3e-4 and abs(v.std() * np.sqrt(2048) - 1.0) < 0.01
+    # its own stream: not the gate or up values of the same seed
+    x = synth.gelu_iid(64, 2048, seed=3)
+    assert not np.array_equal(w, x[:, :2048])
+    f = synth.down_weight(8, 256, seed=4, dtype=synth.F16)
+    assert f.dtype == np.uint16 and np.isfinite(synth.bits_to_float(f, synth.F16)).all()
