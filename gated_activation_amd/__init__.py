@@ -10,6 +10,8 @@ is not built, importing this package raises: there is no fallback.
                                         the round-trip form)
     gelu_and_mul_sparse_noalloc(x, z)   the same for T <= 256 rows, no workspace
                                         (the library's own static array)
+    gelu_and_mul_sparse_down(x, w)      x: [T, 2d], w: [H, d] -> [T, H]: the activation
+                                        fused with the down projection (bf16 / fp16)
     silu_and_mul_bounded(x, live_rows)  x: [M, 2d] -> [M, d] (live rows only)
     gelu_and_mul(x, approximate)        x: [T, 2d] -> [T, d] (tanh or erf GELU)
     squared_relu_bounded(x, live_rows)  x: [M, d]  -> [M, d] (live rows only)
@@ -22,4 +24,6 @@ from ._lib import (  # noqa: F401
     gelu_and_mul, squared_relu_bounded, z_from_sparsity,
     plan_gelu_and_mul_sparse, plan_silu_and_mul_bounded, workspace_for,
     reserve_workspace, held_workspaces, GA_SPLIT_PLAN_ROWS, WORKSPACE_BYTES,
+    DownPlan, GA_DOWN_MAX_ROWS, gelu_and_mul_sparse_down, plan_gelu_and_mul_sparse_down,
+    gelu_and_mul_sparse_down_workspace_bytes, reserve_down_workspace,
 )

@@ -34,6 +34,17 @@ class Plan(ctypes.Structure):
         return {k: getattr(self, k) for k, _ in self._fields_}
 
 
+class DownPlan(ctypes.Structure):
+    """Geometry of the activation fused with the down projection."""
+    _fields_ = [("rows_per_block", ctypes.c_int32), ("waves", ctypes.c_int32),
+                ("k_chunk", ctypes.c_int32), ("splits", ctypes.c_int32),
+                ("grid", ctypes.c_int64), ("spin_limit", ctypes.c_uint32),
+                ("reserved", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
 class GaError(RuntimeError):
     def __init__(self, status, message):
         super().__init__(f"{status}: {message}")
@@ -62,6 +73,11 @@ def _load():
         "ga_stream_xor_rows": [vp, vp, i64, i64, vp],
         "ga_gelu_and_mul": [vp, vp, i64, i64, i32, i32, vp, vp],
         "ga_squared_relu_bounded": [vp, vp, i64, i64, i32, vp, vp],
+        "ga_gelu_and_mul_sparse_down": [vp, vp, vp, i64, i64, i64, i32, ctypes.c_float, vp, vp,
+                                        ctypes.c_size_t, vp],
+        "ga_gelu_and_mul_sparse_down_with_plan": [vp, vp, vp, i64, i64, i64, i32, ctypes.c_float, vp,
+                                                  ctypes.POINTER(DownPlan), vp, ctypes.c_size_t, vp],
+        "ga_plan_gelu_and_mul_sparse_down": [i64, i64, i64, i32, ctypes.POINTER(DownPlan)],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -77,6 +93,8 @@ def _load():
     lib.ga_z_from_sparsity.restype = ctypes.c_double
     lib.ga_gelu_and_mul_sparse_workspace_bytes.argtypes = [i64]
     lib.ga_gelu_and_mul_sparse_workspace_bytes.restype = ctypes.c_size_t
+    lib.ga_gelu_and_mul_sparse_down_workspace_bytes.argtypes = [i64, i64, i64, ctypes.POINTER(DownPlan)]
+    lib.ga_gelu_and_mul_sparse_down_workspace_bytes.restype = ctypes.c_size_t
     return lib
 
 
@@ -214,6 +232,81 @@ def gelu_and_mul_sparse(x, z=Z_SPARSITY_095, out=None, live_rows=None, plan=None
             _check(lib.ga_gelu_and_mul_sparse_ws(*args, ws_ptr, ws_bytes, _stream_of(x)))
         else:
             _check(lib.ga_gelu_and_mul_sparse(*args, _stream_of(x)))
+    return out
+
+
+# Workspaces of the fused down projection: per (device index, stream handle),
+# zero-filled when created and grown (never shrunk) to the largest size a call
+# on that stream has needed.  A grown workspace replaces the old one for later
+# calls, but every one ever made is kept for the life of the process, so a
+# graph captured with an older one can still be replayed.
+GA_DOWN_MAX_ROWS = 256
+_DOWN_WORKSPACES = {}
+
+
+def reserve_down_workspace(nbytes, device=None, stream=None):
+    """The fused down projection's workspace of `stream` (default: the current
+    stream of `device`), grown to at least `nbytes` if it is smaller (a new
+    zero-filled buffer of at least twice the size).  Call it before capturing
+    a graph so the buffer is allocated outside the capture."""
+    device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    if device.index is None:
+        device = torch.device("cuda", torch.cuda.current_device())
+    stream = torch.cuda.current_stream(device) if stream is None else stream
+    held = _DOWN_WORKSPACES.setdefault(_workspace_key(device, stream), [])
+    if not held or held[-1].numel() < nbytes:
+        size = max(int(nbytes), 2 * held[-1].numel() if held else 0, 1 << 20)
+        with torch.cuda.device(device), torch.cuda.stream(stream):
+            held.append(torch.zeros(size, dtype=torch.uint8, device=device))
+    return held[-1]
+
+
+def plan_gelu_and_mul_sparse_down(T, d, H, dtype=GA_BF16):
+    p = DownPlan()
+    _check(lib.ga_plan_gelu_and_mul_sparse_down(T, d, H, dtype, ctypes.byref(p)))
+    return p
+
+
+def gelu_and_mul_sparse_down_workspace_bytes(T, d, H, plan=None):
+    return int(lib.ga_gelu_and_mul_sparse_down_workspace_bytes(T, d, H, None if plan is None else ctypes.byref(plan)))
+
+
+def gelu_and_mul_sparse_down(x, w, z=Z_SPARSITY_095, out=None, live_rows=None, plan=None, workspace=None):
+    """Sparse GELU-and-multiply of x = [gate | up] ([T, 2d]) fused with the
+    down projection: out[T, H] = a . w^T with w [H, d] (a linear layer's
+    weight) and a the activation as gelu_and_mul_sparse stores it.  bf16 or
+    fp16; T <= GA_DOWN_MAX_ROWS, d a multiple of 8, H a multiple of 16.
+    workspace: None = the binding's workspace of the current stream (grown as
+    needed, see reserve_down_workspace), or a zero-filled uint8 tensor owned
+    by the caller."""
+    name = "gelu_and_mul_sparse_down"
+    if not isinstance(x, torch.Tensor) or not x.is_cuda or x.dim() != 2 or x.shape[1] % 2 != 0:
+        raise ValueError(f"{name}: x must be a [T, 2d] CUDA (HIP) tensor")
+    if (not isinstance(w, torch.Tensor) or w.dim() != 2 or w.shape[1] * 2 != x.shape[1]
+            or w.dtype != x.dtype or w.device != x.device):
+        raise ValueError(f"{name}: w must be a [H, d] tensor of x's dtype on x's device")
+    if not x.is_contiguous() or not w.is_contiguous():
+        raise ValueError(f"{name}: x and w must be contiguous")
+    if x.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError(f"{name}: bf16 or fp16 only, got {x.dtype}")
+    T, d, H = x.shape[0], x.shape[1] // 2, w.shape[0]
+    if out is None:
+        out = torch.empty((T, H), dtype=x.dtype, device=x.device)
+    elif (out.shape != (T, H) or out.dtype != x.dtype or out.device != x.device
+          or not out.is_contiguous()):
+        raise ValueError(f"{name}: out must be a contiguous [{T}, {H}] {x.dtype} tensor on {x.device}")
+    live = _live_ptr(live_rows, x, name)
+    with torch.cuda.device(x.device):
+        p = plan if plan is not None else plan_gelu_and_mul_sparse_down(T, d, H, _TORCH_DTYPE[x.dtype])
+        need = gelu_and_mul_sparse_down_workspace_bytes(T, d, H, p)
+        if workspace is None and need > 0 and T > 0:
+            workspace = reserve_down_workspace(need, x.device)
+        ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        _check(lib.ga_gelu_and_mul_sparse_down_with_plan(
+            ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+            T, d, H, _TORCH_DTYPE[x.dtype], ctypes.c_float(z), live, ctypes.byref(p), ws_ptr, ws_bytes,
+            _stream_of(x)))
     return out
 
 

@@ -604,6 +604,65 @@ ga_status device_scratch(ga_stream stream, void **ptr) {
     return GA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// gelu_and_mul_sparse fused with the down projection
+// ---------------------------------------------------------------------------
+// Candidate geometries (tokens per block, waves, k chunk), most preferred
+// first, for three token ranges.
+struct DownGeo {
+    int tm, waves, bk;
+};
+constexpr DownGeo kDownFew[] = {{16, 8, 1024}, {16, 8, 512}, {16, 8, 256}};
+constexpr DownGeo kDownMid[] = {{32, 8, 512}, {16, 8, 1024}, {16, 8, 512}};
+constexpr DownGeo kDownMany[] = {{64, 8, 512}, {32, 8, 512}, {16, 8, 1024}};
+
+void fill_down_plan(const DownGeo &g, int64_t T, int64_t d, int64_t H, ga_down_plan *p) {
+    std::memset(p, 0, sizeof *p);
+    p->rows_per_block = g.tm;
+    p->waves = g.waves;
+    p->k_chunk = g.bk;
+    p->splits = (int32_t)((d + g.bk - 1) / g.bk);
+    p->grid = (T + g.tm - 1) / g.tm * ((H + g.waves * 16 - 1) / (g.waves * 16)) * p->splits;
+    p->spin_limit = kDefaultSpinLimit;
+}
+
+ga_status check_down_sizes(const char *op, int64_t T, int64_t d, int64_t H, int32_t dtype) {
+    if (T < 0 || d < 1 || H < 1)
+        return fail(GA_EINVAL, "%s: negative or zero size (T %lld, d %lld, H %lld)", op, (long long)T,
+                    (long long)d, (long long)H);
+    if (elem_size(dtype) == 0) return fail(GA_EINVAL, "%s: unknown dtype %d", op, (int)dtype);
+    if (dtype == GA_F32) return fail(GA_EUNSUPPORTED, "%s: fp32 has no fused form (bf16 and fp16 only)", op);
+    if (T > GA_DOWN_MAX_ROWS)
+        return fail(GA_EUNSUPPORTED, "%s: %lld tokens above %d", op, (long long)T, GA_DOWN_MAX_ROWS);
+    if (d % 8 != 0 || d > GA_MAX_D)
+        return fail(GA_EUNSUPPORTED, "%s: d = %lld is not a multiple of 8 up to %d", op, (long long)d, GA_MAX_D);
+    if (H % 16 != 0 || H > GA_DOWN_MAX_H)
+        return fail(GA_EUNSUPPORTED, "%s: H = %lld is not a multiple of 16 up to %d", op, (long long)H,
+                    GA_DOWN_MAX_H);
+    return GA_OK;
+}
+
+ga_status check_down_plan(const char *op, const ga_down_plan *p, int64_t T, int64_t d, int64_t H, int32_t dtype) {
+    if (!ga::gelu_down_available(dtype, p->rows_per_block, p->waves, p->k_chunk))
+        return fail(GA_EINVAL, "%s: no kernel for rows_per_block %d, waves %d, k_chunk %d", op,
+                    (int)p->rows_per_block, (int)p->waves, (int)p->k_chunk);
+    ga_down_plan want;
+    fill_down_plan(DownGeo{p->rows_per_block, p->waves, p->k_chunk}, T, d, H, &want);
+    if (p->splits != want.splits || p->grid != want.grid)
+        return fail(GA_EINVAL, "%s: splits %d / grid %lld do not match the geometry (%d / %lld)", op,
+                    (int)p->splits, (long long)p->grid, (int)want.splits, (long long)want.grid);
+    if (p->splits > ga::DOWN_MAX_SPLITS)
+        return fail(GA_EUNSUPPORTED, "%s: %d slices of d above %d", op, (int)p->splits, ga::DOWN_MAX_SPLITS);
+    if (p->spin_limit == 0 || p->reserved != 0) return fail(GA_EINVAL, "%s: spin_limit 0 or reserved set", op);
+    if (p->grid * p->waves * 64 >= kMaxWorkItems)
+        return fail(GA_EUNSUPPORTED, "%s: %lld work-items reach 2^32", op, (long long)(p->grid * p->waves * 64));
+    return GA_OK;
+}
+
+size_t down_workspace_bytes(const ga_down_plan &p, int64_t T, int64_t d, int64_t H) {
+    return ga::gelu_down_workspace_bytes(T, d, H, p.rows_per_block, p.waves, p.k_chunk);
+}
+
 }  // namespace
 
 // The planner.  allow_rep: the replicated-statistics path may be chosen (it
@@ -857,6 +916,79 @@ ga_status ga_stream_xor_rows(const void *in, void *out, int64_t rows, int64_t w_
     if (g > (int64_t)cus * 64) g = (int64_t)cus * 64;
     return launched("ga_stream_xor_rows", ga::launch_xor_rows(g, in, out, (int32_t)rows, (uint32_t)nvec,
                                                               static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
+// gelu_and_mul_sparse fused with the down projection
+// ---------------------------------------------------------------------------
+ga_status ga_plan_gelu_and_mul_sparse_down(int64_t T, int64_t d, int64_t H, int32_t dtype, ga_down_plan *plan) {
+    const char *name = "ga_plan_gelu_and_mul_sparse_down";
+    if (plan == nullptr) return fail(GA_EINVAL, "%s: null plan", name);
+    ga_status st = check_down_sizes(name, T, d, H, dtype);
+    if (st != GA_OK) return st;
+    const DownGeo *cand = T <= 16 ? kDownFew : T <= 32 ? kDownMid : kDownMany;
+    for (int i = 0; i < 3; ++i) {
+        if ((d + cand[i].bk - 1) / cand[i].bk > ga::DOWN_MAX_SPLITS) continue;
+        fill_down_plan(cand[i], T, d, H, plan);
+        return GA_OK;
+    }
+    // Rows of more than 64 chunks of the preferred sizes: the longest chunk.
+    fill_down_plan(DownGeo{16, 8, 1024}, T, d, H, plan);
+    return GA_OK;
+}
+
+size_t ga_gelu_and_mul_sparse_down_workspace_bytes(int64_t T, int64_t d, int64_t H, const ga_down_plan *plan) {
+    ga_down_plan p;
+    if (plan == nullptr) {
+        if (ga_plan_gelu_and_mul_sparse_down(T, d, H, GA_BF16, &p) != GA_OK) return 0;
+        plan = &p;
+    }
+    if (T < 1 || d < 1 || H < 1) return 0;
+    return down_workspace_bytes(*plan, T, d, H);
+}
+
+ga_status ga_gelu_and_mul_sparse_down_with_plan(const void *gu, const void *w, void *y, int64_t T, int64_t d,
+                                                int64_t H, int32_t dtype, float z, const int32_t *live_rows,
+                                                const ga_down_plan *plan, void *workspace,
+                                                size_t workspace_bytes, ga_stream stream) {
+    const char *name = "ga_gelu_and_mul_sparse_down";
+    if (gu == nullptr || w == nullptr || y == nullptr) return fail(GA_EINVAL, "%s: null gu/w/y pointer", name);
+    if (plan == nullptr) return fail(GA_EINVAL, "%s: null plan", name);
+    ga_status st = check_down_sizes(name, T, d, H, dtype);
+    if (st != GA_OK) return st;
+    if (!std::isfinite(z)) return fail(GA_EINVAL, "%s: z is not finite", name);
+    if ((uintptr_t)live_rows % 4 != 0) return fail(GA_EINVAL, "%s: live_rows is not 4-byte aligned", name);
+    if ((uintptr_t)gu % 16 != 0 || (uintptr_t)w % 16 != 0 || (uintptr_t)y % 16 != 0)
+        return fail(GA_EUNSUPPORTED, "%s: gu, w and y must be 16-byte aligned", name);
+    const size_t es = elem_size(dtype);
+    const size_t y_bytes = (size_t)T * (size_t)H * es;
+    if (T > 0 && (overlaps(gu, (size_t)T * 2 * (size_t)d * es, y, y_bytes) ||
+                  overlaps(w, (size_t)H * (size_t)d * es, y, y_bytes)))
+        return fail(GA_EINVAL, "%s: y overlaps gu or w", name);
+    if ((st = check_down_plan(name, plan, T, d, H, dtype)) != GA_OK) return st;
+    if (T == 0) return GA_OK;
+    const size_t need = down_workspace_bytes(*plan, T, d, H);
+    if (need > 0) {
+        if (workspace == nullptr || (uintptr_t)workspace % 256 != 0)
+            return fail(GA_EINVAL, "%s: the plan needs a 256-byte aligned workspace", name);
+        if (workspace_bytes < need)
+            return fail(GA_EINVAL, "%s: workspace of %zu bytes, the plan needs %zu", name, workspace_bytes, need);
+    }
+    return launched(name, ga::launch_gelu_down(dtype, plan->rows_per_block, plan->waves, plan->k_chunk, gu, w, y,
+                                               (int32_t)T, (int32_t)d, (int32_t)H, z, live_rows, workspace,
+                                               plan->spin_limit, static_cast<hipStream_t>(stream)));
+}
+
+ga_status ga_gelu_and_mul_sparse_down(const void *gu, const void *w, void *y, int64_t T, int64_t d, int64_t H,
+                                      int32_t dtype, float z, const int32_t *live_rows, void *workspace,
+                                      size_t workspace_bytes, ga_stream stream) {
+    if (gu == nullptr || w == nullptr || y == nullptr)
+        return fail(GA_EINVAL, "ga_gelu_and_mul_sparse_down: null gu/w/y pointer");
+    ga_down_plan p;
+    ga_status st = ga_plan_gelu_and_mul_sparse_down(T, d, H, dtype, &p);
+    if (st != GA_OK) return st;
+    return ga_gelu_and_mul_sparse_down_with_plan(gu, w, y, T, d, H, dtype, z, live_rows, &p, workspace,
+                                                 workspace_bytes, stream);
 }
 
 const char *ga_status_str(int32_t status) {

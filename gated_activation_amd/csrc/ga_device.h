@@ -300,6 +300,19 @@ __device__ __forceinline__ float sparse_apply(float g, float cut, float up) {
     }
 }
 
+// Chan, Golub and LeVeque's pairwise update: fold the partial statistics
+// (n_b, mean_b, M2_b) of one chunk of a row into (n_a, mean_a, M2_a), where
+// M2 is the sum of squared deviations from the chunk's own mean.
+__device__ __forceinline__ void chan_combine(float &n_a, float &mean_a, float &m2_a, float n_b,
+                                             float mean_b, float m2_b) {
+    const float n = n_a + n_b;
+    const float delta = mean_b - mean_a;
+    const float w = n_b * __builtin_amdgcn_rcpf(n);
+    mean_a = __builtin_fmaf(delta, w, mean_a);
+    m2_a = m2_a + m2_b + delta * delta * n_a * w;
+    n_a = n;
+}
+
 __device__ __forceinline__ int32_t clamp_live(const int32_t *live, int32_t rows) {
     const int32_t n = *live;
     return n < 0 ? 0 : (n > rows ? rows : n);

@@ -38,6 +38,19 @@ int64_t gelu_rep_grid(int64_t T, int rep);
 hipError_t launch_gelu_rep(int dtype, int waves, int vec_per_lane, int rep, const void *in, void *out, int32_t T,
                            int32_t d, int32_t nvec, float z, const int32_t *live, hipStream_t stream);
 
+// The activation fused with the down projection y = a . w^T (w: [H, d]):
+// workgroups of tm tokens x (waves * 16) features x bk elements of d; the
+// ceil(d / bk) workgroups of one token block and feature block exchange
+// statistics and fp32 partial tiles through `workspace`
+// (gelu_down_workspace_bytes; none when bk >= d).  At most DOWN_MAX_SPLITS
+// slices per row.
+constexpr int DOWN_MAX_SPLITS = 64;
+bool gelu_down_available(int dtype, int tm, int waves, int bk);
+size_t gelu_down_workspace_bytes(int64_t T, int64_t d, int64_t H, int tm, int waves, int bk);
+hipError_t launch_gelu_down(int dtype, int tm, int waves, int bk, const void *gu, const void *w, void *y,
+                            int32_t T, int32_t d, int32_t H, float z, const int32_t *live, void *workspace,
+                            uint32_t spin_limit, hipStream_t stream);
+
 // Packed-rows path for short rows: ROWS_BLOCK threads per workgroup,
 // lanes_per_row in {4, 8, 16, 32} lanes per row, vec_per_lane in {1, 2, 4};
 // grid = ceil(T / (ROWS_BLOCK / lanes_per_row)).  nvec: the row's 16-byte

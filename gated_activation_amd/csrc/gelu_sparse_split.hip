@@ -41,21 +41,6 @@
 
 namespace ga {
 
-namespace {
-
-// Chan et al.: combine (n_a, mean_a, M2_a) with (n_b, mean_b, M2_b).
-__device__ __forceinline__ void chan_combine(float &n_a, float &mean_a, float &m2_a, float n_b,
-                                             float mean_b, float m2_b) {
-    const float n = n_a + n_b;
-    const float delta = mean_b - mean_a;
-    const float w = n_b * __builtin_amdgcn_rcpf(n);
-    mean_a = __builtin_fmaf(delta, w, mean_a);
-    m2_a = m2_a + m2_b + delta * delta * n_a * w;
-    n_a = n;
-}
-
-}  // namespace
-
 template <int DT, int WAVES, int VPL, int UP, bool NONTEMP = true>
 __global__ __launch_bounds__(WAVES * 64) void gelu_sparse_split_kernel(
     const uint4 *__restrict__ in, uint4 *__restrict__ out, int32_t T, int32_t d, int32_t nvec,

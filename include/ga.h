@@ -234,6 +234,63 @@ ga_status ga_squared_relu_bounded(const void *in, void *out, int64_t M, int64_t 
                                   const int32_t *live_rows, ga_stream stream);
 
 /*
+ * Sparse GELU-and-multiply fused with the down projection that consumes it
+ * (the vLLM page, Test Result, Correctness: the activation's write feeds the
+ * layer's downstream projection, and a fused build must keep the two in that
+ * order).  For live rows r and output features h:
+ *     a[r, k] = gelu_and_mul_sparse(gu)[r, k], rounded once to `dtype`
+ *               (the value ga_gelu_and_mul_sparse would store);
+ *     y[r, h] = sum over k of a[r, k] * w[h, k], fp32 sums on the matrix
+ *               cores, rounded once to `dtype`.
+ * The activation is formed inside the product's operand staging and never
+ * written to memory.  The sum runs over d in slices of the plan's k_chunk;
+ * the slices' fp32 partials are added in slice order, so results do not
+ * depend on scheduling.
+ *   gu        [T, 2d] device array (gate | up), 16-byte aligned.
+ *   w         [H, d] device array, 16-byte aligned: one row of d weights per
+ *             output feature (a linear layer's weight layout).
+ *   y         [T, H] device array, 16-byte aligned; must not overlap gu or w.
+ *   T         0 <= T <= GA_DOWN_MAX_ROWS tokens (more: GA_EUNSUPPORTED; use
+ *             ga_gelu_and_mul_sparse and a matrix product).
+ *   d         8 <= d <= GA_MAX_D, a multiple of 8 (16-byte rows).
+ *   H         16 <= H <= GA_DOWN_MAX_H, a multiple of 16.
+ *   dtype     GA_BF16 or GA_F16 (GA_F32: GA_EUNSUPPORTED).
+ *   z, live_rows  as for ga_gelu_and_mul_sparse; rows of y at or past the
+ *             live count are left untouched.
+ *   workspace device memory of ga_gelu_and_mul_sparse_down_workspace_bytes()
+ *             bytes (0 when the plan has one slice: then it may be NULL),
+ *             256-byte aligned, zero-filled before its first use.  The kernel
+ *             leaves it ready for the next call (counters back at zero, a
+ *             per-call tag advanced), so it is zeroed once and serves any
+ *             later calls and shapes that fit it, and graph replays.  Calls
+ *             that share a workspace must not overlap in time.
+ * The workgroups of one output tile wait for each other's row statistics for
+ * a bounded number of polls; past it a workgroup computes the statistics of
+ * its rows itself, so a launch always completes.
+ */
+#define GA_DOWN_MAX_ROWS 256
+#define GA_DOWN_MAX_H 65536
+typedef struct {
+    int32_t rows_per_block; /* tokens per workgroup: 16, 32 or 64 */
+    int32_t waves;          /* wavefronts per workgroup, 4 or 8; each owns 16 output features */
+    int32_t k_chunk;        /* elements of d per workgroup: 256, 512 or 1024 */
+    int32_t splits;         /* ceil(d / k_chunk), at most 64: workgroups that share an output tile */
+    int64_t grid;           /* workgroups launched */
+    uint32_t spin_limit;    /* rounds of polls for the row statistics of the other slices */
+    int32_t reserved;       /* zero */
+} ga_down_plan;
+ga_status ga_plan_gelu_and_mul_sparse_down(int64_t T, int64_t d, int64_t H, int32_t dtype, ga_down_plan *plan);
+/* Workspace for this plan (NULL: the planner's plan for T, d, H). */
+size_t ga_gelu_and_mul_sparse_down_workspace_bytes(int64_t T, int64_t d, int64_t H, const ga_down_plan *plan);
+ga_status ga_gelu_and_mul_sparse_down(const void *gu, const void *w, void *y, int64_t T, int64_t d, int64_t H,
+                                      int32_t dtype, float z, const int32_t *live_rows, void *workspace,
+                                      size_t workspace_bytes, ga_stream stream);
+ga_status ga_gelu_and_mul_sparse_down_with_plan(const void *gu, const void *w, void *y, int64_t T, int64_t d,
+                                                int64_t H, int32_t dtype, float z, const int32_t *live_rows,
+                                                const ga_down_plan *plan, void *workspace,
+                                                size_t workspace_bytes, ga_stream stream);
+
+/*
  * Host-only helper: z = Phi^-1(target_sparsity), the cutoff multiplier for
  * a target fraction of zeros (0.95 -> 1.6448536...).  NaN outside (0, 1).
  * Newton's method on the normal CDF, to full double precision.

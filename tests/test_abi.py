@@ -561,3 +561,102 @@ def test_z_from_sparsity_against_scipy_and_closed_form():
     assert ga.z_from_sparsity(0.95) == pytest.approx(1.6448536269514722, rel=1e-15)
     for bad in (0.0, 1.0, -0.5, 2.0, float("nan")):
         assert math.isnan(ga.z_from_sparsity(bad))
+
+
+# ---------------------------------------------------------------------------
+# the activation fused with the down projection
+# ---------------------------------------------------------------------------
+W_ = ctypes.c_void_p(0x7F4000000000)
+Y_ = ctypes.c_void_p(0x7F5000000000)
+
+
+def down(gu=IN, w=W_, y=Y_, T=16, d=16384, H=2048, dt=BF16, z=Z, live=None, ws=WS, ws_bytes=WS_BYTES):
+    return L.ga_gelu_and_mul_sparse_down(gu, w, y, T, d, H, dt, z, live, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(gu=None), EINVAL),
+    (dict(w=None), EINVAL),
+    (dict(y=None), EINVAL),
+    (dict(T=-1), EINVAL),
+    (dict(d=0), EINVAL),
+    (dict(H=0), EINVAL),
+    (dict(dt=7), EINVAL),
+    (dict(dt=F32), EUNSUP),
+    (dict(T=257), EUNSUP),
+    (dict(d=2044), EUNSUP),                                   # not a multiple of 8
+    (dict(d=65544), EUNSUP),
+    (dict(H=2040), EUNSUP),                                   # not a multiple of 16
+    (dict(H=65552), EUNSUP),
+    (dict(gu=ctypes.c_void_p(0x7F0000000008)), EUNSUP),       # 16-byte alignment
+    (dict(y=ctypes.c_void_p(0x7F5000000008)), EUNSUP),
+    (dict(z=ctypes.c_float(float("nan"))), EINVAL),
+    (dict(live=ctypes.c_void_p(0x7F2000000002)), EINVAL),
+    (dict(y=IN), EINVAL),                                     # y over gu
+    (dict(y=ctypes.c_void_p(0x7F4000000000 + 2048 * 16384 * 2 - 16)), EINVAL),   # y over w's tail
+    (dict(ws=None), EINVAL),
+    (dict(ws=ctypes.c_void_p(0x7F3000000010)), EINVAL),       # workspace not 256-byte aligned
+    (dict(ws_bytes=4096), EINVAL),
+    (dict(T=0), OK),
+    (dict(T=0, ws=None, ws_bytes=0), OK),
+])
+def test_down_argument_checks(kwargs, status):
+    assert down(**kwargs) == status
+    if status != OK:
+        assert len(L.ga_last_error()) > 0
+
+
+def _down_plan(T, d, H, dt=BF16):
+    p = ga.DownPlan()
+    assert L.ga_plan_gelu_and_mul_sparse_down(T, d, H, dt, ctypes.byref(p)) == OK
+    return p
+
+
+def test_down_planner_and_workspace():
+    p = _down_plan(16, 16384, 2048)
+    assert (p.rows_per_block, p.waves, p.k_chunk, p.splits, p.grid) == (16, 8, 1024, 16, 256)
+    p = _down_plan(1, 16384, 2048)
+    assert (p.rows_per_block, p.grid) == (16, 256)
+    p = _down_plan(32, 16384, 2048)
+    assert (p.rows_per_block, p.waves, p.k_chunk) == (32, 8, 512)
+    p = _down_plan(256, 8192, 2048)
+    assert (p.rows_per_block, p.waves, p.k_chunk, p.splits, p.grid) == (64, 8, 512, 16, 4 * 16 * 16)
+    # at most 64 slices of d, for every d the kernels take
+    for d in (8, 1024, 1032, 32768, 32776, 65536):
+        for T in (1, 20, 200):
+            p = _down_plan(T, d, 64)
+            assert 1 <= p.splits <= 64 and p.splits == -(-d // p.k_chunk), (T, d)
+    # one slice: no workspace
+    assert ga.gelu_and_mul_sparse_down_workspace_bytes(16, 1024, 2048) == 0
+    # the layout: header, group counters, statistics words, partial tiles
+    T, d, H = 16, 16384, 2048
+    groups, nK = 1 * 16, 16
+    assert ga.gelu_and_mul_sparse_down_workspace_bytes(T, d, H) == 256 + 256 + groups * nK * 16 * 16 + \
+        groups * nK * 16 * 128 * 8
+    assert L.ga_plan_gelu_and_mul_sparse_down(300, 1024, 64, BF16, ctypes.byref(ga.DownPlan())) == EUNSUP
+    assert L.ga_plan_gelu_and_mul_sparse_down(4, 1024, 64, F32, ctypes.byref(ga.DownPlan())) == EUNSUP
+    assert L.ga_plan_gelu_and_mul_sparse_down(4, 1024, 64, BF16, None) == EINVAL
+
+
+def test_down_with_plan_rejects_bad_geometry():
+    T, d, H = 16, 4096, 512
+
+    def run(**kw):
+        p = _down_plan(T, d, H)
+        for k, v in kw.items():
+            setattr(p, k, v)
+        return L.ga_gelu_and_mul_sparse_down_with_plan(IN, W_, Y_, T, d, H, BF16, Z, None, ctypes.byref(p),
+                                                       WS, WS_BYTES, None)
+    assert run(waves=2) == EINVAL                     # no kernel
+    assert run(rows_per_block=8) == EINVAL
+    assert run(k_chunk=2048) == EINVAL
+    assert run(splits=3) == EINVAL                    # not ceil(d / k_chunk)
+    assert run(grid=7) == EINVAL
+    assert run(spin_limit=0) == EINVAL
+    assert run(reserved=1) == EINVAL
+    p = ga.DownPlan(rows_per_block=16, waves=8, k_chunk=256, splits=-(-65536 // 256), grid=0, spin_limit=1)
+    p.grid = 1 * 4 * p.splits
+    assert L.ga_gelu_and_mul_sparse_down_with_plan(IN, W_, Y_, 16, 65536, 512, BF16, Z, None, ctypes.byref(p),
+                                                   WS, WS_BYTES, None) == EUNSUP      # 256 slices
+    assert L.ga_gelu_and_mul_sparse_down_with_plan(IN, W_, Y_, T, d, H, BF16, Z, None, None, WS, WS_BYTES,
+                                                   None) == EINVAL

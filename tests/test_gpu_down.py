@@ -1,0 +1,181 @@
+"""The activation fused with the down projection (ga_gelu_and_mul_sparse_down)
+against the oracle's fp64 composition.
+
+Tolerance, per output element y[r, h] (bf16 or fp16):
+    |y_gpu - y_ref| <= ulp(y_ref) + 2^-13 * sum_k |a[r,k] w[h,k]| + 1e-6
+where y_ref is the oracle's unrounded sum over its stored activation a.  The
+first term covers the final rounding to the element type (half an ulp, doubled
+for the fp32 sum being off by a little at a midpoint); the second the fp32
+accumulation over d terms on the matrix cores (each product is exact in fp32;
+one rounding per 32-term instruction and per slice add gives at most about
+(d / 32) * 2^-24 of the absolute sum, 2^-15 at d = 16384, and a random-walk
+typical error near 2^-19) plus activation elements that land one ulp apart
+from the oracle's (rare, since both round the same fp32 / fp64 value once)
+or flip at the cutoff (their value is under 1e-4 std, hence tiny).  A single
+wrong term of the sum moves y by about the rms of one product, far above
+this bound at the tested sizes.  Weights that pick out single activation
+elements make the sum exact and reduce the check to the activation's own
+bar (test_selection_weights_reproduce_the_activation).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_activation_amd as ga
+import synth
+from parity import BF16, F16, Z95, bits_of, compare, decode, to_device, ulp
+
+pytestmark = pytest.mark.gpu
+
+GEOMETRIES = [(16, 4, 256), (16, 4, 512), (16, 4, 1024), (16, 8, 256), (16, 8, 512), (16, 8, 1024),
+              (32, 4, 512), (32, 8, 512), (64, 4, 256), (64, 4, 512), (64, 8, 512)]
+
+
+def _plan(T, d, H, tm, waves, bk):
+    nK = -(-d // bk)
+    return ga.DownPlan(rows_per_block=tm, waves=waves, k_chunk=bk, splits=nK,
+                       grid=-(-T // tm) * -(-H // (waves * 16)) * nK, spin_limit=1 << 16)
+
+
+def _inputs(T, d, H, dt, seed):
+    x = synth.gelu_iid(T, d, seed=seed, dtype=dt, gate_std=1.0 + (seed % 3) * 0.5)
+    w = synth.down_weight(H, d, seed=seed, dtype=dt)
+    return x, w
+
+
+def _check(y_gpu_bits, oracle_lib, x, w, dt, z, live=None, label=""):
+    T = x.shape[0]
+    n = T if live is None else min(max(live, 0), T)
+    y_bits, f64, mag = oracle_lib.gelu_and_mul_sparse_down(x, w, dt, z, live=live, want_f64=True)
+    g = decode(y_gpu_bits[:n], dt)
+    ref = f64[:n]
+    tol = ulp(ref, dt) + 2.0 ** -13 * mag[:n] + 1e-6
+    err = np.abs(g - ref)
+    bad = ~(err <= tol)
+    if bad.any():
+        r, c = np.argwhere(bad)[0]
+        raise AssertionError(f"{label}: {int(bad.sum())} of {bad.size} outputs out of tolerance; first at "
+                             f"({r}, {c}): gpu {g[r, c]!r} ref {ref[r, c]!r} tol {tol[r, c]!r}")
+    return {"max_err_over_tol": float((err / tol).max()) if err.size else 0.0,
+            "bitexact_frac": float((y_gpu_bits[:n] == y_bits[:n]).mean()) if n else 1.0}
+
+
+def _run(x, w, dt, z=Z95, live=None, plan=None, out=None, workspace=None):
+    xd, wd = to_device(x, dt), to_device(w, dt)
+    lv = None if live is None else torch.tensor([live], dtype=torch.int32, device="cuda")
+    y = ga.gelu_and_mul_sparse_down(xd, wd, z=z, live_rows=lv, plan=plan, out=out, workspace=workspace)
+    torch.cuda.synchronize()
+    return bits_of(y, dt)
+
+
+@pytest.mark.parametrize("T,d,H", [(4, 2048, 256), (1, 16384, 2048), (16, 16384, 2048), (7, 1000, 48),
+                                   (33, 4104, 112), (64, 8192, 512), (200, 3072, 64), (256, 1024, 32),
+                                   (3, 8, 16)])
+def test_matches_the_oracle(T, d, H, oracle_lib):
+    print(f"down T={T} d={d} H={H}", flush=True)
+    x, w = _inputs(T, d, H, BF16, seed=T * 7 + d % 97)
+    s = _check(_run(x, w, BF16), oracle_lib, x, w, BF16, Z95, label=f"T={T} d={d} H={H}")
+    assert s["bitexact_frac"] > 0.9, s
+
+
+@pytest.mark.parametrize("T,d,H", [(16, 16384, 2048), (40, 2056, 96)])
+def test_fp16(T, d, H, oracle_lib):
+    x, w = _inputs(T, d, H, F16, seed=5)
+    _check(_run(x, w, F16), oracle_lib, x, w, F16, Z95, label=f"f16 T={T} d={d} H={H}")
+
+
+@pytest.mark.parametrize("geo", GEOMETRIES, ids=lambda g: "tm%d_w%d_bk%d" % g)
+def test_every_geometry(geo, oracle_lib):
+    tm, waves, bk = geo
+    for T, d, H in ((tm + 3, 3 * bk + 136, 16 * waves + 48), (5, 2 * bk, 32), (2 * tm, bk // 2, 16 * waves)):
+        print(f"down geo {geo} T={T} d={d} H={H}", flush=True)
+        x, w = _inputs(T, d, H, BF16, seed=tm + waves + bk)
+        plan = _plan(T, d, H, tm, waves, bk)
+        _check(_run(x, w, BF16, plan=plan), oracle_lib, x, w, BF16, Z95, label=f"{geo} T={T} d={d} H={H}")
+
+
+def test_selection_weights_reproduce_the_activation(oracle_lib):
+    """w[h, p(h)] = 2^e(h), zero elsewhere: y[r, h] = a[r, p(h)] * 2^e(h) exactly,
+    so y must meet the activation's own parity bar against the oracle."""
+    for T, d, H in ((16, 4096, 4096), (9, 1032, 512), (64, 2048, 1024)):
+        x = synth.gelu_iid(T, d, seed=T + 1)
+        rng = np.random.default_rng(d)
+        p = rng.permutation(d)[:H] if H <= d else rng.integers(0, d, H)
+        e = rng.integers(-2, 3, H)
+        wv = np.zeros((H, d))
+        wv[np.arange(H), p] = 2.0 ** e
+        w = synth.to_bits(wv, BF16)
+        y = decode(_run(x, w, BF16), BF16)
+        a_bits, _, st = oracle_lib.gelu_and_mul_sparse(x, BF16, Z95, want_f64=True, want_stats=True)
+        got = synth.to_bits(y / 2.0 ** e[None, :], BF16)      # exact: a power-of-two scale
+        gate = decode(x[:, :d], BF16)
+        compare(got, a_bits[:, p], BF16, gate=gate[:, p], stats=st, label=f"selection T={T} d={d} H={H}")
+
+
+def test_live_rows_and_untouched_tail(oracle_lib):
+    T, d, H = 40, 4096, 256
+    x, w = _inputs(T, d, H, BF16, seed=11)
+    s = int(synth.SENTINEL[BF16])
+    s = s - (1 << 16) if s >= 1 << 15 else s
+    for live in (0, 1, 17, 33, 40, 55, -3):
+        out = torch.full((T, H), s, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        got = _run(x, w, BF16, live=live, out=out)
+        n = min(max(live, 0), T)
+        assert np.all(got[n:] == synth.SENTINEL[BF16]), live
+        if n:
+            _check(got, oracle_lib, x, w, BF16, Z95, live=live, label=f"live={live}")
+
+
+def test_deterministic_and_workspace_reuse_across_shapes(oracle_lib):
+    """Calls of changing shapes share the binding's workspace (tags advance
+    per call); repeating a call gives the same bits."""
+    cases = [(16, 16384, 2048), (3, 4096, 64), (64, 8192, 512), (16, 16384, 2048), (1, 2048, 128)]
+    first = {}
+    for T, d, H in cases + cases[::-1]:
+        x, w = _inputs(T, d, H, BF16, seed=T + d)
+        got = _run(x, w, BF16)
+        if (T, d, H) in first:
+            assert np.array_equal(got, first[(T, d, H)]), (T, d, H)
+        else:
+            first[(T, d, H)] = got
+            _check(got, oracle_lib, x, w, BF16, Z95, label=f"reuse T={T} d={d} H={H}")
+
+
+def test_bounded_wait_fallback_statistics(oracle_lib):
+    """spin_limit 1: workgroups give up on the exchanged statistics almost at
+    once and compute their rows' statistics from memory; the result stays
+    within tolerance."""
+    T, d, H = 16, 8192, 512
+    x, w = _inputs(T, d, H, BF16, seed=21)
+    plan = _plan(T, d, H, 16, 8, 512)
+    plan.spin_limit = 1
+    _check(_run(x, w, BF16, plan=plan), oracle_lib, x, w, BF16, Z95, label="fallback")
+
+
+def test_graph_replay_with_changing_live_count(oracle_lib):
+    T, d, H = 32, 8192, 1024
+    x, w = _inputs(T, d, H, BF16, seed=31)
+    xd, wd = to_device(x, BF16), to_device(w, BF16)
+    live = torch.tensor([T], dtype=torch.int32, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        plan = ga.plan_gelu_and_mul_sparse_down(T, d, H)
+        ga.reserve_down_workspace(ga.gelu_and_mul_sparse_down_workspace_bytes(T, d, H, plan))
+        out = torch.zeros((T, H), dtype=torch.bfloat16, device="cuda")
+        ga.gelu_and_mul_sparse_down(xd, wd, live_rows=live, out=out)      # warm-up, outside the graph
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            ga.gelu_and_mul_sparse_down(xd, wd, live_rows=live, out=out)
+    torch.cuda.synchronize()
+    for n in (T, 5, 20, 1, T):
+        out.zero_()
+        live.fill_(n)
+        g.replay()
+        torch.cuda.synchronize()
+        got = bits_of(out, BF16)
+        assert np.all(got[n:] == 0)
+        _check(got, oracle_lib, x, w, BF16, Z95, live=n, label=f"replay live={n}")
+        # eager work on the same stream between replays
+        with torch.cuda.stream(s):
+            ga.gelu_and_mul_sparse_down(xd[:3], wd)
+        torch.cuda.synchronize()
