@@ -10,8 +10,10 @@ Cache; timing uses HIP events on the stream the kernels are launched on.
 Also measured in the same run: a streaming kernel with the same access
 pattern (the ceiling), silu_and_mul_bounded on the MoE decode buffer
 (M = 16384, d = 768, live 16384, 2048 and 64; its own roofline object, and
-the fp64 oracle's silu timed on the host beside it), and the fp64 CPU oracle
-on a bounded sample of the headline workload (the CPU baseline).
+the fp64 oracle's silu timed on the host beside it), the activation fused
+with the down projection at decode token counts against the unfused pair
+(its own roofline object and oracle timing), and the fp64 CPU oracle on a
+bounded sample of the headline workload (the CPU baseline).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 
@@ -63,6 +65,17 @@ def parse():
                    help="instead of the benchmark: launch each of the counter cases N times (and the "
                         "same-pattern streaming kernel N times where it applies), printing one 'D <label>' "
                         "line per launch, for rocprofv3 counter runs joined by dispatch order")
+    p.add_argument("--down-only", action="store_true",
+                   help="instead of the benchmark: only the fused down-projection measurements")
+    p.add_argument("--down-geometries", action="store_true",
+                   help="instead of the benchmark: time every fused down-projection geometry at each "
+                        "token count of the planner's sweep (CSV lines in the JSON)")
+    p.add_argument("--down-calls", type=int, default=0, metavar="N",
+                   help="instead of the benchmark: N fused down-projection calls at each --down-ts token count "
+                        "(default 1) on rotating weights, untimed, one 'D <label>' line per call (for rocprofv3 "
+                        "counter runs)")
+    p.add_argument("--down-ts", default="", metavar="T1,T2,...",
+                   help="token counts of the fused down-projection measurements (default 1,4,16,64,256)")
     return p.parse_args()
 
 
@@ -234,6 +247,17 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.profile_cases > 0:
         profile_cases(args.profile_cases)
+        return
+    if args.down_calls > 0:
+        down_calls(args.down_calls, tuple(int(t) for t in (args.down_ts or "1").split(",")))
+        return
+    if args.down_only or args.down_geometries:
+        dev = torch.device("cuda", 0)
+        torch.cuda.set_device(dev)
+        ts = tuple(int(t) for t in args.down_ts.split(",")) if args.down_ts else None
+        print(json.dumps({"down_projection": down_projection(
+            dev, Markers(args.markers), geometries=args.down_geometries,
+            cpu_seconds=0.0 if args.down_geometries else args.cpu_seconds, token_counts=ts)}), flush=True)
         return
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -413,6 +437,7 @@ def main():
         result["graph_replay_us_per_call"] = round(ms_g * 1e3, 3)
 
         if not args.no_sweep:
+            result["down_projection"] = down_projection(dev, markers, cpu_seconds=args.cpu_seconds)
             result["sweep"] = sweep(dev, stream, props.multi_processor_count, markers)
             markers.push("siblings")
             result["siblings"] = siblings(dev, stream)
@@ -500,6 +525,221 @@ def sweep(dev, stream, num_cus, markers):
                     "working_set_MB": round(n_sets * bytes_call / 1e6, 1), "plan": geom})
         del xs, outs, ws
     return out
+
+
+# The activation fused with the down projection: decode and small-batch
+# token counts at d = 16384 (the headline rows' width) into H = 2048 output
+# features (the pages give d, not the model width; 2048 is a synthetic choice).
+DOWN_D, DOWN_H = 16384, 2048
+DOWN_TS = (1, 4, 16, 64, 256)
+DOWN_ROOFLINE_T = 1
+DOWN_SWEEP_TS = (1, 2, 4, 8, 16, 32, 64, 128, 256)
+# (tokens, features, waves, k step) of every instantiated product kernel; the
+# geometry sweep times each at k chunks of 1, 2, 4 and 8 steps.
+DOWN_GEOMETRIES = [(16, 64, 8, 512), (16, 128, 8, 256), (16, 64, 4, 512), (16, 64, 8, 256), (16, 64, 4, 256),
+                  (16, 32, 4, 512), (16, 32, 2, 512), (16, 64, 4, 128), (32, 64, 8, 512), (32, 64, 8, 256),
+                  (32, 64, 4, 256), (64, 64, 8, 256), (64, 128, 8, 256), (64, 64, 4, 256)]
+
+
+def time_graph_on(fn, n_sets, reps, per_graph, s, warmup=8):
+    """ms per call: `per_graph` calls recorded into a HIP graph on stream s
+    and replayed `reps` times between events on s (after eager warmup calls
+    and one untimed replay)."""
+    import torch
+    with torch.cuda.stream(s):
+        for i in range(warmup):
+            fn(i % n_sets)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(per_graph):
+            fn(i % n_sets)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        g.replay()
+        start.record(s)
+        for _ in range(reps):
+            g.replay()
+        end.record(s)
+    torch.cuda.synchronize()
+    del g
+    return start.elapsed_time(end) / (reps * per_graph)
+
+
+def down_projection(dev, markers, geometries=False, cpu_seconds=0.0, token_counts=None):
+    """gelu_and_mul_sparse_down (the activation fused with the down
+    projection y = a . w^T) against the unfused pair on the same stream: the
+    activation stored by ga_gelu_and_mul_sparse, then torch.mm with the
+    weights (hipBLASLt).  Both are graph-replayed (64 launches per graph)
+    over rotating (gu, w, y) sets whose weights total 1 GiB, so each call's
+    64 MB of weights comes from HBM, as when a model's layers take turns.
+    Algorithmic bytes per fused call: w (H*d*2) + gu (T*2d*2) + y (T*H*2);
+    flops 2*T*d*H.  geometries: also time every instantiated geometry at
+    each of DOWN_SWEEP_TS (the planner's measurements)."""
+    import ctypes
+    import numpy as np
+    import torch
+    import gated_activation_amd as ga
+    import synth
+    d, H = DOWN_D, DOWN_H
+    w_bytes = H * d * 2
+    n_sets = max(2, math.ceil(ROTATE_BYTES / w_bytes))
+    w0 = torch.from_numpy(synth.down_weight(H, d, seed=1).view(np.int16)).to(dev).view(torch.bfloat16)
+    wts = [w0] + [w0.clone() for _ in range(n_sets - 1)]
+    s = torch.cuda.Stream(device=dev)
+    hs = ctypes.c_void_p(s.cuda_stream)
+    zc = ctypes.c_float(Z)
+    res = {"d": d, "H": H, "io_dtype": "bf16", "weight_sets": n_sets,
+           "workload": "gelu_and_mul_sparse then y = a . w^T, gate and up N(0,1) seed T, w N(0,1/d) seed 1, "
+                       "z=1.6448536", "rows": []}
+    sweep_rows = []
+    for T in token_counts or (DOWN_SWEEP_TS if geometries else DOWN_TS):
+        x0 = torch.from_numpy(synth.gelu_iid(T, d, seed=T).view(np.int16)).to(dev).view(torch.bfloat16)
+        xs = [x0] + [x0.clone() for _ in range(n_sets - 1)]
+        ys = [torch.empty(T, H, dtype=torch.bfloat16, device=dev) for _ in range(n_sets)]
+        acts = [torch.empty(T, d, dtype=torch.bfloat16, device=dev) for _ in range(n_sets)]
+        plan = ga.plan_gelu_and_mul_sparse_down(T, d, H)
+        plans = [plan]
+        if geometries:
+            for tm, bh, wv, step in DOWN_GEOMETRIES:
+                for ks in (step, 2 * step, 4 * step, 8 * step):
+                    if -(-d // ks) <= 64:
+                        plans.append(ga.DownPlan.of(T, d, H, tm, bh, wv, step, ks))
+        need = max(ga.gelu_and_mul_sparse_down_workspace_bytes(T, d, H, p) for p in plans)
+        wsp = ga.reserve_down_workspace(need, dev, s)
+        statuses = []
+        bytes_call = w_bytes + T * 2 * d * 2 + T * H * 2
+        flops = 2 * T * d * H
+
+        def fused_for(p):
+            args = [(ctypes.c_void_p(xs[i].data_ptr()), ctypes.c_void_p(wts[i].data_ptr()),
+                     ctypes.c_void_p(ys[i].data_ptr()), T, d, H, ga.GA_BF16, zc, None, ctypes.byref(p),
+                     ctypes.c_void_p(wsp.data_ptr()), wsp.numel(), hs) for i in range(n_sets)]
+
+            def call(i):
+                statuses.append(ga.lib.ga_gelu_and_mul_sparse_down_with_plan(*args[i]))
+            return call
+        act_args = [(ctypes.c_void_p(xs[i].data_ptr()), ctypes.c_void_p(acts[i].data_ptr()), T, d, ga.GA_BF16,
+                     zc, None, hs) for i in range(n_sets)]
+
+        def act(i):
+            statuses.append(ga.lib.ga_gelu_and_mul_sparse(*act_args[i]))
+
+        def unfused(i):
+            act(i)
+            torch.mm(acts[i], wts[i].t(), out=ys[i])
+
+        def mm_only(i):
+            torch.mm(acts[i], wts[i].t(), out=ys[i])
+        reps = 8
+        markers.push(f"down fused T={T}")
+        ms_f = time_graph_on(fused_for(plan), n_sets, reps, 64, s)
+        markers.pop()
+        if geometries:
+            for p in plans[1:]:
+                markers.push(f"down geometry T={T} tm={p.rows_per_block} bh={p.features_per_block} "
+                             f"waves={p.waves} step={p.k_step} chunk={p.k_chunk}")
+                ms_p = time_graph_on(fused_for(p), n_sets, reps, 64, s)
+                markers.pop()
+                sweep_rows.append(f"{T},{d},{H},{p.rows_per_block},{p.features_per_block},{p.waves},{p.k_step},"
+                                  f"{p.k_chunk},{ms_p * 1e3!r}")
+                print(sweep_rows[-1], file=sys.stderr, flush=True)
+            continue
+        with torch.cuda.stream(s):
+            fused_for(plan)(0)
+        torch.cuda.synchronize()
+        y_fused = ys[0].float().clone()
+        markers.push(f"down unfused T={T}")
+        ms_u = time_graph_on(unfused, n_sets, reps, 64, s)
+        markers.pop()
+        markers.push(f"down activation T={T}")
+        ms_a = time_graph_on(act, n_sets, reps, 64, s)
+        markers.pop()
+        markers.push(f"down mm T={T}")
+        ms_m = time_graph_on(mm_only, n_sets, reps, 64, s)
+        markers.pop()
+        with torch.cuda.stream(s):
+            unfused(0)
+        torch.cuda.synchronize()
+        y_unf = ys[0].float()
+        rel = float((y_fused - y_unf).abs().max() / y_unf.abs().max().clamp_min(1e-30))
+        gbps = bytes_call / (ms_f * 1e-3) / 1e9
+        res["rows"].append({
+            "T": T, "plan": plan.as_dict(), "bytes": bytes_call, "flops": flops,
+            "fused_us": round(ms_f * 1e3, 3), "unfused_us": round(ms_u * 1e3, 3),
+            "activation_us": round(ms_a * 1e3, 3), "mm_us": round(ms_m * 1e3, 3),
+            "speedup_vs_unfused": round(ms_u / ms_f, 3),
+            "GBps": round(gbps, 1), "pct_of_peak_hbm": round(100 * gbps / PEAK_HBM_GBPS, 2),
+            "TFLOPs": round(flops / (ms_f * 1e-3) / 1e12, 2),
+            "max_rel_diff_vs_unfused": rel})
+        assert all(st == ga.GA_OK for st in statuses), "a fused or activation call returned an error"
+        if T == DOWN_ROOFLINE_T:
+            res["roofline"] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                               "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                               "kernel": "down_product_kernel<bf16, tokens %d, features %d, waves %d, step %d>"
+                                         " k_chunk %d" % (plan.rows_per_block, plan.features_per_block,
+                                                          plan.waves, plan.k_step, plan.k_chunk),
+                               "T": T}
+            if cpu_seconds > 0:
+                res["cpu_baseline"], res["parity_sample"] = down_cpu_baseline(
+                    synth.gelu_iid(T, d, seed=T), synth.down_weight(H, d, seed=1), ys, xs, wts, fused_for(plan), s)
+        del xs, ys, acts
+    if geometries:
+        res["geometry_sweep_csv"] = sweep_rows
+    return res
+
+
+def down_calls(n, token_counts):
+    """n eager calls of the fused op per token count (d = 16384, H = 2048,
+    weights rotating over 1 GiB), for counter runs: each call is two
+    dispatches, the cutoffs then the product."""
+    import numpy as np
+    import torch
+    import gated_activation_amd as ga
+    import synth
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    d, H = DOWN_D, DOWN_H
+    n_sets = max(2, math.ceil(ROTATE_BYTES / (H * d * 2)))
+    w0 = torch.from_numpy(synth.down_weight(H, d, seed=1).view(np.int16)).to(dev).view(torch.bfloat16)
+    wts = [w0] + [w0.clone() for _ in range(n_sets - 1)]
+    for T in token_counts:
+        x = torch.from_numpy(synth.gelu_iid(T, d, seed=T).view(np.int16)).to(dev).view(torch.bfloat16)
+        y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+        for i in range(n):
+            ga.gelu_and_mul_sparse_down(x, wts[i % n_sets], Z, out=y)
+            torch.cuda.synchronize()
+            print(f"D down T={T} d={d} H={H} call {i}", flush=True)
+
+
+def down_cpu_baseline(xb, wb, ys, xs, wts, fused, s):
+    """The oracle's fused composition (fp64, one thread) on the roofline
+    call, timed on the host, and the GPU output of that call checked against
+    it (the parity tests' tolerance: ulp + 2^-13 of the absolute sum)."""
+    import numpy as np
+    import torch
+    import oracle
+    o = oracle.get()
+    t0 = time.perf_counter()
+    y_bits, f64, mag = o.gelu_and_mul_sparse_down(xb, wb, oracle.BF16, Z, want_f64=True)
+    dt = time.perf_counter() - t0
+    with torch.cuda.stream(s):
+        fused(0)
+    torch.cuda.synchronize()
+    g = ys[0].float().cpu().numpy().astype(np.float64)
+    a = np.abs(f64)
+    _, e = np.frexp(a)
+    ulp = np.ldexp(1.0, np.maximum(e - 1, -126) - 7)
+    tol = ulp + 2.0 ** -13 * mag + 1e-6
+    err = np.abs(g - f64)
+    T, H = f64.shape
+    bytes_call = wb.size * 2 + xb.size * 2 + T * H * 2
+    return ({"value": round(bytes_call / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+             "sample": f"one whole call, T={T} d={wb.shape[1]} H={H}: {dt:.2f} s"},
+            {"outputs": int(g.size), "max_err_over_tol": float((err / tol).max()),
+             "bitexact_frac": float((ys[0].view(torch.int16).cpu().numpy().view(np.uint16) == y_bits).mean())})
 
 
 def siblings(dev, stream):

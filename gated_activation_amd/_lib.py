@@ -36,10 +36,17 @@ class Plan(ctypes.Structure):
 
 class DownPlan(ctypes.Structure):
     """Geometry of the activation fused with the down projection."""
-    _fields_ = [("rows_per_block", ctypes.c_int32), ("waves", ctypes.c_int32),
-                ("k_chunk", ctypes.c_int32), ("splits", ctypes.c_int32),
-                ("grid", ctypes.c_int64), ("spin_limit", ctypes.c_uint32),
-                ("reserved", ctypes.c_int32)]
+    _fields_ = [("rows_per_block", ctypes.c_int32), ("features_per_block", ctypes.c_int32),
+                ("waves", ctypes.c_int32), ("k_step", ctypes.c_int32), ("k_chunk", ctypes.c_int32),
+                ("splits", ctypes.c_int32), ("grid", ctypes.c_int64)]
+
+    @classmethod
+    def of(cls, T, d, H, rows_per_block, features_per_block, waves, k_step, k_chunk):
+        """The plan of one geometry for these sizes (splits and grid derived)."""
+        splits = -(-d // k_chunk)
+        return cls(rows_per_block=rows_per_block, features_per_block=features_per_block, waves=waves,
+                   k_step=k_step, k_chunk=k_chunk, splits=splits,
+                   grid=-(-T // rows_per_block) * -(-H // features_per_block) * splits)
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -299,7 +306,7 @@ def gelu_and_mul_sparse_down(x, w, z=Z_SPARSITY_095, out=None, live_rows=None, p
     with torch.cuda.device(x.device):
         p = plan if plan is not None else plan_gelu_and_mul_sparse_down(T, d, H, _TORCH_DTYPE[x.dtype])
         need = gelu_and_mul_sparse_down_workspace_bytes(T, d, H, p)
-        if workspace is None and need > 0 and T > 0:
+        if workspace is None and T > 0:
             workspace = reserve_down_workspace(need, x.device)
         ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0

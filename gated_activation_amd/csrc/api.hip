@@ -607,23 +607,46 @@ ga_status device_scratch(ga_stream stream, void **ptr) {
 // ---------------------------------------------------------------------------
 // gelu_and_mul_sparse fused with the down projection
 // ---------------------------------------------------------------------------
-// Candidate geometries (tokens per block, waves, k chunk), most preferred
-// first, for three token ranges.
+// The geometry (tokens, waves, features, k step per workgroup) and the
+// launch size the k chunk is sized for, by token count: the fastest of the
+// measured sweep over every instantiated geometry and chunks of 1 to 8 steps
+// (d = 16384, H = 2048, bf16, token counts 1 to 256).
 struct DownGeo {
-    int tm, waves, bk;
+    int tm, waves, bh, step;
 };
-constexpr DownGeo kDownFew[] = {{16, 8, 1024}, {16, 8, 512}, {16, 8, 256}};
-constexpr DownGeo kDownMid[] = {{32, 8, 512}, {16, 8, 1024}, {16, 8, 512}};
-constexpr DownGeo kDownMany[] = {{64, 8, 512}, {32, 8, 512}, {16, 8, 1024}};
+struct DownChoice {
+    int max_T;
+    DownGeo geo;
+    int64_t groups;   // target workgroups of the product launch ...
+    int chunk_steps;  // ... or, when nonzero, a fixed k chunk of this many steps
+};
+constexpr DownChoice kDownChoice[] = {
+    {4, {16, 4, 64, 512}, 512, 0},  {8, {16, 4, 32, 512}, 512, 0},  {16, {16, 4, 64, 512}, 256, 0},
+    {64, {32, 8, 64, 512}, 256, 0}, {GA_DOWN_MAX_ROWS, {64, 8, 128, 256}, 0, 8},
+};
 
-void fill_down_plan(const DownGeo &g, int64_t T, int64_t d, int64_t H, ga_down_plan *p) {
+void fill_down_plan(const DownGeo &g, int64_t ks, int64_t T, int64_t d, int64_t H, ga_down_plan *p) {
     std::memset(p, 0, sizeof *p);
     p->rows_per_block = g.tm;
+    p->features_per_block = g.bh;
     p->waves = g.waves;
-    p->k_chunk = g.bk;
-    p->splits = (int32_t)((d + g.bk - 1) / g.bk);
-    p->grid = (T + g.tm - 1) / g.tm * ((H + g.waves * 16 - 1) / (g.waves * 16)) * p->splits;
-    p->spin_limit = kDefaultSpinLimit;
+    p->k_step = g.step;
+    p->k_chunk = (int32_t)ks;
+    p->splits = (int32_t)((d + ks - 1) / ks);
+    p->grid = (T + g.tm - 1) / g.tm * ((H + g.bh - 1) / g.bh) * p->splits;
+}
+
+// The k chunk for a geometry: whole steps, as many slices of d as bring the
+// launch to about `groups` workgroups, at most DOWN_MAX_SPLITS.
+int64_t down_chunk(const DownGeo &g, int64_t groups, int64_t T, int64_t d, int64_t H) {
+    int64_t tiles = (T + g.tm - 1) / g.tm * ((H + g.bh - 1) / g.bh);
+    if (tiles < 1) tiles = 1;  // T == 0: nothing is launched
+    int64_t slices = (groups + tiles - 1) / tiles;
+    if (slices < 1) slices = 1;
+    int64_t ks = (d + slices - 1) / slices;
+    ks = (ks + g.step - 1) / g.step * g.step;
+    const int64_t min_ks = ((d + ga::DOWN_MAX_SPLITS - 1) / ga::DOWN_MAX_SPLITS + g.step - 1) / g.step * g.step;
+    return ks < min_ks ? min_ks : ks;
 }
 
 ga_status check_down_sizes(const char *op, int64_t T, int64_t d, int64_t H, int32_t dtype) {
@@ -643,24 +666,27 @@ ga_status check_down_sizes(const char *op, int64_t T, int64_t d, int64_t H, int3
 }
 
 ga_status check_down_plan(const char *op, const ga_down_plan *p, int64_t T, int64_t d, int64_t H, int32_t dtype) {
-    if (!ga::gelu_down_available(dtype, p->rows_per_block, p->waves, p->k_chunk))
-        return fail(GA_EINVAL, "%s: no kernel for rows_per_block %d, waves %d, k_chunk %d", op,
-                    (int)p->rows_per_block, (int)p->waves, (int)p->k_chunk);
+    if (!ga::gelu_down_available(dtype, p->rows_per_block, p->waves, p->features_per_block, p->k_step))
+        return fail(GA_EINVAL, "%s: no kernel for rows_per_block %d, waves %d, features_per_block %d, k_step %d",
+                    op, (int)p->rows_per_block, (int)p->waves, (int)p->features_per_block, (int)p->k_step);
+    if (p->k_chunk < p->k_step || p->k_chunk % p->k_step != 0)
+        return fail(GA_EINVAL, "%s: k_chunk %d is not a positive multiple of k_step %d", op, (int)p->k_chunk,
+                    (int)p->k_step);
     ga_down_plan want;
-    fill_down_plan(DownGeo{p->rows_per_block, p->waves, p->k_chunk}, T, d, H, &want);
+    fill_down_plan(DownGeo{p->rows_per_block, p->waves, p->features_per_block, p->k_step}, p->k_chunk, T, d, H,
+                   &want);
     if (p->splits != want.splits || p->grid != want.grid)
         return fail(GA_EINVAL, "%s: splits %d / grid %lld do not match the geometry (%d / %lld)", op,
                     (int)p->splits, (long long)p->grid, (int)want.splits, (long long)want.grid);
     if (p->splits > ga::DOWN_MAX_SPLITS)
         return fail(GA_EUNSUPPORTED, "%s: %d slices of d above %d", op, (int)p->splits, ga::DOWN_MAX_SPLITS);
-    if (p->spin_limit == 0 || p->reserved != 0) return fail(GA_EINVAL, "%s: spin_limit 0 or reserved set", op);
     if (p->grid * p->waves * 64 >= kMaxWorkItems)
         return fail(GA_EUNSUPPORTED, "%s: %lld work-items reach 2^32", op, (long long)(p->grid * p->waves * 64));
     return GA_OK;
 }
 
 size_t down_workspace_bytes(const ga_down_plan &p, int64_t T, int64_t d, int64_t H) {
-    return ga::gelu_down_workspace_bytes(T, d, H, p.rows_per_block, p.waves, p.k_chunk);
+    return ga::gelu_down_workspace_bytes(T, d, H, p.rows_per_block, p.features_per_block, p.k_chunk);
 }
 
 }  // namespace
@@ -926,14 +952,13 @@ ga_status ga_plan_gelu_and_mul_sparse_down(int64_t T, int64_t d, int64_t H, int3
     if (plan == nullptr) return fail(GA_EINVAL, "%s: null plan", name);
     ga_status st = check_down_sizes(name, T, d, H, dtype);
     if (st != GA_OK) return st;
-    const DownGeo *cand = T <= 16 ? kDownFew : T <= 32 ? kDownMid : kDownMany;
-    for (int i = 0; i < 3; ++i) {
-        if ((d + cand[i].bk - 1) / cand[i].bk > ga::DOWN_MAX_SPLITS) continue;
-        fill_down_plan(cand[i], T, d, H, plan);
-        return GA_OK;
-    }
-    // Rows of more than 64 chunks of the preferred sizes: the longest chunk.
-    fill_down_plan(DownGeo{16, 8, 1024}, T, d, H, plan);
+    const DownChoice *c = &kDownChoice[0];
+    while (T > c->max_T) ++c;
+    int64_t ks = c->chunk_steps > 0 ? (int64_t)c->chunk_steps * c->geo.step : down_chunk(c->geo, c->groups, T, d, H);
+    const int64_t min_ks =
+        ((d + ga::DOWN_MAX_SPLITS - 1) / ga::DOWN_MAX_SPLITS + c->geo.step - 1) / c->geo.step * c->geo.step;
+    if (ks < min_ks) ks = min_ks;
+    fill_down_plan(c->geo, ks, T, d, H, plan);
     return GA_OK;
 }
 
@@ -968,15 +993,14 @@ ga_status ga_gelu_and_mul_sparse_down_with_plan(const void *gu, const void *w, v
     if ((st = check_down_plan(name, plan, T, d, H, dtype)) != GA_OK) return st;
     if (T == 0) return GA_OK;
     const size_t need = down_workspace_bytes(*plan, T, d, H);
-    if (need > 0) {
-        if (workspace == nullptr || (uintptr_t)workspace % 256 != 0)
-            return fail(GA_EINVAL, "%s: the plan needs a 256-byte aligned workspace", name);
-        if (workspace_bytes < need)
-            return fail(GA_EINVAL, "%s: workspace of %zu bytes, the plan needs %zu", name, workspace_bytes, need);
-    }
-    return launched(name, ga::launch_gelu_down(dtype, plan->rows_per_block, plan->waves, plan->k_chunk, gu, w, y,
-                                               (int32_t)T, (int32_t)d, (int32_t)H, z, live_rows, workspace,
-                                               plan->spin_limit, static_cast<hipStream_t>(stream)));
+    if (workspace == nullptr || (uintptr_t)workspace % 256 != 0)
+        return fail(GA_EINVAL, "%s: a 256-byte aligned workspace is required", name);
+    if (workspace_bytes < need)
+        return fail(GA_EINVAL, "%s: workspace of %zu bytes, the plan needs %zu", name, workspace_bytes, need);
+    return launched(name, ga::launch_gelu_down(dtype, plan->rows_per_block, plan->waves, plan->features_per_block,
+                                               plan->k_step, plan->k_chunk, gu, w, y, (int32_t)T, (int32_t)d,
+                                               (int32_t)H, z, live_rows, workspace,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 ga_status ga_gelu_and_mul_sparse_down(const void *gu, const void *w, void *y, int64_t T, int64_t d, int64_t H,

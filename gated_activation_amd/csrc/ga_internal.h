@@ -39,17 +39,26 @@ hipError_t launch_gelu_rep(int dtype, int waves, int vec_per_lane, int rep, cons
                            int32_t d, int32_t nvec, float z, const int32_t *live, hipStream_t stream);
 
 // The activation fused with the down projection y = a . w^T (w: [H, d]):
-// workgroups of tm tokens x (waves * 16) features x bk elements of d; the
-// ceil(d / bk) workgroups of one token block and feature block exchange
-// statistics and fp32 partial tiles through `workspace`
-// (gelu_down_workspace_bytes; none when bk >= d).  At most DOWN_MAX_SPLITS
-// slices per row.
+// a cutoff launch (one workgroup per row) and a product launch of
+// workgroups of tm tokens x bh features (16 per wavefront row group) x ks
+// elements of d; the ceil(d / ks) workgroups of one output tile add their
+// fp32 partials through the workspace (gelu_down_workspace_bytes).  At most
+// DOWN_MAX_SPLITS slices per row.  Workspace layout: [0, 256) the call
+// counter, the cutoffs (T floats) from byte 256, the output tiles' counters,
+// then the partial tiles.
 constexpr int DOWN_MAX_SPLITS = 64;
-bool gelu_down_available(int dtype, int tm, int waves, int bk);
-size_t gelu_down_workspace_bytes(int64_t T, int64_t d, int64_t H, int tm, int waves, int bk);
-hipError_t launch_gelu_down(int dtype, int tm, int waves, int bk, const void *gu, const void *w, void *y,
-                            int32_t T, int32_t d, int32_t H, float z, const int32_t *live, void *workspace,
-                            uint32_t spin_limit, hipStream_t stream);
+__host__ __device__ inline int64_t down_cut_offset() { return 256; }
+__host__ __device__ inline int64_t down_cnt_offset(int64_t T) { return 256 + (T * 4 + 255) / 256 * 256; }
+__host__ __device__ inline int64_t down_part_offset(int64_t T, int64_t ngroups) {
+    return down_cnt_offset(T) + (ngroups * 4 + 255) / 256 * 256;
+}
+bool gelu_down_available(int dtype, int tm, int waves, int bh, int step);
+size_t gelu_down_workspace_bytes(int64_t T, int64_t d, int64_t H, int tm, int bh, int64_t ks);
+// ks: elements of d per workgroup, a multiple of step (the k elements per
+// iteration of its loop).
+hipError_t launch_gelu_down(int dtype, int tm, int waves, int bh, int step, int32_t ks, const void *gu,
+                            const void *w, void *y, int32_t T, int32_t d, int32_t H, float z, const int32_t *live,
+                            void *workspace, hipStream_t stream);
 
 // Packed-rows path for short rows: ROWS_BLOCK threads per workgroup,
 // lanes_per_row in {4, 8, 16, 32} lanes per row, vec_per_lane in {1, 2, 4};

@@ -242,10 +242,11 @@ ga_status ga_squared_relu_bounded(const void *in, void *out, int64_t M, int64_t 
  *               (the value ga_gelu_and_mul_sparse would store);
  *     y[r, h] = sum over k of a[r, k] * w[h, k], fp32 sums on the matrix
  *               cores, rounded once to `dtype`.
- * The activation is formed inside the product's operand staging and never
- * written to memory.  The sum runs over d in slices of the plan's k_chunk;
- * the slices' fp32 partials are added in slice order, so results do not
- * depend on scheduling.
+ * The activation is formed while the product's operand is staged and is
+ * never written to memory.  Two launches on `stream`: the rows' cutoffs
+ * (into the workspace), then the product.  The sum runs over d in slices of
+ * the plan's k_chunk; the slices' fp32 partials are added in slice order, so
+ * results do not depend on scheduling.
  *   gu        [T, 2d] device array (gate | up), 16-byte aligned.
  *   w         [H, d] device array, 16-byte aligned: one row of d weights per
  *             output feature (a linear layer's weight layout).
@@ -258,26 +259,23 @@ ga_status ga_squared_relu_bounded(const void *in, void *out, int64_t M, int64_t 
  *   z, live_rows  as for ga_gelu_and_mul_sparse; rows of y at or past the
  *             live count are left untouched.
  *   workspace device memory of ga_gelu_and_mul_sparse_down_workspace_bytes()
- *             bytes (0 when the plan has one slice: then it may be NULL),
- *             256-byte aligned, zero-filled before its first use.  The kernel
- *             leaves it ready for the next call (counters back at zero, a
- *             per-call tag advanced), so it is zeroed once and serves any
- *             later calls and shapes that fit it, and graph replays.  Calls
- *             that share a workspace must not overlap in time.
- * The workgroups of one output tile wait for each other's row statistics for
- * a bounded number of polls; past it a workgroup computes the statistics of
- * its rows itself, so a launch always completes.
+ *             bytes, 256-byte aligned, zero-filled before its first use.
+ *             Each call leaves it ready for the next (tile counters back at
+ *             zero, its call counter advanced), so it is zeroed once and then
+ *             serves any later calls and shapes that fit it, and graph
+ *             replays.  Calls that share a workspace must not overlap in
+ *             time (one stream serialises them).
  */
 #define GA_DOWN_MAX_ROWS 256
 #define GA_DOWN_MAX_H 65536
 typedef struct {
-    int32_t rows_per_block; /* tokens per workgroup: 16, 32 or 64 */
-    int32_t waves;          /* wavefronts per workgroup, 4 or 8; each owns 16 output features */
-    int32_t k_chunk;        /* elements of d per workgroup: 256, 512 or 1024 */
-    int32_t splits;         /* ceil(d / k_chunk), at most 64: workgroups that share an output tile */
-    int64_t grid;           /* workgroups launched */
-    uint32_t spin_limit;    /* rounds of polls for the row statistics of the other slices */
-    int32_t reserved;       /* zero */
+    int32_t rows_per_block;     /* tokens per workgroup: 16, 32, 64 or 128 */
+    int32_t features_per_block; /* output features per workgroup: 16 per wavefront row group */
+    int32_t waves;              /* wavefronts per workgroup: row groups x parts of each step */
+    int32_t k_step;             /* elements of d per iteration of a workgroup's loop: 256 or 512 */
+    int32_t k_chunk;            /* elements of d per workgroup, a multiple of k_step */
+    int32_t splits;             /* ceil(d / k_chunk), at most 64: workgroups that share an output tile */
+    int64_t grid;               /* workgroups of the product launch */
 } ga_down_plan;
 ga_status ga_plan_gelu_and_mul_sparse_down(int64_t T, int64_t d, int64_t H, int32_t dtype, ga_down_plan *plan);
 /* Workspace for this plan (NULL: the planner's plan for T, d, H). */

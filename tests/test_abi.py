@@ -597,6 +597,7 @@ def down(gu=IN, w=W_, y=Y_, T=16, d=16384, H=2048, dt=BF16, z=Z, live=None, ws=W
     (dict(ws=None), EINVAL),
     (dict(ws=ctypes.c_void_p(0x7F3000000010)), EINVAL),       # workspace not 256-byte aligned
     (dict(ws_bytes=4096), EINVAL),
+    (dict(d=512, H=16, ws=None), EINVAL),                     # one slice still needs the cutoffs
     (dict(T=0), OK),
     (dict(T=0, ws=None, ws_bytes=0), OK),
 ])
@@ -613,26 +614,24 @@ def _down_plan(T, d, H, dt=BF16):
 
 
 def test_down_planner_and_workspace():
-    p = _down_plan(16, 16384, 2048)
-    assert (p.rows_per_block, p.waves, p.k_chunk, p.splits, p.grid) == (16, 8, 1024, 16, 256)
-    p = _down_plan(1, 16384, 2048)
-    assert (p.rows_per_block, p.grid) == (16, 256)
-    p = _down_plan(32, 16384, 2048)
-    assert (p.rows_per_block, p.waves, p.k_chunk) == (32, 8, 512)
-    p = _down_plan(256, 8192, 2048)
-    assert (p.rows_per_block, p.waves, p.k_chunk, p.splits, p.grid) == (64, 8, 512, 16, 4 * 16 * 16)
-    # at most 64 slices of d, for every d the kernels take
+    # the measured choice by token count (d = 16384, H = 2048)
+    for T, want in ((1, (16, 64, 4, 512, 1024)), (4, (16, 64, 4, 512, 1024)), (8, (16, 32, 4, 512, 2048)),
+                    (16, (16, 64, 4, 512, 2048)), (64, (32, 64, 8, 512, 4096)), (256, (64, 128, 8, 256, 2048))):
+        p = _down_plan(T, 16384, 2048)
+        assert (p.rows_per_block, p.features_per_block, p.waves, p.k_step, p.k_chunk) == want, T
+        assert p.grid == -(-T // p.rows_per_block) * (2048 // p.features_per_block) * p.splits
+    # whole steps, at most 64 slices of d, for every d the kernels take
     for d in (8, 1024, 1032, 32768, 32776, 65536):
-        for T in (1, 20, 200):
+        for T in (1, 20, 50, 200):
             p = _down_plan(T, d, 64)
             assert 1 <= p.splits <= 64 and p.splits == -(-d // p.k_chunk), (T, d)
-    # one slice: no workspace
-    assert ga.gelu_and_mul_sparse_down_workspace_bytes(16, 1024, 2048) == 0
-    # the layout: header, group counters, statistics words, partial tiles
-    T, d, H = 16, 16384, 2048
-    groups, nK = 1 * 16, 16
-    assert ga.gelu_and_mul_sparse_down_workspace_bytes(T, d, H) == 256 + 256 + groups * nK * 16 * 16 + \
-        groups * nK * 16 * 128 * 8
+            assert p.k_chunk % p.k_step == 0
+    # one slice: the workspace holds the call counter and the cutoffs only
+    assert ga.gelu_and_mul_sparse_down_workspace_bytes(16, 512, 16) == 256 + 256
+    # the layout: call counter, cutoffs, tile counters, partial tiles
+    T, d, H = 4, 16384, 2048
+    groups, nK = 32, 16
+    assert ga.gelu_and_mul_sparse_down_workspace_bytes(T, d, H) == 256 + 256 + 256 + groups * nK * 16 * 64 * 8
     assert L.ga_plan_gelu_and_mul_sparse_down(300, 1024, 64, BF16, ctypes.byref(ga.DownPlan())) == EUNSUP
     assert L.ga_plan_gelu_and_mul_sparse_down(4, 1024, 64, F32, ctypes.byref(ga.DownPlan())) == EUNSUP
     assert L.ga_plan_gelu_and_mul_sparse_down(4, 1024, 64, BF16, None) == EINVAL
@@ -649,14 +648,14 @@ def test_down_with_plan_rejects_bad_geometry():
                                                        WS, WS_BYTES, None)
     assert run(waves=2) == EINVAL                     # no kernel
     assert run(rows_per_block=8) == EINVAL
-    assert run(k_chunk=2048) == EINVAL
+    assert run(features_per_block=48) == EINVAL
+    assert run(k_step=384) == EINVAL
+    assert run(k_chunk=768) == EINVAL                 # not a multiple of the step
+    assert run(k_chunk=0) == EINVAL
     assert run(splits=3) == EINVAL                    # not ceil(d / k_chunk)
     assert run(grid=7) == EINVAL
-    assert run(spin_limit=0) == EINVAL
-    assert run(reserved=1) == EINVAL
-    p = ga.DownPlan(rows_per_block=16, waves=8, k_chunk=256, splits=-(-65536 // 256), grid=0, spin_limit=1)
-    p.grid = 1 * 4 * p.splits
+    p = ga.DownPlan.of(16, 65536, 512, 16, 64, 8, 512, 512)       # 128 slices
     assert L.ga_gelu_and_mul_sparse_down_with_plan(IN, W_, Y_, 16, 65536, 512, BF16, Z, None, ctypes.byref(p),
-                                                   WS, WS_BYTES, None) == EUNSUP      # 256 slices
+                                                   WS, WS_BYTES, None) == EUNSUP
     assert L.ga_gelu_and_mul_sparse_down_with_plan(IN, W_, Y_, T, d, H, BF16, Z, None, None, WS, WS_BYTES,
                                                    None) == EINVAL

@@ -27,14 +27,14 @@ from parity import BF16, F16, Z95, bits_of, compare, decode, to_device, ulp
 
 pytestmark = pytest.mark.gpu
 
-GEOMETRIES = [(16, 4, 256), (16, 4, 512), (16, 4, 1024), (16, 8, 256), (16, 8, 512), (16, 8, 1024),
-              (32, 4, 512), (32, 8, 512), (64, 4, 256), (64, 4, 512), (64, 8, 512)]
+# (tokens, features, waves, k step) of every instantiated product kernel
+GEOMETRIES = [(16, 64, 8, 512), (16, 128, 8, 256), (16, 64, 4, 512), (16, 64, 8, 256), (16, 64, 4, 256),
+             (16, 32, 4, 512), (16, 32, 2, 512), (16, 64, 4, 128), (32, 64, 8, 512), (32, 64, 8, 256),
+             (32, 64, 4, 256), (64, 64, 8, 256), (64, 128, 8, 256), (64, 64, 4, 256)]
 
 
-def _plan(T, d, H, tm, waves, bk):
-    nK = -(-d // bk)
-    return ga.DownPlan(rows_per_block=tm, waves=waves, k_chunk=bk, splits=nK,
-                       grid=-(-T // tm) * -(-H // (waves * 16)) * nK, spin_limit=1 << 16)
+def _plan(T, d, H, tm, bh, waves, step, ks):
+    return ga.DownPlan.of(T, d, H, tm, bh, waves, step, ks)
 
 
 def _inputs(T, d, H, dt, seed):
@@ -84,13 +84,16 @@ def test_fp16(T, d, H, oracle_lib):
     _check(_run(x, w, F16), oracle_lib, x, w, F16, Z95, label=f"f16 T={T} d={d} H={H}")
 
 
-@pytest.mark.parametrize("geo", GEOMETRIES, ids=lambda g: "tm%d_w%d_bk%d" % g)
+@pytest.mark.parametrize("geo", GEOMETRIES, ids=lambda g: "tm%d_bh%d_w%d_step%d" % g)
 def test_every_geometry(geo, oracle_lib):
-    tm, waves, bk = geo
-    for T, d, H in ((tm + 3, 3 * bk + 136, 16 * waves + 48), (5, 2 * bk, 32), (2 * tm, bk // 2, 16 * waves)):
-        print(f"down geo {geo} T={T} d={d} H={H}", flush=True)
-        x, w = _inputs(T, d, H, BF16, seed=tm + waves + bk)
-        plan = _plan(T, d, H, tm, waves, bk)
+    """Each kernel at k chunks of one and of several steps (one slice and
+    several), ragged d (a partial last step), T and H past whole blocks."""
+    tm, bh, waves, step = geo
+    for T, d, H, ks in ((tm + 3, 3 * step + 136, bh + 48, step), (5, 7 * step + 8, 32, 3 * step),
+                        (2 * tm, step // 2, bh, step), (tm, 4 * step, 2 * bh, 4 * step)):
+        print(f"down geo {geo} T={T} d={d} H={H} k_chunk={ks}", flush=True)
+        x, w = _inputs(T, d, H, BF16, seed=tm + waves + step)
+        plan = _plan(T, d, H, tm, bh, waves, step, ks)
         _check(_run(x, w, BF16, plan=plan), oracle_lib, x, w, BF16, Z95, label=f"{geo} T={T} d={d} H={H}")
 
 
@@ -128,8 +131,11 @@ def test_live_rows_and_untouched_tail(oracle_lib):
 
 def test_deterministic_and_workspace_reuse_across_shapes(oracle_lib):
     """Calls of changing shapes share the binding's workspace (tags advance
-    per call); repeating a call gives the same bits."""
-    cases = [(16, 16384, 2048), (3, 4096, 64), (64, 8192, 512), (16, 16384, 2048), (1, 2048, 128)]
+    per call, and a call's tile counters may lie where an earlier call of
+    another shape left partial tiles: T = 64 then T = 200); repeating a call
+    gives the same bits."""
+    cases = [(16, 16384, 2048), (3, 4096, 64), (64, 8192, 512), (200, 3072, 64), (16, 16384, 2048),
+             (1, 2048, 128), (256, 1024, 32)]
     first = {}
     for T, d, H in cases + cases[::-1]:
         x, w = _inputs(T, d, H, BF16, seed=T + d)
@@ -141,15 +147,14 @@ def test_deterministic_and_workspace_reuse_across_shapes(oracle_lib):
             _check(got, oracle_lib, x, w, BF16, Z95, label=f"reuse T={T} d={d} H={H}")
 
 
-def test_bounded_wait_fallback_statistics(oracle_lib):
-    """spin_limit 1: workgroups give up on the exchanged statistics almost at
-    once and compute their rows' statistics from memory; the result stays
-    within tolerance."""
-    T, d, H = 16, 8192, 512
-    x, w = _inputs(T, d, H, BF16, seed=21)
-    plan = _plan(T, d, H, 16, 8, 512)
-    plan.spin_limit = 1
-    _check(_run(x, w, BF16, plan=plan), oracle_lib, x, w, BF16, Z95, label="fallback")
+def test_cutoffs_are_per_row_statistics(oracle_lib):
+    """Rows of very different scale and offset in one call (the edge-row mix:
+    near-constant, constant, heavy-tailed): each row's cutoff comes from its
+    own statistics."""
+    T, d, H = 15, 3000, 64
+    x = synth.edge_rows(T, d, BF16)
+    w = synth.down_weight(H, d, seed=3)
+    _check(_run(x, w, BF16), oracle_lib, x, w, BF16, Z95, label="edge rows")
 
 
 def test_graph_replay_with_changing_live_count(oracle_lib):
