@@ -539,6 +539,12 @@ DOWN_SWEEP_TS = (1, 2, 4, 8, 16, 32, 64, 128, 256)
 DOWN_GEOMETRIES = [(16, 64, 8, 512), (16, 128, 8, 256), (16, 64, 4, 512), (16, 64, 8, 256), (16, 64, 4, 256),
                   (16, 32, 4, 512), (16, 32, 2, 512), (16, 64, 4, 128), (32, 64, 8, 512), (32, 64, 8, 256),
                   (32, 64, 4, 256), (64, 64, 8, 256), (64, 128, 8, 256), (64, 64, 4, 256)]
+# Decode kernels (most tokens, features per workgroup, wavefronts) and the
+# longest row each reaches.
+DOWN_DECODE_REACH = {(1, 4, 8): 16384, (1, 4, 16): 32768, (1, 4, 4): 16384, (1, 2, 8): 16384,
+                     (1, 2, 16): 32768, (1, 8, 16): 16384, (2, 4, 16): 16384, (2, 4, 8): 16384,
+                     (2, 2, 16): 16384}
+DOWN_DECODE = list(DOWN_DECODE_REACH)
 
 
 def time_graph_on(fn, n_sets, reps, per_graph, s, warmup=8):
@@ -607,6 +613,9 @@ def down_projection(dev, markers, geometries=False, cpu_seconds=0.0, token_count
                 for ks in (step, 2 * step, 4 * step, 8 * step):
                     if -(-d // ks) <= 64:
                         plans.append(ga.DownPlan.of(T, d, H, tm, bh, wv, step, ks))
+            for tmax, f, wv in DOWN_DECODE:         # the decode form (k_step 0)
+                if T <= tmax and d <= DOWN_DECODE_REACH[(tmax, f, wv)]:
+                    plans.append(ga.DownPlan.decode(T, d, H, tmax, f, wv))
         need = max(ga.gelu_and_mul_sparse_down_workspace_bytes(T, d, H, p) for p in plans)
         wsp = ga.reserve_down_workspace(need, dev, s)
         statuses = []

@@ -48,6 +48,13 @@ class DownPlan(ctypes.Structure):
                    k_step=k_step, k_chunk=k_chunk, splits=splits,
                    grid=-(-T // rows_per_block) * -(-H // features_per_block) * splits)
 
+    @classmethod
+    def decode(cls, T, d, H, rows_per_block, features_per_block, waves):
+        """The decode form (k_step 0): rows_per_block (1 or 2) >= T tokens,
+        features_per_block (2, 4 or 8) output features per workgroup."""
+        return cls(rows_per_block=rows_per_block, features_per_block=features_per_block, waves=waves, k_step=0,
+                   k_chunk=d, splits=1, grid=-(-H // features_per_block))
+
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
 
@@ -306,7 +313,7 @@ def gelu_and_mul_sparse_down(x, w, z=Z_SPARSITY_095, out=None, live_rows=None, p
     with torch.cuda.device(x.device):
         p = plan if plan is not None else plan_gelu_and_mul_sparse_down(T, d, H, _TORCH_DTYPE[x.dtype])
         need = gelu_and_mul_sparse_down_workspace_bytes(T, d, H, p)
-        if workspace is None and T > 0:
+        if workspace is None and T > 0 and need > 0:
             workspace = reserve_down_workspace(need, x.device)
         ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0

@@ -665,7 +665,49 @@ ga_status check_down_sizes(const char *op, int64_t T, int64_t d, int64_t H, int3
     return GA_OK;
 }
 
+// The decode form: k_step 0 marks a plan whose workgroups each cover all of
+// d for features_per_block output features and at most rows_per_block (1 or
+// 2) tokens.
+void fill_down_decode_plan(int tmax, int f, int waves, int64_t d, int64_t H, ga_down_plan *p) {
+    std::memset(p, 0, sizeof *p);
+    p->rows_per_block = tmax;
+    p->features_per_block = f;
+    p->waves = waves;
+    p->k_step = 0;
+    p->k_chunk = (int32_t)d;
+    p->splits = 1;
+    p->grid = (H + f - 1) / f;
+}
+
+// The planner's decode geometry for one or two tokens, by the longest row it
+// serves (measured on MI355X at H = 2048).
+struct DecodeChoice {
+    int tmax;
+    int64_t max_d;
+    int f, waves;
+};
+const DecodeChoice kDecodeChoice[] = {
+    {1, 16384, 4, 8},
+    {1, 32768, 4, 16},
+    {2, 16384, 4, 16},
+};
+
 ga_status check_down_plan(const char *op, const ga_down_plan *p, int64_t T, int64_t d, int64_t H, int32_t dtype) {
+    if (p->k_step == 0) {
+        if (!ga::gelu_down_decode_available(dtype, p->rows_per_block, p->features_per_block, p->waves, d))
+            return fail(GA_EINVAL,
+                        "%s: no decode kernel for rows_per_block %d, features_per_block %d, waves %d at d = %lld",
+                        op, (int)p->rows_per_block, (int)p->features_per_block, (int)p->waves, (long long)d);
+        if (T > p->rows_per_block)
+            return fail(GA_EINVAL, "%s: %lld tokens above the decode plan's %d", op, (long long)T,
+                        (int)p->rows_per_block);
+        ga_down_plan want;
+        fill_down_decode_plan(p->rows_per_block, p->features_per_block, p->waves, d, H, &want);
+        if (std::memcmp(&want, p, sizeof want) != 0)
+            return fail(GA_EINVAL, "%s: a decode plan has k_chunk d, splits 1 and grid ceil(H / features_per_block)",
+                        op);
+        return GA_OK;
+    }
     if (!ga::gelu_down_available(dtype, p->rows_per_block, p->waves, p->features_per_block, p->k_step))
         return fail(GA_EINVAL, "%s: no kernel for rows_per_block %d, waves %d, features_per_block %d, k_step %d",
                     op, (int)p->rows_per_block, (int)p->waves, (int)p->features_per_block, (int)p->k_step);
@@ -686,6 +728,7 @@ ga_status check_down_plan(const char *op, const ga_down_plan *p, int64_t T, int6
 }
 
 size_t down_workspace_bytes(const ga_down_plan &p, int64_t T, int64_t d, int64_t H) {
+    if (p.k_step == 0) return 0;  // the decode form keeps everything on chip
     return ga::gelu_down_workspace_bytes(T, d, H, p.rows_per_block, p.features_per_block, p.k_chunk);
 }
 
@@ -952,6 +995,16 @@ ga_status ga_plan_gelu_and_mul_sparse_down(int64_t T, int64_t d, int64_t H, int3
     if (plan == nullptr) return fail(GA_EINVAL, "%s: null plan", name);
     ga_status st = check_down_sizes(name, T, d, H, dtype);
     if (st != GA_OK) return st;
+    // One or two tokens: the decode form (one launch, no workspace), where
+    // its row fits.
+    if (T <= 2) {
+        const int tmax = T < 1 ? 1 : (int)T;
+        for (const DecodeChoice &c : kDecodeChoice)
+            if (c.tmax == tmax && d <= c.max_d && ga::gelu_down_decode_available(dtype, tmax, c.f, c.waves, d)) {
+                fill_down_decode_plan(tmax, c.f, c.waves, d, H, plan);
+                return GA_OK;
+            }
+    }
     const DownChoice *c = &kDownChoice[0];
     while (T > c->max_T) ++c;
     int64_t ks = c->chunk_steps > 0 ? (int64_t)c->chunk_steps * c->geo.step : down_chunk(c->geo, c->groups, T, d, H);
@@ -992,6 +1045,11 @@ ga_status ga_gelu_and_mul_sparse_down_with_plan(const void *gu, const void *w, v
         return fail(GA_EINVAL, "%s: y overlaps gu or w", name);
     if ((st = check_down_plan(name, plan, T, d, H, dtype)) != GA_OK) return st;
     if (T == 0) return GA_OK;
+    if (plan->k_step == 0)
+        return launched(name, ga::launch_gelu_down_decode(dtype, plan->rows_per_block, plan->features_per_block,
+                                                          plan->waves, gu, w, y,
+                                                          (int32_t)T, (int32_t)d, (int32_t)H, z, live_rows,
+                                                          static_cast<hipStream_t>(stream)));
     const size_t need = down_workspace_bytes(*plan, T, d, H);
     if (workspace == nullptr || (uintptr_t)workspace % 256 != 0)
         return fail(GA_EINVAL, "%s: a 256-byte aligned workspace is required", name);

@@ -60,6 +60,14 @@ hipError_t launch_gelu_down(int dtype, int tm, int waves, int bh, int step, int3
                             const void *w, void *y, int32_t T, int32_t d, int32_t H, float z, const int32_t *live,
                             void *workspace, hipStream_t stream);
 
+// Decode form of the fused op, for T <= tmax tokens (1 or 2): one launch, no
+// workspace; workgroups of f output features (2, 4 or 8) over all of d,
+// grid ceil(H / f).  Available where a kernel of that geometry reaches d.
+bool gelu_down_decode_available(int dtype, int tmax, int f, int waves, int64_t d);
+hipError_t launch_gelu_down_decode(int dtype, int tmax, int f, int waves, const void *gu, const void *w, void *y,
+                                   int32_t T, int32_t d, int32_t H, float z, const int32_t *live,
+                                   hipStream_t stream);
+
 // Packed-rows path for short rows: ROWS_BLOCK threads per workgroup,
 // lanes_per_row in {4, 8, 16, 32} lanes per row, vec_per_lane in {1, 2, 4};
 // grid = ceil(T / (ROWS_BLOCK / lanes_per_row)).  nvec: the row's 16-byte

@@ -243,8 +243,10 @@ ga_status ga_squared_relu_bounded(const void *in, void *out, int64_t M, int64_t 
  *     y[r, h] = sum over k of a[r, k] * w[h, k], fp32 sums on the matrix
  *               cores, rounded once to `dtype`.
  * The activation is formed while the product's operand is staged and is
- * never written to memory.  Two launches on `stream`: the rows' cutoffs
- * (into the workspace), then the product.  The sum runs over d in slices of
+ * never written to memory.  One or two tokens (rows of up to 16384
+ * elements): one launch, each workgroup reducing its tokens' statistics
+ * itself.  Otherwise two launches on `stream`: the rows' cutoffs (into the
+ * workspace), then the product.  The sum runs over d in slices of
  * the plan's k_chunk; the slices' fp32 partials are added in slice order, so
  * results do not depend on scheduling.
  *   gu        [T, 2d] device array (gate | up), 16-byte aligned.
@@ -259,7 +261,8 @@ ga_status ga_squared_relu_bounded(const void *in, void *out, int64_t M, int64_t 
  *   z, live_rows  as for ga_gelu_and_mul_sparse; rows of y at or past the
  *             live count are left untouched.
  *   workspace device memory of ga_gelu_and_mul_sparse_down_workspace_bytes()
- *             bytes, 256-byte aligned, zero-filled before its first use.
+ *             bytes, 256-byte aligned, zero-filled before its first use (the
+ *             decode form of one or two tokens needs none: NULL is accepted).
  *             Each call leaves it ready for the next (tile counters back at
  *             zero, its call counter advanced), so it is zeroed once and then
  *             serves any later calls and shapes that fit it, and graph
@@ -269,10 +272,13 @@ ga_status ga_squared_relu_bounded(const void *in, void *out, int64_t M, int64_t 
 #define GA_DOWN_MAX_ROWS 256
 #define GA_DOWN_MAX_H 65536
 typedef struct {
-    int32_t rows_per_block;     /* tokens per workgroup: 16, 32, 64 or 128 */
+    int32_t rows_per_block;     /* tokens per workgroup: 16, 32 or 64 (1 or 2 in the decode form) */
     int32_t features_per_block; /* output features per workgroup: 16 per wavefront row group */
     int32_t waves;              /* wavefronts per workgroup: row groups x parts of each step */
-    int32_t k_step;             /* elements of d per iteration of a workgroup's loop: 256 or 512 */
+    int32_t k_step;             /* elements of d per iteration of a workgroup's loop: 128, 256 or 512;
+                                   0: the decode form (rows_per_block 1 or 2 tokens,
+                                   features_per_block 2, 4 or 8 over all of d, one launch, no
+                                   workspace) */
     int32_t k_chunk;            /* elements of d per workgroup, a multiple of k_step */
     int32_t splits;             /* ceil(d / k_chunk), at most 64: workgroups that share an output tile */
     int64_t grid;               /* workgroups of the product launch */

@@ -615,7 +615,16 @@ def _down_plan(T, d, H, dt=BF16):
 
 def test_down_planner_and_workspace():
     # the measured choice by token count (d = 16384, H = 2048)
-    for T, want in ((1, (16, 64, 4, 512, 1024)), (4, (16, 64, 4, 512, 1024)), (8, (16, 32, 4, 512, 2048)),
+    for T, f, waves in ((1, 4, 8), (2, 4, 16)):   # the decode form: one launch, no workspace
+        p = _down_plan(T, 16384, 2048)
+        assert (p.rows_per_block, p.features_per_block, p.waves, p.k_step, p.k_chunk, p.splits, p.grid) == \
+            (T, f, waves, 0, 16384, 1, 2048 // f)
+        assert ga.gelu_and_mul_sparse_down_workspace_bytes(T, 16384, 2048) == 0
+    p = _down_plan(1, 32768, 2048)
+    assert (p.k_step, p.features_per_block, p.waves, p.grid) == (0, 4, 16, 512)
+    assert _down_plan(1, 32776, 2048).k_step > 0       # rows past the decode form's reach
+    assert _down_plan(2, 16392, 2048).k_step > 0
+    for T, want in ((3, (16, 64, 4, 512, 1024)), (4, (16, 64, 4, 512, 1024)), (8, (16, 32, 4, 512, 2048)),
                     (16, (16, 64, 4, 512, 2048)), (64, (32, 64, 8, 512, 4096)), (256, (64, 128, 8, 256, 2048))):
         p = _down_plan(T, 16384, 2048)
         assert (p.rows_per_block, p.features_per_block, p.waves, p.k_step, p.k_chunk) == want, T
@@ -625,9 +634,10 @@ def test_down_planner_and_workspace():
         for T in (1, 20, 50, 200):
             p = _down_plan(T, d, 64)
             assert 1 <= p.splits <= 64 and p.splits == -(-d // p.k_chunk), (T, d)
-            assert p.k_chunk % p.k_step == 0
+            assert p.k_step == 0 or p.k_chunk % p.k_step == 0
     # one slice: the workspace holds the call counter and the cutoffs only
     assert ga.gelu_and_mul_sparse_down_workspace_bytes(16, 512, 16) == 256 + 256
+    assert ga.gelu_and_mul_sparse_down_workspace_bytes(2, 512, 16) == 0        # the decode form
     # the layout: call counter, cutoffs, tile counters, partial tiles
     T, d, H = 4, 16384, 2048
     groups, nK = 32, 16
@@ -659,3 +669,19 @@ def test_down_with_plan_rejects_bad_geometry():
                                                    WS, WS_BYTES, None) == EUNSUP
     assert L.ga_gelu_and_mul_sparse_down_with_plan(IN, W_, Y_, T, d, H, BF16, Z, None, None, WS, WS_BYTES,
                                                    None) == EINVAL
+    # decode plans
+    def run_dec(T=2, d=4096, H=512, **kw):
+        p = ga.DownPlan.decode(T, d, H, 2, 4, 8)
+        for k, v in kw.items():
+            setattr(p, k, v)
+        return L.ga_gelu_and_mul_sparse_down_with_plan(IN, W_, Y_, T, d, H, BF16, Z, None, ctypes.byref(p),
+                                                       None, 0, None)
+    assert run_dec(T=3) == EINVAL                     # more tokens than the plan holds
+    assert run_dec(d=32768) == EINVAL                 # row past the kernel's reach
+    assert run_dec(rows_per_block=4) == EINVAL        # no such kernel
+    assert run_dec(features_per_block=16) == EINVAL
+    assert run_dec(features_per_block=8, grid=64) == EINVAL   # no 8-feature, 8-wave kernel for two tokens
+    assert run_dec(waves=4) == EINVAL
+    assert run_dec(k_chunk=2048) == EINVAL
+    assert run_dec(grid=3) == EINVAL
+    assert run_dec(T=0) == OK                         # nothing to do

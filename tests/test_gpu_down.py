@@ -97,10 +97,50 @@ def test_every_geometry(geo, oracle_lib):
         _check(_run(x, w, BF16, plan=plan), oracle_lib, x, w, BF16, Z95, label=f"{geo} T={T} d={d} H={H}")
 
 
+# (most tokens, features per workgroup, wavefronts): every decode kernel
+DECODE = [(1, 4, 8), (1, 4, 16), (1, 4, 4), (1, 2, 8), (1, 2, 16), (1, 8, 16), (2, 4, 16), (2, 4, 8), (2, 2, 16)]
+# those that also reach 32768-element rows
+DECODE_LONG = {(1, 4, 16), (1, 2, 16)}
+
+
+@pytest.mark.parametrize("tmax,f,waves", DECODE)
+def test_decode_form(tmax, f, waves, oracle_lib):
+    """The one-launch decode form (k_step 0: each workgroup f features over
+    all of d, its tokens' statistics reduced in the workgroup), at full rows,
+    ragged d (a partial last vector group), the smallest shapes and every
+    live count up to its token capacity."""
+    shapes = [(tmax, 16384, 2048), (tmax, 1000, 48), (1, 8, 16), (tmax, 4104, 16)]
+    if (tmax, f, waves) in DECODE_LONG:
+        shapes.append((tmax, 32768, 64))
+    for T, d, H in shapes:
+        if T > tmax:
+            continue
+        x, w = _inputs(T, d, H, BF16, seed=tmax * 10 + waves + f + d % 13)
+        plan = ga.DownPlan.decode(T, d, H, tmax, f, waves)
+        print(f"decode tmax={tmax} f={f} waves={waves} T={T} d={d} H={H}", flush=True)
+        _check(_run(x, w, BF16, plan=plan), oracle_lib, x, w, BF16, Z95, label=f"decode T={T} d={d} H={H}")
+        for live in range(0, T + 1):
+            s = int(synth.SENTINEL[BF16])
+            s = s - (1 << 16) if s >= 1 << 15 else s
+            out = torch.full((T, H), s, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+            got = _run(x, w, BF16, plan=plan, live=live, out=out)
+            assert np.all(got[live:] == synth.SENTINEL[BF16])
+            if live:
+                _check(got, oracle_lib, x, w, BF16, Z95, live=live, label=f"decode live={live}")
+
+
+@pytest.mark.parametrize("tmax,f,waves", [(1, 4, 8), (2, 4, 16)])
+def test_decode_form_fp16(tmax, f, waves, oracle_lib):
+    for T, d, H in ((tmax, 16384, 256), (tmax, 2056, 32)):
+        x, w = _inputs(T, d, H, F16, seed=d + T)
+        plan = ga.DownPlan.decode(T, d, H, tmax, f, waves)
+        _check(_run(x, w, F16, plan=plan), oracle_lib, x, w, F16, Z95, label=f"decode fp16 T={T} d={d} H={H}")
+
+
 def test_selection_weights_reproduce_the_activation(oracle_lib):
     """w[h, p(h)] = 2^e(h), zero elsewhere: y[r, h] = a[r, p(h)] * 2^e(h) exactly,
     so y must meet the activation's own parity bar against the oracle."""
-    for T, d, H in ((16, 4096, 4096), (9, 1032, 512), (64, 2048, 1024)):
+    for T, d, H in ((16, 4096, 4096), (9, 1032, 512), (64, 2048, 1024), (1, 4096, 4096), (2, 2048, 1024)):
         x = synth.gelu_iid(T, d, seed=T + 1)
         rng = np.random.default_rng(d)
         p = rng.permutation(d)[:H] if H <= d else rng.integers(0, d, H)
