@@ -44,6 +44,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gelu_and_mul_sparse_T2048_d16384_
 KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("gelu_sparse.hip", "ga_device.h")]
 SILU_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "silu_and_mul_bounded_M16384_d768_bf16.traffic.txt")
 SILU_SOURCES = [os.path.join(CSRC, f) for f in ("elementwise.hip", "ga_device.h")]
+DOWN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gelu_and_mul_sparse_down_d16384_H2048_bf16.traffic.txt")
+DOWN_SOURCES = [os.path.join(CSRC, f) for f in ("gelu_sparse_decode.hip", "ga_device.h")]
 
 
 def parse():
@@ -685,12 +687,17 @@ def down_projection(dev, markers, geometries=False, cpu_seconds=0.0, token_count
             "max_rel_diff_vs_unfused": rel})
         assert all(st == ga.GA_OK for st in statuses), "a fused or activation call returned an error"
         if T == DOWN_ROOFLINE_T:
+            if plan.k_step == 0:
+                kname = "down_decode_kernel<bf16, tokens %d, features %d, waves %d>" % (
+                    plan.rows_per_block, plan.features_per_block, plan.waves)
+            else:
+                kname = "down_product_kernel<bf16, tokens %d, features %d, waves %d, step %d> k_chunk %d" % (
+                    plan.rows_per_block, plan.features_per_block, plan.waves, plan.k_step, plan.k_chunk)
             res["roofline"] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                               "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None,
-                               "kernel": "down_product_kernel<bf16, tokens %d, features %d, waves %d, step %d>"
-                                         " k_chunk %d" % (plan.rows_per_block, plan.features_per_block,
-                                                          plan.waves, plan.k_step, plan.k_chunk),
-                               "T": T}
+                               "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                               "traffic": recorded_traffic(DOWN_TRAFFIC_FILE, DOWN_SOURCES,
+                                                           f"T{T}_hbm_bytes_per_call"),
+                               "kernel": kname, "launches_per_call": 1 if plan.k_step == 0 else 2, "T": T}
             if cpu_seconds > 0:
                 res["cpu_baseline"], res["parity_sample"] = down_cpu_baseline(
                     synth.gelu_iid(T, d, seed=T), synth.down_weight(H, d, seed=1), ys, xs, wts, fused_for(plan), s)
@@ -702,8 +709,9 @@ def down_projection(dev, markers, geometries=False, cpu_seconds=0.0, token_count
 
 def down_calls(n, token_counts):
     """n eager calls of the fused op per token count (d = 16384, H = 2048,
-    weights rotating over 1 GiB), for counter runs: each call is two
-    dispatches, the cutoffs then the product."""
+    weights rotating over 1 GiB), for counter runs: each call is one
+    dispatch for one or two tokens (the decode form), else two (the cutoffs,
+    then the product)."""
     import numpy as np
     import torch
     import gated_activation_amd as ga
