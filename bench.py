@@ -533,7 +533,7 @@ def sweep(dev, stream, num_cus, markers):
 # token counts at d = 16384 (the headline rows' width) into H = 2048 output
 # features (the pages give d, not the model width; 2048 is a synthetic choice).
 DOWN_D, DOWN_H = 16384, 2048
-DOWN_TS = (1, 4, 16, 64, 256)
+DOWN_TS = (1, 2, 4, 16, 64, 256)
 DOWN_ROOFLINE_T = 1
 DOWN_SWEEP_TS = (1, 2, 4, 8, 16, 32, 64, 128, 256)
 # (tokens, features, waves, k step) of every instantiated product kernel; the

@@ -6,12 +6,13 @@ Tolerance, per output element y[r, h] (bf16 or fp16):
 where y_ref is the oracle's unrounded sum over its stored activation a.  The
 first term covers the final rounding to the element type (half an ulp, doubled
 for the fp32 sum being off by a little at a midpoint); the second the fp32
-accumulation over d terms on the matrix cores (each product is exact in fp32;
+accumulation over d terms (each product is exact in fp32; on the matrix cores
 one rounding per 32-term instruction and per slice add gives at most about
 (d / 32) * 2^-24 of the absolute sum, 2^-15 at d = 16384, and a random-walk
-typical error near 2^-19) plus activation elements that land one ulp apart
-from the oracle's (rare, since both round the same fp32 / fp64 value once)
-or flip at the cutoff (their value is under 1e-4 std, hence tiny).  A single
+typical error near 2^-19; the decode form's chains of at most 32 FMAs per
+lane, then 6 lane and at most 16 wavefront adds, stay below 2^-18) plus
+activation elements that land one ulp apart from the oracle's (rare, since
+both round the same fp32 / fp64 value once) or flip at the cutoff (their value is under 1e-4 std, hence tiny).  A single
 wrong term of the sum moves y by about the rms of one product, far above
 this bound at the tested sizes.  Weights that pick out single activation
 elements make the sum exact and reduce the check to the activation's own
