@@ -547,6 +547,8 @@ DOWN_DECODE_REACH = {(1, 4, 8): 16384, (1, 4, 16): 32768, (1, 4, 4): 16384, (1, 
                      (1, 2, 16): 32768, (1, 8, 16): 16384, (2, 4, 16): 16384, (2, 4, 8): 16384,
                      (2, 2, 16): 16384}
 DOWN_DECODE = list(DOWN_DECODE_REACH)
+# Staged-form product kernels (most tokens, features per workgroup, wavefronts) and their reach.
+DOWN_STAGED_REACH = {(2, 4, 16): 16384, (4, 4, 16): 16384}
 
 
 def time_graph_on(fn, n_sets, reps, per_graph, s, warmup=8):
@@ -615,9 +617,12 @@ def down_projection(dev, markers, geometries=False, cpu_seconds=0.0, token_count
                 for ks in (step, 2 * step, 4 * step, 8 * step):
                     if -(-d // ks) <= 64:
                         plans.append(ga.DownPlan.of(T, d, H, tm, bh, wv, step, ks))
-            for tmax, f, wv in DOWN_DECODE:         # the decode form (k_step 0)
+            for tmax, f, wv in DOWN_DECODE:         # the decode form
                 if T <= tmax and d <= DOWN_DECODE_REACH[(tmax, f, wv)]:
                     plans.append(ga.DownPlan.decode(T, d, H, tmax, f, wv))
+            for (tmax, f, wv), reach in DOWN_STAGED_REACH.items():   # the staged form
+                if T <= tmax and d <= reach:
+                    plans.append(ga.DownPlan.staged(T, d, H, tmax, f, wv))
         need = max(ga.gelu_and_mul_sparse_down_workspace_bytes(T, d, H, p) for p in plans)
         wsp = ga.reserve_down_workspace(need, dev, s)
         statuses = []
@@ -650,12 +655,12 @@ def down_projection(dev, markers, geometries=False, cpu_seconds=0.0, token_count
         markers.pop()
         if geometries:
             for p in plans[1:]:
-                markers.push(f"down geometry T={T} tm={p.rows_per_block} bh={p.features_per_block} "
+                markers.push(f"down geometry T={T} form={p.form} tm={p.rows_per_block} bh={p.features_per_block} "
                              f"waves={p.waves} step={p.k_step} chunk={p.k_chunk}")
                 ms_p = time_graph_on(fused_for(p), n_sets, reps, 64, s)
                 markers.pop()
-                sweep_rows.append(f"{T},{d},{H},{p.rows_per_block},{p.features_per_block},{p.waves},{p.k_step},"
-                                  f"{p.k_chunk},{ms_p * 1e3!r}")
+                sweep_rows.append(f"{T},{d},{H},{p.form},{p.rows_per_block},{p.features_per_block},{p.waves},"
+                                  f"{p.k_step},{p.k_chunk},{ms_p * 1e3!r}")
                 print(sweep_rows[-1], file=sys.stderr, flush=True)
             continue
         with torch.cuda.stream(s):
@@ -687,9 +692,12 @@ def down_projection(dev, markers, geometries=False, cpu_seconds=0.0, token_count
             "max_rel_diff_vs_unfused": rel})
         assert all(st == ga.GA_OK for st in statuses), "a fused or activation call returned an error"
         if T == DOWN_ROOFLINE_T:
-            if plan.k_step == 0:
+            if plan.form == ga.GA_DOWN_DECODE:
                 kname = "down_decode_kernel<bf16, tokens %d, features %d, waves %d>" % (
                     plan.rows_per_block, plan.features_per_block, plan.waves)
+            elif plan.form == ga.GA_DOWN_STAGED:
+                kname = "gelu_and_mul_sparse row kernel, then down_staged_kernel<bf16, tokens %d, features %d, " \
+                        "waves %d>" % (plan.rows_per_block, plan.features_per_block, plan.waves)
             else:
                 kname = "down_product_kernel<bf16, tokens %d, features %d, waves %d, step %d> k_chunk %d" % (
                     plan.rows_per_block, plan.features_per_block, plan.waves, plan.k_step, plan.k_chunk)
@@ -697,7 +705,8 @@ def down_projection(dev, markers, geometries=False, cpu_seconds=0.0, token_count
                                "frac": round(gbps / PEAK_HBM_GBPS, 4),
                                "traffic": recorded_traffic(DOWN_TRAFFIC_FILE, DOWN_SOURCES,
                                                            f"T{T}_hbm_bytes_per_call"),
-                               "kernel": kname, "launches_per_call": 1 if plan.k_step == 0 else 2, "T": T}
+                               "kernel": kname, "launches_per_call": 1 if plan.form == ga.GA_DOWN_DECODE else 2,
+                               "T": T}
             if cpu_seconds > 0:
                 res["cpu_baseline"], res["parity_sample"] = down_cpu_baseline(
                     synth.gelu_iid(T, d, seed=T), synth.down_weight(H, d, seed=1), ys, xs, wts, fused_for(plan), s)
@@ -710,8 +719,8 @@ def down_projection(dev, markers, geometries=False, cpu_seconds=0.0, token_count
 def down_calls(n, token_counts):
     """n eager calls of the fused op per token count (d = 16384, H = 2048,
     weights rotating over 1 GiB), for counter runs: each call is one
-    dispatch for one or two tokens (the decode form), else two (the cutoffs,
-    then the product)."""
+    dispatch in the decode form, two otherwise (the activation or the
+    cutoffs, then the product)."""
     import numpy as np
     import torch
     import gated_activation_amd as ga

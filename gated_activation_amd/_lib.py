@@ -34,26 +34,40 @@ class Plan(ctypes.Structure):
         return {k: getattr(self, k) for k, _ in self._fields_}
 
 
+GA_DOWN_KLOOP, GA_DOWN_DECODE, GA_DOWN_STAGED = 0, 1, 2
+
+
 class DownPlan(ctypes.Structure):
     """Geometry of the activation fused with the down projection."""
     _fields_ = [("rows_per_block", ctypes.c_int32), ("features_per_block", ctypes.c_int32),
                 ("waves", ctypes.c_int32), ("k_step", ctypes.c_int32), ("k_chunk", ctypes.c_int32),
-                ("splits", ctypes.c_int32), ("grid", ctypes.c_int64)]
+                ("splits", ctypes.c_int32), ("form", ctypes.c_int32), ("grid", ctypes.c_int64)]
 
     @classmethod
     def of(cls, T, d, H, rows_per_block, features_per_block, waves, k_step, k_chunk):
-        """The plan of one geometry for these sizes (splits and grid derived)."""
+        """The k-loop form's plan of one geometry for these sizes (splits and
+        grid derived)."""
         splits = -(-d // k_chunk)
         return cls(rows_per_block=rows_per_block, features_per_block=features_per_block, waves=waves,
-                   k_step=k_step, k_chunk=k_chunk, splits=splits,
+                   k_step=k_step, k_chunk=k_chunk, splits=splits, form=GA_DOWN_KLOOP,
                    grid=-(-T // rows_per_block) * -(-H // features_per_block) * splits)
 
     @classmethod
-    def decode(cls, T, d, H, rows_per_block, features_per_block, waves):
-        """The decode form (k_step 0): rows_per_block (1 or 2) >= T tokens,
-        features_per_block (2, 4 or 8) output features per workgroup."""
+    def _whole(cls, form, d, H, rows_per_block, features_per_block, waves):
         return cls(rows_per_block=rows_per_block, features_per_block=features_per_block, waves=waves, k_step=0,
-                   k_chunk=d, splits=1, grid=-(-H // features_per_block))
+                   k_chunk=d, splits=1, form=form, grid=-(-H // features_per_block))
+
+    @classmethod
+    def decode(cls, T, d, H, rows_per_block, features_per_block, waves):
+        """The decode form: rows_per_block (1 or 2) >= T tokens,
+        features_per_block output features per workgroup over all of d."""
+        return cls._whole(GA_DOWN_DECODE, d, H, rows_per_block, features_per_block, waves)
+
+    @classmethod
+    def staged(cls, T, d, H, rows_per_block, features_per_block, waves):
+        """The staged form: rows_per_block (2 or 4) >= T tokens; the
+        activation is stored into the workspace, then multiplied."""
+        return cls._whole(GA_DOWN_STAGED, d, H, rows_per_block, features_per_block, waves)
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}

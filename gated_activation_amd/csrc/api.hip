@@ -10,6 +10,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
+#include <cstddef>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -665,10 +666,19 @@ ga_status check_down_sizes(const char *op, int64_t T, int64_t d, int64_t H, int3
     return GA_OK;
 }
 
-// The decode form: k_step 0 marks a plan whose workgroups each cover all of
-// d for features_per_block output features and at most rows_per_block (1 or
-// 2) tokens.
-void fill_down_decode_plan(int tmax, int f, int waves, int64_t d, int64_t H, ga_down_plan *p) {
+static_assert(sizeof(ga_down_plan) == 40 && offsetof(ga_down_plan, grid) == 32, "ga_down_plan layout");
+
+// Field by field: the struct has padding before `grid`, which a caller need
+// not have cleared.
+bool same_down_plan(const ga_down_plan &a, const ga_down_plan &b) {
+    return a.rows_per_block == b.rows_per_block && a.features_per_block == b.features_per_block &&
+           a.waves == b.waves && a.k_step == b.k_step && a.k_chunk == b.k_chunk && a.splits == b.splits &&
+           a.form == b.form && a.grid == b.grid;
+}
+
+// The decode and staged forms: every workgroup covers all of d for
+// features_per_block output features and at most rows_per_block tokens.
+void fill_down_whole_plan(int form, int tmax, int f, int waves, int64_t d, int64_t H, ga_down_plan *p) {
     std::memset(p, 0, sizeof *p);
     p->rows_per_block = tmax;
     p->features_per_block = f;
@@ -676,38 +686,49 @@ void fill_down_decode_plan(int tmax, int f, int waves, int64_t d, int64_t H, ga_
     p->k_step = 0;
     p->k_chunk = (int32_t)d;
     p->splits = 1;
+    p->form = form;
     p->grid = (H + f - 1) / f;
 }
 
-// The planner's decode geometry for one or two tokens, by the longest row it
-// serves (measured on MI355X at H = 2048).
-struct DecodeChoice {
-    int tmax;
+bool down_whole_available(int form, int32_t dtype, int tmax, int f, int waves, int64_t d) {
+    return form == GA_DOWN_DECODE ? ga::gelu_down_decode_available(dtype, tmax, f, waves, d)
+                                  : ga::gelu_down_staged_available(dtype, tmax, f, waves, d);
+}
+
+// The planner's choice for one to four tokens, by the longest row it serves
+// (measured on MI355X at H = 2048): the first entry whose token capacity is
+// the call's rounded up to 1, 2 or 4 and whose reach covers d.
+struct WholeChoice {
+    int form, tmax;
     int64_t max_d;
     int f, waves;
 };
-const DecodeChoice kDecodeChoice[] = {
-    {1, 16384, 4, 8},
-    {1, 32768, 4, 16},
-    {2, 16384, 4, 16},
+const WholeChoice kWholeChoice[] = {
+    {GA_DOWN_DECODE, 1, 16384, 4, 8},
+    {GA_DOWN_DECODE, 1, 32768, 4, 16},
+    {GA_DOWN_STAGED, 2, 16384, 4, 16},
+    {GA_DOWN_STAGED, 4, 16384, 4, 16},
 };
 
 ga_status check_down_plan(const char *op, const ga_down_plan *p, int64_t T, int64_t d, int64_t H, int32_t dtype) {
-    if (p->k_step == 0) {
-        if (!ga::gelu_down_decode_available(dtype, p->rows_per_block, p->features_per_block, p->waves, d))
+    if (p->form == GA_DOWN_DECODE || p->form == GA_DOWN_STAGED) {
+        const char *what = p->form == GA_DOWN_DECODE ? "decode" : "staged";
+        if (!down_whole_available(p->form, dtype, p->rows_per_block, p->features_per_block, p->waves, d))
             return fail(GA_EINVAL,
-                        "%s: no decode kernel for rows_per_block %d, features_per_block %d, waves %d at d = %lld",
-                        op, (int)p->rows_per_block, (int)p->features_per_block, (int)p->waves, (long long)d);
+                        "%s: no %s kernel for rows_per_block %d, features_per_block %d, waves %d at d = %lld", op,
+                        what, (int)p->rows_per_block, (int)p->features_per_block, (int)p->waves, (long long)d);
         if (T > p->rows_per_block)
-            return fail(GA_EINVAL, "%s: %lld tokens above the decode plan's %d", op, (long long)T,
+            return fail(GA_EINVAL, "%s: %lld tokens above the %s plan's %d", op, (long long)T, what,
                         (int)p->rows_per_block);
         ga_down_plan want;
-        fill_down_decode_plan(p->rows_per_block, p->features_per_block, p->waves, d, H, &want);
-        if (std::memcmp(&want, p, sizeof want) != 0)
-            return fail(GA_EINVAL, "%s: a decode plan has k_chunk d, splits 1 and grid ceil(H / features_per_block)",
-                        op);
+        fill_down_whole_plan(p->form, p->rows_per_block, p->features_per_block, p->waves, d, H, &want);
+        if (!same_down_plan(want, *p))
+            return fail(GA_EINVAL,
+                        "%s: a %s plan has k_step 0, k_chunk d, splits 1 and grid ceil(H / features_per_block)",
+                        op, what);
         return GA_OK;
     }
+    if (p->form != GA_DOWN_KLOOP) return fail(GA_EINVAL, "%s: unknown plan form %d", op, (int)p->form);
     if (!ga::gelu_down_available(dtype, p->rows_per_block, p->waves, p->features_per_block, p->k_step))
         return fail(GA_EINVAL, "%s: no kernel for rows_per_block %d, waves %d, features_per_block %d, k_step %d",
                     op, (int)p->rows_per_block, (int)p->waves, (int)p->features_per_block, (int)p->k_step);
@@ -728,7 +749,8 @@ ga_status check_down_plan(const char *op, const ga_down_plan *p, int64_t T, int6
 }
 
 size_t down_workspace_bytes(const ga_down_plan &p, int64_t T, int64_t d, int64_t H) {
-    if (p.k_step == 0) return 0;  // the decode form keeps everything on chip
+    if (p.form == GA_DOWN_DECODE) return 0;  // everything stays on chip
+    if (p.form == GA_DOWN_STAGED) return (size_t)((T * d * 2 + 255) / 256 * 256);  // the stored activation
     return ga::gelu_down_workspace_bytes(T, d, H, p.rows_per_block, p.features_per_block, p.k_chunk);
 }
 
@@ -997,11 +1019,11 @@ ga_status ga_plan_gelu_and_mul_sparse_down(int64_t T, int64_t d, int64_t H, int3
     if (st != GA_OK) return st;
     // One or two tokens: the decode form (one launch, no workspace), where
     // its row fits.
-    if (T <= 2) {
-        const int tmax = T < 1 ? 1 : (int)T;
-        for (const DecodeChoice &c : kDecodeChoice)
-            if (c.tmax == tmax && d <= c.max_d && ga::gelu_down_decode_available(dtype, tmax, c.f, c.waves, d)) {
-                fill_down_decode_plan(tmax, c.f, c.waves, d, H, plan);
+    if (T <= 4) {
+        const int tmax = T <= 1 ? 1 : T <= 2 ? 2 : 4;
+        for (const WholeChoice &c : kWholeChoice)
+            if (c.tmax == tmax && d <= c.max_d && down_whole_available(c.form, dtype, tmax, c.f, c.waves, d)) {
+                fill_down_whole_plan(c.form, tmax, c.f, c.waves, d, H, plan);
                 return GA_OK;
             }
     }
@@ -1045,7 +1067,7 @@ ga_status ga_gelu_and_mul_sparse_down_with_plan(const void *gu, const void *w, v
         return fail(GA_EINVAL, "%s: y overlaps gu or w", name);
     if ((st = check_down_plan(name, plan, T, d, H, dtype)) != GA_OK) return st;
     if (T == 0) return GA_OK;
-    if (plan->k_step == 0)
+    if (plan->form == GA_DOWN_DECODE)
         return launched(name, ga::launch_gelu_down_decode(dtype, plan->rows_per_block, plan->features_per_block,
                                                           plan->waves, gu, w, y,
                                                           (int32_t)T, (int32_t)d, (int32_t)H, z, live_rows,
@@ -1055,6 +1077,22 @@ ga_status ga_gelu_and_mul_sparse_down_with_plan(const void *gu, const void *w, v
         return fail(GA_EINVAL, "%s: a 256-byte aligned workspace is required", name);
     if (workspace_bytes < need)
         return fail(GA_EINVAL, "%s: workspace of %zu bytes, the plan needs %zu", name, workspace_bytes, need);
+    if (overlaps(workspace, need, gu, (size_t)T * 2 * (size_t)d * es) ||
+        overlaps(workspace, need, w, (size_t)H * (size_t)d * es) || overlaps(workspace, need, y, y_bytes))
+        return fail(GA_EINVAL, "%s: the workspace overlaps gu, w or y", name);
+    if (plan->form == GA_DOWN_STAGED) {
+        // The activation of the call's rows into the workspace, by the row
+        // kernel ga_gelu_and_mul_sparse would run (no workspace of its own),
+        // then the product against it.
+        ga_plan act;
+        if ((st = ga_plan_gelu_and_mul_sparse(T, d, dtype, vector_aligned(gu, workspace, d, dtype), 256, 0, &act)) !=
+            GA_OK)
+            return st;
+        if ((st = launch_gelu(gu, workspace, T, d, dtype, z, live_rows, act, nullptr, stream)) != GA_OK) return st;
+        return launched(name, ga::launch_gelu_down_staged(dtype, plan->rows_per_block, plan->features_per_block,
+                                                          plan->waves, workspace, w, y, (int32_t)T, (int32_t)d,
+                                                          (int32_t)H, live_rows, static_cast<hipStream_t>(stream)));
+    }
     return launched(name, ga::launch_gelu_down(dtype, plan->rows_per_block, plan->waves, plan->features_per_block,
                                                plan->k_step, plan->k_chunk, gu, w, y, (int32_t)T, (int32_t)d,
                                                (int32_t)H, z, live_rows, workspace,

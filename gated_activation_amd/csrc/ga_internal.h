@@ -68,6 +68,13 @@ hipError_t launch_gelu_down_decode(int dtype, int tmax, int f, int waves, const 
                                    int32_t T, int32_t d, int32_t H, float z, const int32_t *live,
                                    hipStream_t stream);
 
+// Staged form's product launch, for T <= tmax tokens (2 or 4): y = a . w^T
+// with a the stored activation ([T, d], rows past the live count not read);
+// workgroups of f output features over all of d, grid ceil(H / f).
+bool gelu_down_staged_available(int dtype, int tmax, int f, int waves, int64_t d);
+hipError_t launch_gelu_down_staged(int dtype, int tmax, int f, int waves, const void *a, const void *w, void *y,
+                                   int32_t T, int32_t d, int32_t H, const int32_t *live, hipStream_t stream);
+
 // Packed-rows path for short rows: ROWS_BLOCK threads per workgroup,
 // lanes_per_row in {4, 8, 16, 32} lanes per row, vec_per_lane in {1, 2, 4};
 // grid = ceil(T / (ROWS_BLOCK / lanes_per_row)).  nvec: the row's 16-byte

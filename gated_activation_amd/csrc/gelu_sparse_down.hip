@@ -7,9 +7,9 @@
 // write feed the layer's downstream projection; here the activation never
 // reaches memory: it is formed while the product's operand is staged.
 //
-// This file holds the form for three or more tokens (one or two tokens: the
-// one-launch decode form, gelu_sparse_decode.hip).  Two launches on the
-// caller's stream.
+// This file holds the k-loop form, for five or more tokens (one token: the
+// one-launch decode form, gelu_sparse_decode.hip; two to four: the staged
+// form, gelu_sparse_staged.hip).  Two launches on the caller's stream.
 //
 // 1. down_cutoff_kernel, one workgroup per row: the row's mean and
 //    population variance (two passes over the gate, fp32) and the cutoff

@@ -240,15 +240,21 @@ ga_status ga_squared_relu_bounded(const void *in, void *out, int64_t M, int64_t 
  * order).  For live rows r and output features h:
  *     a[r, k] = gelu_and_mul_sparse(gu)[r, k], rounded once to `dtype`
  *               (the value ga_gelu_and_mul_sparse would store);
- *     y[r, h] = sum over k of a[r, k] * w[h, k], fp32 sums on the matrix
- *               cores, rounded once to `dtype`.
- * The activation is formed while the product's operand is staged and is
- * never written to memory.  One or two tokens (rows of up to 16384
- * elements): one launch, each workgroup reducing its tokens' statistics
- * itself.  Otherwise two launches on `stream`: the rows' cutoffs (into the
- * workspace), then the product.  The sum runs over d in slices of
- * the plan's k_chunk; the slices' fp32 partials are added in slice order, so
- * results do not depend on scheduling.
+ *     y[r, h] = sum over k of a[r, k] * w[h, k], summed in fp32, rounded
+ *               once to `dtype`.
+ * The plan's form decides how (results within one rounding of the sum of
+ * each other; every form is deterministic: fixed summation orders):
+ *   GA_DOWN_DECODE  one or two tokens, d up to 16384 (32768 for one token):
+ *                   one launch; each workgroup forms its tokens' statistics
+ *                   and activation in registers; no workspace.
+ *   GA_DOWN_STAGED  two to four tokens, d up to 16384: the activation is
+ *                   stored once into the workspace by the library's own
+ *                   activation kernel, then a second launch streams the
+ *                   weights against it.
+ *   GA_DOWN_KLOOP   otherwise: the rows' cutoffs into the workspace, then a
+ *                   matrix-core product that forms the activation as it
+ *                   stages its operand; the sum runs over d in slices of
+ *                   k_chunk whose fp32 partials are added in slice order.
  *   gu        [T, 2d] device array (gate | up), 16-byte aligned.
  *   w         [H, d] device array, 16-byte aligned: one row of d weights per
  *             output feature (a linear layer's weight layout).
@@ -262,25 +268,31 @@ ga_status ga_squared_relu_bounded(const void *in, void *out, int64_t M, int64_t 
  *             live count are left untouched.
  *   workspace device memory of ga_gelu_and_mul_sparse_down_workspace_bytes()
  *             bytes, 256-byte aligned, zero-filled before its first use (the
- *             decode form of one or two tokens needs none: NULL is accepted).
- *             Each call leaves it ready for the next (tile counters back at
- *             zero, its call counter advanced), so it is zeroed once and then
- *             serves any later calls and shapes that fit it, and graph
- *             replays.  Calls that share a workspace must not overlap in
- *             time (one stream serialises them).
+ *             decode form needs none: NULL is accepted).  Each call leaves it
+ *             ready for the next (tile counters back at zero, its call
+ *             counter advanced), so it is zeroed once and then serves any
+ *             later calls and shapes that fit it, and graph replays.  It
+ *             must not overlap gu, w or y (GA_EINVAL).  Calls that share a
+ *             workspace must not overlap in time (one stream serialises
+ *             them).
  */
 #define GA_DOWN_MAX_ROWS 256
 #define GA_DOWN_MAX_H 65536
+#define GA_DOWN_KLOOP 0
+#define GA_DOWN_DECODE 1
+#define GA_DOWN_STAGED 2
 typedef struct {
-    int32_t rows_per_block;     /* tokens per workgroup: 16, 32 or 64 (1 or 2 in the decode form) */
-    int32_t features_per_block; /* output features per workgroup: 16 per wavefront row group */
-    int32_t waves;              /* wavefronts per workgroup: row groups x parts of each step */
+    int32_t rows_per_block;     /* tokens per workgroup: 16, 32 or 64; decode form: 1 or 2; staged
+                                   form: 2 or 4 (at least T) */
+    int32_t features_per_block; /* output features per workgroup: 16 per wavefront row group; decode
+                                   and staged forms: 2, 4 or 8 */
+    int32_t waves;              /* wavefronts per workgroup */
     int32_t k_step;             /* elements of d per iteration of a workgroup's loop: 128, 256 or 512;
-                                   0: the decode form (rows_per_block 1 or 2 tokens,
-                                   features_per_block 2, 4 or 8 over all of d, one launch, no
-                                   workspace) */
-    int32_t k_chunk;            /* elements of d per workgroup, a multiple of k_step */
+                                   0 in the decode and staged forms (each workgroup covers all of d) */
+    int32_t k_chunk;            /* elements of d per workgroup, a multiple of k_step; d in the decode
+                                   and staged forms */
     int32_t splits;             /* ceil(d / k_chunk), at most 64: workgroups that share an output tile */
+    int32_t form;               /* GA_DOWN_KLOOP, GA_DOWN_DECODE or GA_DOWN_STAGED */
     int64_t grid;               /* workgroups of the product launch */
 } ga_down_plan;
 ga_status ga_plan_gelu_and_mul_sparse_down(int64_t T, int64_t d, int64_t H, int32_t dtype, ga_down_plan *plan);

@@ -615,19 +615,26 @@ def _down_plan(T, d, H, dt=BF16):
 
 def test_down_planner_and_workspace():
     # the measured choice by token count (d = 16384, H = 2048)
-    for T, f, waves in ((1, 4, 8), (2, 4, 16)):   # the decode form: one launch, no workspace
+    assert ctypes.sizeof(ga.DownPlan) == 40 and ga.DownPlan.grid.offset == 32     # the C layout
+    # one token: the decode form (one launch, no workspace); two to four: the
+    # staged form (the activation stored into the workspace, then the product)
+    for T, form, tmax, f, waves in ((1, ga.GA_DOWN_DECODE, 1, 4, 8), (2, ga.GA_DOWN_STAGED, 2, 4, 16),
+                                    (3, ga.GA_DOWN_STAGED, 4, 4, 16), (4, ga.GA_DOWN_STAGED, 4, 4, 16)):
         p = _down_plan(T, 16384, 2048)
-        assert (p.rows_per_block, p.features_per_block, p.waves, p.k_step, p.k_chunk, p.splits, p.grid) == \
-            (T, f, waves, 0, 16384, 1, 2048 // f)
-        assert ga.gelu_and_mul_sparse_down_workspace_bytes(T, 16384, 2048) == 0
+        assert (p.form, p.rows_per_block, p.features_per_block, p.waves, p.k_step, p.k_chunk, p.splits,
+                p.grid) == (form, tmax, f, waves, 0, 16384, 1, 2048 // f), T
+        want_ws = 0 if form == ga.GA_DOWN_DECODE else -(-T * 16384 * 2 // 256) * 256
+        assert ga.gelu_and_mul_sparse_down_workspace_bytes(T, 16384, 2048) == want_ws
     p = _down_plan(1, 32768, 2048)
-    assert (p.k_step, p.features_per_block, p.waves, p.grid) == (0, 4, 16, 512)
-    assert _down_plan(1, 32776, 2048).k_step > 0       # rows past the decode form's reach
-    assert _down_plan(2, 16392, 2048).k_step > 0
-    for T, want in ((3, (16, 64, 4, 512, 1024)), (4, (16, 64, 4, 512, 1024)), (8, (16, 32, 4, 512, 2048)),
+    assert (p.form, p.features_per_block, p.waves, p.grid) == (ga.GA_DOWN_DECODE, 4, 16, 512)
+    for T, d in ((1, 32776), (2, 16392), (4, 16392)):        # rows past the decode and staged forms' reach
+        p = _down_plan(T, d, 2048)
+        assert p.form == ga.GA_DOWN_KLOOP and p.k_step > 0, (T, d)
+    for T, want in ((5, (16, 32, 4, 512, 2048)), (8, (16, 32, 4, 512, 2048)),
                     (16, (16, 64, 4, 512, 2048)), (64, (32, 64, 8, 512, 4096)), (256, (64, 128, 8, 256, 2048))):
         p = _down_plan(T, 16384, 2048)
         assert (p.rows_per_block, p.features_per_block, p.waves, p.k_step, p.k_chunk) == want, T
+        assert p.form == ga.GA_DOWN_KLOOP
         assert p.grid == -(-T // p.rows_per_block) * (2048 // p.features_per_block) * p.splits
     # whole steps, at most 64 slices of d, for every d the kernels take
     for d in (8, 1024, 1032, 32768, 32776, 65536):
@@ -637,11 +644,14 @@ def test_down_planner_and_workspace():
             assert p.k_step == 0 or p.k_chunk % p.k_step == 0
     # one slice: the workspace holds the call counter and the cutoffs only
     assert ga.gelu_and_mul_sparse_down_workspace_bytes(16, 512, 16) == 256 + 256
-    assert ga.gelu_and_mul_sparse_down_workspace_bytes(2, 512, 16) == 0        # the decode form
-    # the layout: call counter, cutoffs, tile counters, partial tiles
-    T, d, H = 4, 16384, 2048
-    groups, nK = 32, 16
-    assert ga.gelu_and_mul_sparse_down_workspace_bytes(T, d, H) == 256 + 256 + 256 + groups * nK * 16 * 64 * 8
+    assert ga.gelu_and_mul_sparse_down_workspace_bytes(1, 512, 16) == 0        # the decode form
+    assert ga.gelu_and_mul_sparse_down_workspace_bytes(3, 520, 16) == 3 * 520 * 2 // 256 * 256 + 256  # staged
+    # the k-loop layout: call counter, cutoffs, tile counters, partial tiles
+    T, d, H = 5, 16384, 2048
+    p = _down_plan(T, d, H)
+    groups = -(-T // p.rows_per_block) * (H // p.features_per_block)
+    assert ga.gelu_and_mul_sparse_down_workspace_bytes(T, d, H) == \
+        256 + 256 + -(-groups * 4 // 256) * 256 + groups * p.splits * p.rows_per_block * p.features_per_block * 8
     assert L.ga_plan_gelu_and_mul_sparse_down(300, 1024, 64, BF16, ctypes.byref(ga.DownPlan())) == EUNSUP
     assert L.ga_plan_gelu_and_mul_sparse_down(4, 1024, 64, F32, ctypes.byref(ga.DownPlan())) == EUNSUP
     assert L.ga_plan_gelu_and_mul_sparse_down(4, 1024, 64, BF16, None) == EINVAL
@@ -682,6 +692,27 @@ def test_down_with_plan_rejects_bad_geometry():
     assert run_dec(features_per_block=16) == EINVAL
     assert run_dec(features_per_block=8, grid=64) == EINVAL   # no 8-feature, 8-wave kernel for two tokens
     assert run_dec(waves=4) == EINVAL
+    assert run_dec(form=7) == EINVAL                  # unknown form
+    assert run_dec(k_step=128) == EINVAL
+    # staged plans (two or four tokens, a workspace for the activation)
+    ws_need = 4 * 4096 * 2
+
+    def run_st(T=4, d=4096, H=512, ws=WS, ws_bytes=None, y=Y_, **kw):
+        p = ga.DownPlan.staged(T, d, H, 4, 4, 16)
+        for k, v in kw.items():
+            setattr(p, k, v)
+        return L.ga_gelu_and_mul_sparse_down_with_plan(IN, W_, y, T, d, H, BF16, Z, None, ctypes.byref(p),
+                                                       ws, WS_BYTES if ws_bytes is None else ws_bytes, None)
+    assert run_st(T=0) == OK
+    assert run_st(T=5) == EINVAL                      # more tokens than the plan holds
+    assert run_st(d=16392) == EINVAL                  # row past the kernel's reach
+    assert run_st(waves=8) == EINVAL                  # no such kernel
+    assert run_st(rows_per_block=8, T=0) == EINVAL
+    assert run_st(grid=64) == EINVAL
+    assert run_st(T=2, ws=None) == EINVAL             # the activation needs a workspace
+    assert run_st(T=4, ws_bytes=ws_need - 256) == EINVAL
+    assert run_st(T=4, ws=Y_) == EINVAL               # the workspace overlaps y
+    assert run_st(T=4, ws=ctypes.c_void_p(IN.value + 256)) == EINVAL     # ... or gu
     assert run_dec(k_chunk=2048) == EINVAL
     assert run_dec(grid=3) == EINVAL
     assert run_dec(T=0) == OK                         # nothing to do

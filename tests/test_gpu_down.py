@@ -130,6 +130,35 @@ def test_decode_form(tmax, f, waves, oracle_lib):
                 _check(got, oracle_lib, x, w, BF16, Z95, live=live, label=f"decode live={live}")
 
 
+# (most tokens, features per workgroup, waves): every staged product kernel
+STAGED = [(2, 4, 16), (4, 4, 16)]
+
+
+@pytest.mark.parametrize("tmax,f,waves", STAGED)
+def test_staged_form(tmax, f, waves, oracle_lib):
+    """The staged form (the activation stored into the workspace by the row
+    kernel, then a weight-streaming product against it): full rows, the
+    shorter-row kernel's reach, ragged d, the smallest shapes and every live
+    count up to its token capacity; fp16 once."""
+    for T, d, H in ((tmax, 16384, 2048), (tmax, 8192, 512), (tmax, 1000, 48), (1, 8, 16), (tmax - 1, 4104, 16)):
+        x, w = _inputs(T, d, H, BF16, seed=tmax * 100 + d % 17 + T)
+        plan = ga.DownPlan.staged(T, d, H, tmax, f, waves)
+        print(f"staged tmax={tmax} T={T} d={d} H={H}", flush=True)
+        _check(_run(x, w, BF16, plan=plan), oracle_lib, x, w, BF16, Z95, label=f"staged T={T} d={d} H={H}")
+        for live in range(-1, T + 2):
+            s = int(synth.SENTINEL[BF16])
+            s = s - (1 << 16) if s >= 1 << 15 else s
+            out = torch.full((T, H), s, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+            got = _run(x, w, BF16, plan=plan, live=live, out=out)
+            n = min(max(live, 0), T)
+            assert np.all(got[n:] == synth.SENTINEL[BF16]), live
+            if n:
+                _check(got, oracle_lib, x, w, BF16, Z95, live=live, label=f"staged live={live}")
+    x, w = _inputs(tmax, 16384, 256, F16, seed=tmax)
+    plan = ga.DownPlan.staged(tmax, 16384, 256, tmax, f, waves)
+    _check(_run(x, w, F16, plan=plan), oracle_lib, x, w, F16, Z95, label=f"staged fp16 T={tmax}")
+
+
 @pytest.mark.parametrize("tmax,f,waves", [(1, 4, 8), (2, 4, 16)])
 def test_decode_form_fp16(tmax, f, waves, oracle_lib):
     for T, d, H in ((tmax, 16384, 256), (tmax, 2056, 32)):
@@ -141,7 +170,8 @@ def test_decode_form_fp16(tmax, f, waves, oracle_lib):
 def test_selection_weights_reproduce_the_activation(oracle_lib):
     """w[h, p(h)] = 2^e(h), zero elsewhere: y[r, h] = a[r, p(h)] * 2^e(h) exactly,
     so y must meet the activation's own parity bar against the oracle."""
-    for T, d, H in ((16, 4096, 4096), (9, 1032, 512), (64, 2048, 1024), (1, 4096, 4096), (2, 2048, 1024)):
+    for T, d, H in ((16, 4096, 4096), (9, 1032, 512), (64, 2048, 1024), (1, 4096, 4096), (2, 2048, 1024),
+                    (4, 4096, 2048), (3, 1000, 512)):
         x = synth.gelu_iid(T, d, seed=T + 1)
         rng = np.random.default_rng(d)
         p = rng.permutation(d)[:H] if H <= d else rng.integers(0, d, H)
@@ -198,8 +228,9 @@ def test_cutoffs_are_per_row_statistics(oracle_lib):
     _check(_run(x, w, BF16), oracle_lib, x, w, BF16, Z95, label="edge rows")
 
 
-def test_graph_replay_with_changing_live_count(oracle_lib):
-    T, d, H = 32, 8192, 1024
+@pytest.mark.parametrize("T", [32, 4, 1])      # the k-loop, staged and decode forms
+def test_graph_replay_with_changing_live_count(T, oracle_lib):
+    d, H = 8192, 1024
     x, w = _inputs(T, d, H, BF16, seed=31)
     xd, wd = to_device(x, BF16), to_device(w, BF16)
     live = torch.tensor([T], dtype=torch.int32, device="cuda")
@@ -213,7 +244,7 @@ def test_graph_replay_with_changing_live_count(oracle_lib):
         with torch.cuda.graph(g, stream=s):
             ga.gelu_and_mul_sparse_down(xd, wd, live_rows=live, out=out)
     torch.cuda.synchronize()
-    for n in (T, 5, 20, 1, T):
+    for n in (T, min(5, T), min(20, T), 1, max(T - 1, 1), T):
         out.zero_()
         live.fill_(n)
         g.replay()
