@@ -533,14 +533,15 @@ def sweep(dev, stream, num_cus, markers):
 # token counts at d = 16384 (the headline rows' width) into H = 2048 output
 # features (the pages give d, not the model width; 2048 is a synthetic choice).
 DOWN_D, DOWN_H = 16384, 2048
-DOWN_TS = (1, 2, 4, 16, 64, 256)
+DOWN_TS = (1, 2, 4, 16, 64, 128, 256)
 DOWN_ROOFLINE_T = 1
-DOWN_SWEEP_TS = (1, 2, 4, 8, 16, 32, 64, 128, 256)
-# (tokens, features, waves, k step) of every instantiated product kernel; the
-# geometry sweep times each at k chunks of 1, 2, 4 and 8 steps.
-DOWN_GEOMETRIES = [(16, 64, 8, 512), (16, 128, 8, 256), (16, 64, 4, 512), (16, 64, 8, 256), (16, 64, 4, 256),
-                  (16, 32, 4, 512), (16, 32, 2, 512), (16, 64, 4, 128), (32, 64, 8, 512), (32, 64, 8, 256),
-                  (32, 64, 4, 256), (64, 64, 8, 256), (64, 128, 8, 256), (64, 64, 4, 256)]
+DOWN_SWEEP_TS = (1, 2, 3, 4, 5, 8, 16, 32, 64, 128, 256)
+# (tokens, features, waves, k step, depth) of every instantiated tiled kernel;
+# the geometry sweep times each at 4 to 32 slices of d.
+DOWN_TILED = [(16, 64, 4, 128, 1), (16, 64, 4, 256, 1), (16, 64, 4, 64, 3), (16, 128, 8, 128, 2),
+              (32, 64, 4, 128, 1), (32, 64, 4, 64, 3),
+              (64, 128, 8, 128, 1), (64, 128, 8, 64, 3), (64, 128, 4, 64, 2),
+              (128, 128, 8, 64, 1), (128, 128, 8, 64, 2), (128, 256, 8, 64, 2)]
 # Decode kernels (most tokens, features per workgroup, wavefronts) and the
 # longest row each reaches.
 DOWN_DECODE_REACH = {(1, 4, 8): 16384, (1, 4, 16): 32768, (1, 4, 4): 16384, (1, 2, 8): 16384,
@@ -613,10 +614,12 @@ def down_projection(dev, markers, geometries=False, cpu_seconds=0.0, token_count
         plan = ga.plan_gelu_and_mul_sparse_down(T, d, H)
         plans = [plan]
         if geometries:
-            for tm, bh, wv, step in DOWN_GEOMETRIES:
-                for ks in (step, 2 * step, 4 * step, 8 * step):
-                    if -(-d // ks) <= 64:
-                        plans.append(ga.DownPlan.of(T, d, H, tm, bh, wv, step, ks))
+            for tm, bh, wv, step, depth in DOWN_TILED:        # the tiled form
+                if T < 3 or (tm > 16 and tm >= 2 * T):
+                    continue
+                for sp in (4, 8, 16, 32):
+                    ks = -(-(-(-d // sp)) // step) * step
+                    plans.append(ga.DownPlan.tiled(T, d, H, tm, bh, wv, step, ks, depth))
             for tmax, f, wv in DOWN_DECODE:         # the decode form
                 if T <= tmax and d <= DOWN_DECODE_REACH[(tmax, f, wv)]:
                     plans.append(ga.DownPlan.decode(T, d, H, tmax, f, wv))
@@ -656,11 +659,11 @@ def down_projection(dev, markers, geometries=False, cpu_seconds=0.0, token_count
         if geometries:
             for p in plans[1:]:
                 markers.push(f"down geometry T={T} form={p.form} tm={p.rows_per_block} bh={p.features_per_block} "
-                             f"waves={p.waves} step={p.k_step} chunk={p.k_chunk}")
+                             f"waves={p.waves} step={p.k_step} depth={p.depth} chunk={p.k_chunk}")
                 ms_p = time_graph_on(fused_for(p), n_sets, reps, 64, s)
                 markers.pop()
                 sweep_rows.append(f"{T},{d},{H},{p.form},{p.rows_per_block},{p.features_per_block},{p.waves},"
-                                  f"{p.k_step},{p.k_chunk},{ms_p * 1e3!r}")
+                                  f"{p.k_step},{p.depth},{p.k_chunk},{ms_p * 1e3!r}")
                 print(sweep_rows[-1], file=sys.stderr, flush=True)
             continue
         with torch.cuda.stream(s):
@@ -699,8 +702,9 @@ def down_projection(dev, markers, geometries=False, cpu_seconds=0.0, token_count
                 kname = "gelu_and_mul_sparse row kernel, then down_staged_kernel<bf16, tokens %d, features %d, " \
                         "waves %d>" % (plan.rows_per_block, plan.features_per_block, plan.waves)
             else:
-                kname = "down_product_kernel<bf16, tokens %d, features %d, waves %d, step %d> k_chunk %d" % (
-                    plan.rows_per_block, plan.features_per_block, plan.waves, plan.k_step, plan.k_chunk)
+                kname = "gelu_and_mul_sparse row kernel, then down_tiled_kernel<bf16, tokens %d, features %d, " \
+                        "waves %d, step %d, depth %d> k_chunk %d" % (plan.rows_per_block, plan.features_per_block,
+                                                                    plan.waves, plan.k_step, plan.depth, plan.k_chunk)
             res["roofline"] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                "frac": round(gbps / PEAK_HBM_GBPS, 4),
                                "traffic": recorded_traffic(DOWN_TRAFFIC_FILE, DOWN_SOURCES,

@@ -24,7 +24,7 @@ from ._lib import (  # noqa: F401
     gelu_and_mul, squared_relu_bounded, z_from_sparsity,
     plan_gelu_and_mul_sparse, plan_silu_and_mul_bounded, workspace_for,
     reserve_workspace, held_workspaces, GA_SPLIT_PLAN_ROWS, WORKSPACE_BYTES,
-    DownPlan, GA_DOWN_MAX_ROWS, GA_DOWN_KLOOP, GA_DOWN_DECODE, GA_DOWN_STAGED,
+    DownPlan, GA_DOWN_MAX_ROWS, GA_DOWN_DECODE, GA_DOWN_STAGED, GA_DOWN_TILED,
     gelu_and_mul_sparse_down, plan_gelu_and_mul_sparse_down,
     gelu_and_mul_sparse_down_workspace_bytes, reserve_down_workspace,
 )

@@ -34,22 +34,24 @@ class Plan(ctypes.Structure):
         return {k: getattr(self, k) for k, _ in self._fields_}
 
 
-GA_DOWN_KLOOP, GA_DOWN_DECODE, GA_DOWN_STAGED = 0, 1, 2
+GA_DOWN_DECODE, GA_DOWN_STAGED, GA_DOWN_TILED = 1, 2, 3
 
 
 class DownPlan(ctypes.Structure):
     """Geometry of the activation fused with the down projection."""
     _fields_ = [("rows_per_block", ctypes.c_int32), ("features_per_block", ctypes.c_int32),
                 ("waves", ctypes.c_int32), ("k_step", ctypes.c_int32), ("k_chunk", ctypes.c_int32),
-                ("splits", ctypes.c_int32), ("form", ctypes.c_int32), ("grid", ctypes.c_int64)]
+                ("splits", ctypes.c_int32), ("form", ctypes.c_int32), ("depth", ctypes.c_int32),
+                ("grid", ctypes.c_int64)]
 
     @classmethod
-    def of(cls, T, d, H, rows_per_block, features_per_block, waves, k_step, k_chunk):
-        """The k-loop form's plan of one geometry for these sizes (splits and
-        grid derived)."""
+    def tiled(cls, T, d, H, rows_per_block, features_per_block, waves, k_step, k_chunk, depth):
+        """The tiled form's plan of one geometry (the activation stored into
+        the workspace, then a matrix-core product over slices of k_chunk with
+        `depth` steps of weights in flight)."""
         splits = -(-d // k_chunk)
         return cls(rows_per_block=rows_per_block, features_per_block=features_per_block, waves=waves,
-                   k_step=k_step, k_chunk=k_chunk, splits=splits, form=GA_DOWN_KLOOP,
+                   k_step=k_step, k_chunk=k_chunk, splits=splits, form=GA_DOWN_TILED, depth=depth,
                    grid=-(-T // rows_per_block) * -(-H // features_per_block) * splits)
 
     @classmethod

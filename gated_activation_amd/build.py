@@ -15,7 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libga.so")
 SOURCES = ["api.hip", "gelu_sparse.hip", "gelu_sparse_split.hip", "gelu_sparse_unaligned.hip", "gelu_sparse_rows.hip",
-           "gelu_sparse_rep.hip", "gelu_sparse_down.hip", "gelu_sparse_decode.hip", "gelu_sparse_staged.hip", "elementwise.hip"]
+           "gelu_sparse_rep.hip", "gelu_sparse_decode.hip", "gelu_sparse_staged.hip", "gelu_sparse_tiled.hip",
+           "elementwise.hip"]
 ARCH = "gfx950"
 
 

@@ -608,46 +608,51 @@ ga_status device_scratch(ga_stream stream, void **ptr) {
 // ---------------------------------------------------------------------------
 // gelu_and_mul_sparse fused with the down projection
 // ---------------------------------------------------------------------------
-// The geometry (tokens, waves, features, k step per workgroup) and the
-// launch size the k chunk is sized for, by token count: the fastest of the
-// measured sweep over every instantiated geometry and chunks of 1 to 8 steps
-// (d = 16384, H = 2048, bf16, token counts 1 to 256).
-struct DownGeo {
-    int tm, waves, bh, step;
-};
-struct DownChoice {
+// The tiled form's geometry by token count (tokens, 16-feature groups per
+// wavefront, wavefronts, elements of d per step, steps of loads in flight)
+// and the workgroups the launch is sized for: the fastest of a measured
+// sweep over the instantiated geometries and slice counts (d = 16384,
+// H = 2048, bf16, 3 to 256 tokens).
+struct TiledChoice {
     int max_T;
-    DownGeo geo;
-    int64_t groups;   // target workgroups of the product launch ...
-    int chunk_steps;  // ... or, when nonzero, a fixed k chunk of this many steps
+    int tm, fw, waves, kstep, depth;
+    int64_t groups;
 };
-constexpr DownChoice kDownChoice[] = {
-    {4, {16, 4, 64, 512}, 512, 0},  {8, {16, 4, 32, 512}, 512, 0},  {16, {16, 4, 64, 512}, 256, 0},
-    {64, {32, 8, 64, 512}, 256, 0}, {GA_DOWN_MAX_ROWS, {64, 8, 128, 256}, 0, 8},
+constexpr TiledChoice kTiledChoice[] = {
+    {16, 16, 1, 4, 128, 1, 512},
+    {32, 32, 1, 4, 128, 1, 512},
+    {128, 64, 1, 8, 128, 1, 256},
+    {GA_DOWN_MAX_ROWS, 128, 1, 8, 64, 1, 256},
 };
+// Token counts from which the tiled form is chosen (below: decode, staged).
+constexpr int64_t kTiledFromT = 3;
 
-void fill_down_plan(const DownGeo &g, int64_t ks, int64_t T, int64_t d, int64_t H, ga_down_plan *p) {
+// The tiled form: workgroups of tm tokens x bh features x kc elements of d.
+void fill_down_tiled_plan(int tm, int bh, int waves, int kstep, int depth, int64_t kc, int64_t T, int64_t d,
+                          int64_t H, ga_down_plan *p) {
     std::memset(p, 0, sizeof *p);
-    p->rows_per_block = g.tm;
-    p->features_per_block = g.bh;
-    p->waves = g.waves;
-    p->k_step = g.step;
-    p->k_chunk = (int32_t)ks;
-    p->splits = (int32_t)((d + ks - 1) / ks);
-    p->grid = (T + g.tm - 1) / g.tm * ((H + g.bh - 1) / g.bh) * p->splits;
+    p->rows_per_block = tm;
+    p->features_per_block = bh;
+    p->waves = waves;
+    p->k_step = kstep;
+    p->k_chunk = (int32_t)kc;
+    p->splits = (int32_t)((d + kc - 1) / kc);
+    p->form = GA_DOWN_TILED;
+    p->depth = depth;
+    p->grid = (T + tm - 1) / tm * ((H + bh - 1) / bh) * p->splits;
 }
 
-// The k chunk for a geometry: whole steps, as many slices of d as bring the
-// launch to about `groups` workgroups, at most DOWN_MAX_SPLITS.
-int64_t down_chunk(const DownGeo &g, int64_t groups, int64_t T, int64_t d, int64_t H) {
-    int64_t tiles = (T + g.tm - 1) / g.tm * ((H + g.bh - 1) / g.bh);
+// The slice of d for a tiled geometry: whole steps, as many slices as bring
+// the launch to about `groups` workgroups, at most DOWN_MAX_SPLITS.
+int64_t tiled_chunk(const TiledChoice &c, int64_t T, int64_t d, int64_t H) {
+    const int64_t bh = (int64_t)c.fw * 16 * c.waves;
+    int64_t tiles = (T + c.tm - 1) / c.tm * ((H + bh - 1) / bh);
     if (tiles < 1) tiles = 1;  // T == 0: nothing is launched
-    int64_t slices = (groups + tiles - 1) / tiles;
+    int64_t slices = (c.groups + tiles - 1) / tiles;
     if (slices < 1) slices = 1;
-    int64_t ks = (d + slices - 1) / slices;
-    ks = (ks + g.step - 1) / g.step * g.step;
-    const int64_t min_ks = ((d + ga::DOWN_MAX_SPLITS - 1) / ga::DOWN_MAX_SPLITS + g.step - 1) / g.step * g.step;
-    return ks < min_ks ? min_ks : ks;
+    if (slices > ga::DOWN_MAX_SPLITS) slices = ga::DOWN_MAX_SPLITS;
+    const int64_t kc = (d + slices - 1) / slices;
+    return (kc + c.kstep - 1) / c.kstep * c.kstep;
 }
 
 ga_status check_down_sizes(const char *op, int64_t T, int64_t d, int64_t H, int32_t dtype) {
@@ -673,7 +678,7 @@ static_assert(sizeof(ga_down_plan) == 40 && offsetof(ga_down_plan, grid) == 32, 
 bool same_down_plan(const ga_down_plan &a, const ga_down_plan &b) {
     return a.rows_per_block == b.rows_per_block && a.features_per_block == b.features_per_block &&
            a.waves == b.waves && a.k_step == b.k_step && a.k_chunk == b.k_chunk && a.splits == b.splits &&
-           a.form == b.form && a.grid == b.grid;
+           a.form == b.form && a.depth == b.depth && a.grid == b.grid;
 }
 
 // The decode and staged forms: every workgroup covers all of d for
@@ -695,9 +700,9 @@ bool down_whole_available(int form, int32_t dtype, int tmax, int f, int waves, i
                                   : ga::gelu_down_staged_available(dtype, tmax, f, waves, d);
 }
 
-// The planner's choice for one to four tokens, by the longest row it serves
+// The planner's choice for one or two tokens, by the longest row it serves
 // (measured on MI355X at H = 2048): the first entry whose token capacity is
-// the call's rounded up to 1, 2 or 4 and whose reach covers d.
+// the call's and whose reach covers d.
 struct WholeChoice {
     int form, tmax;
     int64_t max_d;
@@ -707,7 +712,6 @@ const WholeChoice kWholeChoice[] = {
     {GA_DOWN_DECODE, 1, 16384, 4, 8},
     {GA_DOWN_DECODE, 1, 32768, 4, 16},
     {GA_DOWN_STAGED, 2, 16384, 4, 16},
-    {GA_DOWN_STAGED, 4, 16384, 4, 16},
 };
 
 ga_status check_down_plan(const char *op, const ga_down_plan *p, int64_t T, int64_t d, int64_t H, int32_t dtype) {
@@ -728,30 +732,38 @@ ga_status check_down_plan(const char *op, const ga_down_plan *p, int64_t T, int6
                         op, what);
         return GA_OK;
     }
-    if (p->form != GA_DOWN_KLOOP) return fail(GA_EINVAL, "%s: unknown plan form %d", op, (int)p->form);
-    if (!ga::gelu_down_available(dtype, p->rows_per_block, p->waves, p->features_per_block, p->k_step))
-        return fail(GA_EINVAL, "%s: no kernel for rows_per_block %d, waves %d, features_per_block %d, k_step %d",
-                    op, (int)p->rows_per_block, (int)p->waves, (int)p->features_per_block, (int)p->k_step);
-    if (p->k_chunk < p->k_step || p->k_chunk % p->k_step != 0)
-        return fail(GA_EINVAL, "%s: k_chunk %d is not a positive multiple of k_step %d", op, (int)p->k_chunk,
-                    (int)p->k_step);
-    ga_down_plan want;
-    fill_down_plan(DownGeo{p->rows_per_block, p->waves, p->features_per_block, p->k_step}, p->k_chunk, T, d, H,
-                   &want);
-    if (p->splits != want.splits || p->grid != want.grid)
-        return fail(GA_EINVAL, "%s: splits %d / grid %lld do not match the geometry (%d / %lld)", op,
-                    (int)p->splits, (long long)p->grid, (int)want.splits, (long long)want.grid);
-    if (p->splits > ga::DOWN_MAX_SPLITS)
-        return fail(GA_EUNSUPPORTED, "%s: %d slices of d above %d", op, (int)p->splits, ga::DOWN_MAX_SPLITS);
-    if (p->grid * p->waves * 64 >= kMaxWorkItems)
-        return fail(GA_EUNSUPPORTED, "%s: %lld work-items reach 2^32", op, (long long)(p->grid * p->waves * 64));
-    return GA_OK;
+    if (p->form == GA_DOWN_TILED) {
+        if (!ga::gelu_down_tiled_available(dtype, p->rows_per_block, p->features_per_block, p->waves, p->k_step,
+                                           p->depth))
+            return fail(GA_EINVAL,
+                        "%s: no tiled kernel for rows_per_block %d, features_per_block %d, waves %d, k_step %d, "
+                        "depth %d", op, (int)p->rows_per_block, (int)p->features_per_block, (int)p->waves,
+                        (int)p->k_step, (int)p->depth);
+        if (p->k_chunk < p->k_step || p->k_chunk % p->k_step != 0)
+            return fail(GA_EINVAL, "%s: k_chunk %d is not a positive multiple of k_step %d", op, (int)p->k_chunk,
+                        (int)p->k_step);
+        ga_down_plan want;
+        fill_down_tiled_plan(p->rows_per_block, p->features_per_block, p->waves, p->k_step, p->depth, p->k_chunk, T,
+                             d, H, &want);
+        if (!same_down_plan(want, *p))
+            return fail(GA_EINVAL, "%s: splits %d / grid %lld do not match the geometry (%d / %lld)", op,
+                        (int)p->splits, (long long)p->grid, (int)want.splits, (long long)want.grid);
+        if (p->splits > ga::DOWN_MAX_SPLITS)
+            return fail(GA_EUNSUPPORTED, "%s: %d slices of d above %d", op, (int)p->splits, ga::DOWN_MAX_SPLITS);
+        if (p->splits > 1 && p->grid / p->splits > ga::DOWN_MAX_TILES)
+            return fail(GA_EUNSUPPORTED, "%s: %lld output tiles above %lld", op, (long long)(p->grid / p->splits),
+                        (long long)ga::DOWN_MAX_TILES);
+        if (p->grid * p->waves * 64 >= kMaxWorkItems)
+            return fail(GA_EUNSUPPORTED, "%s: %lld work-items reach 2^32", op, (long long)(p->grid * p->waves * 64));
+        return GA_OK;
+    }
+    return fail(GA_EINVAL, "%s: unknown plan form %d", op, (int)p->form);
 }
 
 size_t down_workspace_bytes(const ga_down_plan &p, int64_t T, int64_t d, int64_t H) {
     if (p.form == GA_DOWN_DECODE) return 0;  // everything stays on chip
-    if (p.form == GA_DOWN_STAGED) return (size_t)((T * d * 2 + 255) / 256 * 256);  // the stored activation
-    return ga::gelu_down_workspace_bytes(T, d, H, p.rows_per_block, p.features_per_block, p.k_chunk);
+    if (p.form == GA_DOWN_STAGED) return (size_t)ga::down_tiled_part_offset(T, d);  // the stored activation
+    return ga::gelu_down_tiled_workspace_bytes(T, d, H, p.rows_per_block, p.features_per_block, p.k_chunk);
 }
 
 }  // namespace
@@ -1017,23 +1029,20 @@ ga_status ga_plan_gelu_and_mul_sparse_down(int64_t T, int64_t d, int64_t H, int3
     if (plan == nullptr) return fail(GA_EINVAL, "%s: null plan", name);
     ga_status st = check_down_sizes(name, T, d, H, dtype);
     if (st != GA_OK) return st;
-    // One or two tokens: the decode form (one launch, no workspace), where
-    // its row fits.
-    if (T <= 4) {
-        const int tmax = T <= 1 ? 1 : T <= 2 ? 2 : 4;
+    // One token: the decode form (one launch, no workspace); two: the staged
+    // form; where their rows fit.
+    if (T < kTiledFromT) {
+        const int tmax = T <= 1 ? 1 : 2;
         for (const WholeChoice &c : kWholeChoice)
             if (c.tmax == tmax && d <= c.max_d && down_whole_available(c.form, dtype, tmax, c.f, c.waves, d)) {
                 fill_down_whole_plan(c.form, tmax, c.f, c.waves, d, H, plan);
                 return GA_OK;
             }
     }
-    const DownChoice *c = &kDownChoice[0];
+    const TiledChoice *c = &kTiledChoice[0];
     while (T > c->max_T) ++c;
-    int64_t ks = c->chunk_steps > 0 ? (int64_t)c->chunk_steps * c->geo.step : down_chunk(c->geo, c->groups, T, d, H);
-    const int64_t min_ks =
-        ((d + ga::DOWN_MAX_SPLITS - 1) / ga::DOWN_MAX_SPLITS + c->geo.step - 1) / c->geo.step * c->geo.step;
-    if (ks < min_ks) ks = min_ks;
-    fill_down_plan(c->geo, ks, T, d, H, plan);
+    fill_down_tiled_plan(c->tm, c->fw * 16 * c->waves, c->waves, c->kstep, c->depth, tiled_chunk(*c, T, d, H), T, d,
+                         H, plan);
     return GA_OK;
 }
 
@@ -1080,23 +1089,26 @@ ga_status ga_gelu_and_mul_sparse_down_with_plan(const void *gu, const void *w, v
     if (overlaps(workspace, need, gu, (size_t)T * 2 * (size_t)d * es) ||
         overlaps(workspace, need, w, (size_t)H * (size_t)d * es) || overlaps(workspace, need, y, y_bytes))
         return fail(GA_EINVAL, "%s: the workspace overlaps gu, w or y", name);
-    if (plan->form == GA_DOWN_STAGED) {
+    if (plan->form == GA_DOWN_STAGED || plan->form == GA_DOWN_TILED) {
         // The activation of the call's rows into the workspace, by the row
         // kernel ga_gelu_and_mul_sparse would run (no workspace of its own),
         // then the product against it.
+        void *a = static_cast<unsigned char *>(workspace) + ga::DOWN_ACT_OFFSET;
         ga_plan act;
-        if ((st = ga_plan_gelu_and_mul_sparse(T, d, dtype, vector_aligned(gu, workspace, d, dtype), 256, 0, &act)) !=
-            GA_OK)
+        if ((st = ga_plan_gelu_and_mul_sparse(T, d, dtype, vector_aligned(gu, a, d, dtype), 256, 0, &act)) != GA_OK)
             return st;
-        if ((st = launch_gelu(gu, workspace, T, d, dtype, z, live_rows, act, nullptr, stream)) != GA_OK) return st;
-        return launched(name, ga::launch_gelu_down_staged(dtype, plan->rows_per_block, plan->features_per_block,
-                                                          plan->waves, workspace, w, y, (int32_t)T, (int32_t)d,
-                                                          (int32_t)H, live_rows, static_cast<hipStream_t>(stream)));
+        if ((st = launch_gelu(gu, a, T, d, dtype, z, live_rows, act, nullptr, stream)) != GA_OK) return st;
+        if (plan->form == GA_DOWN_STAGED)
+            return launched(name, ga::launch_gelu_down_staged(dtype, plan->rows_per_block, plan->features_per_block,
+                                                              plan->waves, a, w, y, (int32_t)T, (int32_t)d,
+                                                              (int32_t)H, live_rows,
+                                                              static_cast<hipStream_t>(stream)));
+        return launched(name, ga::launch_gelu_down_tiled(dtype, plan->rows_per_block, plan->features_per_block,
+                                                         plan->waves, plan->k_step, plan->depth, plan->k_chunk, a, w, y,
+                                                         (int32_t)T, (int32_t)d, (int32_t)H, live_rows, workspace,
+                                                         static_cast<hipStream_t>(stream)));
     }
-    return launched(name, ga::launch_gelu_down(dtype, plan->rows_per_block, plan->waves, plan->features_per_block,
-                                               plan->k_step, plan->k_chunk, gu, w, y, (int32_t)T, (int32_t)d,
-                                               (int32_t)H, z, live_rows, workspace,
-                                               static_cast<hipStream_t>(stream)));
+    return fail(GA_EINVAL, "%s: unknown plan form %d", name, (int)plan->form);  // unreachable: checked above
 }
 
 ga_status ga_gelu_and_mul_sparse_down(const void *gu, const void *w, void *y, int64_t T, int64_t d, int64_t H,

@@ -38,27 +38,9 @@ int64_t gelu_rep_grid(int64_t T, int rep);
 hipError_t launch_gelu_rep(int dtype, int waves, int vec_per_lane, int rep, const void *in, void *out, int32_t T,
                            int32_t d, int32_t nvec, float z, const int32_t *live, hipStream_t stream);
 
-// The activation fused with the down projection y = a . w^T (w: [H, d]):
-// a cutoff launch (one workgroup per row) and a product launch of
-// workgroups of tm tokens x bh features (16 per wavefront row group) x ks
-// elements of d; the ceil(d / ks) workgroups of one output tile add their
-// fp32 partials through the workspace (gelu_down_workspace_bytes).  At most
-// DOWN_MAX_SPLITS slices per row.  Workspace layout: [0, 256) the call
-// counter, the cutoffs (T floats) from byte 256, the output tiles' counters,
-// then the partial tiles.
+// The activation fused with the down projection y = a . w^T (w: [H, d]).
+// At most DOWN_MAX_SPLITS slices of d per row in the tiled form.
 constexpr int DOWN_MAX_SPLITS = 64;
-__host__ __device__ inline int64_t down_cut_offset() { return 256; }
-__host__ __device__ inline int64_t down_cnt_offset(int64_t T) { return 256 + (T * 4 + 255) / 256 * 256; }
-__host__ __device__ inline int64_t down_part_offset(int64_t T, int64_t ngroups) {
-    return down_cnt_offset(T) + (ngroups * 4 + 255) / 256 * 256;
-}
-bool gelu_down_available(int dtype, int tm, int waves, int bh, int step);
-size_t gelu_down_workspace_bytes(int64_t T, int64_t d, int64_t H, int tm, int bh, int64_t ks);
-// ks: elements of d per workgroup, a multiple of step (the k elements per
-// iteration of its loop).
-hipError_t launch_gelu_down(int dtype, int tm, int waves, int bh, int step, int32_t ks, const void *gu,
-                            const void *w, void *y, int32_t T, int32_t d, int32_t H, float z, const int32_t *live,
-                            void *workspace, hipStream_t stream);
 
 // Decode form of the fused op, for T <= tmax tokens (1 or 2): one launch, no
 // workspace; workgroups of f output features (2, 4 or 8) over all of d,
@@ -67,6 +49,29 @@ bool gelu_down_decode_available(int dtype, int tmax, int f, int waves, int64_t d
 hipError_t launch_gelu_down_decode(int dtype, int tmax, int f, int waves, const void *gu, const void *w, void *y,
                                    int32_t T, int32_t d, int32_t H, float z, const int32_t *live,
                                    hipStream_t stream);
+
+// Workspace of the staged and tiled forms: [0, 256) unused, the tiled
+// product's output-tile counters at a fixed place (DOWN_MAX_TILES words,
+// zero between calls: each tile's last workgroup resets its own), the stored
+// activation ([T, d]) from DOWN_ACT_OFFSET, then the tiled product's fp32
+// partial tiles.
+constexpr int64_t DOWN_TILE_CNT_OFFSET = 256;
+constexpr int64_t DOWN_MAX_TILES = 16384;
+constexpr int64_t DOWN_ACT_OFFSET = DOWN_TILE_CNT_OFFSET + DOWN_MAX_TILES * 4;
+__host__ __device__ inline int64_t down_tiled_part_offset(int64_t T, int64_t d) {
+    return DOWN_ACT_OFFSET + (T * d * 2 + 255) / 256 * 256;
+}
+
+// Tiled form's product launch, for any T: y = a . w^T with a the stored
+// activation at workspace + DOWN_ACT_OFFSET; workgroups of tm tokens x bh
+// features x kc elements of d (grid ceil(T / tm) * ceil(H / bh) * ceil(d / kc));
+// several slices of d add their partials through the workspace
+// (gelu_down_tiled_workspace_bytes), at most DOWN_MAX_TILES output tiles.
+bool gelu_down_tiled_available(int dtype, int tm, int bh, int waves, int kstep, int depth);
+size_t gelu_down_tiled_workspace_bytes(int64_t T, int64_t d, int64_t H, int tm, int bh, int64_t kc);
+hipError_t launch_gelu_down_tiled(int dtype, int tm, int bh, int waves, int kstep, int depth, int32_t kc, const void *a,
+                                  const void *w, void *y, int32_t T, int32_t d, int32_t H, const int32_t *live,
+                                  void *workspace, hipStream_t stream);
 
 // Staged form's product launch, for T <= tmax tokens (2 or 4): y = a . w^T
 // with a the stored activation ([T, d], rows past the live count not read);

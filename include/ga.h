@@ -250,11 +250,11 @@ ga_status ga_squared_relu_bounded(const void *in, void *out, int64_t M, int64_t 
  *   GA_DOWN_STAGED  two to four tokens, d up to 16384: the activation is
  *                   stored once into the workspace by the library's own
  *                   activation kernel, then a second launch streams the
- *                   weights against it.
- *   GA_DOWN_KLOOP   otherwise: the rows' cutoffs into the workspace, then a
- *                   matrix-core product that forms the activation as it
- *                   stages its operand; the sum runs over d in slices of
- *                   k_chunk whose fp32 partials are added in slice order.
+ *                   weights against it (fp32 dot products).
+ *   GA_DOWN_TILED   any T: the activation stored once as in the staged form,
+ *                   then a matrix-core product over it; the sum runs over d
+ *                   in slices of k_chunk whose fp32 partials are added in
+ *                   slice order.  The planner's choice from three tokens.
  *   gu        [T, 2d] device array (gate | up), 16-byte aligned.
  *   w         [H, d] device array, 16-byte aligned: one row of d weights per
  *             output feature (a linear layer's weight layout).
@@ -269,30 +269,33 @@ ga_status ga_squared_relu_bounded(const void *in, void *out, int64_t M, int64_t 
  *   workspace device memory of ga_gelu_and_mul_sparse_down_workspace_bytes()
  *             bytes, 256-byte aligned, zero-filled before its first use (the
  *             decode form needs none: NULL is accepted).  Each call leaves it
- *             ready for the next (tile counters back at zero, its call
- *             counter advanced), so it is zeroed once and then serves any
- *             later calls and shapes that fit it, and graph replays.  It
- *             must not overlap gu, w or y (GA_EINVAL).  Calls that share a
- *             workspace must not overlap in time (one stream serialises
- *             them).
+ *             ready for the next (the tiled form's output-tile counters,
+ *             kept in a region of their own, are back at zero), so it is
+ *             zeroed once and then serves any later calls and shapes that
+ *             fit it, and graph replays.  It must not overlap gu, w or y
+ *             (GA_EINVAL).  Calls that share a workspace must not overlap in
+ *             time (one stream serialises them).
  */
 #define GA_DOWN_MAX_ROWS 256
 #define GA_DOWN_MAX_H 65536
-#define GA_DOWN_KLOOP 0
 #define GA_DOWN_DECODE 1
 #define GA_DOWN_STAGED 2
+#define GA_DOWN_TILED 3
 typedef struct {
-    int32_t rows_per_block;     /* tokens per workgroup: 16, 32 or 64; decode form: 1 or 2; staged
-                                   form: 2 or 4 (at least T) */
-    int32_t features_per_block; /* output features per workgroup: 16 per wavefront row group; decode
-                                   and staged forms: 2, 4 or 8 */
+    int32_t rows_per_block;     /* tokens per workgroup: 16, 32, 64 or 128 in the tiled form; decode
+                                   form: 1 or 2; staged form: 2 or 4 (at least T) */
+    int32_t features_per_block; /* output features per workgroup: 16 per wavefront feature group in
+                                   the tiled form; decode and staged forms: 2, 4 or 8 */
     int32_t waves;              /* wavefronts per workgroup */
-    int32_t k_step;             /* elements of d per iteration of a workgroup's loop: 128, 256 or 512;
-                                   0 in the decode and staged forms (each workgroup covers all of d) */
+    int32_t k_step;             /* tiled form: elements of d per iteration of a workgroup's loop (64,
+                                   128 or 256); 0 in the decode and staged forms (each workgroup
+                                   covers all of d) */
     int32_t k_chunk;            /* elements of d per workgroup, a multiple of k_step; d in the decode
                                    and staged forms */
     int32_t splits;             /* ceil(d / k_chunk), at most 64: workgroups that share an output tile */
-    int32_t form;               /* GA_DOWN_KLOOP, GA_DOWN_DECODE or GA_DOWN_STAGED */
+    int32_t form;               /* GA_DOWN_DECODE, GA_DOWN_STAGED or GA_DOWN_TILED */
+    int32_t depth;              /* tiled form: steps of loads each wavefront keeps in flight (1-3);
+                                   0 in the other forms */
     int64_t grid;               /* workgroups of the product launch */
 } ga_down_plan;
 ga_status ga_plan_gelu_and_mul_sparse_down(int64_t T, int64_t d, int64_t H, int32_t dtype, ga_down_plan *plan);

@@ -597,7 +597,7 @@ def down(gu=IN, w=W_, y=Y_, T=16, d=16384, H=2048, dt=BF16, z=Z, live=None, ws=W
     (dict(ws=None), EINVAL),
     (dict(ws=ctypes.c_void_p(0x7F3000000010)), EINVAL),       # workspace not 256-byte aligned
     (dict(ws_bytes=4096), EINVAL),
-    (dict(d=512, H=16, ws=None), EINVAL),                     # one slice still needs the cutoffs
+    (dict(d=512, H=16, ws=None), EINVAL),                     # one slice still needs the stored activation
     (dict(T=0), OK),
     (dict(T=0, ws=None, ws_bytes=0), OK),
 ])
@@ -613,45 +613,58 @@ def _down_plan(T, d, H, dt=BF16):
     return p
 
 
+# Workspace layout of the staged and tiled forms: 256 bytes, the tiled form's
+# output-tile counters (16384 words, a fixed region), the stored activation,
+# then the tiled form's fp32 partial tiles.
+ACT_OFFSET = 256 + 16384 * 4
+
+
 def test_down_planner_and_workspace():
     # the measured choice by token count (d = 16384, H = 2048)
     assert ctypes.sizeof(ga.DownPlan) == 40 and ga.DownPlan.grid.offset == 32     # the C layout
-    # one token: the decode form (one launch, no workspace); two to four: the
-    # staged form (the activation stored into the workspace, then the product)
-    for T, form, tmax, f, waves in ((1, ga.GA_DOWN_DECODE, 1, 4, 8), (2, ga.GA_DOWN_STAGED, 2, 4, 16),
-                                    (3, ga.GA_DOWN_STAGED, 4, 4, 16), (4, ga.GA_DOWN_STAGED, 4, 4, 16)):
+    assert ga.DownPlan.depth.offset == 28                                           # in the padding before grid
+    # one token: the decode form (one launch, no workspace); two: the staged
+    # form (the activation stored into the workspace, then the product)
+    for T, form, tmax, f, waves in ((1, ga.GA_DOWN_DECODE, 1, 4, 8), (2, ga.GA_DOWN_STAGED, 2, 4, 16)):
         p = _down_plan(T, 16384, 2048)
         assert (p.form, p.rows_per_block, p.features_per_block, p.waves, p.k_step, p.k_chunk, p.splits,
-                p.grid) == (form, tmax, f, waves, 0, 16384, 1, 2048 // f), T
-        want_ws = 0 if form == ga.GA_DOWN_DECODE else -(-T * 16384 * 2 // 256) * 256
+                p.depth, p.grid) == (form, tmax, f, waves, 0, 16384, 1, 0, 2048 // f), T
+        want_ws = 0 if form == ga.GA_DOWN_DECODE else ACT_OFFSET + -(-T * 16384 * 2 // 256) * 256
         assert ga.gelu_and_mul_sparse_down_workspace_bytes(T, 16384, 2048) == want_ws
     p = _down_plan(1, 32768, 2048)
     assert (p.form, p.features_per_block, p.waves, p.grid) == (ga.GA_DOWN_DECODE, 4, 16, 512)
-    for T, d in ((1, 32776), (2, 16392), (4, 16392)):        # rows past the decode and staged forms' reach
+    for T, d in ((1, 32776), (2, 16392)):        # rows past the decode and staged forms' reach
         p = _down_plan(T, d, 2048)
-        assert p.form == ga.GA_DOWN_KLOOP and p.k_step > 0, (T, d)
-    for T, want in ((5, (16, 32, 4, 512, 2048)), (8, (16, 32, 4, 512, 2048)),
-                    (16, (16, 64, 4, 512, 2048)), (64, (32, 64, 8, 512, 4096)), (256, (64, 128, 8, 256, 2048))):
+        assert p.form == ga.GA_DOWN_TILED and p.k_step > 0, (T, d)
+    # three tokens on: the tiled form, sized to about 512 (up to 32 tokens)
+    # or 256 workgroups by the number of slices of d
+    for T, want in ((3, (16, 64, 4, 128, 1, 1024)), (5, (16, 64, 4, 128, 1, 1024)), (16, (16, 64, 4, 128, 1, 1024)),
+                    (17, (32, 64, 4, 128, 1, 1024)), (32, (32, 64, 4, 128, 1, 1024)),
+                    (64, (64, 128, 8, 128, 1, 1024)), (128, (64, 128, 8, 128, 1, 2048)),
+                    (129, (128, 128, 8, 64, 1, 2048)), (256, (128, 128, 8, 64, 1, 2048))):
         p = _down_plan(T, 16384, 2048)
-        assert (p.rows_per_block, p.features_per_block, p.waves, p.k_step, p.k_chunk) == want, T
-        assert p.form == ga.GA_DOWN_KLOOP
+        assert (p.rows_per_block, p.features_per_block, p.waves, p.k_step, p.depth, p.k_chunk) == want, T
+        assert p.form == ga.GA_DOWN_TILED
+        assert p.splits == 16384 // p.k_chunk
         assert p.grid == -(-T // p.rows_per_block) * (2048 // p.features_per_block) * p.splits
     # whole steps, at most 64 slices of d, for every d the kernels take
     for d in (8, 1024, 1032, 32768, 32776, 65536):
-        for T in (1, 20, 50, 200):
-            p = _down_plan(T, d, 64)
-            assert 1 <= p.splits <= 64 and p.splits == -(-d // p.k_chunk), (T, d)
-            assert p.k_step == 0 or p.k_chunk % p.k_step == 0
-    # one slice: the workspace holds the call counter and the cutoffs only
-    assert ga.gelu_and_mul_sparse_down_workspace_bytes(16, 512, 16) == 256 + 256
+        for T in (1, 3, 20, 50, 200):
+            for H in (16, 64, 2048, 65536):
+                p = _down_plan(T, d, H)
+                assert 1 <= p.splits <= 64 and p.splits == -(-d // p.k_chunk), (T, d, H)
+                assert p.k_step == 0 or p.k_chunk % p.k_step == 0
+                if p.form == ga.GA_DOWN_TILED and p.splits > 1:
+                    assert p.grid // p.splits <= 16384, (T, d, H)        # output tiles with a counter
     assert ga.gelu_and_mul_sparse_down_workspace_bytes(1, 512, 16) == 0        # the decode form
-    assert ga.gelu_and_mul_sparse_down_workspace_bytes(3, 520, 16) == 3 * 520 * 2 // 256 * 256 + 256  # staged
-    # the k-loop layout: call counter, cutoffs, tile counters, partial tiles
-    T, d, H = 5, 16384, 2048
-    p = _down_plan(T, d, H)
-    groups = -(-T // p.rows_per_block) * (H // p.features_per_block)
-    assert ga.gelu_and_mul_sparse_down_workspace_bytes(T, d, H) == \
-        256 + 256 + -(-groups * 4 // 256) * 256 + groups * p.splits * p.rows_per_block * p.features_per_block * 8
+    assert ga.gelu_and_mul_sparse_down_workspace_bytes(2, 520, 16) == ACT_OFFSET + 2 * 520 * 2 // 256 * 256 + 256
+    # the tiled layout: counters, activation, partial tiles of every slice
+    for T, d, H in ((5, 16384, 2048), (200, 3072, 64), (16, 512, 16)):
+        p = _down_plan(T, d, H)
+        tiles = -(-T // p.rows_per_block) * -(-H // p.features_per_block)
+        part = tiles * p.splits * p.rows_per_block * p.features_per_block * 4 if p.splits > 1 else 0
+        assert ga.gelu_and_mul_sparse_down_workspace_bytes(T, d, H) == \
+            ACT_OFFSET + -(-T * d * 2 // 256) * 256 + part, (T, d, H)
     assert L.ga_plan_gelu_and_mul_sparse_down(300, 1024, 64, BF16, ctypes.byref(ga.DownPlan())) == EUNSUP
     assert L.ga_plan_gelu_and_mul_sparse_down(4, 1024, 64, F32, ctypes.byref(ga.DownPlan())) == EUNSUP
     assert L.ga_plan_gelu_and_mul_sparse_down(4, 1024, 64, BF16, None) == EINVAL
@@ -670,14 +683,27 @@ def test_down_with_plan_rejects_bad_geometry():
     assert run(rows_per_block=8) == EINVAL
     assert run(features_per_block=48) == EINVAL
     assert run(k_step=384) == EINVAL
-    assert run(k_chunk=768) == EINVAL                 # not a multiple of the step
+    assert run(depth=0) == EINVAL
+    assert run(depth=4) == EINVAL
+    assert run(k_chunk=1000) == EINVAL                # not a multiple of the step
     assert run(k_chunk=0) == EINVAL
     assert run(splits=3) == EINVAL                    # not ceil(d / k_chunk)
     assert run(grid=7) == EINVAL
-    p = ga.DownPlan.of(16, 65536, 512, 16, 64, 8, 512, 512)       # 128 slices
+    assert run(form=0) == EINVAL                      # no such form
+    p = ga.DownPlan.tiled(16, 65536, 512, 16, 64, 4, 128, 512, 1)       # 128 slices
     assert L.ga_gelu_and_mul_sparse_down_with_plan(IN, W_, Y_, 16, 65536, 512, BF16, Z, None, ctypes.byref(p),
                                                    WS, WS_BYTES, None) == EUNSUP
+    # the planner's widest launch keeps every output tile within the counters
+    p = _down_plan(256, 1024, 65536)
+    assert p.grid // p.splits <= 16384
     assert L.ga_gelu_and_mul_sparse_down_with_plan(IN, W_, Y_, T, d, H, BF16, Z, None, None, WS, WS_BYTES,
+                                                   None) == EINVAL
+    # the workspace: the tiled form's need, 256-byte aligned, not over gu, w or y
+    need = ga.gelu_and_mul_sparse_down_workspace_bytes(T, d, H)
+    p = _down_plan(T, d, H)
+    assert L.ga_gelu_and_mul_sparse_down_with_plan(IN, W_, Y_, T, d, H, BF16, Z, None, ctypes.byref(p), WS, need - 1,
+                                                   None) == EINVAL
+    assert L.ga_gelu_and_mul_sparse_down_with_plan(IN, W_, Y_, T, d, H, BF16, Z, None, ctypes.byref(p), None, 0,
                                                    None) == EINVAL
     # decode plans
     def run_dec(T=2, d=4096, H=512, **kw):
