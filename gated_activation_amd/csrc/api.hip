@@ -621,8 +621,8 @@ struct TiledChoice {
 constexpr TiledChoice kTiledChoice[] = {
     {16, 16, 1, 4, 128, 1, 512},
     {32, 32, 1, 4, 128, 1, 512},
-    {128, 64, 1, 8, 128, 1, 256},
-    {GA_DOWN_MAX_ROWS, 128, 1, 8, 64, 1, 256},
+    {128, 64, 1, 8, 64, 3, 256},
+    {GA_DOWN_MAX_ROWS, 128, 1, 8, 64, 2, 256},
 };
 // Token counts from which the tiled form is chosen (below: decode, staged).
 constexpr int64_t kTiledFromT = 3;

@@ -107,7 +107,7 @@ __global__ __launch_bounds__(WAVES * 64) void down_tiled_kernel(const uint16_t *
     static_assert(TM % 16 == 0 && KSTEP % 32 == 0 && PD >= 1, "whole operand tiles");
     static_assert(NB * AVEC * 16 <= 65536, "at most 64 KB of LDS per workgroup");
     __shared__ uint4 lds[NB * AVEC];        // activation tiles: [step % NB][(tile * KK + kk) * 64 + lane]
-    __shared__ int s_last;
+    int &s_last = *reinterpret_cast<int *>(lds);  // after the loop: whether this workgroup sums the tile
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wavefront: scalar branches
@@ -172,18 +172,21 @@ __global__ __launch_bounds__(WAVES * 64) void down_tiled_kernel(const uint16_t *
     for (int f = 0; f < FW; ++f)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[f][nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // Every token tile, live or not (tiles past the live rows multiply zeros
+    // and are never stored): a test per tile would put a branch between the
+    // LDS reads and the MFMAs and serialise them.
     auto product = [&](const uint4 (&Wr)[FW][KK], const uint4 *buf) {
         if (!w_live) return;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
+        for (int kk = 0; kk < KK; ++kk) {
+            uint4 bv[NT];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                if (nt * 16 < nrows) {
-                    const uint4 bv = buf[(nt * KK + kk) * 64 + lane];
+            for (int nt = 0; nt < NT; ++nt) bv[nt] = buf[(nt * KK + kk) * 64 + lane];
 #pragma unroll
-                    for (int f = 0; f < FW; ++f) acc[f][nt] = mfma16<DT>(Wr[f][kk], bv, acc[f][nt]);
-                }
-            }
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int f = 0; f < FW; ++f) acc[f][nt] = mfma16<DT>(Wr[f][kk], bv[nt], acc[f][nt]);
+        }
     };
 
     // Loads PD steps ahead: at step j those of step j + PD are issued (the
@@ -263,25 +266,45 @@ __global__ __launch_bounds__(WAVES * 64) void down_tiled_kernel(const uint16_t *
     }
     __syncthreads();
     if (!s_last) return;
-    // The tile's last arrival: the nK partials in slice order, RB slices'
-    // loads in flight at a time.
+    // The tile's last arrival: the nK partials in slice order.  Each thread
+    // sums U of the tile's 4-feature outputs at a time with the loads of QB
+    // slices of all U in flight together (16 or 32 loads), so a thread's
+    // outputs take a few memory round trips, not one each.
     constexpr int C4 = BH / 4;
-    constexpr int RB = 16;
-    for (int p = tid; p < nrows * C4; p += NTH) {
-        const int i = p / C4, c = p % C4;
-        if (c * 4 >= hrows) continue;
-        f32x4_t s4 = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int q0 = 0; q0 < nK; q0 += RB) {
-            f32x4_t v[RB];
+    constexpr int PER = (TM * C4 + NTH - 1) / NTH;  // outputs per thread in a full tile
+    constexpr int U = PER < 1 ? 1 : PER > 4 ? 4 : PER;
+    constexpr int QB = U == 1 ? 16 : 32 / U;
+    const int n4 = nrows * C4;
+    for (int p0 = tid; p0 < n4; p0 += NTH * U) {
+        f32x4_t s4[U];
 #pragma unroll
-            for (int q = 0; q < RB; ++q)
-                v[q] = coherent_load4(psrc, q0 + q < nK ? (((q0 + q) * TM + i) * BH + c * 4) * 4 : kOob);
+        for (int u = 0; u < U; ++u) s4[u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int q0 = 0; q0 < nK; q0 += QB) {
+            f32x4_t v[U][QB];
 #pragma unroll
-            for (int q = 0; q < RB; ++q)
-                if (q0 + q < nK) s4 += v[q];
+            for (int u = 0; u < U; ++u) {
+                const int p = p0 + u * NTH;
+                const int i = p / C4, c = p % C4;
+                const bool ok = p < n4 && c * 4 < hrows;
+#pragma unroll
+                for (int q = 0; q < QB; ++q)
+                    v[u][q] = coherent_load4(psrc, ok && q0 + q < nK ? (((q0 + q) * TM + i) * BH + c * 4) * 4 : kOob);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int q = 0; q < QB; ++q)
+                    if (q0 + q < nK) s4[u] += v[u][q];
         }
-        const uint32_t lo = E::pack2(s4[0], s4[1]), hi = E::pack2(s4[2], s4[3]);
-        *reinterpret_cast<uint2 *>(y + (int64_t)(r0 + i) * H + h_first + c * 4) = uint2{lo, hi};
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int p = p0 + u * NTH;
+            const int i = p / C4, c = p % C4;
+            if (p < n4 && c * 4 < hrows) {
+                const uint32_t lo = E::pack2(s4[u][0], s4[u][1]), hi = E::pack2(s4[u][2], s4[u][3]);
+                *reinterpret_cast<uint2 *>(y + (int64_t)(r0 + i) * H + h_first + c * 4) = uint2{lo, hi};
+            }
+        }
     }
     if (tid == 0) __hip_atomic_store(cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -310,7 +333,7 @@ const TiledEntry kTiled[] = {
     GA_TILED(16, 1, 4, 128, 1), GA_TILED(16, 1, 4, 256, 1), GA_TILED(16, 1, 4, 64, 3), GA_TILED(16, 1, 8, 128, 2),
     GA_TILED(32, 1, 4, 128, 1), GA_TILED(32, 1, 4, 64, 3),
     GA_TILED(64, 1, 8, 128, 1), GA_TILED(64, 1, 8, 64, 3), GA_TILED(64, 2, 4, 64, 2),
-    GA_TILED(128, 1, 8, 64, 1), GA_TILED(128, 1, 8, 64, 2), GA_TILED(128, 2, 8, 64, 2),
+    GA_TILED(128, 1, 8, 64, 1), GA_TILED(128, 1, 8, 64, 2), GA_TILED(128, 2, 8, 64, 2), GA_TILED(128, 1, 8, 128, 1),
 };
 
 #undef GA_TILED

@@ -640,8 +640,8 @@ def test_down_planner_and_workspace():
     # or 256 workgroups by the number of slices of d
     for T, want in ((3, (16, 64, 4, 128, 1, 1024)), (5, (16, 64, 4, 128, 1, 1024)), (16, (16, 64, 4, 128, 1, 1024)),
                     (17, (32, 64, 4, 128, 1, 1024)), (32, (32, 64, 4, 128, 1, 1024)),
-                    (64, (64, 128, 8, 128, 1, 1024)), (128, (64, 128, 8, 128, 1, 2048)),
-                    (129, (128, 128, 8, 64, 1, 2048)), (256, (128, 128, 8, 64, 1, 2048))):
+                    (64, (64, 128, 8, 64, 3, 1024)), (128, (64, 128, 8, 64, 3, 2048)),
+                    (129, (128, 128, 8, 64, 2, 2048)), (256, (128, 128, 8, 64, 2, 2048))):
         p = _down_plan(T, 16384, 2048)
         assert (p.rows_per_block, p.features_per_block, p.waves, p.k_step, p.depth, p.k_chunk) == want, T
         assert p.form == ga.GA_DOWN_TILED
