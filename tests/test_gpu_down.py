@@ -301,3 +301,29 @@ def test_graph_replay_with_changing_live_count(T, oracle_lib):
         with torch.cuda.stream(s):
             ga.gelu_and_mul_sparse_down(xd[:3], wd)
         torch.cuda.synchronize()
+
+
+def test_tiled_repeats_are_bit_identical():
+    """The split-sum exchange under repetition: 40 calls of each of two tiled
+    shapes, interleaved with calls of other shapes and forms on the same
+    workspace (so the partial tiles and counters are rewritten in between),
+    must reproduce the first call's bits every time (a partial read before
+    its store had landed would change the sum)."""
+    shapes = [(16, 16384, 2048), (256, 4096, 2048)]
+    others = [(64, 8192, 512), (2, 4096, 256), (200, 3072, 64)]
+    xs = {}
+    for T, d, H in shapes + others:
+        x, w = _inputs(T, d, H, BF16, seed=T + H)
+        xs[(T, d, H)] = (to_device(x, BF16), to_device(w, BF16))
+    first = {}
+    for i in range(40):
+        for k in shapes:
+            xd, wd = xs[k]
+            y = bits_of(ga.gelu_and_mul_sparse_down(xd, wd), BF16)
+            if k in first:
+                assert np.array_equal(y, first[k]), (k, i, int((y != first[k]).sum()))
+            else:
+                first[k] = y
+            xo, wo = xs[others[i % len(others)]]
+            ga.gelu_and_mul_sparse_down(xo, wo)
+    torch.cuda.synchronize()
