@@ -268,12 +268,12 @@ __global__ __launch_bounds__(WAVES * 64) void down_tiled_kernel(const uint16_t *
     if (!s_last) return;
     // The tile's last arrival: the nK partials in slice order.  Each thread
     // sums U of the tile's 4-feature outputs at a time with the loads of QB
-    // slices of all U in flight together (16 or 32 loads), so a thread's
-    // outputs take a few memory round trips, not one each.
+    // slices of all U in flight together (16 loads), so a thread's outputs
+    // take a few memory round trips, not one each.
     constexpr int C4 = BH / 4;
     constexpr int PER = (TM * C4 + NTH - 1) / NTH;  // outputs per thread in a full tile
     constexpr int U = PER < 1 ? 1 : PER > 4 ? 4 : PER;
-    constexpr int QB = U == 1 ? 16 : 32 / U;
+    constexpr int QB = 16 / U;
     const int n4 = nrows * C4;
     for (int p0 = tid; p0 < n4; p0 += NTH * U) {
         f32x4_t s4[U];
