@@ -608,24 +608,56 @@ ga_status device_scratch(ga_stream stream, void **ptr) {
 // ---------------------------------------------------------------------------
 // gelu_and_mul_sparse fused with the down projection
 // ---------------------------------------------------------------------------
-// The tiled form's geometry by token count (tokens, 16-feature groups per
-// wavefront, wavefronts, elements of d per step, steps of loads in flight)
-// and the workgroups the launch is sized for: the fastest of a measured
-// sweep over the instantiated geometries and slice counts (d = 16384,
-// H = 2048, bf16, 3 to 256 tokens).
-struct TiledChoice {
-    int max_T;
-    int tm, fw, waves, kstep, depth;
-    int64_t groups;
+// The tiled form's plan from a measured table (planner_table_down.inc,
+// written by tests/planner_rule.py --down from profiles/
+// planner_sweep_down_bf16.csv): every instantiated geometry and slice count
+// timed at (d, H) = (4096, 1024), (8192, 2048), (8192, 8192), (12288, 3072),
+// (16384, 2048), (16384, 8192), (32768, 2048) and 13 token counts from 3 to
+// 256.  A call takes the measured token count nearest to T in log2, then the
+// nearest measured (d, H) in log2 distance, and that point's geometry with as
+// many slices of d as bring its launch to that point's workgroup count.
+#include "planner_table_down.inc"
+
+struct TiledPick {
+    bool staged;  // the staged form measured faster there (three or four tokens)
+    int tm, bh, waves, kstep, depth;
+    int64_t kc;
 };
-constexpr TiledChoice kTiledChoice[] = {
-    {16, 16, 1, 4, 128, 1, 512},
-    {32, 32, 1, 4, 128, 1, 512},
-    {128, 64, 1, 8, 64, 3, 256},
-    {GA_DOWN_MAX_ROWS, 128, 1, 8, 64, 2, 256},
-};
-// Token counts from which the tiled form is chosen (below: decode, staged).
-constexpr int64_t kTiledFromT = 3;
+
+TiledPick pick_down_tiled(int64_t T, int64_t d, int64_t H) {
+    int lo = -1, hi = -1;  // the measured token counts around T
+    for (int i = 0; i < kDownTableN; ++i) {
+        const int t = kDownTable[i].T;
+        if (t <= T && (lo < 0 || t > lo)) lo = t;
+        if (t >= T && (hi < 0 || t < hi)) hi = t;
+    }
+    const int64_t Tn = lo < 0 ? hi : hi < 0 ? lo : (T * T < (int64_t)lo * hi ? lo : hi);
+    const DownTableEntry *best = nullptr;
+    double best_dist = 0.0;
+    for (int i = 0; i < kDownTableN; ++i) {
+        const DownTableEntry &e = kDownTable[i];
+        if (e.T != Tn) continue;
+        const double a = std::log2((double)d / e.d), b = std::log2((double)H / e.H);
+        const double dist = a * a + b * b;
+        if (best == nullptr || dist < best_dist) {
+            best = &e;
+            best_dist = dist;
+        }
+    }
+    TiledPick p{};
+    p.staged = best->staged != 0 && T <= 4;
+    p.tm = best->tm;
+    p.bh = best->bh;
+    p.waves = best->waves;
+    p.kstep = best->kstep;
+    p.depth = best->depth;
+    const int64_t tiles = std::max<int64_t>((T + p.tm - 1) / p.tm * ((H + p.bh - 1) / p.bh), 1);
+    int64_t slices = (best->grid + tiles / 2) / tiles;
+    slices = std::min<int64_t>({std::max<int64_t>(slices, 1), ga::DOWN_MAX_SPLITS, (d + p.kstep - 1) / p.kstep});
+    const int64_t kc = (d + slices - 1) / slices;
+    p.kc = (kc + p.kstep - 1) / p.kstep * p.kstep;
+    return p;
+}
 
 // The tiled form: workgroups of tm tokens x bh features x kc elements of d.
 void fill_down_tiled_plan(int tm, int bh, int waves, int kstep, int depth, int64_t kc, int64_t T, int64_t d,
@@ -640,19 +672,6 @@ void fill_down_tiled_plan(int tm, int bh, int waves, int kstep, int depth, int64
     p->form = GA_DOWN_TILED;
     p->depth = depth;
     p->grid = (T + tm - 1) / tm * ((H + bh - 1) / bh) * p->splits;
-}
-
-// The slice of d for a tiled geometry: whole steps, as many slices as bring
-// the launch to about `groups` workgroups, at most DOWN_MAX_SPLITS.
-int64_t tiled_chunk(const TiledChoice &c, int64_t T, int64_t d, int64_t H) {
-    const int64_t bh = (int64_t)c.fw * 16 * c.waves;
-    int64_t tiles = (T + c.tm - 1) / c.tm * ((H + bh - 1) / bh);
-    if (tiles < 1) tiles = 1;  // T == 0: nothing is launched
-    int64_t slices = (c.groups + tiles - 1) / tiles;
-    if (slices < 1) slices = 1;
-    if (slices > ga::DOWN_MAX_SPLITS) slices = ga::DOWN_MAX_SPLITS;
-    const int64_t kc = (d + slices - 1) / slices;
-    return (kc + c.kstep - 1) / c.kstep * c.kstep;
 }
 
 ga_status check_down_sizes(const char *op, int64_t T, int64_t d, int64_t H, int32_t dtype) {
@@ -700,9 +719,9 @@ bool down_whole_available(int form, int32_t dtype, int tmax, int f, int waves, i
                                   : ga::gelu_down_staged_available(dtype, tmax, f, waves, d);
 }
 
-// The planner's choice for one or two tokens, by the longest row it serves
-// (measured on MI355X at H = 2048): the first entry whose token capacity is
-// the call's and whose reach covers d.
+// The decode and staged kernels the planner takes, by the longest row each
+// serves (measured on MI355X at H = 2048): the first entry whose token
+// capacity is the call's (rounded up to 1, 2 or 4) and whose reach covers d.
 struct WholeChoice {
     int form, tmax;
     int64_t max_d;
@@ -712,6 +731,7 @@ const WholeChoice kWholeChoice[] = {
     {GA_DOWN_DECODE, 1, 16384, 4, 8},
     {GA_DOWN_DECODE, 1, 32768, 4, 16},
     {GA_DOWN_STAGED, 2, 16384, 4, 16},
+    {GA_DOWN_STAGED, 4, 16384, 4, 16},
 };
 
 ga_status check_down_plan(const char *op, const ga_down_plan *p, int64_t T, int64_t d, int64_t H, int32_t dtype) {
@@ -1030,19 +1050,20 @@ ga_status ga_plan_gelu_and_mul_sparse_down(int64_t T, int64_t d, int64_t H, int3
     ga_status st = check_down_sizes(name, T, d, H, dtype);
     if (st != GA_OK) return st;
     // One token: the decode form (one launch, no workspace); two: the staged
-    // form; where their rows fit.
-    if (T < kTiledFromT) {
-        const int tmax = T <= 1 ? 1 : 2;
-        for (const WholeChoice &c : kWholeChoice)
-            if (c.tmax == tmax && d <= c.max_d && down_whole_available(c.form, dtype, tmax, c.f, c.waves, d)) {
-                fill_down_whole_plan(c.form, tmax, c.f, c.waves, d, H, plan);
-                return GA_OK;
-            }
+    // form; where their rows fit.  Three or more: the measured table's
+    // tiled plan, or the staged form where the table found it faster (three
+    // or four tokens) and its row fits.
+    const TiledPick t = pick_down_tiled(T < 1 ? 1 : T, d, H);
+    if (T <= 4) {
+        const int tmax = T <= 1 ? 1 : T <= 2 ? 2 : 4;
+        if (T <= 2 || t.staged)
+            for (const WholeChoice &c : kWholeChoice)
+                if (c.tmax == tmax && d <= c.max_d && down_whole_available(c.form, dtype, tmax, c.f, c.waves, d)) {
+                    fill_down_whole_plan(c.form, tmax, c.f, c.waves, d, H, plan);
+                    return GA_OK;
+                }
     }
-    const TiledChoice *c = &kTiledChoice[0];
-    while (T > c->max_T) ++c;
-    fill_down_tiled_plan(c->tm, c->fw * 16 * c->waves, c->waves, c->kstep, c->depth, tiled_chunk(*c, T, d, H), T, d,
-                         H, plan);
+    fill_down_tiled_plan(t.tm, t.bh, t.waves, t.kstep, t.depth, t.kc, T, d, H, plan);
     return GA_OK;
 }
 

@@ -331,9 +331,12 @@ struct TiledEntry {
 // d = 16384, H = 2048) and their neighbours in the sweep.
 const TiledEntry kTiled[] = {
     GA_TILED(16, 1, 4, 128, 1), GA_TILED(16, 1, 4, 256, 1), GA_TILED(16, 1, 4, 64, 3), GA_TILED(16, 1, 8, 128, 2),
-    GA_TILED(32, 1, 4, 128, 1), GA_TILED(32, 1, 4, 64, 3),
-    GA_TILED(64, 1, 8, 128, 1), GA_TILED(64, 1, 8, 64, 3), GA_TILED(64, 2, 4, 64, 2),
+    GA_TILED(16, 1, 4, 256, 2), GA_TILED(16, 1, 4, 128, 3), GA_TILED(16, 1, 2, 256, 2),
+    GA_TILED(32, 1, 4, 128, 1), GA_TILED(32, 1, 4, 64, 3), GA_TILED(32, 1, 4, 128, 2), GA_TILED(32, 1, 4, 128, 3),
+    GA_TILED(64, 1, 8, 128, 1), GA_TILED(64, 1, 8, 64, 3), GA_TILED(64, 2, 4, 64, 2), GA_TILED(64, 1, 8, 128, 2),
+    GA_TILED(64, 1, 4, 128, 2), GA_TILED(64, 1, 4, 128, 3), GA_TILED(64, 2, 4, 128, 3),
     GA_TILED(128, 1, 8, 64, 1), GA_TILED(128, 1, 8, 64, 2), GA_TILED(128, 2, 8, 64, 2), GA_TILED(128, 1, 8, 128, 1),
+    GA_TILED(128, 1, 8, 64, 3), GA_TILED(128, 2, 8, 64, 3), GA_TILED(128, 2, 4, 64, 3),
 };
 
 #undef GA_TILED

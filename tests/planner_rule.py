@@ -22,6 +22,20 @@ regenerates a table.
 the packed-rows path: for every shape, the library's own choice (from
 ga_plan_gelu_and_mul_sparse, host-only) against the fastest measured plan.
 
+--down writes the fused down projection's table (csrc/planner_table_down.inc)
+from a sweep of ga_gelu_and_mul_sparse_down_with_plan over (d, H, T): lines
+"d,H,T,kind,form,tokens,features,waves,k_step,depth,splits,us" with kind
+tiled, staged or unfused (the activation then a hipBLASLt GEMM, for
+reference).  For every (d, H, T) point it keeps the fastest tiled plan as its
+geometry and its workgroup count, and whether the staged form was faster
+still.  choose_down() is the lookup the planner applies
+(csrc/api.hip, pick_down_tiled): the measured token count nearest to T in
+log2 (T^2 against the product of the two neighbours, in integers), then, among
+that token count's points, the (d, H) nearest in log2 distance (the first in
+table order on a tie); the geometry is that point's and the slices of d are
+as many as bring the launch to its workgroup count, rounded, 1 to 64 and at
+most ceil(d / k_step).
+
 The prefix names the table's symbols: kPlan (default) for the vector path,
 kUna for the unaligned path (its kernel also takes 3, 5, 6 or 7 vectors per
 lane, but the table, and so the planner, keeps to 1, 2, 4, 8).
@@ -381,8 +395,105 @@ def summarize(out, paths):
     return len(lines)
 
 
+DOWN_MAX_SPLITS = 64
+
+
+def read_down_sweep(paths):
+    """{(d, H, T): {key: us}}, key ("staged",), ("unfused",) or
+    (tokens, features, waves, k_step, depth, splits) of a tiled plan."""
+    times = collections.defaultdict(dict)
+    for path in paths:
+        for line in open(path):
+            if not line.strip() or line.startswith("#"):
+                continue
+            f = line.strip().split(",")
+            d, H, T = int(f[0]), int(f[1]), int(f[2])
+            us = float(f[11])
+            if f[3] == "tiled":
+                key = tuple(int(v) for v in f[5:11])
+            elif f[3] in ("staged", "unfused"):
+                key = (f[3],)
+            else:
+                continue
+            times[(d, H, T)][key] = min(us, times[(d, H, T)].get(key, float("inf")))
+    return times
+
+
+def build_down(times):
+    """Entries (d, H, T, staged, tokens, features, waves, k_step, depth,
+    grid) sorted by (T, d, H): each point's fastest tiled plan, its
+    workgroup count, and whether the staged form beat it."""
+    entries = []
+    for (d, H, T), g in times.items():
+        tiled = {k: v for k, v in g.items() if len(k) == 6}
+        (tm, bh, w, ks, pd, sp), us = min(tiled.items(), key=lambda kv: (kv[1], kv[0]))
+        staged = int(g.get(("staged",), float("inf")) < us)
+        grid = -(-T // tm) * -(-H // bh) * sp
+        entries.append((d, H, T, staged, tm, bh, w, ks, pd, grid))
+    return sorted(entries, key=lambda e: (e[2], e[0], e[1]))
+
+
+def write_down_inc(path, entries, sources):
+    out = ["// Generated by tests/planner_rule.py --down from a sweep of the fused down projection",
+           "// (gelu_and_mul_sparse then y = a . w^T, bf16, one MI355X): " + ", ".join(sources) + ".",
+           "// For each measured (d, H, T): the fastest tiled plan's geometry (tokens, features,",
+           "// waves, k step, steps of loads in flight) and workgroups, and whether the staged form",
+           "// was faster still.  Sorted by T, then d, then H.",
+           "struct DownTableEntry {",
+           "    int d, H, T, staged, tm, bh, waves, kstep, depth, grid;",
+           "};",
+           f"constexpr int kDownTableN = {len(entries)};",
+           "constexpr DownTableEntry kDownTable[kDownTableN] = {"]
+    for e in entries:
+        out.append("    {" + ", ".join(map(str, e)) + "},")
+    out.append("};")
+    open(path, "w").write("\n".join(out) + "\n")
+
+
+def read_down_inc(path):
+    text = open(path).read()
+    rows = re.findall(r"^\s*\{([0-9, ]+)\},\s*$", text, flags=re.M)
+    return [tuple(int(x) for x in r.split(",")) for r in rows]
+
+
+def choose_down(entries, T, d, H):
+    """The table lookup for T >= 1 tokens: ("staged",) or the tiled plan
+    (tokens, features, waves, k_step, depth, k_chunk)."""
+    Ts = sorted({e[2] for e in entries})
+    if T <= Ts[0]:
+        Tn = Ts[0]
+    elif T >= Ts[-1]:
+        Tn = Ts[-1]
+    else:
+        hi = next(t for t in Ts if t >= T)
+        lo = max(t for t in Ts if t <= T)
+        Tn = lo if T * T < lo * hi else hi
+    best = None
+    for e in entries:
+        if e[2] != Tn:
+            continue
+        dist = (math.log2(d / e[0])) ** 2 + (math.log2(H / e[1])) ** 2
+        if best is None or dist < best[0]:
+            best = (dist, e)
+    _, (_, _, _, staged, tm, bh, w, ks, pd, grid) = best
+    if staged and T <= 4:
+        return ("staged",)
+    tiles = -(-T // tm) * -(-H // bh)
+    slices = (grid + tiles // 2) // tiles
+    slices = min(max(slices, 1), DOWN_MAX_SPLITS, -(-d // ks))
+    kc = -(-(-(-d // slices)) // ks) * ks
+    return (tm, bh, w, ks, pd, kc)
+
+
 def main(argv):
     argv = list(argv)
+    if "--down" in argv:
+        argv.remove("--down")
+        out, sources = argv[1], argv[2:]
+        entries = build_down(read_down_sweep(sources))
+        write_down_inc(out, entries, [p.split("/")[-1] for p in sources])
+        print(f"{out}: {len(entries)} points")
+        return 0
     if "--summarize" in argv:
         argv.remove("--summarize")
         print(f"{argv[1]}: {summarize(argv[1], argv[2:])} lines")

@@ -636,17 +636,31 @@ def test_down_planner_and_workspace():
     for T, d in ((1, 32776), (2, 16392)):        # rows past the decode and staged forms' reach
         p = _down_plan(T, d, 2048)
         assert p.form == ga.GA_DOWN_TILED and p.k_step > 0, (T, d)
-    # three tokens on: the tiled form, sized to about 512 (up to 32 tokens)
-    # or 256 workgroups by the number of slices of d
-    for T, want in ((3, (16, 64, 4, 128, 1, 1024)), (5, (16, 64, 4, 128, 1, 1024)), (16, (16, 64, 4, 128, 1, 1024)),
-                    (17, (32, 64, 4, 128, 1, 1024)), (32, (32, 64, 4, 128, 1, 1024)),
-                    (64, (64, 128, 8, 64, 3, 1024)), (128, (64, 128, 8, 64, 3, 2048)),
-                    (129, (128, 128, 8, 64, 2, 2048)), (256, (128, 128, 8, 64, 2, 2048))):
-        p = _down_plan(T, 16384, 2048)
-        assert (p.rows_per_block, p.features_per_block, p.waves, p.k_step, p.depth, p.k_chunk) == want, T
-        assert p.form == ga.GA_DOWN_TILED
-        assert p.splits == 16384 // p.k_chunk
-        assert p.grid == -(-T // p.rows_per_block) * (2048 // p.features_per_block) * p.splits
+    # three tokens on: the measured table's plan (tests/planner_rule.py
+    # states the lookup independently), or the staged form at three or four
+    # tokens where the table found it faster and its row fits
+    import planner_rule
+    table = planner_rule.read_down_inc(os.path.join(os.path.dirname(ga.library_path), "csrc",
+                                                    "planner_table_down.inc"))
+    assert len(table) >= 91
+    checked = staged = 0
+    for T in (3, 4, 5, 9, 16, 17, 20, 31, 32, 33, 40, 64, 100, 128, 129, 150, 180, 200, 256):
+        for d in (8, 1000, 4096, 6144, 8192, 8200, 12288, 16384, 24576, 32768, 65536):
+            for H in (16, 1024, 2048, 3072, 4096, 8192, 65536):
+                p = _down_plan(T, d, H)
+                want = planner_rule.choose_down(table, T, d, H)
+                if want == ("staged",) and d <= 16384:
+                    assert (p.form, p.rows_per_block) == (ga.GA_DOWN_STAGED, 4), (T, d, H)
+                    staged += 1
+                    continue
+                if want == ("staged",):                  # past the staged kernel's reach: the tiled plan
+                    want = planner_rule.choose_down([e[:3] + (0,) + e[4:] for e in table], T, d, H)
+                assert p.form == ga.GA_DOWN_TILED, (T, d, H)
+                got = (p.rows_per_block, p.features_per_block, p.waves, p.k_step, p.depth, p.k_chunk)
+                assert got == want, (T, d, H, got, want)
+                assert p.grid == -(-T // p.rows_per_block) * -(-H // p.features_per_block) * p.splits
+                checked += 1
+    assert checked > 1000 and staged > 10
     # whole steps, at most 64 slices of d, for every d the kernels take
     for d in (8, 1024, 1032, 32768, 32776, 65536):
         for T in (1, 3, 20, 50, 200):
@@ -679,7 +693,7 @@ def test_down_with_plan_rejects_bad_geometry():
             setattr(p, k, v)
         return L.ga_gelu_and_mul_sparse_down_with_plan(IN, W_, Y_, T, d, H, BF16, Z, None, ctypes.byref(p),
                                                        WS, WS_BYTES, None)
-    assert run(waves=2) == EINVAL                     # no kernel
+    assert run(waves=3) == EINVAL                     # no kernel
     assert run(rows_per_block=8) == EINVAL
     assert run(features_per_block=48) == EINVAL
     assert run(k_step=384) == EINVAL

@@ -25,6 +25,36 @@ def test_committed_tables_regenerate_from_the_sweep_summaries(tmp_path):
         assert _body(str(out)) == _body(os.path.join(CSRC, inc)), inc
 
 
+def test_committed_down_table_regenerates_from_its_sweep(tmp_path):
+    out = tmp_path / "planner_table_down.inc"
+    assert mt.main(["planner_rule.py", "--down", str(out),
+                    os.path.join(PROFILES, "planner_sweep_down_bf16.csv")]) == 0
+    assert open(out).read() == open(os.path.join(CSRC, "planner_table_down.inc")).read()
+
+
+def test_down_lookup_on_a_synthetic_table():
+    # two measured shapes at two token counts; a query takes the nearest
+    # token count (T^2 against the neighbours' product), then the nearest
+    # (d, H) in log2, and that point's workgroups over its own tiles
+    table = [(4096, 1024, 4, 1, 16, 64, 4, 128, 3, 256), (16384, 4096, 4, 0, 16, 64, 4, 128, 1, 512),
+             (4096, 1024, 64, 0, 64, 64, 4, 128, 2, 256), (16384, 4096, 64, 0, 64, 128, 8, 64, 3, 256)]
+    assert mt.choose_down(table, 3, 4096, 1024) == ("staged",)
+    assert mt.choose_down(table, 4, 8000, 2000) == ("staged",)          # nearer (4096, 1024)
+    assert mt.choose_down(table, 4, 9000, 2100)[0] == 16                  # nearer (16384, 4096): tiled
+    assert mt.choose_down(table, 16, 4096, 1024)[0] == 64                 # 16^2 = 4 * 64: the tie goes up
+    assert mt.choose_down(table, 17, 4096, 1024)[0] == 64                 # 17^2 > 4 * 64: nearest is 64
+    # (16384, 4096) at T = 64: 1 x 32 tiles, 256 workgroups -> 8 slices of 2048
+    assert mt.choose_down(table, 64, 16384, 4096) == (64, 128, 8, 64, 3, 2048)
+    # a wider H at the same point: 1 x 64 tiles -> 4 slices of 4096
+    assert mt.choose_down(table, 64, 16384, 8192) == (64, 128, 8, 64, 3, 4096)
+    # (16384, 2048) is nearer (16384, 4096): 1 x 16 tiles -> 16 slices of 1024
+    assert mt.choose_down(table, 64, 16384, 2048) == (64, 128, 8, 64, 3, 1024)
+    # slices capped at 64, and at ceil(d / k_step): (16384, 256) and (128, 128)
+    # are nearer (4096, 1024), 256 workgroups over 1 x 4 and 1 x 2 tiles
+    assert mt.choose_down(table, 64, 16384, 256) == (64, 64, 4, 128, 2, 256)
+    assert mt.choose_down(table, 64, 128, 128) == (64, 64, 4, 128, 2, 128)
+
+
 def test_table_builder_round_trip(tmp_path):
     # A synthetic sweep on a 2 x 2 grid: at every point one geometry is
     # fastest; a second one is 10 % slower everywhere.
