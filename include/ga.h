@@ -115,7 +115,9 @@ typedef struct {
  * row mean, the row std, z, z * std, the cutoff mean + z * std, gate -
  * cutoff, the GELU output, and the product.  Statistics are still computed
  * in fp32 from the input values.  For fp32 data the form differs from the
- * default only by the fp32 roundings of those intermediates.
+ * default only by the fp32 roundings of those intermediates.  The match with
+ * the eager composition covers finite inputs: a NaN in a gate row makes that
+ * composition's whole row NaN, while both forms here take max(NaN, 0) as 0.
  */
 #define GA_ROUND_INTERMEDIATES 1
 
