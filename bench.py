@@ -80,6 +80,9 @@ def parse():
                         "counter runs)")
     p.add_argument("--down-ts", default="", metavar="T1,T2,...",
                    help="token counts of the fused down-projection measurements (default 1,4,16,64,256)")
+    p.add_argument("--down-shapes", default="", metavar="DxH,...",
+                   help="with --down-only or --down-geometries: the (d, H) shapes to measure, one result per "
+                        "shape (default: d = 16384, H = 2048 only)")
     return p.parse_args()
 
 
@@ -259,9 +262,12 @@ def main():
         dev = torch.device("cuda", 0)
         torch.cuda.set_device(dev)
         ts = tuple(int(t) for t in args.down_ts.split(",")) if args.down_ts else None
-        print(json.dumps({"down_projection": down_projection(
-            dev, Markers(args.markers), geometries=args.down_geometries,
-            cpu_seconds=0.0 if args.down_geometries else args.cpu_seconds, token_counts=ts)}), flush=True)
+        shapes = [tuple(int(v) for v in sh.split("x")) for sh in args.down_shapes.split(",")] \
+            if args.down_shapes else [(DOWN_D, DOWN_H)]
+        res = [down_projection(dev, Markers(args.markers), geometries=args.down_geometries,
+                               cpu_seconds=0.0 if args.down_geometries else args.cpu_seconds, token_counts=ts,
+                               shape=sh) for sh in shapes]
+        print(json.dumps({"down_projection": res[0] if not args.down_shapes else res}), flush=True)
         return
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -585,7 +591,7 @@ def time_graph_on(fn, n_sets, reps, per_graph, s, warmup=8):
     return start.elapsed_time(end) / (reps * per_graph)
 
 
-def down_projection(dev, markers, geometries=False, cpu_seconds=0.0, token_counts=None):
+def down_projection(dev, markers, geometries=False, cpu_seconds=0.0, token_counts=None, shape=(DOWN_D, DOWN_H)):
     """gelu_and_mul_sparse_down (the activation fused with the down
     projection y = a . w^T) against the unfused pair on the same stream: the
     activation stored by ga_gelu_and_mul_sparse, then torch.mm with the
@@ -594,13 +600,15 @@ def down_projection(dev, markers, geometries=False, cpu_seconds=0.0, token_count
     64 MB of weights comes from HBM, as when a model's layers take turns.
     Algorithmic bytes per fused call: w (H*d*2) + gu (T*2d*2) + y (T*H*2);
     flops 2*T*d*H.  geometries: also time every instantiated geometry at
-    each of DOWN_SWEEP_TS (the planner's measurements)."""
+    each of DOWN_SWEEP_TS (the planner's measurements).  shape: (d, H); the
+    roofline object and the CPU baseline are taken at d = 16384, H = 2048
+    only.  One progress line per token count goes to stderr."""
     import ctypes
     import numpy as np
     import torch
     import gated_activation_amd as ga
     import synth
-    d, H = DOWN_D, DOWN_H
+    d, H = shape
     w_bytes = H * d * 2
     n_sets = max(2, math.ceil(ROTATE_BYTES / w_bytes))
     w0 = torch.from_numpy(synth.down_weight(H, d, seed=1).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -700,7 +708,9 @@ def down_projection(dev, markers, geometries=False, cpu_seconds=0.0, token_count
             "TFLOPs": round(flops / (ms_f * 1e-3) / 1e12, 2),
             "max_rel_diff_vs_unfused": rel})
         assert all(st == ga.GA_OK for st in statuses), "a fused or activation call returned an error"
-        if T == DOWN_ROOFLINE_T:
+        print(f"down d={d} H={H} T={T}: fused {ms_f * 1e3:.2f} us, unfused {ms_u * 1e3:.2f} us", file=sys.stderr,
+              flush=True)
+        if T == DOWN_ROOFLINE_T and (d, H) == (DOWN_D, DOWN_H):
             if plan.form == ga.GA_DOWN_DECODE:
                 kname = "down_decode_kernel<bf16, tokens %d, features %d, waves %d>" % (
                     plan.rows_per_block, plan.features_per_block, plan.waves)
